@@ -1,0 +1,141 @@
+"""Seeded generators.  Data only: nothing here computes any step of the decoder.
+
+bf16 tensors are returned as numpy uint16 arrays holding the bf16 bit patterns;
+callers view them as torch.bfloat16 (CPU or GPU) without conversion.
+"""
+import os
+import zlib
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+from .shapes import tensor_names, tensor_shape
+
+CHUNK = 1 << 22
+WEIGHT_STD = 0.02
+BF16_ONE = 0x3F80
+
+
+def seeds(config_index):
+    """Sub-seeds of workload `config_index` (1-based): weights, prompt, draft, contexts, kv."""
+    base = 1000 * int(config_index)
+    return {"weights": base + 1, "prompt": base + 2, "draft": base + 3, "contexts": base + 4,
+            "kv": base + 5}
+
+
+def _f32_to_bf16_bits(f):
+    """Round float32 values to the nearest bf16 (ties to even); returns uint16 bit patterns."""
+    u = f.view(np.uint32)
+    u = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return (u >> np.uint32(16)).astype(np.uint16)
+
+
+def _stream(seed, name, chunk):
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(
+        [int(seed) & 0xFFFFFFFF, zlib.crc32(name.encode()), int(chunk)])))
+
+
+def _threads(threads):
+    if threads:
+        return threads
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def bf16_normal(shape, std, seed, name, threads=None, pool=None):
+    """bf16(std * z), z ~ N(0,1) float32, as uint16 bits; chunked so bytes are thread-count independent."""
+    n = 1
+    for s in shape:
+        n *= int(s)
+    out = np.empty(n, dtype=np.uint16)
+    std32 = np.float32(std)
+
+    def fill(c):
+        lo, hi = c * CHUNK, min(n, (c + 1) * CHUNK)
+        z = _stream(seed, name, c).standard_normal(hi - lo, dtype=np.float32)
+        z *= std32
+        out[lo:hi] = _f32_to_bf16_bits(z)
+
+    nchunks = (n + CHUNK - 1) // CHUNK
+    if nchunks <= 1:
+        for c in range(nchunks):
+            fill(c)
+    elif pool is not None:
+        list(pool.map(fill, range(nchunks)))
+    else:
+        with ThreadPoolExecutor(_threads(threads)) as p:
+            list(p.map(fill, range(nchunks)))
+    return out.reshape(shape)
+
+
+def model_weights(shape, seed, names=None, threads=None):
+    """All weight tensors of `shape` (or the subset `names`).
+
+    Linear, bias and embedding tensors are bf16(0.02*z); RMSNorm gains are 1.0.
+    A tensor's bytes depend only on (seed, tensor name), so the hidden-only half
+    stack is exactly the first layers of the full stack under the same seed.
+    """
+    names = tensor_names(shape) if names is None else names
+    out = {}
+    with ThreadPoolExecutor(_threads(threads)) as pool:
+        for name in names:
+            shp = tensor_shape(shape, name)
+            if name.endswith("ln1") or name.endswith("ln2") or name == "final_norm":
+                out[name] = np.full(shp, BF16_ONE, dtype=np.uint16)
+            else:
+                out[name] = bf16_normal(shp, WEIGHT_STD, seed, name, pool=pool)
+    return out
+
+
+def prompt_ids(vocab, n, seed):
+    """n token ids uniform in [0, vocab)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.integers(0, vocab, size=n, dtype=np.int64).astype(np.int32)
+
+
+def corrupt_draft(continuation, vocab, rng):
+    """Replace one token of a K-token continuation at a uniform slot p in 0..K (K = no change).
+
+    The replacement at p is (g + 1 + U{0..V-2}) mod V, so it always differs from g.
+    Returns (draft int32[K], p).
+    """
+    d = np.array(continuation, dtype=np.int64).copy()
+    K = len(d)
+    p = int(rng.integers(0, K + 1))
+    if p < K:
+        d[p] = (d[p] + 1 + int(rng.integers(0, vocab - 1))) % vocab
+    return d.astype(np.int32), p
+
+
+def rejected_suffix(rng, k):
+    """Number of rejected drafts r ~ U{0..k}."""
+    return int(rng.integers(0, k + 1))
+
+
+def synthetic_kv(shape, n_pos, seed, std=1.0, n_layers=None, threads=None):
+    """Synthetic cache contents: K and V, each uint16 bf16 bits [layers][n_kv][n_pos][head_dim]."""
+    L = shape.n_layers if n_layers is None else n_layers
+    shp = (L, shape.n_kv_heads, n_pos, shape.head_dim)
+    k = bf16_normal(shp, std, seed, "kv.k", threads=threads)
+    v = bf16_normal(shp, std, seed, "kv.v", threads=threads)
+    return k, v
+
+
+def lookup_history(vocab, n, seed, n_spans=16, span_len=32, p_sub=0.10):
+    """A token stream that repeats itself: spans drawn with replacement from a pool of
+    `n_spans` random `span_len`-token spans, each token replaced with probability
+    `p_sub` by a uniform id.  Gives a prompt-lookup drafter something to find."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    pool = rng.integers(0, vocab, size=(n_spans, span_len), dtype=np.int64)
+    out = []
+    while len(out) < n:
+        out.extend(pool[int(rng.integers(0, n_spans))].tolist())
+    out = np.array(out[:n], dtype=np.int64)
+    sub = rng.random(n) < p_sub
+    out[sub] = rng.integers(0, vocab, size=int(sub.sum()), dtype=np.int64)
+    return out.astype(np.int32)
+
+
+def batch_contexts(n_seqs, lo, hi, seed):
+    """Per-sequence context lengths uniform in lo..hi (inclusive)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.integers(lo, hi + 1, size=n_seqs, dtype=np.int64).astype(np.int32)
