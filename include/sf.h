@@ -1,0 +1,220 @@
+/*
+ * sf.h - C ABI of the speculative-decoding verify library for MI355X (gfx950).
+ *
+ * One decoder stack scores a draft of K tokens in a single pass over K+1
+ * positions, takes its own greedy choice at every position, accepts the longest
+ * agreeing prefix and rewinds its static KV cache in place.
+ *
+ * Sources (cited by page title and section):
+ *   [ShardFlow] "I Got 28 TPS Out of Free Kaggle GPUs: Here's What It Took"
+ *   [Sangama]   "Qwen3.5-397B on 20 GPUs, through a relay"
+ *
+ * Conventions for every call:
+ *   - Returns sf_status: SF_OK (0) or a negative error code.  No C++ exception
+ *     crosses this boundary.  sf_last_error() gives a message for the calling
+ *     thread's most recent failure.
+ *   - Arguments are checked on the host before any device work is enqueued; a
+ *     call that fails leaves the committed length and pending token of every
+ *     sequence unchanged.
+ *   - "host" pointers are ordinary CPU memory owned by the caller and only read
+ *     or written during the call.  "device" pointers are HIP device memory owned
+ *     by the caller.  Everything else (packed weights, KV pool, scratch,
+ *     counters, captured graphs) is owned by the library.
+ *   - The library allocates device memory only in sf_model_create and
+ *     sf_cache_alloc; every later call reuses fixed addresses, so captured graph
+ *     replays stay valid ([ShardFlow] "Why It Kept Breaking (and How I Fixed
+ *     It)": captured addresses must not change; fixes 1 and 2).
+ *   - All device work runs on the stream given to sf_model_create.
+ *   - bf16 = 16-bit brain float stored as uint16 bit patterns.
+ */
+#ifndef SF_H
+#define SF_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t sf_status;
+#define SF_OK          0
+#define SF_E_ARG      -1  /* bad argument: null pointer, size, token id, k > k_max, flags */
+#define SF_E_CAPACITY -2  /* the pass would write past the cache capacity */
+#define SF_E_STATE    -3  /* call not valid in the current state (e.g. rollback past length) */
+#define SF_E_HIP      -4  /* a HIP runtime call failed; see sf_last_error() */
+#define SF_E_NOMEM    -5  /* device or pinned host allocation failed */
+
+typedef struct sf_model sf_model;   /* opaque, library-owned */
+typedef struct sf_cache sf_cache;   /* opaque, library-owned */
+
+/* Decoder shape (Qwen2.5 decoder layer: pre-norm RMSNorm, rotate-half RoPE,
+ * grouped-query attention, SwiGLU FFN, optional q/k/v biases). */
+typedef struct sf_model_desc {
+    int32_t n_layers;
+    int32_t hidden;       /* H; multiple of 32 */
+    int32_t n_q_heads;
+    int32_t n_kv_heads;   /* divides n_q_heads */
+    int32_t head_dim;     /* 64 or 128 */
+    int32_t ffn;          /* F; multiple of 32 */
+    int32_t vocab;        /* V; multiple of 16 */
+    float rope_base;
+    float rms_eps;
+    int32_t has_head;     /* 1: final RMSNorm + LM head + argmax; 0: stack emits hidden states */
+    int32_t tied_head;    /* 1: the LM head is the embedding matrix */
+    int32_t qkv_bias;     /* 1: q/k/v projections have biases */
+} sf_model_desc;
+
+/* sf_model_create: pack the weights into library-owned device memory.
+ *   desc     host, read during the call.
+ *   weights  host array of device pointers to bf16 tensors in this order
+ *            ([out][in] row-major for linear layers):
+ *              embed[V][H];
+ *              per layer i: ln1[H], wq[nq*dh][H], bq[nq*dh] (if qkv_bias),
+ *                wk[nkv*dh][H], bk (if qkv_bias), wv[nkv*dh][H], bv (if qkv_bias),
+ *                wo[H][nq*dh], ln2[H], wg[F][H], wu[F][H], wd[H][F];
+ *              final_norm[H] (if has_head); lm_head[V][H] (if has_head and not tied_head).
+ *            The tensors are copied; the caller may free them after the call.
+ *   stream   a hipStream_t (NULL: the library creates its own non-blocking stream).
+ *   out      receives the model handle.
+ * Errors: SF_E_ARG for unsupported shapes, SF_E_NOMEM, SF_E_HIP. */
+sf_status sf_model_create(const sf_model_desc* desc, const void* const* weights, void* stream,
+                          sf_model** out);
+sf_status sf_model_free(sf_model* model);
+
+/* sf_cache_alloc: static KV pool for n_seqs sequences of `capacity` positions
+ * each, plus all scratch, device counters and the captured verify (T = k_max+1)
+ * and single-token draft (T = 1) graphs ([ShardFlow] "Why It Kept Breaking":
+ * fix 1, a pre-allocated fixed-size cache).  Every sequence starts with length 0
+ * and pending token 0.  KV layout: [layer][seq][kv_head][position][head_dim] bf16;
+ * K is stored after RoPE.
+ * Limits: n_seqs * (k_max+1) <= 64, 0 <= k_max <= 15, capacity >= k_max+1. */
+sf_status sf_cache_alloc(sf_model* model, int32_t n_seqs, int32_t capacity, int32_t k_max,
+                         sf_cache** out);
+sf_status sf_cache_free(sf_cache* cache);
+
+/* sf_prefill: score the prompt tokens[0..n) of sequence `seq` from position 0
+ * (any previous content of that sequence is discarded) and commit all of them.
+ * Afterwards length = n and the pending token is the greedy choice after the
+ * last prompt token, returned in *next_token (host, may be NULL; hidden-state
+ * stacks return 0).  Runs in chunks of up to 64 positions, not graph-captured.
+ * Errors: SF_E_ARG (token id outside [0,V), n < 1), SF_E_CAPACITY (n > capacity). */
+sf_status sf_prefill(sf_cache* cache, int32_t seq, const int32_t* tokens, int32_t n,
+                     int32_t* next_token);
+
+/* Flags of sf_verify / sf_verify_device. */
+#define SF_NO_COMMIT     1u  /* do not advance length / pending token (the pass still writes KV past length) */
+#define SF_FORCE_ACCEPT  2u  /* accept all k drafts (feed known tokens) */
+#define SF_DEBUG_LOGITS  4u  /* eager launch that also writes fp32 logits to dev_out */
+
+/* sf_verify: one verify pass for every sequence of the cache ([ShardFlow]
+ * "Speculative Decoding: The Idea": all K guesses checked in one pass;
+ * [Sangama] "Speculative decoding: correct, but slower (for now)": the model's
+ * own choice is returned at every position).
+ *   draft     host int32 [n_seqs][k_max]: d_1..d_k of each sequence (slots past k ignored).
+ *   k         host int32 [n_seqs] drafts per sequence (0..k_max), or NULL for k_max.
+ *   flags     SF_* above.
+ *   accepted  host int32 [n_seqs] (may be NULL): M, the number of leading drafts
+ *             equal to the model's greedy choice, capped at k.
+ *   target    host int32 [n_seqs][k_max+1] (may be NULL): the greedy choice at
+ *             positions L..L+k_max, where L is the length before the call; slot j
+ *             is the choice for the token after draft j (slot 0: after the pending token).
+ *   dev_out   device pointer or NULL.  Hidden-state stacks: bf16 [n_seqs][k_max+1][H]
+ *             residual stream after the last layer.  With SF_DEBUG_LOGITS: fp32
+ *             [n_seqs][k_max+1][V] logits.
+ * The pass feeds [pending, d_1..d_k, 0...] at positions L..L+k_max.  On commit
+ * (default) a stack with a head sets length = L+M+1 and pending = target[M]
+ * (M accepted drafts plus the model's own token at the first mismatch); a
+ * hidden-state stack sets length = L+k+1 and leaves the decision to the caller
+ * (sf_rollback + sf_set_next).  Positions past the new length keep stale KV that
+ * later passes overwrite.  Replays a captured graph unless SF_DEBUG_LOGITS is set.
+ * Returns after the results have been copied back.
+ * Errors: SF_E_ARG, SF_E_CAPACITY (L + k_max + 1 > capacity for some sequence). */
+sf_status sf_verify(sf_cache* cache, const int32_t* draft, const int32_t* k, uint32_t flags,
+                    int32_t* accepted, int32_t* target, void* dev_out);
+
+/* sf_verify_device: enqueue one verify pass whose drafts are already in device
+ * memory, without waiting (inputs resident in HBM; results stay on the device).
+ *   dev_draft  device int32 [n_seqs][k_max]; dev_k device int32 [n_seqs] or NULL (k_max).
+ *   Drafts are copied into the library's fixed staging buffer on the stream, then
+ *   the captured graph is replayed.  Token ids are not range-checked here (they
+ *   are never read on the host); ids outside [0,V) are clamped by the kernels.
+ *   Results: see sf_results_device.  Host-side length bookkeeping assumes the
+ *   worst case (length + k_max + 1 per committing call) until sf_sync.
+ * Errors: SF_E_ARG, SF_E_CAPACITY. */
+sf_status sf_verify_device(sf_cache* cache, const int32_t* dev_draft, const int32_t* dev_k,
+                           uint32_t flags);
+
+/* sf_results_device: device addresses (fixed for the cache's lifetime) of the
+ * last pass's results: accepted int32 [n_seqs] and target int32 [n_seqs][k_max+1]. */
+sf_status sf_results_device(sf_cache* cache, int32_t** dev_accepted, int32_t** dev_target);
+
+/* sf_rollback: in-place rewind of sequence `seq` to length `pos` (0 <= pos <=
+ * length).  An index write only: no KV data moves ([ShardFlow] "Why It Kept
+ * Breaking": fix 4, in-place KV rewind).  The pending token is unchanged.
+ * Errors: SF_E_ARG (bad seq), SF_E_STATE (pos > length or pos < 0). */
+sf_status sf_rollback(sf_cache* cache, int32_t seq, int32_t pos);
+
+/* sf_set_next: set the pending token of `seq` (the token the next pass places at
+ * position `length`).  Errors: SF_E_ARG (bad seq or token outside [0,V)). */
+sf_status sf_set_next(sf_cache* cache, int32_t seq, int32_t token);
+
+/* sf_cache_state: waits for the stream, then returns the committed length and
+ * pending token of `seq` (host outputs, either may be NULL). */
+sf_status sf_cache_state(sf_cache* cache, int32_t seq, int32_t* length, int32_t* next_token);
+
+/* sf_draft_step: n_steps greedy single-token passes for every sequence, each a
+ * replay of the captured T = 1 graph (whole forward + LM head + argmax + commit:
+ * [ShardFlow] "CUDA Graphs: What They Are and Why They Helped").  tokens: host
+ * int32 [n_seqs][n_steps] receives the generated tokens (may be NULL).  Each step
+ * commits: length += 1, pending = the new token.
+ * Errors: SF_E_STATE (hidden-state stack), SF_E_ARG (n_steps < 1 or > 4096),
+ * SF_E_CAPACITY (length + n_steps > capacity). */
+sf_status sf_draft_step(sf_cache* cache, int32_t n_steps, int32_t* tokens);
+
+/* sf_ngram_propose: prompt-lookup drafter ([Sangama] "Speculative decoding:
+ * correct, but slower (for now)": if the last 2-4 tokens appeared earlier, guess
+ * what followed them then).  Host only.  For n = max_n down to min_n, finds the
+ * most recent earlier start j < n_hist-n with hist[j..j+n) equal to the last n
+ * tokens and writes hist[j+n .. min(j+n+k_max, n_hist)) to out (host int32
+ * [k_max]).  Returns the number of proposed tokens (0..k_max), or SF_E_ARG. */
+int32_t sf_ngram_propose(const int32_t* hist, int32_t n_hist, int32_t min_n, int32_t max_n,
+                         int32_t k_max, int32_t* out);
+
+/* sf_kv_write / sf_kv_read: copy positions [0, n_pos) of sequence `seq` between
+ * the KV pool and caller device buffers k, v laid out bf16
+ * [n_layers][n_kv_heads][src_positions][head_dim] (src_positions >= n_pos).
+ * sf_kv_write also sets length = n_pos (pending token unchanged).
+ * Errors: SF_E_ARG, SF_E_CAPACITY (n_pos > capacity). */
+sf_status sf_kv_write(sf_cache* cache, int32_t seq, const void* dev_k, const void* dev_v,
+                      int32_t n_pos, int32_t src_positions);
+sf_status sf_kv_read(sf_cache* cache, int32_t seq, void* dev_k, void* dev_v, int32_t n_pos,
+                     int32_t dst_positions);
+
+/* sf_sync: wait for all work on the stream; refresh host-side length bookkeeping. */
+sf_status sf_sync(sf_cache* cache);
+
+/* Kernels that sf_time_kernel can time, each at the verify shape (rows =
+ * n_seqs*(k_max+1)), cycling through the layers so weights come from HBM. */
+#define SF_KERNEL_QKV        0
+#define SF_KERNEL_ATTENTION  1
+#define SF_KERNEL_OPROJ      2
+#define SF_KERNEL_GATEUP     3
+#define SF_KERNEL_DOWN       4
+#define SF_KERNEL_LMHEAD     5
+
+/* sf_time_kernel: launch one kernel of the verify pass `iters` times back to back
+ * on the library stream between two HIP events and return the mean time per
+ * launch in microseconds (host *avg_us) and the algorithmic bytes one launch
+ * must move (host *bytes: weights once, activations once, KV once).
+ * Overwrites scratch, so call it between passes only. */
+sf_status sf_time_kernel(sf_cache* cache, int32_t kernel, int32_t iters, float* avg_us,
+                         double* bytes);
+
+/* sf_last_error: message of the calling thread's last failed call ("" if none). */
+const char* sf_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SF_H */

@@ -1,0 +1,289 @@
+"""Python binding of libsf, the MI355X speculative-decoding verify library.
+
+Argument marshalling only: every step of the verify pass runs in the HIP
+kernels behind the C ABI declared in include/sf.h; this module turns numpy
+arrays and torch tensors into pointers and status codes into exceptions.
+PyTorch is used for device memory (weights, caller buffers) and streams.
+
+The functions keep the C names (sf_model_create, sf_cache_alloc, sf_verify,
+sf_rollback, sf_draft_step, sf_ngram_propose, ...).  There is no fallback: if
+libsf.so has not been built, loading fails with an error.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsf.so")
+
+SF_OK = 0
+SF_E_ARG = -1
+SF_E_CAPACITY = -2
+SF_E_STATE = -3
+SF_E_HIP = -4
+SF_E_NOMEM = -5
+
+SF_NO_COMMIT = 1
+SF_FORCE_ACCEPT = 2
+SF_DEBUG_LOGITS = 4
+
+SF_KERNEL_QKV = 0
+SF_KERNEL_ATTENTION = 1
+SF_KERNEL_OPROJ = 2
+SF_KERNEL_GATEUP = 3
+SF_KERNEL_DOWN = 4
+SF_KERNEL_LMHEAD = 5
+
+_NAMES = {SF_E_ARG: "SF_E_ARG", SF_E_CAPACITY: "SF_E_CAPACITY", SF_E_STATE: "SF_E_STATE",
+          SF_E_HIP: "SF_E_HIP", SF_E_NOMEM: "SF_E_NOMEM"}
+
+
+class SFError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+class sf_model_desc(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("hidden", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("rope_base", ctypes.c_float), ("rms_eps", ctypes.c_float),
+                ("has_head", ctypes.c_int32), ("tied_head", ctypes.c_int32), ("qkv_bias", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_PI = ctypes.POINTER(ctypes.c_int32)
+_lib = None
+
+
+def lib():
+    """Load libsf.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m "
+                              "speculative_decoding_verification_decode_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        sig = {
+            "sf_model_create": [ctypes.POINTER(sf_model_desc), ctypes.POINTER(_P), _P, ctypes.POINTER(_P)],
+            "sf_model_free": [_P],
+            "sf_cache_alloc": [_P, _I, _I, _I, ctypes.POINTER(_P)],
+            "sf_cache_free": [_P],
+            "sf_prefill": [_P, _I, _PI, _I, _PI],
+            "sf_verify": [_P, _PI, _PI, ctypes.c_uint32, _PI, _PI, _P],
+            "sf_verify_device": [_P, _P, _P, ctypes.c_uint32],
+            "sf_results_device": [_P, ctypes.POINTER(_P), ctypes.POINTER(_P)],
+            "sf_rollback": [_P, _I, _I],
+            "sf_set_next": [_P, _I, _I],
+            "sf_cache_state": [_P, _I, _PI, _PI],
+            "sf_draft_step": [_P, _I, _PI],
+            "sf_ngram_propose": [_PI, _I, _I, _I, _I, _PI],
+            "sf_kv_write": [_P, _I, _P, _P, _I, _I],
+            "sf_kv_read": [_P, _I, _P, _P, _I, _I],
+            "sf_sync": [_P],
+            "sf_time_kernel": [_P, _I, _I, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double)],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int32
+        L.sf_last_error.argtypes = []
+        L.sf_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def sf_last_error():
+    return lib().sf_last_error().decode()
+
+
+def _check(st):
+    if st != SF_OK:
+        raise SFError(st, sf_last_error())
+    return st
+
+
+def _i32(a):
+    """int32 C-contiguous numpy array and a pointer to it (None stays NULL)."""
+    if a is None:
+        return None, None
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return arr, arr.ctypes.data_as(_PI)
+
+
+def _ptr(x):
+    """Device pointer of a torch tensor, an int address, or None."""
+    if x is None:
+        return None
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    return int(x)
+
+
+# ------------------------------------------------------------------ description and weights
+
+def desc_from_shape(shape):
+    """sf_model_desc from an object with the fields of a decoder shape."""
+    return sf_model_desc(shape.n_layers, shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
+                         shape.ffn, shape.vocab, float(shape.rope_base), float(shape.rms_eps),
+                         int(shape.has_head), int(shape.tied_head), int(shape.qkv_bias))
+
+
+def weight_order(desc):
+    """Tensor names in the order sf_model_create expects them."""
+    names = ["embed"]
+    for i in range(desc.n_layers):
+        p = f"l{i}."
+        names += [p + "ln1", p + "wq"] + ([p + "bq"] if desc.qkv_bias else [])
+        names += [p + "wk"] + ([p + "bk"] if desc.qkv_bias else [])
+        names += [p + "wv"] + ([p + "bv"] if desc.qkv_bias else [])
+        names += [p + "wo", p + "ln2", p + "wg", p + "wu", p + "wd"]
+    if desc.has_head:
+        names += ["final_norm"] + ([] if desc.tied_head else ["lm_head"])
+    return names
+
+
+# ------------------------------------------------------------------ C functions
+
+def sf_model_create(desc, weight_ptrs, stream=None):
+    """weight_ptrs: device addresses in weight_order(desc).  Returns the model handle."""
+    arr = (_P * len(weight_ptrs))(*[int(p) for p in weight_ptrs])
+    out = _P()
+    _check(lib().sf_model_create(ctypes.byref(desc), arr, _ptr(stream), ctypes.byref(out)))
+    return out
+
+
+def sf_model_free(model):
+    _check(lib().sf_model_free(model))
+
+
+def sf_cache_alloc(model, n_seqs, capacity, k_max):
+    out = _P()
+    _check(lib().sf_cache_alloc(model, n_seqs, capacity, k_max, ctypes.byref(out)))
+    return out
+
+
+def sf_cache_free(cache):
+    _check(lib().sf_cache_free(cache))
+
+
+def sf_prefill(cache, seq, tokens):
+    arr, p = _i32(tokens)
+    nxt = ctypes.c_int32(0)
+    _check(lib().sf_prefill(cache, seq, p, len(arr), ctypes.byref(nxt)))
+    return nxt.value
+
+
+def sf_verify(cache, draft, k=None, flags=0, n_seqs=1, k_max=None, dev_out=None):
+    """draft: int array [n_seqs][k_max].  Returns (accepted [n_seqs], target [n_seqs][k_max+1])."""
+    d, dp = _i32(draft)
+    if k_max is None:
+        k_max = d.shape[-1] if d.ndim else 0
+    kk, kp = _i32(k)
+    acc = np.zeros(n_seqs, dtype=np.int32)
+    tgt = np.zeros((n_seqs, k_max + 1), dtype=np.int32)
+    _check(lib().sf_verify(cache, dp, kp, flags, acc.ctypes.data_as(_PI), tgt.ctypes.data_as(_PI),
+                           _ptr(dev_out)))
+    return acc, tgt
+
+
+def sf_verify_device(cache, dev_draft, dev_k=None, flags=0):
+    _check(lib().sf_verify_device(cache, _ptr(dev_draft), _ptr(dev_k), flags))
+
+
+def sf_results_device(cache):
+    a, t = _P(), _P()
+    _check(lib().sf_results_device(cache, ctypes.byref(a), ctypes.byref(t)))
+    return a.value, t.value
+
+
+def sf_rollback(cache, seq, pos):
+    _check(lib().sf_rollback(cache, seq, pos))
+
+
+def sf_set_next(cache, seq, token):
+    _check(lib().sf_set_next(cache, seq, token))
+
+
+def sf_cache_state(cache, seq):
+    ln, nx = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib().sf_cache_state(cache, seq, ctypes.byref(ln), ctypes.byref(nx)))
+    return ln.value, nx.value
+
+
+def sf_draft_step(cache, n_steps, n_seqs=1):
+    out = np.zeros((n_seqs, n_steps), dtype=np.int32)
+    _check(lib().sf_draft_step(cache, n_steps, out.ctypes.data_as(_PI)))
+    return out
+
+
+def sf_ngram_propose(hist, min_n=2, max_n=4, k_max=8):
+    h, hp = _i32(hist)
+    out = np.zeros(max(k_max, 1), dtype=np.int32)
+    n = lib().sf_ngram_propose(hp, len(h), min_n, max_n, k_max, out.ctypes.data_as(_PI))
+    if n < 0:
+        raise SFError(n, sf_last_error())
+    return out[:n].copy()
+
+
+def sf_kv_write(cache, seq, dev_k, dev_v, n_pos, src_positions):
+    _check(lib().sf_kv_write(cache, seq, _ptr(dev_k), _ptr(dev_v), n_pos, src_positions))
+
+
+def sf_kv_read(cache, seq, dev_k, dev_v, n_pos, dst_positions):
+    _check(lib().sf_kv_read(cache, seq, _ptr(dev_k), _ptr(dev_v), n_pos, dst_positions))
+
+
+def sf_sync(cache):
+    _check(lib().sf_sync(cache))
+
+
+def sf_time_kernel(cache, kernel, iters):
+    """Returns (mean microseconds per launch, algorithmic bytes per launch)."""
+    us, by = ctypes.c_float(0), ctypes.c_double(0)
+    _check(lib().sf_time_kernel(cache, kernel, iters, ctypes.byref(us), ctypes.byref(by)))
+    return us.value, by.value
+
+
+# ------------------------------------------------------------------ torch conveniences
+
+def upload_weights(weights, desc, device="cuda"):
+    """Copy bf16 bit arrays (numpy uint16, by name) to the device; returns (tensors, pointers)."""
+    import torch
+    tensors = []
+    for name in weight_order(desc):
+        a = np.ascontiguousarray(weights[name])
+        tensors.append(torch.from_numpy(a.view(np.int16)).to(device))
+    return tensors, [t.data_ptr() for t in tensors]
+
+
+class Engine:
+    """A model plus one cache on a dedicated torch stream."""
+
+    def __init__(self, shape, weights, n_seqs=1, capacity=128, k_max=4, keep_weights=False):
+        import torch
+        self.stream = torch.cuda.Stream()
+        self.desc = desc_from_shape(shape)
+        self.n_seqs, self.capacity, self.k_max = n_seqs, capacity, k_max
+        tensors, ptrs = upload_weights(weights, self.desc)
+        torch.cuda.synchronize()
+        self.model = sf_model_create(self.desc, ptrs, self.stream.cuda_stream)
+        self._weights = tensors if keep_weights else None
+        del tensors
+        self.cache = sf_cache_alloc(self.model, n_seqs, capacity, k_max)
+
+    def close(self):
+        if self.cache is not None:
+            sf_cache_free(self.cache)
+            self.cache = None
+        if self.model is not None:
+            sf_model_free(self.model)
+            self.model = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

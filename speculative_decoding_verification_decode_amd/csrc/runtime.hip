@@ -1,0 +1,825 @@
+// Host runtime of libsf: the C ABI declared in include/sf.h.
+//
+// Ownership and allocation: device memory is allocated only in sf_model_create (packed
+// weights) and sf_cache_alloc (KV pool, scratch, counters, staging, graphs).  Every later
+// call reuses those fixed addresses, which is what keeps captured graph replays valid
+// ("I Got 28 TPS Out of Free Kaggle GPUs", section "Why It Kept Breaking (and How I Fixed
+// It)": a graph reads the addresses it was captured with).
+#include "sf.h"
+#include "sf_internal.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+using namespace sf;
+
+static thread_local std::string g_err;
+
+static sf_status fail(sf_status code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+#define HIPCHK(expr)                                                                          \
+  do {                                                                                        \
+    hipError_t e_ = (expr);                                                                   \
+    if (e_ != hipSuccess) return fail(SF_E_HIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+namespace {
+
+struct Layer {
+  uint4 *wqkv, *wo, *wgu, *wd;
+  float *bqkv, *g1, *g2;
+};
+
+struct DevAllocs {
+  std::vector<void*> ptrs;
+  hipError_t alloc(void** p, size_t bytes) {
+    hipError_t e = hipMalloc(p, std::max<size_t>(bytes, 256));
+    if (e == hipSuccess) ptrs.push_back(*p);
+    return e;
+  }
+  void release() {
+    for (void* p : ptrs) (void)hipFree(p);
+    ptrs.clear();
+  }
+};
+
+}  // namespace
+
+struct sf_model {
+  sf_model_desc d;
+  hipStream_t stream = nullptr;
+  bool own_stream = false;
+  int H, Q, KV, F, V, dh, nq, nkv, L;
+  int nb_qkv, nb_h, nb_gu, nb_head;
+  uint16_t* embed = nullptr;
+  std::vector<Layer> layers;
+  float* gfinal = nullptr;
+  float* ones = nullptr;
+  uint4* head = nullptr;
+  DevAllocs mem;
+};
+
+struct Run {
+  int B, T, seq0, kmax;
+  float* logits;
+  bool draft_mode;
+};
+
+struct sf_cache {
+  sf_model* m;
+  int B, cap, kmax, T, nchunk;
+  size_t layer_stride, seq_stride;  // elements
+  uint16_t *kpool = nullptr, *vpool = nullptr;
+  int32_t *len = nullptr, *next = nullptr;
+  Stage* stage_d = nullptr;
+  Stage* stage_h = nullptr;
+  float* x = nullptr;
+  uint16_t *a_h = nullptr, *a_o = nullptr, *a_f = nullptr, *hidden = nullptr;
+  float *ssq = nullptr, *q = nullptr, *apart = nullptr, *gpart = nullptr;
+  float2* amax = nullptr;
+  float2* rope = nullptr;
+  int* counters = nullptr;
+  int32_t *res_d = nullptr, *res_h = nullptr, *dout_d = nullptr, *dout_h = nullptr;
+  int sp_qkv, sp_o, sp_gu, sp_d, sp_head;
+  hipGraphExec_t gx_verify = nullptr, gx_draft = nullptr;
+  std::vector<int> len_h, next_h, len_hi;
+  bool dirty = false;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  DevAllocs mem;
+};
+
+// ------------------------------------------------------------------------------------------
+// Work split of a GEMM with nb n-blocks and kb k-tiles: each wave takes at most kBatch tiles;
+// small GEMMs are spread over more workgroups (at least two tiles per wave).
+static int choose_sp(int nb, int kb, const char* env) {
+  int sp = (kb + kGemmWaves * kBatch - 1) / (kGemmWaves * kBatch);
+  while (nb * sp < 512 && sp * kGemmWaves * 4 <= kb) sp *= 2;
+  if (const char* v = getenv(env)) {
+    int o = atoi(v);
+    if (o >= 1 && o <= 64) sp = o;
+  }
+  return sp;
+}
+
+static sf_status check_desc(const sf_model_desc* d) {
+  if (!d) return fail(SF_E_ARG, "desc is NULL");
+  if (d->n_layers < 1 || d->hidden < 32 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->ffn < 32 || d->vocab < 16)
+    return fail(SF_E_ARG, "non-positive dimension");
+  if (d->hidden % 32 || d->ffn % 32 || d->vocab % 16)
+    return fail(SF_E_ARG, "hidden and ffn must be multiples of 32, vocab of 16");
+  if (d->head_dim != 64 && d->head_dim != 128) return fail(SF_E_ARG, "head_dim must be 64 or 128");
+  if (d->n_q_heads % d->n_kv_heads) return fail(SF_E_ARG, "n_kv_heads must divide n_q_heads");
+  if ((d->n_q_heads * d->head_dim) % 32) return fail(SF_E_ARG, "n_q_heads*head_dim must be a multiple of 32");
+  if (d->hidden > 4096) return fail(SF_E_ARG, "hidden must be <= 4096");
+  if (!(d->rms_eps >= 0.f) || !(d->rope_base > 1.f)) return fail(SF_E_ARG, "bad rms_eps or rope_base");
+  return SF_OK;
+}
+
+// Upload a pointer table, run `fn(dev_table)`, wait, free the table.
+template <typename Fn>
+static sf_status with_table(const std::vector<const uint16_t*>& tab, hipStream_t s, Fn fn) {
+  const uint16_t** dt = nullptr;
+  HIPCHK(hipMalloc((void**)&dt, tab.size() * sizeof(void*)));
+  hipError_t e = hipMemcpyAsync(dt, tab.data(), tab.size() * sizeof(void*), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = fn(dt);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  (void)hipFree(dt);
+  if (e != hipSuccess) return fail(SF_E_HIP, std::string("weight packing: ") + hipGetErrorString(e));
+  return SF_OK;
+}
+
+extern "C" sf_status sf_model_create(const sf_model_desc* desc, const void* const* weights, void* stream,
+                                     sf_model** out) {
+  if (sf_status st = check_desc(desc)) return st;
+  if (!weights || !out) return fail(SF_E_ARG, "weights or out is NULL");
+  sf_model* m = new sf_model();
+  m->d = *desc;
+  const sf_model_desc& d = *desc;
+  m->H = d.hidden; m->nq = d.n_q_heads; m->nkv = d.n_kv_heads; m->dh = d.head_dim;
+  m->Q = d.n_q_heads * d.head_dim; m->KV = d.n_kv_heads * d.head_dim; m->F = d.ffn; m->V = d.vocab;
+  m->L = d.n_layers;
+  m->nb_qkv = (m->Q + 2 * m->KV) / 16;
+  m->nb_h = m->H / 16;
+  m->nb_gu = m->F / 8;
+  m->nb_head = m->V / 16;
+
+  // Count and validate the weight table.
+  const int per_layer = d.qkv_bias ? 12 : 9;
+  const int n_tensors = 1 + d.n_layers * per_layer + (d.has_head ? 1 + (d.tied_head ? 0 : 1) : 0);
+  for (int i = 0; i < n_tensors; ++i)
+    if (!weights[i]) { delete m; return fail(SF_E_ARG, "weight pointer " + std::to_string(i) + " is NULL"); }
+
+  auto cleanup = [&](sf_status st) {
+    m->mem.release();
+    if (m->own_stream && m->stream) (void)hipStreamDestroy(m->stream);
+    delete m;
+    return st;
+  };
+  if (stream) {
+    m->stream = (hipStream_t)stream;
+  } else {
+    hipError_t e = hipStreamCreateWithFlags(&m->stream, hipStreamNonBlocking);
+    if (e != hipSuccess) return cleanup(fail(SF_E_HIP, std::string("stream: ") + hipGetErrorString(e)));
+    m->own_stream = true;
+  }
+  hipStream_t s = m->stream;
+  const int H = m->H, Q = m->Q, KV = m->KV, F = m->F, V = m->V, dh = m->dh, half = dh / 2;
+  auto W = [&](int i) { return (const uint16_t*)weights[i]; };
+
+  auto dalloc = [&](void** p, size_t bytes) -> sf_status {
+    hipError_t e = m->mem.alloc(p, bytes);
+    if (e != hipSuccess) return fail(SF_E_NOMEM, std::string("hipMalloc: ") + hipGetErrorString(e));
+    return SF_OK;
+  };
+#define TRY(x)                           \
+  do {                                   \
+    sf_status st_ = (x);                 \
+    if (st_ != SF_OK) return cleanup(st_); \
+  } while (0)
+
+  TRY(dalloc((void**)&m->embed, (size_t)V * H * 2));
+  {
+    hipError_t e = hipMemcpyAsync(m->embed, W(0), (size_t)V * H * 2, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return cleanup(fail(SF_E_HIP, std::string("embed copy: ") + hipGetErrorString(e)));
+  }
+  TRY(dalloc((void**)&m->ones, (size_t)H * 4));
+  {
+    std::vector<float> ones(H, 1.0f);
+    hipError_t e = hipMemcpy(m->ones, ones.data(), (size_t)H * 4, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return cleanup(fail(SF_E_HIP, std::string("ones: ") + hipGetErrorString(e)));
+  }
+
+  int idx = 1;
+  m->layers.resize(d.n_layers);
+  for (int l = 0; l < d.n_layers; ++l) {
+    Layer& Ly = m->layers[l];
+    const uint16_t* ln1 = W(idx++);
+    const uint16_t* wq = W(idx++);
+    const uint16_t* bq = d.qkv_bias ? W(idx++) : nullptr;
+    const uint16_t* wk = W(idx++);
+    const uint16_t* bk = d.qkv_bias ? W(idx++) : nullptr;
+    const uint16_t* wv = W(idx++);
+    const uint16_t* bv = d.qkv_bias ? W(idx++) : nullptr;
+    const uint16_t* wo = W(idx++);
+    const uint16_t* ln2 = W(idx++);
+    const uint16_t* wg = W(idx++);
+    const uint16_t* wu = W(idx++);
+    const uint16_t* wd = W(idx++);
+
+    // QKV rows: n block -> (section, head, dims i0..i0+7 and their RoPE partners).
+    const int N = Q + 2 * KV, bph = dh / 16;
+    std::vector<const uint16_t*> rows(N), bias(N);
+    for (int n = 0; n < N; ++n) {
+      const int nb = n / 16, nl = n % 16;
+      const int qb = m->nq * bph, kvb = m->nkv * bph;
+      int head, blk;
+      const uint16_t *wsrc, *bsrc;
+      if (nb < qb) { head = nb / bph; blk = nb % bph; wsrc = wq; bsrc = bq; }
+      else if (nb < qb + kvb) { head = (nb - qb) / bph; blk = (nb - qb) % bph; wsrc = wk; bsrc = bk; }
+      else { head = (nb - qb - kvb) / bph; blk = (nb - qb - kvb) % bph; wsrc = wv; bsrc = bv; }
+      const int dim = blk * 8 + (nl % 8) + (nl >= 8 ? half : 0);
+      const int r = head * dh + dim;
+      rows[n] = wsrc + (size_t)r * H;
+      bias[n] = bsrc ? bsrc + r : nullptr;
+    }
+    TRY(dalloc((void**)&Ly.wqkv, (size_t)N * H * 2));
+    TRY(with_table(rows, s, [&](const uint16_t* const* t) { return launch_pack(Ly.wqkv, t, N / 16, H / 32, s); }));
+    TRY(dalloc((void**)&Ly.bqkv, (size_t)N * 4));
+    TRY(with_table(bias, s, [&](const uint16_t* const* t) { return launch_gather_f32(Ly.bqkv, t, N, s); }));
+
+    std::vector<const uint16_t*> ro(H);
+    for (int n = 0; n < H; ++n) ro[n] = wo + (size_t)n * Q;
+    TRY(dalloc((void**)&Ly.wo, (size_t)H * Q * 2));
+    TRY(with_table(ro, s, [&](const uint16_t* const* t) { return launch_pack(Ly.wo, t, H / 16, Q / 32, s); }));
+
+    // gate/up rows: n block nb -> gate rows 8nb..8nb+7 then up rows 8nb..8nb+7.
+    std::vector<const uint16_t*> rgu(2 * F);
+    for (int n = 0; n < 2 * F; ++n) {
+      const int nb = n / 16, nl = n % 16;
+      const int j = nb * 8 + (nl % 8);
+      rgu[n] = (nl < 8 ? wg : wu) + (size_t)j * H;
+    }
+    TRY(dalloc((void**)&Ly.wgu, (size_t)2 * F * H * 2));
+    TRY(with_table(rgu, s, [&](const uint16_t* const* t) { return launch_pack(Ly.wgu, t, 2 * F / 16, H / 32, s); }));
+
+    std::vector<const uint16_t*> rd(H);
+    for (int n = 0; n < H; ++n) rd[n] = wd + (size_t)n * F;
+    TRY(dalloc((void**)&Ly.wd, (size_t)H * F * 2));
+    TRY(with_table(rd, s, [&](const uint16_t* const* t) { return launch_pack(Ly.wd, t, H / 16, F / 32, s); }));
+
+    std::vector<const uint16_t*> g1(H), g2(H);
+    for (int n = 0; n < H; ++n) { g1[n] = ln1 + n; g2[n] = ln2 + n; }
+    TRY(dalloc((void**)&Ly.g1, (size_t)H * 4));
+    TRY(dalloc((void**)&Ly.g2, (size_t)H * 4));
+    TRY(with_table(g1, s, [&](const uint16_t* const* t) { return launch_gather_f32(Ly.g1, t, H, s); }));
+    TRY(with_table(g2, s, [&](const uint16_t* const* t) { return launch_gather_f32(Ly.g2, t, H, s); }));
+  }
+  if (d.has_head) {
+    const uint16_t* gf = W(idx++);
+    const uint16_t* hsrc = d.tied_head ? W(0) : W(idx++);
+    std::vector<const uint16_t*> gfv(H), rh(V);
+    for (int n = 0; n < H; ++n) gfv[n] = gf + n;
+    for (int n = 0; n < V; ++n) rh[n] = hsrc + (size_t)n * H;
+    TRY(dalloc((void**)&m->gfinal, (size_t)H * 4));
+    TRY(with_table(gfv, s, [&](const uint16_t* const* t) { return launch_gather_f32(m->gfinal, t, H, s); }));
+    TRY(dalloc((void**)&m->head, (size_t)V * H * 2));
+    TRY(with_table(rh, s, [&](const uint16_t* const* t) { return launch_pack(m->head, t, V / 16, H / 32, s); }));
+  }
+#undef TRY
+  *out = m;
+  return SF_OK;
+}
+
+extern "C" sf_status sf_model_free(sf_model* m) {
+  if (!m) return fail(SF_E_ARG, "model is NULL");
+  (void)hipStreamSynchronize(m->stream);
+  m->mem.release();
+  if (m->own_stream) (void)hipStreamDestroy(m->stream);
+  delete m;
+  return SF_OK;
+}
+
+// ------------------------------------------------------------------------------------------
+// One forward pass (embed .. accept) enqueued on the model stream.  Used both eagerly and
+// under stream capture, so it must not allocate or synchronise.
+static hipError_t enqueue_forward(sf_cache* c, const Run& r) {
+  sf_model* m = c->m;
+  const sf_model_desc& d = m->d;
+  hipStream_t s = m->stream;
+  const int rows = r.B * r.T;
+  int32_t* len = c->len + r.seq0;
+  int32_t* next = c->next + r.seq0;
+  const size_t kvoff = (size_t)r.seq0 * c->seq_stride;
+  hipError_t e;
+
+  EmbedArgs ea{};
+  ea.embed = m->embed; ea.stage = c->stage_d; ea.len = len; ea.next = next; ea.gain = m->layers[0].g1;
+  ea.x = c->x; ea.a = c->a_h; ea.ssq = c->ssq; ea.rows = rows; ea.T = r.T; ea.H = m->H; ea.V = m->V;
+  ea.kmax = r.kmax;
+  if ((e = launch_embed(ea, s)) != hipSuccess) return e;
+
+  GemmArgs base{};
+  base.rows = rows; base.part = c->gpart; base.counters = c->counters; base.ssq_in = c->ssq;
+  base.nparts_in = m->H / 16; base.eps = d.rms_eps; base.T = r.T; base.len = len; base.cap = c->cap;
+  base.seq_stride = (long)c->seq_stride; base.rope = c->rope; base.nq = m->nq; base.nkv = m->nkv; base.dh = m->dh;
+
+  AttnArgs aa{};
+  aa.q = c->q; aa.seq_stride = (long)c->seq_stride; aa.cap = c->cap; aa.len = len; aa.T = r.T; aa.nq = m->nq;
+  aa.nkv = m->nkv; aa.nchunk = c->nchunk; aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)m->dh));
+  aa.part = c->apart; aa.out = c->a_o; aa.rows = rows;
+
+  for (int l = 0; l < m->L; ++l) {
+    const Layer& Ly = m->layers[l];
+    uint16_t* kc = c->kpool + (size_t)l * c->layer_stride + kvoff;
+    uint16_t* vc = c->vpool + (size_t)l * c->layer_stride + kvoff;
+
+    GemmArgs g = base;
+    g.w = Ly.wqkv; g.a = c->a_h; g.k = m->H; g.kb = m->H / 32; g.nb = m->nb_qkv; g.sp = c->sp_qkv;
+    g.bias = Ly.bqkv; g.q = c->q; g.kc = kc; g.vc = vc;
+    if ((e = launch_gemm(kEpiQkv, g, s)) != hipSuccess) return e;
+
+    aa.kc = kc; aa.vc = vc;
+    if ((e = launch_attention(aa, m->dh, r.B, s)) != hipSuccess) return e;
+
+    g = base;
+    g.w = Ly.wo; g.a = c->a_o; g.k = m->Q; g.kb = m->Q / 32; g.nb = m->nb_h; g.sp = c->sp_o;
+    g.x = c->x; g.a_next = c->a_h; g.gain_next = Ly.g2; g.ssq_out = c->ssq; g.n_out = m->H;
+    if ((e = launch_gemm(kEpiResid, g, s)) != hipSuccess) return e;
+
+    g = base;
+    g.w = Ly.wgu; g.a = c->a_h; g.k = m->H; g.kb = m->H / 32; g.nb = m->nb_gu; g.sp = c->sp_gu;
+    g.h = c->a_f; g.ffn = m->F;
+    if ((e = launch_gemm(kEpiSwiglu, g, s)) != hipSuccess) return e;
+
+    const bool last = (l + 1 == m->L);
+    g = base;
+    g.w = Ly.wd; g.a = c->a_f; g.k = m->F; g.kb = m->F / 32; g.nb = m->nb_h; g.sp = c->sp_d;
+    g.x = c->x; g.a_next = c->a_h;
+    g.gain_next = !last ? m->layers[l + 1].g1 : (d.has_head ? m->gfinal : m->ones);
+    g.ssq_out = c->ssq; g.n_out = m->H;
+    g.hidden = (last && !d.has_head) ? c->hidden : nullptr;
+    if ((e = launch_gemm(kEpiResid, g, s)) != hipSuccess) return e;
+  }
+
+  if (d.has_head) {
+    GemmArgs g = base;
+    g.w = m->head; g.a = c->a_h; g.k = m->H; g.kb = m->H / 32; g.nb = m->nb_head; g.sp = c->sp_head;
+    g.amax = c->amax; g.logits = r.logits; g.vocab = m->V;
+    if ((e = launch_gemm(kEpiArgmax, g, s)) != hipSuccess) return e;
+  }
+
+  AcceptArgs ac{};
+  ac.amax = c->amax; ac.nparts = m->nb_head; ac.stage = c->stage_d; ac.len = len; ac.next = next;
+  ac.result = c->res_d; ac.draft_out = r.draft_mode ? c->dout_d : nullptr; ac.B = r.B; ac.T = r.T;
+  ac.has_head = d.has_head;
+  return launch_accept(ac, s);
+}
+
+static sf_status capture(sf_cache* c, const Run& r, hipGraphExec_t* out) {
+  hipStream_t s = c->m->stream;
+  hipGraph_t graph = nullptr;
+  HIPCHK(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+  hipError_t e = enqueue_forward(c, r);
+  hipError_t e2 = hipStreamEndCapture(s, &graph);
+  if (e != hipSuccess) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return fail(SF_E_HIP, std::string("capture: ") + hipGetErrorString(e));
+  }
+  if (e2 != hipSuccess) return fail(SF_E_HIP, std::string("end capture: ") + hipGetErrorString(e2));
+  e = hipGraphInstantiate(out, graph, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(graph);
+  if (e != hipSuccess) return fail(SF_E_HIP, std::string("instantiate: ") + hipGetErrorString(e));
+  return SF_OK;
+}
+
+static void cache_release(sf_cache* c) {
+  if (c->gx_verify) (void)hipGraphExecDestroy(c->gx_verify);
+  if (c->gx_draft) (void)hipGraphExecDestroy(c->gx_draft);
+  if (c->stage_h) (void)hipHostFree(c->stage_h);
+  if (c->res_h) (void)hipHostFree(c->res_h);
+  if (c->dout_h) (void)hipHostFree(c->dout_h);
+  if (c->ev0) (void)hipEventDestroy(c->ev0);
+  if (c->ev1) (void)hipEventDestroy(c->ev1);
+  c->mem.release();
+  delete c;
+}
+
+extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacity, int32_t k_max,
+                                    sf_cache** out) {
+  if (!m || !out) return fail(SF_E_ARG, "model or out is NULL");
+  if (k_max < 0 || k_max >= kMaxK) return fail(SF_E_ARG, "k_max must be in 0..15");
+  if (n_seqs < 1 || n_seqs * (k_max + 1) > kMaxRows) return fail(SF_E_ARG, "n_seqs*(k_max+1) must be in 1..64");
+  if (capacity < k_max + 1 || capacity > (1 << 20)) return fail(SF_E_ARG, "capacity out of range");
+  sf_cache* c = new sf_cache();
+  c->m = m; c->B = n_seqs; c->cap = capacity; c->kmax = k_max; c->T = k_max + 1;
+  c->nchunk = (capacity + kChunk - 1) / kChunk;
+  c->seq_stride = (size_t)m->nkv * capacity * m->dh;
+  c->layer_stride = c->seq_stride * n_seqs;
+  c->len_h.assign(n_seqs, 0); c->next_h.assign(n_seqs, 0); c->len_hi.assign(n_seqs, 0);
+  c->sp_qkv = choose_sp(m->nb_qkv, m->H / 32, "SF_SP_QKV");
+  c->sp_o = choose_sp(m->nb_h, m->Q / 32, "SF_SP_O");
+  c->sp_gu = choose_sp(m->nb_gu, m->H / 32, "SF_SP_GU");
+  c->sp_d = choose_sp(m->nb_h, m->F / 32, "SF_SP_D");
+  c->sp_head = choose_sp(m->nb_head, m->H / 32, "SF_SP_HEAD");
+
+  hipStream_t s = m->stream;
+  auto bail = [&](sf_status st) { cache_release(c); return st; };
+  auto dalloc = [&](void** p, size_t bytes) -> sf_status {
+    hipError_t e = c->mem.alloc(p, bytes);
+    if (e != hipSuccess) return fail(SF_E_NOMEM, std::string("hipMalloc: ") + hipGetErrorString(e));
+    e = hipMemsetAsync(*p, 0, std::max<size_t>(bytes, 256), s);
+    if (e != hipSuccess) return fail(SF_E_HIP, std::string("hipMemset: ") + hipGetErrorString(e));
+    return SF_OK;
+  };
+#define TRY(x)                        \
+  do {                                \
+    sf_status st_ = (x);              \
+    if (st_ != SF_OK) return bail(st_); \
+  } while (0)
+  const size_t R = kMaxRows;
+  const size_t pool = c->layer_stride * m->L * 2;
+  TRY(dalloc((void**)&c->kpool, pool));
+  TRY(dalloc((void**)&c->vpool, pool));
+  TRY(dalloc((void**)&c->len, n_seqs * 4));
+  TRY(dalloc((void**)&c->next, n_seqs * 4));
+  TRY(dalloc((void**)&c->stage_d, sizeof(Stage)));
+  TRY(dalloc((void**)&c->x, R * m->H * 4));
+  TRY(dalloc((void**)&c->a_h, R * m->H * 2));
+  TRY(dalloc((void**)&c->a_o, R * m->Q * 2));
+  TRY(dalloc((void**)&c->a_f, R * m->F * 2));
+  TRY(dalloc((void**)&c->hidden, R * m->H * 2));
+  TRY(dalloc((void**)&c->ssq, R * (m->H / 16) * 4));
+  TRY(dalloc((void**)&c->q, R * m->Q * 4));
+  TRY(dalloc((void**)&c->apart, R * m->nq * (size_t)c->nchunk * (m->dh + 2) * 4));
+  TRY(dalloc((void**)&c->amax, R * m->nb_head * 8));
+  size_t gp = 0;
+  gp = std::max(gp, (size_t)m->nb_qkv * c->sp_qkv);
+  gp = std::max(gp, (size_t)m->nb_h * c->sp_o);
+  gp = std::max(gp, (size_t)m->nb_gu * c->sp_gu);
+  gp = std::max(gp, (size_t)m->nb_h * c->sp_d);
+  gp = std::max(gp, (size_t)m->nb_head * c->sp_head);
+  TRY(dalloc((void**)&c->gpart, gp * 4 * 256 * 4));
+  TRY(dalloc((void**)&c->counters, (size_t)std::max({m->nb_qkv, m->nb_gu, m->nb_head, m->nb_h}) * 4));
+  TRY(dalloc((void**)&c->rope, (size_t)capacity * (m->dh / 2) * 8));
+  TRY(dalloc((void**)&c->res_d, 4 * kMaxRows * 4));
+  TRY(dalloc((void**)&c->dout_d, (size_t)n_seqs * kMaxDraftSteps * 4));
+  {
+    hipError_t e = hipHostMalloc((void**)&c->stage_h, sizeof(Stage), hipHostMallocDefault);
+    if (e == hipSuccess) e = hipHostMalloc((void**)&c->res_h, 4 * kMaxRows * 4, hipHostMallocDefault);
+    if (e == hipSuccess) e = hipHostMalloc((void**)&c->dout_h, (size_t)n_seqs * kMaxDraftSteps * 4, hipHostMallocDefault);
+    if (e != hipSuccess) return bail(fail(SF_E_NOMEM, std::string("hipHostMalloc: ") + hipGetErrorString(e)));
+    memset(c->stage_h, 0, sizeof(Stage));
+  }
+  {
+    hipError_t e = launch_rope_table(c->rope, capacity, m->dh / 2, (double)m->d.rope_base, s);
+    if (e == hipSuccess) e = hipEventCreate(&c->ev0);
+    if (e == hipSuccess) e = hipEventCreate(&c->ev1);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return bail(fail(SF_E_HIP, std::string("cache init: ") + hipGetErrorString(e)));
+  }
+  TRY(capture(c, Run{n_seqs, c->T, 0, k_max, nullptr, false}, &c->gx_verify));
+  if (m->d.has_head) TRY(capture(c, Run{n_seqs, 1, 0, 0, nullptr, true}, &c->gx_draft));
+#undef TRY
+  *out = c;
+  return SF_OK;
+}
+
+extern "C" sf_status sf_cache_free(sf_cache* c) {
+  if (!c) return fail(SF_E_ARG, "cache is NULL");
+  (void)hipStreamSynchronize(c->m->stream);
+  cache_release(c);
+  return SF_OK;
+}
+
+// Refresh the host copies of length / pending token from the device.
+static sf_status refresh(sf_cache* c) {
+  hipStream_t s = c->m->stream;
+  HIPCHK(hipStreamSynchronize(s));
+  HIPCHK(hipMemcpy(c->res_h, c->len, c->B * 4, hipMemcpyDeviceToHost));
+  for (int b = 0; b < c->B; ++b) c->len_h[b] = c->res_h[b];
+  HIPCHK(hipMemcpy(c->res_h, c->next, c->B * 4, hipMemcpyDeviceToHost));
+  for (int b = 0; b < c->B; ++b) c->next_h[b] = c->res_h[b];
+  c->len_hi = c->len_h;
+  c->dirty = false;
+  return SF_OK;
+}
+
+static size_t stage_bytes(int B, int kmax) { return offsetof(Stage, draft) + (size_t)B * std::max(kmax, 1) * 4; }
+
+extern "C" sf_status sf_verify(sf_cache* c, const int32_t* draft, const int32_t* k, uint32_t flags,
+                               int32_t* accepted, int32_t* target, void* dev_out) {
+  if (!c) return fail(SF_E_ARG, "cache is NULL");
+  sf_model* m = c->m;
+  if (flags & ~(SF_NO_COMMIT | SF_FORCE_ACCEPT | SF_DEBUG_LOGITS)) return fail(SF_E_ARG, "unknown flags");
+  if (!draft && c->kmax > 0) return fail(SF_E_ARG, "draft is NULL");
+  const bool dbg = (flags & SF_DEBUG_LOGITS) != 0;
+  if (dbg && (!m->d.has_head || !dev_out)) return fail(SF_E_ARG, "SF_DEBUG_LOGITS needs a head and dev_out");
+  if (c->dirty) {
+    if (sf_status st = refresh(c)) return st;
+  }
+  for (int b = 0; b < c->B; ++b) {
+    const int kb = k ? k[b] : c->kmax;
+    if (kb < 0 || kb > c->kmax) return fail(SF_E_ARG, "k out of range");
+    for (int j = 0; j < kb; ++j) {
+      const int t = draft[b * c->kmax + j];
+      if (t < 0 || t >= m->V) return fail(SF_E_ARG, "draft token outside [0,V)");
+    }
+    if (c->len_h[b] + c->T > c->cap)
+      return fail(SF_E_CAPACITY, "sequence " + std::to_string(b) + ": length + k_max + 1 exceeds capacity");
+  }
+  hipStream_t s = m->stream;
+  Stage* st = c->stage_h;
+  st->flags = (int)(flags & (SF_NO_COMMIT | SF_FORCE_ACCEPT));
+  st->kmax = c->kmax;
+  for (int b = 0; b < c->B; ++b) {
+    const int kb = k ? k[b] : c->kmax;
+    st->k[b] = kb;
+    st->step[b] = 0;
+    for (int j = 0; j < c->kmax; ++j) st->draft[b * c->kmax + j] = (j < kb) ? draft[b * c->kmax + j] : 0;
+  }
+  HIPCHK(hipMemcpyAsync(c->stage_d, st, stage_bytes(c->B, c->kmax), hipMemcpyHostToDevice, s));
+  if (dbg) {
+    hipError_t e = enqueue_forward(c, Run{c->B, c->T, 0, c->kmax, (float*)dev_out, false});
+    if (e != hipSuccess) return fail(SF_E_HIP, std::string("forward: ") + hipGetErrorString(e));
+  } else {
+    HIPCHK(hipGraphLaunch(c->gx_verify, s));
+  }
+  const int nres = c->B + c->B * c->T;
+  HIPCHK(hipMemcpyAsync(c->res_h, c->res_d, nres * 4, hipMemcpyDeviceToHost, s));
+  if (!m->d.has_head && dev_out)
+    HIPCHK(hipMemcpyAsync(dev_out, c->hidden, (size_t)c->B * c->T * m->H * 2, hipMemcpyDeviceToDevice, s));
+  HIPCHK(hipStreamSynchronize(s));
+  for (int b = 0; b < c->B; ++b) {
+    const int M = c->res_h[b];
+    if (accepted) accepted[b] = M;
+    if (target)
+      for (int j = 0; j < c->T; ++j) target[b * c->T + j] = c->res_h[c->B + b * c->T + j];
+    if (!(flags & SF_NO_COMMIT)) {
+      if (m->d.has_head) {
+        c->len_h[b] += M + 1;
+        c->next_h[b] = c->res_h[c->B + b * c->T + M];
+      } else {
+        c->len_h[b] += (k ? k[b] : c->kmax) + 1;
+      }
+    }
+  }
+  c->len_hi = c->len_h;
+  return SF_OK;
+}
+
+extern "C" sf_status sf_verify_device(sf_cache* c, const int32_t* dev_draft, const int32_t* dev_k, uint32_t flags) {
+  if (!c) return fail(SF_E_ARG, "cache is NULL");
+  if (flags & ~(SF_NO_COMMIT | SF_FORCE_ACCEPT)) return fail(SF_E_ARG, "unsupported flags");
+  if (!dev_draft && c->kmax > 0) return fail(SF_E_ARG, "dev_draft is NULL");
+  for (int b = 0; b < c->B; ++b)
+    if (c->len_hi[b] + c->T > c->cap)
+      return fail(SF_E_CAPACITY, "sequence " + std::to_string(b) + ": length may exceed capacity (sf_sync first)");
+  hipStream_t s = c->m->stream;
+  const int32_t* dd = dev_draft ? dev_draft : c->res_d;
+  hipError_t e = launch_stage_device(c->stage_d, dd, dev_k, c->B, c->kmax, (int)flags, s);
+  if (e != hipSuccess) return fail(SF_E_HIP, std::string("stage: ") + hipGetErrorString(e));
+  HIPCHK(hipGraphLaunch(c->gx_verify, s));
+  if (!(flags & SF_NO_COMMIT)) {
+    for (int b = 0; b < c->B; ++b) c->len_hi[b] += c->T;
+    c->dirty = true;
+  }
+  return SF_OK;
+}
+
+extern "C" sf_status sf_results_device(sf_cache* c, int32_t** dev_accepted, int32_t** dev_target) {
+  if (!c) return fail(SF_E_ARG, "cache is NULL");
+  if (dev_accepted) *dev_accepted = c->res_d;
+  if (dev_target) *dev_target = c->res_d + c->B;
+  return SF_OK;
+}
+
+extern "C" sf_status sf_prefill(sf_cache* c, int32_t seq, const int32_t* tokens, int32_t n, int32_t* next_token) {
+  if (!c || !tokens) return fail(SF_E_ARG, "cache or tokens is NULL");
+  sf_model* m = c->m;
+  if (seq < 0 || seq >= c->B) return fail(SF_E_ARG, "seq out of range");
+  if (n < 1) return fail(SF_E_ARG, "n < 1");
+  if (n > c->cap) return fail(SF_E_CAPACITY, "prompt longer than capacity");
+  for (int i = 0; i < n; ++i)
+    if (tokens[i] < 0 || tokens[i] >= m->V) return fail(SF_E_ARG, "token outside [0,V)");
+  if (c->dirty) {
+    if (sf_status st = refresh(c)) return st;
+  }
+  hipStream_t s = m->stream;
+  HIPCHK(launch_set_state(c->len, c->next, seq, 0, 0, 1, s));
+  int last_cnt = 1;
+  for (int j0 = 0; j0 < n; j0 += kPrefillChunk) {
+    const int cnt = std::min(kPrefillChunk, n - j0);
+    Stage* st = c->stage_h;
+    st->flags = kFlagForce | kFlagFirst;
+    st->kmax = cnt - 1;
+    st->k[0] = cnt - 1;
+    st->first[0] = tokens[j0];
+    st->step[0] = 0;
+    for (int j = 1; j < cnt; ++j) st->draft[j - 1] = tokens[j0 + j];
+    HIPCHK(hipMemcpyAsync(c->stage_d, st, stage_bytes(1, cnt - 1), hipMemcpyHostToDevice, s));
+    hipError_t e = enqueue_forward(c, Run{1, cnt, seq, cnt - 1, nullptr, false});
+    if (e != hipSuccess) return fail(SF_E_HIP, std::string("prefill forward: ") + hipGetErrorString(e));
+    HIPCHK(hipStreamSynchronize(s));  // the pinned stage block is reused by the next chunk
+    last_cnt = cnt;
+  }
+  HIPCHK(hipMemcpy(c->res_h, c->res_d, (1 + last_cnt) * 4, hipMemcpyDeviceToHost));
+  c->len_h[seq] = n;
+  c->len_hi[seq] = n;
+  int nxt = 0;
+  if (m->d.has_head) {
+    nxt = c->res_h[1 + last_cnt - 1];
+    c->next_h[seq] = nxt;
+  }
+  if (next_token) *next_token = nxt;
+  return SF_OK;
+}
+
+extern "C" sf_status sf_rollback(sf_cache* c, int32_t seq, int32_t pos) {
+  if (!c) return fail(SF_E_ARG, "cache is NULL");
+  if (seq < 0 || seq >= c->B) return fail(SF_E_ARG, "seq out of range");
+  if (c->dirty) {
+    if (sf_status st = refresh(c)) return st;
+  }
+  if (pos < 0 || pos > c->len_h[seq]) return fail(SF_E_STATE, "rollback position outside 0..length");
+  HIPCHK(launch_set_state(c->len, c->next, seq, pos, 0, 1, c->m->stream));
+  c->len_h[seq] = pos;
+  c->len_hi[seq] = pos;
+  return SF_OK;
+}
+
+extern "C" sf_status sf_set_next(sf_cache* c, int32_t seq, int32_t token) {
+  if (!c) return fail(SF_E_ARG, "cache is NULL");
+  if (seq < 0 || seq >= c->B) return fail(SF_E_ARG, "seq out of range");
+  if (token < 0 || token >= c->m->V) return fail(SF_E_ARG, "token outside [0,V)");
+  HIPCHK(launch_set_state(c->len, c->next, seq, 0, token, 2, c->m->stream));
+  c->next_h[seq] = token;
+  return SF_OK;
+}
+
+extern "C" sf_status sf_cache_state(sf_cache* c, int32_t seq, int32_t* length, int32_t* next_token) {
+  if (!c) return fail(SF_E_ARG, "cache is NULL");
+  if (seq < 0 || seq >= c->B) return fail(SF_E_ARG, "seq out of range");
+  if (sf_status st = refresh(c)) return st;
+  if (length) *length = c->len_h[seq];
+  if (next_token) *next_token = c->next_h[seq];
+  return SF_OK;
+}
+
+extern "C" sf_status sf_sync(sf_cache* c) {
+  if (!c) return fail(SF_E_ARG, "cache is NULL");
+  return refresh(c);
+}
+
+extern "C" sf_status sf_draft_step(sf_cache* c, int32_t n_steps, int32_t* tokens) {
+  if (!c) return fail(SF_E_ARG, "cache is NULL");
+  if (!c->m->d.has_head || !c->gx_draft) return fail(SF_E_STATE, "draft steps need a stack with a head");
+  if (n_steps < 1 || n_steps > kMaxDraftSteps) return fail(SF_E_ARG, "n_steps must be in 1..256");
+  if (c->dirty) {
+    if (sf_status st = refresh(c)) return st;
+  }
+  for (int b = 0; b < c->B; ++b)
+    if (c->len_h[b] + n_steps > c->cap) return fail(SF_E_CAPACITY, "length + n_steps exceeds capacity");
+  hipStream_t s = c->m->stream;
+  Stage* st = c->stage_h;
+  st->flags = 0;
+  st->kmax = 0;
+  for (int b = 0; b < c->B; ++b) { st->k[b] = 0; st->step[b] = 0; }
+  HIPCHK(hipMemcpyAsync(c->stage_d, st, stage_bytes(c->B, 0), hipMemcpyHostToDevice, s));
+  for (int i = 0; i < n_steps; ++i) HIPCHK(hipGraphLaunch(c->gx_draft, s));
+  HIPCHK(hipMemcpyAsync(c->dout_h, c->dout_d, (size_t)c->B * kMaxDraftSteps * 4, hipMemcpyDeviceToHost, s));
+  HIPCHK(hipStreamSynchronize(s));
+  for (int b = 0; b < c->B; ++b) {
+    for (int i = 0; i < n_steps; ++i)
+      if (tokens) tokens[b * n_steps + i] = c->dout_h[b * kMaxDraftSteps + i];
+    c->len_h[b] += n_steps;
+    c->next_h[b] = c->dout_h[b * kMaxDraftSteps + n_steps - 1];
+  }
+  c->len_hi = c->len_h;
+  return SF_OK;
+}
+
+extern "C" int32_t sf_ngram_propose(const int32_t* hist, int32_t n_hist, int32_t min_n, int32_t max_n,
+                                    int32_t k_max, int32_t* out) {
+  if ((!hist && n_hist > 0) || n_hist < 0 || min_n < 1 || max_n < min_n || k_max < 0 || (!out && k_max > 0))
+    return fail(SF_E_ARG, "bad n-gram arguments");
+  for (int n = max_n; n >= min_n; --n) {
+    if (n_hist < n + 1) continue;
+    const int32_t* suf = hist + n_hist - n;
+    for (int j = n_hist - n - 1; j >= 0; --j) {
+      if (memcmp(hist + j, suf, (size_t)n * sizeof(int32_t)) == 0) {
+        const int cnt = std::min(k_max, n_hist - (j + n));
+        for (int i = 0; i < cnt; ++i) out[i] = hist[j + n + i];
+        return cnt;
+      }
+    }
+  }
+  return 0;
+}
+
+extern "C" sf_status sf_kv_write(sf_cache* c, int32_t seq, const void* dev_k, const void* dev_v, int32_t n_pos,
+                                 int32_t src_positions) {
+  if (!c || !dev_k || !dev_v) return fail(SF_E_ARG, "NULL argument");
+  if (seq < 0 || seq >= c->B) return fail(SF_E_ARG, "seq out of range");
+  if (n_pos < 0 || src_positions < n_pos) return fail(SF_E_ARG, "bad n_pos / src_positions");
+  if (n_pos > c->cap) return fail(SF_E_CAPACITY, "n_pos exceeds capacity");
+  if (c->dirty) {
+    if (sf_status st = refresh(c)) return st;
+  }
+  sf_model* m = c->m;
+  hipStream_t s = m->stream;
+  const size_t off = (size_t)seq * c->seq_stride;
+  HIPCHK(launch_copy_kv(c->kpool + off, (uint16_t*)dev_k, (long)c->layer_stride, m->nkv, c->cap, m->dh, m->L, n_pos,
+                        src_positions, 1, s));
+  HIPCHK(launch_copy_kv(c->vpool + off, (uint16_t*)dev_v, (long)c->layer_stride, m->nkv, c->cap, m->dh, m->L, n_pos,
+                        src_positions, 1, s));
+  HIPCHK(launch_set_state(c->len, c->next, seq, n_pos, 0, 1, s));
+  HIPCHK(hipStreamSynchronize(s));
+  c->len_h[seq] = n_pos;
+  c->len_hi[seq] = n_pos;
+  return SF_OK;
+}
+
+extern "C" sf_status sf_kv_read(sf_cache* c, int32_t seq, void* dev_k, void* dev_v, int32_t n_pos,
+                                int32_t dst_positions) {
+  if (!c || !dev_k || !dev_v) return fail(SF_E_ARG, "NULL argument");
+  if (seq < 0 || seq >= c->B) return fail(SF_E_ARG, "seq out of range");
+  if (n_pos < 0 || dst_positions < n_pos || n_pos > c->cap) return fail(SF_E_ARG, "bad n_pos / dst_positions");
+  sf_model* m = c->m;
+  hipStream_t s = m->stream;
+  const size_t off = (size_t)seq * c->seq_stride;
+  HIPCHK(launch_copy_kv(c->kpool + off, (uint16_t*)dev_k, (long)c->layer_stride, m->nkv, c->cap, m->dh, m->L, n_pos,
+                        dst_positions, 0, s));
+  HIPCHK(launch_copy_kv(c->vpool + off, (uint16_t*)dev_v, (long)c->layer_stride, m->nkv, c->cap, m->dh, m->L, n_pos,
+                        dst_positions, 0, s));
+  HIPCHK(hipStreamSynchronize(s));
+  return SF_OK;
+}
+
+extern "C" sf_status sf_time_kernel(sf_cache* c, int32_t kernel, int32_t iters, float* avg_us, double* bytes) {
+  if (!c || !avg_us) return fail(SF_E_ARG, "NULL argument");
+  if (iters < 1 || iters > 100000) return fail(SF_E_ARG, "iters out of range");
+  sf_model* m = c->m;
+  if (kernel < SF_KERNEL_QKV || kernel > SF_KERNEL_LMHEAD) return fail(SF_E_ARG, "unknown kernel");
+  if (kernel == SF_KERNEL_LMHEAD && !m->d.has_head) return fail(SF_E_ARG, "no LM head");
+  if (c->dirty) {
+    if (sf_status st = refresh(c)) return st;
+  }
+  for (int b = 0; b < c->B; ++b)
+    if (c->len_h[b] + c->T > c->cap) return fail(SF_E_CAPACITY, "length + k_max + 1 exceeds capacity");
+  hipStream_t s = m->stream;
+  const int rows = c->B * c->T;
+  double L_total = 0;
+  for (int b = 0; b < c->B; ++b) L_total += c->len_h[b] + c->T;
+  GemmArgs base{};
+  base.rows = rows; base.part = c->gpart; base.counters = c->counters; base.ssq_in = c->ssq;
+  base.nparts_in = m->H / 16; base.eps = m->d.rms_eps; base.T = c->T; base.len = c->len; base.cap = c->cap;
+  base.seq_stride = (long)c->seq_stride; base.rope = c->rope; base.nq = m->nq; base.nkv = m->nkv; base.dh = m->dh;
+  double by = 0;
+  auto launch = [&](int it) -> hipError_t {
+    const int l = it % m->L;
+    const Layer& Ly = m->layers[l];
+    uint16_t* kc = c->kpool + (size_t)l * c->layer_stride;
+    uint16_t* vc = c->vpool + (size_t)l * c->layer_stride;
+    GemmArgs g = base;
+    switch (kernel) {
+      case SF_KERNEL_QKV:
+        g.w = Ly.wqkv; g.a = c->a_h; g.k = m->H; g.kb = m->H / 32; g.nb = m->nb_qkv; g.sp = c->sp_qkv;
+        g.bias = Ly.bqkv; g.q = c->q; g.kc = kc; g.vc = vc;
+        by = (double)(m->Q + 2 * m->KV) * m->H * 2 + (double)rows * (m->H * 2 + m->Q * 4 + 2 * m->KV * 2);
+        return launch_gemm(kEpiQkv, g, s);
+      case SF_KERNEL_ATTENTION: {
+        AttnArgs aa{};
+        aa.q = c->q; aa.kc = kc; aa.vc = vc; aa.seq_stride = (long)c->seq_stride; aa.cap = c->cap; aa.len = c->len;
+        aa.T = c->T; aa.nq = m->nq; aa.nkv = m->nkv; aa.nchunk = c->nchunk;
+        aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)m->dh));
+        aa.part = c->apart; aa.out = c->a_o; aa.rows = rows;
+        by = L_total * 2.0 * m->KV * 2 + (double)rows * (m->Q * 4 + m->Q * 2);
+        return launch_attention(aa, m->dh, c->B, s);
+      }
+      case SF_KERNEL_OPROJ:
+        g.w = Ly.wo; g.a = c->a_o; g.k = m->Q; g.kb = m->Q / 32; g.nb = m->nb_h; g.sp = c->sp_o;
+        g.x = c->x; g.a_next = c->a_h; g.gain_next = Ly.g2; g.ssq_out = c->ssq; g.n_out = m->H;
+        by = (double)m->H * m->Q * 2 + (double)rows * (m->Q * 2 + m->H * (4 + 4 + 2));
+        return launch_gemm(kEpiResid, g, s);
+      case SF_KERNEL_GATEUP:
+        g.w = Ly.wgu; g.a = c->a_h; g.k = m->H; g.kb = m->H / 32; g.nb = m->nb_gu; g.sp = c->sp_gu;
+        g.h = c->a_f; g.ffn = m->F;
+        by = (double)2 * m->F * m->H * 2 + (double)rows * (m->H * 2 + m->F * 2);
+        return launch_gemm(kEpiSwiglu, g, s);
+      case SF_KERNEL_DOWN:
+        g.w = Ly.wd; g.a = c->a_f; g.k = m->F; g.kb = m->F / 32; g.nb = m->nb_h; g.sp = c->sp_d;
+        g.x = c->x; g.a_next = c->a_h; g.gain_next = Ly.g1; g.ssq_out = c->ssq; g.n_out = m->H;
+        by = (double)m->H * m->F * 2 + (double)rows * (m->F * 2 + m->H * (4 + 4 + 2));
+        return launch_gemm(kEpiResid, g, s);
+      default:
+        g.w = m->head; g.a = c->a_h; g.k = m->H; g.kb = m->H / 32; g.nb = m->nb_head; g.sp = c->sp_head;
+        g.amax = c->amax; g.vocab = m->V;
+        by = (double)m->V * m->H * 2 + (double)rows * (m->H * 2 + m->nb_head * 8);
+        return launch_gemm(kEpiArgmax, g, s);
+    }
+  };
+  hipError_t e = launch(0);  // warm-up
+  if (e != hipSuccess) return fail(SF_E_HIP, std::string("launch: ") + hipGetErrorString(e));
+  HIPCHK(hipEventRecord(c->ev0, s));
+  for (int it = 0; it < iters; ++it) {
+    e = launch(it + 1);
+    if (e != hipSuccess) return fail(SF_E_HIP, std::string("launch: ") + hipGetErrorString(e));
+  }
+  HIPCHK(hipEventRecord(c->ev1, s));
+  HIPCHK(hipEventSynchronize(c->ev1));
+  float ms = 0;
+  HIPCHK(hipEventElapsedTime(&ms, c->ev0, c->ev1));
+  *avg_us = ms * 1000.f / iters;
+  if (bytes) *bytes = by;
+  return SF_OK;
+}
+
+extern "C" const char* sf_last_error(void) { return g_err.c_str(); }

@@ -1,0 +1,132 @@
+// Internal declarations shared by the kernels and the host runtime of libsf.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sf {
+
+constexpr int kWave = 64;
+constexpr int kGemmWaves = 8;                 // waves per GEMM workgroup
+constexpr int kGemmThreads = kGemmWaves * kWave;
+constexpr int kTileN = 16;                    // output features per MFMA tile
+constexpr int kTileK = 32;                    // reduction depth per MFMA tile
+constexpr int kBatch = 16;                    // weight tiles a wave loads before using them
+constexpr int kChunk = 64;                    // attention: KV positions per chunk (position aligned)
+constexpr int kAttnRows = 16;                 // attention: query rows per workgroup
+constexpr int kMaxRows = 64;                  // rows (sequences x positions) per pass
+constexpr int kMaxSeqs = 64;
+constexpr int kMaxK = 16;                     // drafts per sequence (k_max <= 15, T <= 16)
+constexpr int kMaxDraftSteps = 256;
+constexpr int kPrefillChunk = 64;
+
+// Stage flags (device side).
+constexpr int kFlagNoCommit = 1;
+constexpr int kFlagForce = 2;
+constexpr int kFlagFirst = 8;                 // row 0 of each sequence takes stage.first, not the pending token
+
+// Staging block: one host->device copy per pass.
+struct Stage {
+  int32_t flags;
+  int32_t kmax;
+  int32_t pad[2];
+  int32_t k[kMaxSeqs];
+  int32_t first[kMaxSeqs];
+  int32_t step[kMaxSeqs];
+  int32_t draft[kMaxSeqs * kMaxK];
+};
+
+enum Epi { kEpiQkv = 0, kEpiResid = 1, kEpiSwiglu = 2, kEpiArgmax = 3 };
+
+struct GemmArgs {
+  const uint4* w;          // packed weight tiles [nb][kb][64 lanes] x 16 B
+  const uint16_t* a;       // bf16 activations [rows_pad][k]
+  int k, kb, nb, rows, sp; // in-features, k tiles, n blocks, valid rows, workgroups per n block
+  float* part;             // split partials [nb][sp][mt*256]
+  int* counters;           // [nb], zero between launches
+  // RMSNorm folded into the consumer: row scale = 1/sqrt(sum(ssq_in[r][*])/k + eps)
+  const float* ssq_in;
+  int nparts_in;
+  float eps;
+  // positions
+  int T;                   // positions per sequence; row r -> sequence r/T, slot r%T
+  const int32_t* len;      // committed length per sequence
+  int cap;
+  // kEpiQkv
+  const float* bias;       // packed bias, fp32 [nb*16]
+  float* q;                // [rows][nq][dh]
+  uint16_t* kc;            // layer base of K pool, [seq][nkv][cap][dh]
+  uint16_t* vc;
+  long seq_stride;         // elements between sequences in the pool
+  const float2* rope;      // (cos, sin) [cap][dh/2]
+  int nq, nkv, dh;
+  // kEpiResid
+  float* x;                // residual [rows][n_out]
+  uint16_t* a_next;        // bf16(x * gain_next) [rows][n_out]
+  const float* gain_next;  // [n_out]
+  float* ssq_out;          // [rows][nb]
+  uint16_t* hidden;        // optional bf16(x) [rows][n_out]
+  int n_out;
+  // kEpiSwiglu
+  uint16_t* h;             // [rows][ffn]
+  int ffn;
+  // kEpiArgmax
+  float2* amax;            // [rows][nb] (value, index bits)
+  float* logits;           // optional fp32 [rows][vocab]
+  int vocab;
+};
+
+struct EmbedArgs {
+  const uint16_t* embed;   // [V][H]
+  const Stage* stage;
+  const int32_t* len;
+  const int32_t* next;
+  const float* gain;       // first layer's ln1
+  float* x;
+  uint16_t* a;
+  float* ssq;              // [rows][H/16]
+  int rows, T, H, V, kmax;
+};
+
+struct AttnArgs {
+  const float* q;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  long seq_stride;
+  int cap;
+  const int32_t* len;
+  int T, nq, nkv, nchunk;
+  float scale_log2;        // log2(e)/sqrt(dh)
+  float* part;             // [seq][nkv][nchunk][T*G][dh+2]
+  uint16_t* out;           // combine output bf16 [rows][nq*dh]
+  int rows;
+};
+
+struct AcceptArgs {
+  const float2* amax;      // [rows][nparts]
+  int nparts;
+  Stage* stage;
+  int32_t* len;
+  int32_t* next;
+  int32_t* result;         // accepted[B] then target[B][T]
+  int32_t* draft_out;      // [B][kMaxDraftSteps]
+  int B, T, has_head;
+};
+
+// Launchers (kernels.hip).
+hipError_t launch_gemm(int epi, const GemmArgs& g, hipStream_t s);
+hipError_t launch_embed(const EmbedArgs& e, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, int dh, int B, hipStream_t s);
+hipError_t launch_accept(const AcceptArgs& a, hipStream_t s);
+hipError_t launch_pack(uint4* dst, const uint16_t* const* rowptr, int nb, int kb, hipStream_t s);
+hipError_t launch_gather_f32(float* dst, const uint16_t* const* eltptr, int n, hipStream_t s);
+hipError_t launch_rope_table(float2* rope, int cap, int half, double base, hipStream_t s);
+hipError_t launch_set_state(int32_t* len, int32_t* next, int seq, int new_len, int new_next, int which,
+                            hipStream_t s);
+hipError_t launch_stage_device(Stage* stage, const int32_t* draft, const int32_t* k, int B, int kmax,
+                               int flags, hipStream_t s);
+hipError_t launch_copy_kv(uint16_t* pool, uint16_t* src, long pool_layer_stride, int nkv, int cap,
+                          int dh, int n_layers, int n_pos, int src_positions, int to_pool, hipStream_t s);
+
+}  // namespace sf

@@ -1,0 +1,220 @@
+"""GPU parity of the whole verify path on the two-layer decoder, through the C ABI.
+
+Workload: 2 layers, hidden 256, 4 query / 2 KV heads, head_dim 64, FFN 1024,
+vocab 4096, RoPE base 10000; a 64-token uniform prompt; 16 verify steps with
+K=4 drafts, each the oracle's greedy continuation with one token replaced at a
+seeded slot (4 = none); a 128-position static cache.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import GAP, LOGIT_TOL, Pair, accepted_decided, check_targets, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+S = synth.TINY
+
+
+@pytest.fixture(scope="module")
+def pair():
+    need_gpu()
+    say("[tiny] building engine")
+    p = Pair(S, 1, capacity=128, k_max=4)
+    yield p
+    p.close()
+
+
+def _reset(pair, prompt):
+    sfb, eng = pair.sfb, pair.eng
+    c = oracle.KVCache(S, 128)
+    oracle.prefill(pair.model, c, prompt)
+    nxt = sfb.sf_prefill(eng.cache, 0, prompt)
+    return c, nxt
+
+
+def test_prefill_matches_oracle(pair):
+    sfb, eng = pair.sfb, pair.eng
+    for n in (1, 5, 64, 100, 127):
+        say(f"[tiny] prefill n={n}")
+        prompt = synth.prompt_ids(S.vocab, n, 2000 + n)
+        c = oracle.KVCache(S, 128)
+        z = oracle.prefill(pair.model, c, prompt)
+        nxt = sfb.sf_prefill(eng.cache, 0, prompt)
+        gap = oracle.top_gap(z[-1:])[0].item()
+        if gap > GAP:
+            assert nxt == c.next_token, (n, nxt, c.next_token, gap)
+        assert sfb.sf_cache_state(eng.cache, 0) == (n, nxt)
+
+
+def test_c1_lockstep_16_steps(pair):
+    """The tiny workload end to end: eager debug pass (logits), graph pass (accepted,
+    targets), and the oracle, step by step; both sides are then forced to the oracle's
+    (length, pending token) so a near-tie cannot desynchronise them."""
+    sfb, eng, K = pair.sfb, pair.eng, pair.K
+    prompt = synth.prompt_ids(S.vocab, 64, synth.seeds(1)["prompt"])
+    c, nxt = _reset(pair, prompt)
+    if nxt != c.next_token:
+        sfb.sf_set_next(eng.cache, 0, c.next_token)
+    rng = np.random.default_rng(synth.seeds(1)["draft"])
+    logits = torch.empty((K + 1, S.vocab), dtype=torch.float32, device="cuda")
+    n_exact = n_tot = 0
+    m_checked = 0
+    worst = 0.0
+    for step in range(16):
+        L = c.length
+        cont = oracle.greedy_continuation(pair.model, c, K)
+        draft, p = synth.corrupt_draft(cont, S.vocab, rng)
+        say(f"[tiny] step {step} L={L} p={p}")
+        acc_e, tgt_e = sfb.sf_verify(eng.cache, draft[None], None, sfb.SF_DEBUG_LOGITS | sfb.SF_NO_COMMIT,
+                                     dev_out=logits)
+        torch.cuda.synchronize()
+        acc_g, tgt_g = sfb.sf_verify(eng.cache, draft[None], None, sfb.SF_NO_COMMIT)
+        # The graph replays the same kernels as the eager pass: identical results.
+        assert acc_g[0] == acc_e[0] and (tgt_g == tgt_e).all()
+        r = oracle.verify(pair.model, c, draft, K)
+        assert r["accepted"] == p                       # construction of the drafts
+        err = (logits.double().cpu() - r["logits"]).abs().max().item()
+        worst = max(worst, err)
+        assert err <= LOGIT_TOL, (step, err)
+        ne, nt = check_targets(tgt_g[0], r, K)
+        n_exact += ne
+        n_tot += nt
+        if accepted_decided(r, int(acc_g[0]), K):
+            assert acc_g[0] == r["accepted"], (step, acc_g[0], r["accepted"])
+            m_checked += 1
+        # Lockstep: commit the oracle's decision on the GPU.
+        sfb.sf_verify(eng.cache, draft[None], np.array([r["accepted"]]), sfb.SF_FORCE_ACCEPT)
+        sfb.sf_set_next(eng.cache, 0, c.next_token)
+        assert sfb.sf_cache_state(eng.cache, 0) == (c.length, c.next_token)
+    say(f"[tiny] exact-rule slots {n_exact}/{n_tot}, accepted counts checked {m_checked}/16, "
+        f"max |dlogit| {worst:.4g}")
+    assert n_exact >= n_tot // 4
+
+
+def test_replay_is_bitwise_deterministic(pair):
+    sfb, eng, K = pair.sfb, pair.eng, pair.K
+    prompt = synth.prompt_ids(S.vocab, 40, 77)
+    _reset(pair, prompt)
+    d = np.array([[5, 6, 7, 8]], dtype=np.int32)
+    a = torch.empty((K + 1, S.vocab), dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    sfb.sf_verify(eng.cache, d, None, sfb.SF_DEBUG_LOGITS | sfb.SF_NO_COMMIT, dev_out=a)
+    sfb.sf_verify(eng.cache, d, None, sfb.SF_DEBUG_LOGITS | sfb.SF_NO_COMMIT, dev_out=b)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_rollback_and_replay_reproduce_cache_bytes(pair):
+    sfb, eng, K = pair.sfb, pair.eng, pair.K
+    prompt = synth.prompt_ids(S.vocab, 30, 78)
+    _, nxt = _reset(pair, prompt)
+    L0 = 30
+    d = np.array([[11, 12, 13, 14]], dtype=np.int32)
+    acc1, tgt1 = sfb.sf_verify(eng.cache, d, None, sfb.SF_FORCE_ACCEPT)     # commits L0..L0+4
+    shape = (S.n_layers, S.n_kv_heads, 64, S.head_dim)
+    k1 = torch.zeros(shape, dtype=torch.int16, device="cuda")
+    v1 = torch.zeros_like(k1)
+    sfb.sf_kv_read(eng.cache, 0, k1, v1, L0 + 5, 64)
+    junk = np.array([[100, 200, 300, 400]], dtype=np.int32)
+    sfb.sf_verify(eng.cache, junk, None, 0)                                  # more writes
+    sfb.sf_rollback(eng.cache, 0, L0)
+    sfb.sf_set_next(eng.cache, 0, nxt)
+    assert sfb.sf_cache_state(eng.cache, 0) == (L0, nxt)
+    acc2, tgt2 = sfb.sf_verify(eng.cache, d, None, sfb.SF_FORCE_ACCEPT)
+    k2 = torch.zeros_like(k1)
+    v2 = torch.zeros_like(k1)
+    sfb.sf_kv_read(eng.cache, 0, k2, v2, L0 + 5, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(k1, k2) and torch.equal(v1, v2)
+    assert (tgt1 == tgt2).all() and acc1[0] == acc2[0] == 4
+
+
+def test_kv_append_matches_oracle_cache(pair):
+    """The K (after RoPE) and V the pass appends equal the oracle's, element by element,
+    to a few bf16 ulps."""
+    sfb, eng = pair.sfb, pair.eng
+    prompt = synth.prompt_ids(S.vocab, 50, 79)
+    c, _ = _reset(pair, prompt)
+    shape = (S.n_layers, S.n_kv_heads, 64, S.head_dim)
+    kg = torch.zeros(shape, dtype=torch.int16, device="cuda")
+    vg = torch.zeros_like(kg)
+    sfb.sf_kv_read(eng.cache, 0, kg, vg, 50, 64)
+    torch.cuda.synchronize()
+    kg = kg.cpu().view(torch.bfloat16).double()[:, :, :50]
+    vg = vg.cpu().view(torch.bfloat16).double()[:, :, :50]
+    ko = c.k[:, :, :50].double()
+    vo = c.v[:, :, :50].double()
+    assert (kg - ko).abs().max().item() <= 0.02 * max(1.0, ko.abs().max().item())
+    assert (vg - vo).abs().max().item() <= 0.02 * max(1.0, vo.abs().max().item())
+
+
+def test_draft_steps_match_oracle_greedy(pair):
+    sfb, eng = pair.sfb, pair.eng
+    prompt = synth.prompt_ids(S.vocab, 48, 80)
+    c, nxt = _reset(pair, prompt)
+    if nxt != c.next_token:
+        sfb.sf_set_next(eng.cache, 0, c.next_token)
+    toks = sfb.sf_draft_step(eng.cache, 12)[0]
+    cc = c.copy()
+    for i in range(12):
+        r = oracle.verify(pair.model, cc, [], 0)
+        if r["gap"][0] <= GAP:
+            say(f"[tiny] draft loop: near-tie at step {i}, comparison stops")
+            break
+        assert int(toks[i]) == cc.next_token, (i, toks[:i + 1], cc.next_token)
+    assert sfb.sf_cache_state(eng.cache, 0)[0] == 48 + 12
+
+
+def test_gpu_speculative_equals_gpu_greedy(pair):
+    """I1 on the GPU itself: verify passes and single-token steps produce bitwise-equal
+    decisions, so speculative decoding emits exactly the greedy stream."""
+    sfb, eng, K = pair.sfb, pair.eng, pair.K
+    prompt = synth.prompt_ids(S.vocab, 20, 81)
+    sfb.sf_prefill(eng.cache, 0, prompt)
+    greedy = sfb.sf_draft_step(eng.cache, 40)[0].tolist()
+    nxt0 = sfb.sf_prefill(eng.cache, 0, prompt)
+    stream = [nxt0] + greedy
+    # Speculate with drafts taken from the greedy stream, some of them corrupted.
+    rng = np.random.default_rng(5)
+    emitted = [nxt0]
+    pos = 0
+    while len(emitted) < 30:
+        d = np.array(stream[pos + 1:pos + 1 + K], dtype=np.int32)
+        j = int(rng.integers(0, K + 1))
+        if j < K:
+            d[j] = (d[j] + 1) % S.vocab
+        acc, tgt = sfb.sf_verify(eng.cache, d[None])
+        M = int(acc[0])
+        assert M == j if j < K else M == K
+        emitted += [int(t) for t in d[:M]] + [int(tgt[0][M])]
+        pos += M + 1
+    assert emitted[:30] == stream[:30]
+
+
+def test_errors_leave_state_unchanged(pair):
+    sfb, eng, K = pair.sfb, pair.eng, pair.K
+    sfb.sf_prefill(eng.cache, 0, synth.prompt_ids(S.vocab, 124, 82))
+    st = sfb.sf_cache_state(eng.cache, 0)
+    with pytest.raises(sfb.SFError) as e:
+        sfb.sf_verify(eng.cache, np.zeros((1, K), np.int32))        # 124 + 5 > 128
+    assert e.value.code == sfb.SF_E_CAPACITY
+    with pytest.raises(sfb.SFError) as e:
+        sfb.sf_rollback(eng.cache, 0, 125)
+    assert e.value.code == sfb.SF_E_STATE
+    with pytest.raises(sfb.SFError) as e:
+        sfb.sf_set_next(eng.cache, 0, S.vocab)
+    assert e.value.code == sfb.SF_E_ARG
+    sfb.sf_rollback(eng.cache, 0, 100)
+    with pytest.raises(sfb.SFError) as e:
+        sfb.sf_verify(eng.cache, np.array([[1, 2, S.vocab, 3]], np.int32))
+    assert e.value.code == sfb.SF_E_ARG
+    with pytest.raises(sfb.SFError) as e:
+        sfb.sf_verify(eng.cache, np.zeros((1, K), np.int32), np.array([K + 1]))
+    assert e.value.code == sfb.SF_E_ARG
+    with pytest.raises(sfb.SFError) as e:
+        sfb.sf_draft_step(eng.cache, 29)                              # 100 + 29 > 128
+    assert e.value.code == sfb.SF_E_CAPACITY
+    assert sfb.sf_cache_state(eng.cache, 0) == (100, st[1])
