@@ -1,0 +1,216 @@
+"""Verify-step benchmark on one MI355X.
+
+Workload: the full Qwen2.5-7B-shape stack (28 layers, hidden 3584, 28 q / 4 KV
+heads, head_dim 128, SwiGLU 18944, vocab 152064, untied head), random-init bf16
+weights, verifying K=8 drafts (9 positions) plus argmax and accept at contexts
+512, 2048 and 8192.  One step = one verify at each of the three contexts.  The
+cache holds seeded synthetic K/V for the context; drafts come from the
+prompt-lookup proposer over a seeded repeating history.  Every timed pass runs
+with SF_NO_COMMIT so each step verifies at exactly the nominal context.
+
+Prints one JSON line (see the field list at the end of main()).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+K = 8
+CONTEXTS = (512, 2048, 8192)
+CAPACITY = 8192 + 16
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--kernel-iters", type=int, default=56)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; --gpus above 1 is not supported "
+                                   "(the verify path is single-GPU: no collectives, no sharding)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import speculative_decoding_verification_decode_amd as sfb
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU"}))
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    S = synth.QWEN7B
+    sd = synth.seeds(4)
+
+    t0 = time.time()
+    w = synth.model_weights(S, sd["weights"])
+    log(f"weights generated in {time.time() - t0:.1f}s")
+    desc = sfb.desc_from_shape(S)
+    stream = torch.cuda.Stream()
+    tensors, ptrs = sfb.upload_weights(w, desc)
+    torch.cuda.synchronize()
+    model = sfb.sf_model_create(desc, ptrs, stream.cuda_stream)
+    del tensors, ptrs
+    torch.cuda.synchronize()
+    log("model packed")
+
+    kbits, vbits = synth.synthetic_kv(S, max(CONTEXTS), sd["kv"])
+    kdev = torch.from_numpy(kbits.view(np.int16)).cuda()
+    vdev = torch.from_numpy(vbits.view(np.int16)).cuda()
+    hist = synth.lookup_history(S.vocab, max(CONTEXTS) + 1, sd["prompt"])
+
+    caches, drafts, ks = {}, {}, {}
+    for ctx in CONTEXTS:
+        c = sfb.sf_cache_alloc(model, 1, CAPACITY, K)
+        sfb.sf_kv_write(c, 0, kdev, vdev, ctx, max(CONTEXTS))
+        sfb.sf_set_next(c, 0, int(hist[ctx]))
+        prop = sfb.sf_ngram_propose(hist[:ctx + 1], 2, 4, K)
+        d = np.zeros(K, dtype=np.int32)
+        d[:len(prop)] = prop
+        caches[ctx] = c
+        drafts[ctx] = torch.from_numpy(d).cuda()
+        ks[ctx] = torch.tensor([len(prop)], dtype=torch.int32, device="cuda")
+    del kdev, vdev
+    torch.cuda.synchronize()
+    log("caches ready")
+
+    def step():
+        for ctx in CONTEXTS:
+            sfb.sf_verify_device(caches[ctx], drafts[ctx], ks[ctx], sfb.SF_NO_COMMIT)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Whole-job timing: K steps between device-wide synchronisations.
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dev_ms = ev0.elapsed_time(ev1)
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_step = len(CONTEXTS) * (K + 1)
+    value = tokens_per_step * args.steps / wall
+
+    # Per-context device time (HIP events on the library stream).
+    per_ctx = {}
+    for ctx in CONTEXTS:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        n = max(5, args.steps)
+        e0.record(stream)
+        for _ in range(n):
+            sfb.sf_verify_device(caches[ctx], drafts[ctx], ks[ctx], sfb.SF_NO_COMMIT)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        per_ctx[ctx] = {"ms": round(ms, 4), "verify_tokens_per_s": round((K + 1) / ms * 1e3, 1)}
+
+    # Host-inclusive latency of one synchronous verify (H2D drafts, replay, D2H results).
+    c512 = caches[CONTEXTS[0]]
+    hd = drafts[CONTEXTS[0]].cpu().numpy()[None]
+    hk = ks[CONTEXTS[0]].cpu().numpy()
+    for _ in range(3):
+        sfb.sf_verify(c512, hd, hk, sfb.SF_NO_COMMIT)
+    t0 = time.perf_counter()
+    nh = 10
+    for _ in range(nh):
+        acc, tgt = sfb.sf_verify(c512, hd, hk, sfb.SF_NO_COMMIT)
+    host_ms = (time.perf_counter() - t0) * 1e3 / nh
+
+    # Per-kernel timing at the verify shape, cycling layers so weights stream from HBM.
+    kern = {}
+    names = {sfb.SF_KERNEL_QKV: "qkv", sfb.SF_KERNEL_ATTENTION: "attention", sfb.SF_KERNEL_OPROJ: "o_proj",
+             sfb.SF_KERNEL_GATEUP: "gate_up", sfb.SF_KERNEL_DOWN: "down", sfb.SF_KERNEL_LMHEAD: "lm_head"}
+    for kid, nm in names.items():
+        us, by = sfb.sf_time_kernel(c512, kid, args.kernel_iters)
+        kern[nm] = {"us": round(us, 3), "bytes": int(by), "GBps": round(by / us / 1e3, 1)}
+    layer_bytes = sum(kern[n]["bytes"] for n in ("qkv", "o_proj", "gate_up", "down"))
+    # Algorithmic bytes of one verify: every layer's weights and activations once, the
+    # LM head once, and K/V of positions 0..ctx+K read once per layer.
+    kv_bytes = {ctx: (ctx + K + 1) * 2 * S.kv_dim * 2 * S.n_layers for ctx in CONTEXTS}
+    verify_bytes = {ctx: S.n_layers * layer_bytes + kern["lm_head"]["bytes"] + kv_bytes[ctx] for ctx in CONTEXTS}
+    for ctx in CONTEXTS:
+        per_ctx[ctx]["alg_GBps"] = round(verify_bytes[ctx] / (per_ctx[ctx]["ms"] * 1e-3) / 1e9, 1)
+        per_ctx[ctx]["frac_peak"] = round(per_ctx[ctx]["alg_GBps"] / HBM_PEAK_GBS, 4)
+    total_bytes = sum(verify_bytes.values())
+    g = kern["gate_up"]
+    roofline = {"bound": "hbm", "kernel": "k_gemm<SWIGLU> (gate/up projection, 9 rows)",
+                "achieved": g["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(g["GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "launch_us": g["us"], "alg_bytes_per_launch": g["bytes"]}
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        ctx = CONTEXTS[0]
+        m = oracle.Model(S, w)
+        oc = oracle.KVCache(S, ctx + K + 1)
+        oc.load(kbits, vbits, ctx, next_token=int(hist[ctx]))
+        d = drafts[ctx].cpu().numpy()
+        kk = int(ks[ctx].item())
+        t0 = time.perf_counter()
+        r = oracle.verify(m, oc, d, kk, commit=False)
+        sec = time.perf_counter() - t0
+        # Sanity: the GPU pass at this context agrees with the oracle where the gap rule applies.
+        gap = r["gap"].numpy()
+        agree = sum(1 for j in range(K + 1) if gap[j] > 0.1 and int(tgt[0][j]) == int(r["target"][j]))
+        under = int((gap > 0.1).sum())
+        cpu = {"value": round((K + 1) / sec, 4), "unit": "verify tokens/s", "cores": torch.get_num_threads(),
+               "kind": "oracle", "seconds": round(sec, 2),
+               "sample": f"one verify (9 positions) of the full 28-layer stack + head at context {ctx}, "
+                         f"float64 torch on host; GPU targets agree on {agree}/{under} gap>0.1 slots"}
+
+    out = {
+        "metric": "verify tokens/s (Qwen2.5-7B-shape, K=8, 1 GPU)",
+        "value": round(value, 2),
+        "unit": "verify tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen2.5-7b-shape full stack verify, K=8 drafts (9 positions), 1 sequence, "
+                               "contexts 512/2048/8192, random-init bf16 weights, synthetic KV, n-gram drafts",
+                   "K": K, "contexts": list(CONTEXTS), "n_seqs": 1, "capacity": CAPACITY,
+                   "step": "one verify at each context"},
+        "device_ms_per_step": round(dev_ms / args.steps, 4),
+        "hbm_GBps": round(total_bytes * args.steps / wall / 1e9, 1),
+        "hbm_frac_peak": round(total_bytes * args.steps / wall / 1e9 / HBM_PEAK_GBS, 4),
+        "per_context": {str(k): v for k, v in per_ctx.items()},
+        "host_inclusive_verify_ms_ctx512": round(host_ms, 4),
+        "kernels_at_verify_shape": kern,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+    for c in caches.values():
+        sfb.sf_cache_free(c)
+    sfb.sf_model_free(model)
+
+
+if __name__ == "__main__":
+    main()

@@ -3,8 +3,8 @@
 // Pass structure per layer (rows = sequences x positions, typically 1 x 9):
 //   k_gemm<QKV>    weight-streaming MFMA GEMM; epilogue: RMSNorm row scale, bias,
 //                  RoPE, K/V append into the static cache at position len+slot
-//   k_attn         split-KV causal GQA attention over position-aligned chunks
-//   k_combine      fixed-order merge of the chunk partials -> bf16 attention output
+//   k_attn         split-KV causal GQA attention (MFMA) over position-aligned spans
+//   k_combine      fixed-order merge of the span partials -> bf16 attention output
 //   k_gemm<RESID>  O projection; epilogue: residual add, next RMSNorm's gain and
 //                  sum-of-squares partials
 //   k_gemm<SWIGLU> gate/up projection; epilogue: row scale, silu(gate)*up
@@ -32,10 +32,21 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Activations feeding an MFMA are carried as two bf16 values, hi = bf16(v) and
+// lo = bf16(v - hi) (about 16 significant bits), stored as rows r and rows + r of the
+// operand matrix; the weights are bf16 and the products accumulate in fp32.
+__device__ __forceinline__ void store_split(uint16_t* base, size_t row_stride, int rows, int r, int col, float v) {
+  const uint16_t hi = f2bf(v);
+  base[(size_t)r * row_stride + col] = hi;
+  base[(size_t)(rows + r) * row_stride + col] = f2bf(v - bf2f(hi));
+}
+
 // Word 3 of a raw buffer resource on gfx9-family GPUs (gfx950 included).
 constexpr int kBufferWord3 = 0x00020000;
 // RMSNorm sum-of-squares partials (one per 16 columns) read per lane: hidden <= 64*16*4.
 constexpr int kSsqPerLane = 4;
+// Weight tiles per pipelined half-batch (single m tile).
+constexpr int kHalf = 8;
 // Cache policy of the weight stream: non-temporal (each weight byte is read once per pass).
 constexpr int kCacheStream = 2;
 
@@ -46,23 +57,25 @@ __device__ __forceinline__ int tile_idx(int nl, int m) {
 }
 
 // ----------------------------------------------------------------------------------------------
-// Skinny GEMM: Y[m][n] = sum_k A[m][k] * W[n][k] for m < rows (<= 16*MT).
+// Skinny GEMM: Y[m][n] = sum_k A[m][k] * W[n][k] for m < rows, where A has 2*rows rows
+// (hi parts, then lo parts) and Y[m] = acc[m] + acc[rows + m]; 2*rows <= 16*MT.
 // W is packed in 16x32 tiles, one 16-byte bf16x8 fragment per lane, so a wave's load of one
 // tile is one contiguous kilobyte.  Each wave streams its share of the k tiles of one
 // n block, all loads of a batch issued before the first MFMA.  Waves are combined in LDS;
 // with sp > 1 the workgroups of one n block are combined by the last one to finish, in
 // fixed order, so results do not depend on scheduling.
-template <int EPI, int MT>
-__global__ __launch_bounds__(kGemmThreads) void k_gemm(const GemmArgs g) {
-  __shared__ float red[kGemmWaves][MT * 256];
+template <int EPI, int MT, int NW>
+__global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
+  constexpr int kThreads = NW * 64;
+  __shared__ float red[NW][MT * 256];
   __shared__ float tile[MT * 256];
-  __shared__ float rscale[MT * 16];
+  __shared__ float rscale[MT * 8 + NW];
   __shared__ int last_flag;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int nb = blockIdx.x / g.sp, spi = blockIdx.x - nb * g.sp;
-  const int U = g.sp * kGemmWaves, u = spi * kGemmWaves + wave;
+  const int U = g.sp * NW, u = spi * NW + wave;
   const int kt0 = (int)(((long)g.kb * u) / U), kt1 = (int)(((long)g.kb * (u + 1)) / U);
 
   constexpr bool kScaled = (EPI == kEpiQkv || EPI == kEpiSwiglu || EPI == kEpiArgmax);
@@ -70,14 +83,15 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const GemmArgs g) {
   // l, l+64, l+128, l+192 in that order, then the wave reduces across lanes: the same
   // order for a row whatever the number of rows.  The loads are issued here and summed
   // after the weight stream, so they never delay it.
-  constexpr int kRowsPerWave = (MT * 16) / kGemmWaves;
+  constexpr int kRealRows = MT * 8;
+  constexpr int kRowsPerWave = (kRealRows + NW - 1) / NW;
   float ssq_v[kRowsPerWave][kSsqPerLane];
   if constexpr (kScaled) {
     const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
         (void*)g.ssq_in, (short)0, g.rows * g.nparts_in * 4, kBufferWord3);
 #pragma unroll
     for (int j = 0; j < kRowsPerWave; ++j) {
-      const int m = wave + kGemmWaves * j;
+      const int m = wave + NW * j;
 #pragma unroll
       for (int i = 0; i < kSsqPerLane; ++i) {
         const int p = lane + 64 * i;
@@ -96,25 +110,69 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const GemmArgs g) {
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(g.w + (size_t)nb * g.kb * 64), (short)0, kt1 * 1024, kBufferWord3);
   const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)g.a, (short)0, kMaxRows * g.k * 2, kBufferWord3);
+      (void*)g.a, (short)0, 2 * kMaxRows * g.k * 2, kBufferWord3);
+  // Lanes whose activation row is past 2*rows read zeros without a memory access (below).
+  const int ext_rows = 2 * g.rows;
   const int a_lane = ((lane & 15) * g.k + (lane >> 4) * 8) * 2;
 
-  for (int kt = kt0; kt < kt1; kt += kBatch) {
-    u32x4 w[kBatch];
+  if constexpr (MT <= 2) {
+    // Up to two m tiles: two 8-tile batches in flight, the next batch's weights and
+    // activations requested before the current batch's MFMAs, so a long k range streams
+    // continuously.
+    auto load = [&](int kt, u32x4 (&w)[kHalf], u32x4 (&a)[MT][kHalf]) {
 #pragma unroll
-    for (int t = 0; t < kBatch; ++t)
-      w[t] = __builtin_amdgcn_raw_buffer_load_b128(wres, (kt + t) * 1024 + lane * 16, 0, kCacheStream);
+      for (int t = 0; t < kHalf; ++t)
+        w[t] = __builtin_amdgcn_raw_buffer_load_b128(wres, (kt + t) * 1024 + lane * 16, 0, kCacheStream);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      u32x4 a[kBatch];
+      for (int mt = 0; mt < MT; ++mt) {
+        const bool row_ok = mt * 16 + (lane & 15) < ext_rows;
 #pragma unroll
-      for (int t = 0; t < kBatch; ++t)
-        a[t] = __builtin_amdgcn_raw_buffer_load_b128(ares, a_lane + (mt * 16 * g.k + (kt + t) * kTileK) * 2, 0, 0);
-      // Keep every load of the batch ahead of the first MFMA (memory-level parallelism).
+        for (int t = 0; t < kHalf; ++t) {
+          const int off = (row_ok && kt + t < kt1) ? a_lane + (mt * 16 * g.k + (kt + t) * kTileK) * 2 : 0x7FFFFFF0;
+          a[mt][t] = __builtin_amdgcn_raw_buffer_load_b128(ares, off, 0, 0);
+        }
+      }
+    };
+    auto mma = [&](const u32x4 (&w)[kHalf], const u32x4 (&a)[MT][kHalf]) {
+#pragma unroll
+      for (int t = 0; t < kHalf; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w[t]), as_bf16x8(a[mt][t]), acc[mt], 0, 0, 0);
+    };
+    u32x4 w0[kHalf], w1[kHalf], a0[MT][kHalf], a1[MT][kHalf];
+    load(kt0, w0, a0);
+    for (int kt = kt0; kt < kt1; kt += 2 * kHalf) {
+      load(kt + kHalf, w1, a1);
       __builtin_amdgcn_sched_barrier(0);
+      mma(w0, a0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(kt + 2 * kHalf, w0, a0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(w1, a1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    for (int kt = kt0; kt < kt1; kt += kBatch) {
+      u32x4 w[kBatch];
 #pragma unroll
       for (int t = 0; t < kBatch; ++t)
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w[t]), as_bf16x8(a[t]), acc[mt], 0, 0, 0);
+        w[t] = __builtin_amdgcn_raw_buffer_load_b128(wres, (kt + t) * 1024 + lane * 16, 0, kCacheStream);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const bool row_ok = mt * 16 + (lane & 15) < ext_rows;
+        u32x4 a[kBatch];
+#pragma unroll
+        for (int t = 0; t < kBatch; ++t) {
+          const int off = (row_ok && kt + t < kt1) ? a_lane + (mt * 16 * g.k + (kt + t) * kTileK) * 2 : 0x7FFFFFF0;
+          a[t] = __builtin_amdgcn_raw_buffer_load_b128(ares, off, 0, 0);
+        }
+        // Keep every load of the batch ahead of the first MFMA (memory-level parallelism).
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < kBatch; ++t)
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w[t]), as_bf16x8(a[t]), acc[mt], 0, 0, 0);
+      }
     }
   }
 
@@ -131,22 +189,22 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const GemmArgs g) {
       for (int i = 0; i < kSsqPerLane; ++i) t += ssq_v[j][i];
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) t += __shfl_xor(t, o);
-      const int m = wave + kGemmWaves * j;
-      if (lane == 0) rscale[m] = (m < g.rows) ? 1.0f / sqrtf(t / (float)g.k + g.eps) : 0.f;
+      const int m = wave + NW * j;
+      if (lane == 0 && m < kRealRows) rscale[m] = (m < g.rows) ? 1.0f / sqrtf(t / (float)g.k + g.eps) : 0.f;
     }
   }
   __syncthreads();
-  for (int e = tid; e < MT * 256; e += kGemmThreads) {
+  for (int e = tid; e < MT * 256; e += kThreads) {
     float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < kGemmWaves; ++w) s += red[w][e];
+    for (int w = 0; w < NW; ++w) s += red[w][e];
     tile[e] = s;
   }
   __syncthreads();
 
   if (g.sp > 1) {
     float* mine = g.part + ((size_t)nb * g.sp + spi) * (MT * 256);
-    for (int e = tid; e < MT * 256; e += kGemmThreads) mine[e] = tile[e];
+    for (int e = tid; e < MT * 256; e += kThreads) mine[e] = tile[e];
     __threadfence();
     __syncthreads();
     if (tid == 0) {
@@ -157,7 +215,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const GemmArgs g) {
     if (!last_flag) return;
     __threadfence();
     const float* all = g.part + (size_t)nb * g.sp * (MT * 256);
-    for (int e = tid; e < MT * 256; e += kGemmThreads) {
+    for (int e = tid; e < MT * 256; e += kThreads) {
       float s = 0.f;
       for (int q = 0; q < g.sp; ++q) s += __builtin_nontemporal_load(all + (size_t)q * (MT * 256) + e);
       tile[e] = s;
@@ -167,10 +225,13 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const GemmArgs g) {
   }
 
   // ------------------------------------------------------------------ epilogues
+  // Output (n_local, m) of real row m: hi-part row m plus lo-part row rows + m.
+  auto val = [&](int nl, int m) { return tile[tile_idx(nl, m)] + tile[tile_idx(nl, g.rows + m)]; };
   if constexpr (EPI == kEpiQkv) {
     // Packed rows of n block nb: 0..7 = head dims i0..i0+7, 8..15 = their RoPE partners i0+dh/2..
-    const int p = tid & 7, m = tid >> 3;
-    if (m < g.rows && m < MT * 16) {
+    for (int it = tid; it < 8 * kRealRows; it += kThreads) {
+      const int p = it & 7, m = it >> 3;
+      if (m >= g.rows) continue;
       const int half = g.dh >> 1, bph = g.dh >> 4;
       const int qb = g.nq * bph, kvb = g.nkv * bph;
       int sec, head, blk;
@@ -179,8 +240,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const GemmArgs g) {
       else { sec = 2; head = (nb - qb - kvb) / bph; blk = nb - qb - kvb - head * bph; }
       const int i = blk * 8 + p;
       const float s = rscale[m];
-      const float y1 = tile[tile_idx(p, m)] * s + g.bias[nb * 16 + p];
-      const float y2 = tile[tile_idx(p + 8, m)] * s + g.bias[nb * 16 + p + 8];
+      const float y1 = val(p, m) * s + g.bias[nb * 16 + p];
+      const float y2 = val(p + 8, m) * s + g.bias[nb * 16 + p + 8];
       const int b = m / g.T, slot = m - b * g.T;
       const int pos = g.len[b] + slot;
       if (pos < g.cap) {
@@ -206,21 +267,21 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const GemmArgs g) {
     }
   } else if constexpr (EPI == kEpiResid) {
     float* sq = &red[0][0];
-    for (int e = tid; e < 16 * MT * 16; e += kGemmThreads) {
+    for (int e = tid; e < 16 * kRealRows; e += kThreads) {
       const int nl = e & 15, m = e >> 4;
       float v = 0.f;
       if (m < g.rows) {
         const int n = nb * 16 + nl;
         const size_t o = (size_t)m * g.n_out + n;
-        v = g.x[o] + tile[tile_idx(nl, m)];
+        v = g.x[o] + val(nl, m);
         g.x[o] = v;
-        g.a_next[o] = f2bf(v * g.gain_next[n]);
+        store_split(g.a_next, g.n_out, g.rows, m, n, v * g.gain_next[n]);
         if (g.hidden) g.hidden[o] = f2bf(v);
       }
       sq[e] = v * v;
     }
     __syncthreads();
-    if (tid < MT * 16 && tid < g.rows) {
+    if (tid < kRealRows && tid < g.rows) {
       float s = 0.f;
 #pragma unroll
       for (int nl = 0; nl < 16; ++nl) s += sq[tid * 16 + nl];
@@ -228,22 +289,23 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const GemmArgs g) {
     }
   } else if constexpr (EPI == kEpiSwiglu) {
     // Packed rows of n block nb: 0..7 = gate rows j0..j0+7, 8..15 = up rows j0..j0+7.
-    const int p = tid & 7, m = tid >> 3;
-    if (m < g.rows && m < MT * 16) {
+    for (int it = tid; it < 8 * kRealRows; it += kThreads) {
+      const int p = it & 7, m = it >> 3;
+      if (m >= g.rows) continue;
       const float s = rscale[m];
-      const float gt = tile[tile_idx(p, m)] * s;
-      const float up = tile[tile_idx(p + 8, m)] * s;
+      const float gt = val(p, m) * s;
+      const float up = val(p + 8, m) * s;
       const float hv = gt / (1.0f + expf(-gt)) * up;
-      g.h[(size_t)m * g.ffn + nb * 8 + p] = f2bf(hv);
+      store_split(g.h, g.ffn, g.rows, m, nb * 8 + p, hv);
     }
   } else if constexpr (EPI == kEpiArgmax) {
     const int m = tid;
-    if (m < g.rows && m < MT * 16) {
+    if (m < g.rows && m < kRealRows) {
       const float s = rscale[m];
       float best = -INFINITY;
       int bi = nb * 16;
       for (int nl = 0; nl < 16; ++nl) {
-        const float v = tile[tile_idx(nl, m)] * s;
+        const float v = val(nl, m) * s;
         if (g.logits) g.logits[(size_t)m * g.vocab + nb * 16 + nl] = v;
         if (v > best) { best = v; bi = nb * 16 + nl; }
       }
@@ -252,26 +314,33 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const GemmArgs g) {
   }
 }
 
-template <int EPI>
+template <int EPI, int NW>
 static hipError_t gemm_mt(const GemmArgs& g, hipStream_t s) {
-  const int mt = (g.rows + 15) / 16;
-  const dim3 grid(g.nb * g.sp), block(kGemmThreads);
+  const int mt = (2 * g.rows + 15) / 16;
+  const dim3 grid(g.nb * g.sp), block(NW * 64);
   switch (mt) {
-    case 1: k_gemm<EPI, 1><<<grid, block, 0, s>>>(g); break;
-    case 2: k_gemm<EPI, 2><<<grid, block, 0, s>>>(g); break;
+    case 1: k_gemm<EPI, 1, NW><<<grid, block, 0, s>>>(g); break;
+    case 2: k_gemm<EPI, 2, NW><<<grid, block, 0, s>>>(g); break;
     case 3:
-    case 4: k_gemm<EPI, 4><<<grid, block, 0, s>>>(g); break;
+    case 4: k_gemm<EPI, 4, NW><<<grid, block, 0, s>>>(g); break;
+    case 5: case 6: case 7:
+    case 8: k_gemm<EPI, 8, NW><<<grid, block, 0, s>>>(g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <int EPI>
+static hipError_t gemm_nw(const GemmArgs& g, hipStream_t s) {
+  return g.nw == 4 ? gemm_mt<EPI, 4>(g, s) : gemm_mt<EPI, 8>(g, s);
+}
+
 hipError_t launch_gemm(int epi, const GemmArgs& g, hipStream_t s) {
   switch (epi) {
-    case kEpiQkv: return gemm_mt<kEpiQkv>(g, s);
-    case kEpiResid: return gemm_mt<kEpiResid>(g, s);
-    case kEpiSwiglu: return gemm_mt<kEpiSwiglu>(g, s);
-    case kEpiArgmax: return gemm_mt<kEpiArgmax>(g, s);
+    case kEpiQkv: return gemm_nw<kEpiQkv>(g, s);
+    case kEpiResid: return gemm_nw<kEpiResid>(g, s);
+    case kEpiSwiglu: return gemm_nw<kEpiSwiglu>(g, s);
+    case kEpiArgmax: return gemm_nw<kEpiArgmax>(g, s);
   }
   return hipErrorInvalidValue;
 }
@@ -299,7 +368,7 @@ __global__ __launch_bounds__(256) void k_embed(const EmbedArgs e) {
       const int col = blk * 16 + c;
       const float v = bf2f(src[col]);
       e.x[(size_t)r * e.H + col] = v;
-      e.a[(size_t)r * e.H + col] = f2bf(v * e.gain[col]);
+      store_split(e.a, e.H, e.rows, r, col, v * e.gain[col]);
       s += v * v;
     }
     e.ssq[(size_t)r * nparts + blk] = s;
@@ -312,82 +381,202 @@ hipError_t launch_embed(const EmbedArgs& e, hipStream_t s) {
 }
 
 // ----------------------------------------------------------------------------------------------
-// Attention, phase 1: workgroup (chunk c, kv head, sequence x row group) scores up to 16
-// query rows (slot-major: row = slot*G + head-in-group) against the chunk's 64 positions.
-// Lane j of a wave owns key c*64+j; the causal rule masks keys past the row's position.
-// Output per row: running max m, sum l and unnormalised o[dh] (base-2 exponentials).
+// Attention, phase 1 (MFMA).  Workgroup (span x, kv head, sequence x row group) takes up to 64
+// query rows of one KV head (slot-major: row = slot*G + head-in-group, G = nq/nkv) against
+// the span's positions [x*kSpan, (x+1)*kSpan), in chunks of 64 position-aligned keys.
+// Wave w owns query rows 16w..16w+15: S = Q K^T and O += P V are 16x16x32 bf16 MFMAs, the
+// softmax is the usual running (max, sum) per row in base 2.  K is staged in LDS row-major,
+// V transposed, P goes through LDS to change from the MFMA output layout to the input one.
+// Q and P enter the MFMAs as bf16 hi + lo pairs (two MFMAs each); K and V are the bf16 cache.
+// Spans are fixed by absolute position, so a row's result does not depend on the length.
+constexpr int kSpanChunks = 2;
+constexpr int kSpan = kSpanChunks * kChunk;
+
 template <int DH>
 __global__ __launch_bounds__(256) void k_attn(const AttnArgs a) {
-  __shared__ float Ks[kChunk][DH + 1];
-  __shared__ float Vs[kChunk][DH + 1];
-  const int c = blockIdx.x, kvh = blockIdx.y;
+  constexpr int KP = DH + 8;        // K row pitch (bf16): 16-byte aligned, conflict-free b128 reads
+  constexpr int VP = kChunk + 8;    // V^T row pitch
+  constexpr int PP = kChunk + 8;    // P row pitch
+  __shared__ __attribute__((aligned(16))) uint16_t Kl[kChunk * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[DH * VP];
+  __shared__ __attribute__((aligned(16))) uint16_t Pl[4][2][16 * PP];   // [wave][hi, lo]
+
+  const int x = blockIdx.x, kvh = blockIdx.y;
   const int G = a.nq / a.nkv, nrows = a.T * G;
-  const int ngroups = (nrows + kAttnRows - 1) / kAttnRows;
+  const int ngroups = (nrows + 63) / 64;
   const int b = blockIdx.z / ngroups, rg = blockIdx.z - b * ngroups;
   const int L = a.len[b];
   const int plast = L + a.T - 1;
-  const int c0 = c * kChunk;
-  if (c0 > plast) return;
+  const int span0 = x * kSpan;
+  if (span0 > plast) return;
 
-  const uint16_t* kb = a.kc + (size_t)b * a.seq_stride + ((size_t)kvh * a.cap + c0) * DH;
-  const uint16_t* vb = a.vc + (size_t)b * a.seq_stride + ((size_t)kvh * a.cap + c0) * DH;
-  for (int idx = threadIdx.x; idx < kChunk * DH / 8; idx += 256) {
-    const int j = idx / (DH / 8), d8 = (idx - j * (DH / 8)) * 8;
-    uint4 kv4 = make_uint4(0, 0, 0, 0), vv4 = make_uint4(0, 0, 0, 0);
-    if (c0 + j <= plast && c0 + j < a.cap) {
-      kv4 = *(const uint4*)(kb + (size_t)j * DH + d8);
-      vv4 = *(const uint4*)(vb + (size_t)j * DH + d8);
-    }
-    const uint32_t kw[4] = {kv4.x, kv4.y, kv4.z, kv4.w};
-    const uint32_t vw[4] = {vv4.x, vv4.y, vv4.z, vv4.w};
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int wrow0 = rg * 64 + wave * 16;         // first query row of this wave
+  const bool active = wrow0 < nrows;
+
+  // Q as the MFMA A operand: lane holds row wrow0 + l16, dims ks*32 + 8*g4 .. +8, as a
+  // bf16 hi part (qa) and lo part (ql).
+  bf16x8 qa[DH / 32], ql[DH / 32];
+  {
+    const int qr = wrow0 + l16;
+    const bool ok = qr < nrows;
+    const int slot = ok ? qr / G : 0;
+    const int hh = kvh * G + (ok ? qr - slot * G : 0);
+    const float* qp = a.q + ((size_t)(b * a.T + slot) * a.nq + hh) * DH;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      Ks[j][d8 + 2 * t] = __uint_as_float(kw[t] << 16);
-      Ks[j][d8 + 2 * t + 1] = __uint_as_float(kw[t] & 0xFFFF0000u);
-      Vs[j][d8 + 2 * t] = __uint_as_float(vw[t] << 16);
-      Vs[j][d8 + 2 * t + 1] = __uint_as_float(vw[t] & 0xFFFF0000u);
+    for (int ks = 0; ks < DH / 32; ++ks) {
+      uint16_t t[8], tl[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = ok ? qp[ks * 32 + g4 * 8 + e] : 0.f;
+        t[e] = f2bf(v);
+        tl[e] = f2bf(v - bf2f(t[e]));
+      }
+      u32x4 u, ul;
+      u.x = t[0] | ((uint32_t)t[1] << 16);
+      u.y = t[2] | ((uint32_t)t[3] << 16);
+      u.z = t[4] | ((uint32_t)t[5] << 16);
+      u.w = t[6] | ((uint32_t)t[7] << 16);
+      ul.x = tl[0] | ((uint32_t)tl[1] << 16);
+      ul.y = tl[2] | ((uint32_t)tl[3] << 16);
+      ul.z = tl[4] | ((uint32_t)tl[5] << 16);
+      ul.w = tl[6] | ((uint32_t)tl[7] << 16);
+      qa[ks] = as_bf16x8(u);
+      ql[ks] = as_bf16x8(ul);
     }
   }
-  __syncthreads();
+  // Positions of the 4 rows this lane holds in the MFMA output layout (rows 4*g4 + r).
+  int prow[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int qr = wrow0 + 4 * g4 + r;
+    prow[r] = (qr < nrows) ? L + qr / G : -1;
+  }
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row_end = min(nrows, (rg + 1) * kAttnRows);
-  for (int qr = rg * kAttnRows + wave; qr < row_end; qr += 4) {
-    const int slot = qr / G, hh = kvh * G + (qr - slot * G);
-    const int r = b * a.T + slot;
-    const int p = L + slot;
-    float* out = a.part + ((((size_t)b * a.nkv + kvh) * a.nchunk + c) * nrows + qr) * (DH + 2);
-    if (c0 > p) {
-      for (int d = lane; d < DH; d += 64) out[d] = 0.f;
-      if (lane == 0) { out[DH] = -INFINITY; out[DH + 1] = 0.f; }
-      continue;
-    }
-    const float* qv = a.q + ((size_t)r * a.nq + hh) * DH;
-    float s = 0.f;
-#pragma unroll 8
-    for (int d = 0; d < DH; ++d) s += qv[d] * Ks[lane][d];
-    const bool valid = (c0 + lane <= p);
-    s = valid ? s * a.scale_log2 : -INFINITY;
-    float mx = s;
+  f32x4 o[DH / 16];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    const float pj = valid ? exp2f(s - mx) : 0.f;
-    float l = pj;
+  for (int nt = 0; nt < DH / 16; ++nt) o[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float mrun[4], lrun[4];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
-    float o0 = 0.f, o1 = 0.f;
-    for (int j = 0; j < kChunk; ++j) {
-      const float pb = __shfl(pj, j);
-      o0 += pb * Vs[j][lane];
-      if (DH > 64) o1 += pb * Vs[j][lane + 64];
+  for (int r = 0; r < 4; ++r) { mrun[r] = -INFINITY; lrun[r] = 0.f; }
+
+  const uint16_t* kbase = a.kc + (size_t)b * a.seq_stride + (size_t)kvh * a.cap * DH;
+  const uint16_t* vbase = a.vc + (size_t)b * a.seq_stride + (size_t)kvh * a.cap * DH;
+
+  for (int ci = 0; ci < kSpanChunks; ++ci) {
+    const int c0 = span0 + ci * kChunk;
+    if (c0 > plast) break;
+    __syncthreads();
+    for (int idx = tid; idx < kChunk * DH / 8; idx += 256) {
+      const int j = idx / (DH / 8), d8 = (idx - j * (DH / 8)) * 8;
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (c0 + j <= plast) {
+        kv = *(const u32x4*)(kbase + (size_t)(c0 + j) * DH + d8);
+        vv = *(const u32x4*)(vbase + (size_t)(c0 + j) * DH + d8);
+      }
+      *(u32x4*)(&Kl[j * KP + d8]) = kv;
+      const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        Vt[(d8 + 2 * t) * VP + j] = (uint16_t)(vw[t] & 0xFFFFu);
+        Vt[(d8 + 2 * t + 1) * VP + j] = (uint16_t)(vw[t] >> 16);
+      }
     }
-    out[lane] = o0;
-    if (DH > 64) out[lane + 64] = o1;
-    if (lane == 0) { out[DH] = mx; out[DH + 1] = l; }
+    __syncthreads();
+    float alpha[4];
+    if (active) {
+      f32x4 sc[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        sc[kt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < DH / 32; ++ks) {
+          const bf16x8 kb8 = as_bf16x8(*(const u32x4*)(&Kl[(kt * 16 + l16) * KP + ks * 32 + g4 * 8]));
+          sc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb8, sc[kt], 0, 0, 0);
+          sc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[ks], kb8, sc[kt], 0, 0, 0);
+        }
+      }
+      // Scale, causal mask, running softmax.  Lane holds rows 4*g4+r, keys kt*16 + l16.
+      float mloc[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const int kp = c0 + kt * 16 + l16;
+          float v = sc[kt][r] * a.scale_log2;
+          v = (kp <= prow[r]) ? v : -INFINITY;
+          sc[kt][r] = v;
+          m = fmaxf(m, v);
+        }
+        m = fmaxf(m, __shfl_xor(m, 1));
+        m = fmaxf(m, __shfl_xor(m, 2));
+        m = fmaxf(m, __shfl_xor(m, 4));
+        m = fmaxf(m, __shfl_xor(m, 8));
+        mloc[r] = m;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float mnew = fmaxf(mrun[r], mloc[r]);
+        alpha[r] = (mnew == -INFINITY) ? 1.f : exp2f(mrun[r] - mnew);
+        float ls = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const float pv = (mnew == -INFINITY) ? 0.f : exp2f(sc[kt][r] - mnew);
+          sc[kt][r] = pv;
+          ls += pv;
+        }
+        ls += __shfl_xor(ls, 1);
+        ls += __shfl_xor(ls, 2);
+        ls += __shfl_xor(ls, 4);
+        ls += __shfl_xor(ls, 8);
+        lrun[r] = lrun[r] * alpha[r] + ls;
+        mrun[r] = mnew;
+      }
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint16_t hi = f2bf(sc[kt][r]);
+          Pl[wave][0][(4 * g4 + r) * PP + kt * 16 + l16] = hi;
+          Pl[wave][1][(4 * g4 + r) * PP + kt * 16 + l16] = f2bf(sc[kt][r] - bf2f(hi));
+        }
+    }
+    __syncthreads();
+    if (active) {
+#pragma unroll
+      for (int nt = 0; nt < DH / 16; ++nt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[nt][r] *= alpha[r];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const u32x4 pa = *(const u32x4*)(&Pl[wave][0][l16 * PP + ks * 32 + g4 * 8]);
+          const u32x4 pl = *(const u32x4*)(&Pl[wave][1][l16 * PP + ks * 32 + g4 * 8]);
+          const bf16x8 vb = as_bf16x8(*(const u32x4*)(&Vt[(nt * 16 + l16) * VP + ks * 32 + g4 * 8]));
+          o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pa), vb, o[nt], 0, 0, 0);
+          o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pl), vb, o[nt], 0, 0, 0);
+        }
+      }
+    }
+  }
+  if (!active) return;
+  const size_t rstride = DH + 2;
+  float* pbase = a.part + (((size_t)b * a.nkv + kvh) * a.nchunk + x) * (size_t)nrows * rstride;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int qr = wrow0 + 4 * g4 + r;
+    if (qr >= nrows) continue;
+    float* pr = pbase + (size_t)qr * rstride;
+#pragma unroll
+    for (int nt = 0; nt < DH / 16; ++nt) pr[nt * 16 + l16] = o[nt][r];
+    if (l16 == 0) { pr[DH] = mrun[r]; pr[DH + 1] = lrun[r]; }
   }
 }
 
-// Attention, phase 2: one wave per (row, q head); merge chunks 0..p/64 in order.
+// Attention, phase 2: one wave per (row, q head); merge spans 0..p/kSpan in order.  Span
+// maxima and sums are spread over lanes; the weighted sum of partial outputs runs over
+// spans in increasing order.
 template <int DH>
 __global__ __launch_bounds__(256) void k_combine(const AttnArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -398,28 +587,37 @@ __global__ __launch_bounds__(256) void k_combine(const AttnArgs a) {
   const int b = r / a.T, slot = r - b * a.T;
   const int kvh = h / G, qr = slot * G + (h - kvh * G);
   const int p = a.len[b] + slot;
-  const int nc = p / kChunk + 1;
-  const float* base = a.part + (((size_t)b * a.nkv + kvh) * a.nchunk * nrows + qr) * (DH + 2);
-  const size_t cstride = (size_t)nrows * (DH + 2);
-  float mx = -INFINITY;
-  for (int c = 0; c < nc; ++c) mx = fmaxf(mx, base[c * cstride + DH]);
-  float l = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int c = 0; c < nc; ++c) {
-    const float* pc = base + c * cstride;
-    const float w = exp2f(pc[DH] - mx);
-    l += pc[DH + 1] * w;
-    o0 += pc[lane] * w;
-    if (DH > 64) o1 += pc[lane + 64] * w;
+  const int np = p / kSpan + 1;
+  const size_t rstride = DH + 2;
+  const size_t sstride = (size_t)nrows * rstride;
+  const float* base = a.part + ((size_t)b * a.nkv + kvh) * a.nchunk * sstride + (size_t)qr * rstride;
+  float m0 = -INFINITY, m1 = -INFINITY, l0 = 0.f, l1 = 0.f;
+  if (lane < np) { m0 = base[lane * sstride + DH]; l0 = base[lane * sstride + DH + 1]; }
+  if (lane + 64 < np) { m1 = base[(lane + 64) * sstride + DH]; l1 = base[(lane + 64) * sstride + DH + 1]; }
+  float M = fmaxf(m0, m1);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  const float w0 = (m0 == -INFINITY) ? 0.f : exp2f(m0 - M);
+  const float w1 = (m1 == -INFINITY) ? 0.f : exp2f(m1 - M);
+  float Ls = l0 * w0 + l1 * w1;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) Ls += __shfl_xor(Ls, o);
+  float o0 = 0.f, o1 = 0.f;
+  for (int j = 0; j < np; ++j) {
+    const float w = (j < 64) ? __shfl(w0, j) : __shfl(w1, j - 64);
+    const float* pj = base + (size_t)j * sstride;
+    o0 += w * pj[lane];
+    if (DH > 64) o1 += w * pj[lane + 64];
   }
-  const float inv = 1.0f / l;
-  uint16_t* dst = a.out + (size_t)r * a.nq * DH + (size_t)h * DH;
-  dst[lane] = f2bf(o0 * inv);
-  if (DH > 64) dst[lane + 64] = f2bf(o1 * inv);
+  const float inv = 1.0f / Ls;
+  const size_t qd = (size_t)a.nq * DH;
+  store_split(a.out, qd, a.rows, r, h * DH + lane, o0 * inv);
+  if (DH > 64) store_split(a.out, qd, a.rows, r, h * DH + lane + 64, o1 * inv);
 }
 
 hipError_t launch_attention(const AttnArgs& a, int dh, int B, hipStream_t s) {
   const int G = a.nq / a.nkv;
-  const int ngroups = (a.T * G + kAttnRows - 1) / kAttnRows;
+  const int ngroups = (a.T * G + 63) / 64;
   const dim3 grid(a.nchunk, a.nkv, B * ngroups);
   const int ncomb = (a.rows * a.nq + 3) / 4;
   if (dh == 128) {
@@ -433,6 +631,8 @@ hipError_t launch_attention(const AttnArgs& a, int dh, int B, hipStream_t s) {
   }
   return hipGetLastError();
 }
+
+int attention_spans(int cap) { return (cap + kSpan - 1) / kSpan; }
 
 // ----------------------------------------------------------------------------------------------
 // Accept: per sequence, merge the LM head's per-tile (max, index) pairs into the greedy

@@ -89,6 +89,7 @@ struct sf_cache {
   int* counters = nullptr;
   int32_t *res_d = nullptr, *res_h = nullptr, *dout_d = nullptr, *dout_h = nullptr;
   int sp_qkv, sp_o, sp_gu, sp_d, sp_head;
+  int nw_qkv, nw_o, nw_gu, nw_d, nw_head;
   hipGraphExec_t gx_verify = nullptr, gx_draft = nullptr;
   std::vector<int> len_h, next_h, len_hi;
   bool dirty = false;
@@ -100,13 +101,27 @@ struct sf_cache {
 // Work split of a GEMM with nb n-blocks and kb k-tiles: each wave takes at most kBatch tiles;
 // small GEMMs are spread over more workgroups (at least two tiles per wave).
 static int choose_sp(int nb, int kb, const char* env) {
-  int sp = (kb + kGemmWaves * kBatch - 1) / (kGemmWaves * kBatch);
-  while (nb * sp < 512 && sp * kGemmWaves * 4 <= kb) sp *= 2;
+  // Cross-workgroup split-K needs device-scope fences (an L2 write-back per workgroup on
+  // this GPU), which cost far more than the parallelism gains: one workgroup per n block.
+  (void)nb;
+  (void)kb;
+  int sp = 1;
   if (const char* v = getenv(env)) {
     int o = atoi(v);
     if (o >= 1 && o <= 64) sp = o;
   }
   return sp;
+}
+
+// Waves per GEMM workgroup: with few n blocks, 8 waves split each block's k range; with many,
+// 4-wave workgroups let three of them share a CU so one streams while another finishes.
+static int choose_nw(int nb, const char* env) {
+  int nw = nb >= 1024 ? 4 : 8;
+  if (const char* v = getenv(env)) {
+    int o = atoi(v);
+    if (o == 4 || o == 8) nw = o;
+  }
+  return nw;
 }
 
 static sf_status check_desc(const sf_model_desc* d) {
@@ -322,7 +337,7 @@ static hipError_t enqueue_forward(sf_cache* c, const Run& r) {
     uint16_t* vc = c->vpool + (size_t)l * c->layer_stride + kvoff;
 
     GemmArgs g = base;
-    g.w = Ly.wqkv; g.a = c->a_h; g.k = m->H; g.kb = m->H / 32; g.nb = m->nb_qkv; g.sp = c->sp_qkv;
+    g.w = Ly.wqkv; g.a = c->a_h; g.k = m->H; g.kb = m->H / 32; g.nb = m->nb_qkv; g.sp = c->sp_qkv; g.nw = c->nw_qkv;
     g.bias = Ly.bqkv; g.q = c->q; g.kc = kc; g.vc = vc;
     if ((e = launch_gemm(kEpiQkv, g, s)) != hipSuccess) return e;
 
@@ -330,18 +345,18 @@ static hipError_t enqueue_forward(sf_cache* c, const Run& r) {
     if ((e = launch_attention(aa, m->dh, r.B, s)) != hipSuccess) return e;
 
     g = base;
-    g.w = Ly.wo; g.a = c->a_o; g.k = m->Q; g.kb = m->Q / 32; g.nb = m->nb_h; g.sp = c->sp_o;
+    g.w = Ly.wo; g.a = c->a_o; g.k = m->Q; g.kb = m->Q / 32; g.nb = m->nb_h; g.sp = c->sp_o; g.nw = c->nw_o;
     g.x = c->x; g.a_next = c->a_h; g.gain_next = Ly.g2; g.ssq_out = c->ssq; g.n_out = m->H;
     if ((e = launch_gemm(kEpiResid, g, s)) != hipSuccess) return e;
 
     g = base;
-    g.w = Ly.wgu; g.a = c->a_h; g.k = m->H; g.kb = m->H / 32; g.nb = m->nb_gu; g.sp = c->sp_gu;
+    g.w = Ly.wgu; g.a = c->a_h; g.k = m->H; g.kb = m->H / 32; g.nb = m->nb_gu; g.sp = c->sp_gu; g.nw = c->nw_gu;
     g.h = c->a_f; g.ffn = m->F;
     if ((e = launch_gemm(kEpiSwiglu, g, s)) != hipSuccess) return e;
 
     const bool last = (l + 1 == m->L);
     g = base;
-    g.w = Ly.wd; g.a = c->a_f; g.k = m->F; g.kb = m->F / 32; g.nb = m->nb_h; g.sp = c->sp_d;
+    g.w = Ly.wd; g.a = c->a_f; g.k = m->F; g.kb = m->F / 32; g.nb = m->nb_h; g.sp = c->sp_d; g.nw = c->nw_d;
     g.x = c->x; g.a_next = c->a_h;
     g.gain_next = !last ? m->layers[l + 1].g1 : (d.has_head ? m->gfinal : m->ones);
     g.ssq_out = c->ssq; g.n_out = m->H;
@@ -351,7 +366,7 @@ static hipError_t enqueue_forward(sf_cache* c, const Run& r) {
 
   if (d.has_head) {
     GemmArgs g = base;
-    g.w = m->head; g.a = c->a_h; g.k = m->H; g.kb = m->H / 32; g.nb = m->nb_head; g.sp = c->sp_head;
+    g.w = m->head; g.a = c->a_h; g.k = m->H; g.kb = m->H / 32; g.nb = m->nb_head; g.sp = c->sp_head; g.nw = c->nw_head;
     g.amax = c->amax; g.logits = r.logits; g.vocab = m->V;
     if ((e = launch_gemm(kEpiArgmax, g, s)) != hipSuccess) return e;
   }
@@ -397,10 +412,10 @@ extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacit
   if (!m || !out) return fail(SF_E_ARG, "model or out is NULL");
   if (k_max < 0 || k_max >= kMaxK) return fail(SF_E_ARG, "k_max must be in 0..15");
   if (n_seqs < 1 || n_seqs * (k_max + 1) > kMaxRows) return fail(SF_E_ARG, "n_seqs*(k_max+1) must be in 1..64");
-  if (capacity < k_max + 1 || capacity > (1 << 20)) return fail(SF_E_ARG, "capacity out of range");
+  if (capacity < k_max + 1 || capacity > 16384) return fail(SF_E_ARG, "capacity must be in k_max+1..16384");
   sf_cache* c = new sf_cache();
   c->m = m; c->B = n_seqs; c->cap = capacity; c->kmax = k_max; c->T = k_max + 1;
-  c->nchunk = (capacity + kChunk - 1) / kChunk;
+  c->nchunk = attention_spans(capacity);
   c->seq_stride = (size_t)m->nkv * capacity * m->dh;
   c->layer_stride = c->seq_stride * n_seqs;
   c->len_h.assign(n_seqs, 0); c->next_h.assign(n_seqs, 0); c->len_hi.assign(n_seqs, 0);
@@ -409,6 +424,11 @@ extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacit
   c->sp_gu = choose_sp(m->nb_gu, m->H / 32, "SF_SP_GU");
   c->sp_d = choose_sp(m->nb_h, m->F / 32, "SF_SP_D");
   c->sp_head = choose_sp(m->nb_head, m->H / 32, "SF_SP_HEAD");
+  c->nw_qkv = choose_nw(m->nb_qkv, "SF_NW_QKV");
+  c->nw_o = choose_nw(m->nb_h, "SF_NW_O");
+  c->nw_gu = choose_nw(m->nb_gu, "SF_NW_GU");
+  c->nw_d = choose_nw(m->nb_h, "SF_NW_D");
+  c->nw_head = choose_nw(m->nb_head, "SF_NW_HEAD");
 
   hipStream_t s = m->stream;
   auto bail = [&](sf_status st) { cache_release(c); return st; };
@@ -432,9 +452,9 @@ extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacit
   TRY(dalloc((void**)&c->next, n_seqs * 4));
   TRY(dalloc((void**)&c->stage_d, sizeof(Stage)));
   TRY(dalloc((void**)&c->x, R * m->H * 4));
-  TRY(dalloc((void**)&c->a_h, R * m->H * 2));
-  TRY(dalloc((void**)&c->a_o, R * m->Q * 2));
-  TRY(dalloc((void**)&c->a_f, R * m->F * 2));
+  TRY(dalloc((void**)&c->a_h, 2 * R * m->H * 2));
+  TRY(dalloc((void**)&c->a_o, 2 * R * m->Q * 2));
+  TRY(dalloc((void**)&c->a_f, 2 * R * m->F * 2));
   TRY(dalloc((void**)&c->hidden, R * m->H * 2));
   TRY(dalloc((void**)&c->ssq, R * (m->H / 16) * 4));
   TRY(dalloc((void**)&c->q, R * m->Q * 4));
@@ -771,7 +791,7 @@ extern "C" sf_status sf_time_kernel(sf_cache* c, int32_t kernel, int32_t iters, 
     GemmArgs g = base;
     switch (kernel) {
       case SF_KERNEL_QKV:
-        g.w = Ly.wqkv; g.a = c->a_h; g.k = m->H; g.kb = m->H / 32; g.nb = m->nb_qkv; g.sp = c->sp_qkv;
+        g.w = Ly.wqkv; g.a = c->a_h; g.k = m->H; g.kb = m->H / 32; g.nb = m->nb_qkv; g.sp = c->sp_qkv; g.nw = c->nw_qkv;
         g.bias = Ly.bqkv; g.q = c->q; g.kc = kc; g.vc = vc;
         by = (double)(m->Q + 2 * m->KV) * m->H * 2 + (double)rows * (m->H * 2 + m->Q * 4 + 2 * m->KV * 2);
         return launch_gemm(kEpiQkv, g, s);
@@ -785,22 +805,22 @@ extern "C" sf_status sf_time_kernel(sf_cache* c, int32_t kernel, int32_t iters, 
         return launch_attention(aa, m->dh, c->B, s);
       }
       case SF_KERNEL_OPROJ:
-        g.w = Ly.wo; g.a = c->a_o; g.k = m->Q; g.kb = m->Q / 32; g.nb = m->nb_h; g.sp = c->sp_o;
+        g.w = Ly.wo; g.a = c->a_o; g.k = m->Q; g.kb = m->Q / 32; g.nb = m->nb_h; g.sp = c->sp_o; g.nw = c->nw_o;
         g.x = c->x; g.a_next = c->a_h; g.gain_next = Ly.g2; g.ssq_out = c->ssq; g.n_out = m->H;
         by = (double)m->H * m->Q * 2 + (double)rows * (m->Q * 2 + m->H * (4 + 4 + 2));
         return launch_gemm(kEpiResid, g, s);
       case SF_KERNEL_GATEUP:
-        g.w = Ly.wgu; g.a = c->a_h; g.k = m->H; g.kb = m->H / 32; g.nb = m->nb_gu; g.sp = c->sp_gu;
+        g.w = Ly.wgu; g.a = c->a_h; g.k = m->H; g.kb = m->H / 32; g.nb = m->nb_gu; g.sp = c->sp_gu; g.nw = c->nw_gu;
         g.h = c->a_f; g.ffn = m->F;
         by = (double)2 * m->F * m->H * 2 + (double)rows * (m->H * 2 + m->F * 2);
         return launch_gemm(kEpiSwiglu, g, s);
       case SF_KERNEL_DOWN:
-        g.w = Ly.wd; g.a = c->a_f; g.k = m->F; g.kb = m->F / 32; g.nb = m->nb_h; g.sp = c->sp_d;
+        g.w = Ly.wd; g.a = c->a_f; g.k = m->F; g.kb = m->F / 32; g.nb = m->nb_h; g.sp = c->sp_d; g.nw = c->nw_d;
         g.x = c->x; g.a_next = c->a_h; g.gain_next = Ly.g1; g.ssq_out = c->ssq; g.n_out = m->H;
         by = (double)m->H * m->F * 2 + (double)rows * (m->F * 2 + m->H * (4 + 4 + 2));
         return launch_gemm(kEpiResid, g, s);
       default:
-        g.w = m->head; g.a = c->a_h; g.k = m->H; g.kb = m->H / 32; g.nb = m->nb_head; g.sp = c->sp_head;
+        g.w = m->head; g.a = c->a_h; g.k = m->H; g.kb = m->H / 32; g.nb = m->nb_head; g.sp = c->sp_head; g.nw = c->nw_head;
         g.amax = c->amax; g.vocab = m->V;
         by = (double)m->V * m->H * 2 + (double)rows * (m->H * 2 + m->nb_head * 8);
         return launch_gemm(kEpiArgmax, g, s);

@@ -8,13 +8,10 @@
 namespace sf {
 
 constexpr int kWave = 64;
-constexpr int kGemmWaves = 8;                 // waves per GEMM workgroup
-constexpr int kGemmThreads = kGemmWaves * kWave;
 constexpr int kTileN = 16;                    // output features per MFMA tile
 constexpr int kTileK = 32;                    // reduction depth per MFMA tile
 constexpr int kBatch = 16;                    // weight tiles a wave loads before using them
 constexpr int kChunk = 64;                    // attention: KV positions per chunk (position aligned)
-constexpr int kAttnRows = 16;                 // attention: query rows per workgroup
 constexpr int kMaxRows = 64;                  // rows (sequences x positions) per pass
 constexpr int kMaxSeqs = 64;
 constexpr int kMaxK = 16;                     // drafts per sequence (k_max <= 15, T <= 16)
@@ -41,8 +38,9 @@ enum Epi { kEpiQkv = 0, kEpiResid = 1, kEpiSwiglu = 2, kEpiArgmax = 3 };
 
 struct GemmArgs {
   const uint4* w;          // packed weight tiles [nb][kb][64 lanes] x 16 B
-  const uint16_t* a;       // bf16 activations [rows_pad][k]
+  const uint16_t* a;       // bf16 activations [2*rows][k]: hi parts, then lo parts
   int k, kb, nb, rows, sp; // in-features, k tiles, n blocks, valid rows, workgroups per n block
+  int nw;                  // waves per workgroup: 4 or 8
   float* part;             // split partials [nb][sp][mt*256]
   int* counters;           // [nb], zero between launches
   // RMSNorm folded into the consumer: row scale = 1/sqrt(sum(ssq_in[r][*])/k + eps)
@@ -63,13 +61,13 @@ struct GemmArgs {
   int nq, nkv, dh;
   // kEpiResid
   float* x;                // residual [rows][n_out]
-  uint16_t* a_next;        // bf16(x * gain_next) [rows][n_out]
+  uint16_t* a_next;        // x * gain_next as hi/lo bf16 rows [2*rows][n_out]
   const float* gain_next;  // [n_out]
   float* ssq_out;          // [rows][nb]
   uint16_t* hidden;        // optional bf16(x) [rows][n_out]
   int n_out;
   // kEpiSwiglu
-  uint16_t* h;             // [rows][ffn]
+  uint16_t* h;             // silu(gate)*up as hi/lo bf16 rows [2*rows][ffn]
   int ffn;
   // kEpiArgmax
   float2* amax;            // [rows][nb] (value, index bits)
@@ -84,7 +82,7 @@ struct EmbedArgs {
   const int32_t* next;
   const float* gain;       // first layer's ln1
   float* x;
-  uint16_t* a;
+  uint16_t* a;             // x * gain as hi/lo bf16 rows [2*rows][H]
   float* ssq;              // [rows][H/16]
   int rows, T, H, V, kmax;
 };
@@ -96,10 +94,10 @@ struct AttnArgs {
   long seq_stride;
   int cap;
   const int32_t* len;
-  int T, nq, nkv, nchunk;
+  int T, nq, nkv, nchunk;  // nchunk: number of position spans (attention_spans(cap))
   float scale_log2;        // log2(e)/sqrt(dh)
-  float* part;             // [seq][nkv][nchunk][T*G][dh+2]
-  uint16_t* out;           // combine output bf16 [rows][nq*dh]
+  float* part;             // [seq][nkv][span][T*G][dh+2]
+  uint16_t* out;           // combine output as hi/lo bf16 rows [2*rows][nq*dh]
   int rows;
 };
 
@@ -118,6 +116,7 @@ struct AcceptArgs {
 hipError_t launch_gemm(int epi, const GemmArgs& g, hipStream_t s);
 hipError_t launch_embed(const EmbedArgs& e, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int dh, int B, hipStream_t s);
+int attention_spans(int cap);
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t s);
 hipError_t launch_pack(uint4* dst, const uint16_t* const* rowptr, int nb, int kb, hipStream_t s);
 hipError_t launch_gather_f32(float* dst, const uint16_t* const* eltptr, int n, hipStream_t s);

@@ -1,0 +1,163 @@
+"""GPU parity at the Qwen2.5-7B shape through the C ABI.
+
+Full stack (28 layers, hidden 3584, 28 q / 4 KV heads, head_dim 128, SwiGLU 18944,
+vocab 152064, untied head) in the launch configuration the benchmark times: one
+sequence, K=8 drafts, capacity 8208, captured-graph replay.  Contexts hold seeded
+synthetic K/V; drafts come from the prompt-lookup proposer over a seeded history.
+Every logit of the 9 positions is compared with the float64 oracle (max-abs
+<= 0.05) and tokens / accepted counts bit-exactly where the oracle's gap > 0.1.
+
+First-half shard (embedding + layers 0..13, hidden-state output) at context 1024:
+rows of x/rms(x) compared with max-abs <= 0.05.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import GAP, LOGIT_TOL, accepted_decided, check_targets, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+S = synth.QWEN7B
+K = 8
+CAP = 8192 + 16
+
+
+@pytest.fixture(scope="module")
+def weights():
+    need_gpu()
+    say("[7b] generating weights")
+    return synth.model_weights(S, synth.seeds(4)["weights"])
+
+
+@pytest.fixture(scope="module")
+def kv():
+    return synth.synthetic_kv(S, 8192, synth.seeds(4)["kv"])
+
+
+@pytest.fixture(scope="module")
+def hist():
+    return synth.lookup_history(S.vocab, 8193, synth.seeds(4)["prompt"])
+
+
+@pytest.fixture(scope="module")
+def eng(weights):
+    sfb = need_gpu()
+    say("[7b] packing weights")
+    e = sfb.Engine(S, weights, n_seqs=1, capacity=CAP, k_max=K)
+    yield e
+    e.close()
+
+
+def _load_ctx(sfb, cache, kv, ctx, nxt, n_layers=None):
+    kb, vb = kv
+    if n_layers is not None:
+        kb, vb = kb[:n_layers], vb[:n_layers]
+    kd = torch.from_numpy(np.ascontiguousarray(kb).view(np.int16)).cuda()
+    vd = torch.from_numpy(np.ascontiguousarray(vb).view(np.int16)).cuda()
+    sfb.sf_kv_write(cache, 0, kd, vd, ctx, kb.shape[2])
+    sfb.sf_set_next(cache, 0, nxt)
+    torch.cuda.synchronize()
+
+
+def _oracle_cache(kv, ctx, nxt, shape=S):
+    c = oracle.KVCache(shape, ctx + K + 1)
+    c.load(kv[0][:shape.n_layers], kv[1][:shape.n_layers], ctx, next_token=nxt)
+    return c
+
+
+@pytest.mark.parametrize("ctx", [512, 8192])
+def test_full_stack_verify_matches_oracle(eng, weights, kv, hist, ctx):
+    sfb = need_gpu()
+    nxt = int(hist[ctx])
+    prop = sfb.sf_ngram_propose(hist[:ctx + 1], 2, 4, K)
+    d = np.zeros(K, dtype=np.int32)
+    d[:len(prop)] = prop
+    k = len(prop)
+    say(f"[7b] ctx={ctx} k={k}")
+    _load_ctx(sfb, eng.cache, kv, ctx, nxt)
+    logits = torch.empty((K + 1, S.vocab), dtype=torch.float32, device="cuda")
+    acc_e, tgt_e = sfb.sf_verify(eng.cache, d[None], np.array([k]), sfb.SF_DEBUG_LOGITS | sfb.SF_NO_COMMIT,
+                                 dev_out=logits)
+    acc_g, tgt_g = sfb.sf_verify(eng.cache, d[None], np.array([k]), sfb.SF_NO_COMMIT)
+    torch.cuda.synchronize()
+    assert acc_g[0] == acc_e[0] and (tgt_g == tgt_e).all()
+    model = oracle.Model(S, weights)
+    say(f"[7b] ctx={ctx} oracle")
+    r = oracle.verify(model, _oracle_cache(kv, ctx, nxt), d, k, commit=False)
+    err = (logits.double().cpu() - r["logits"]).abs().max().item()
+    ne, nt = check_targets(tgt_g[0], r, K)
+    say(f"[7b] ctx={ctx} max |dlogit| {err:.4g}; exact-rule slots {ne}/{nt}; accepted gpu {acc_g[0]} "
+        f"oracle {r['accepted']}")
+    assert err <= LOGIT_TOL
+    if accepted_decided(r, int(acc_g[0]), k):
+        assert acc_g[0] == r["accepted"]
+
+    # Second pass: the first draft replaced by the model's own choice after the pending
+    # token, so at least one draft is accepted; committed on the device.
+    d2 = d.copy()
+    d2[0] = int(r["target"][0])
+    acc2, tgt2 = sfb.sf_verify(eng.cache, d2[None], np.array([max(k, 1)]))
+    r2 = oracle.verify(model, _oracle_cache(kv, ctx, nxt), d2, max(k, 1), commit=True)
+    check_targets(tgt2[0], r2, K)
+    if accepted_decided(r2, int(acc2[0]), max(k, 1)):
+        assert acc2[0] == r2["accepted"] >= 1
+        assert sfb.sf_cache_state(eng.cache, 0) == (ctx + r2["accepted"] + 1, int(r2["target"][r2["accepted"]]))
+
+
+def test_prefill_two_chunks_matches_oracle(eng, weights):
+    sfb = need_gpu()
+    prompt = synth.prompt_ids(S.vocab, 70, 4242)
+    say("[7b] prefill 70")
+    nxt = sfb.sf_prefill(eng.cache, 0, prompt)
+    shape = (S.n_layers, S.n_kv_heads, 70, S.head_dim)
+    kg = torch.zeros(shape, dtype=torch.int16, device="cuda")
+    vg = torch.zeros_like(kg)
+    sfb.sf_kv_read(eng.cache, 0, kg, vg, 70, 70)
+    torch.cuda.synchronize()
+    c = oracle.KVCache(S, 80)
+    z = oracle.prefill(oracle.Model(S, weights), c, prompt)
+    gap = oracle.top_gap(z[-1:])[0].item()
+    if gap > GAP:
+        assert nxt == c.next_token
+    kg = kg.cpu().view(torch.bfloat16).double()
+    vg = vg.cpu().view(torch.bfloat16).double()
+    ko, vo = c.k[:, :, :70].double(), c.v[:, :, :70].double()
+    rel_k = ((kg - ko).norm() / ko.norm()).item()
+    rel_v = ((vg - vo).norm() / vo.norm()).item()
+    say(f"[7b] prefill: next gpu {nxt} oracle {c.next_token} gap {gap:.3f}; KV rel err k {rel_k:.2e} v {rel_v:.2e}")
+    # bf16 GEMM inputs and a bf16 cache: relative rounding ~2^-9 per element, a few of them per layer.
+    assert rel_k < 0.02 and rel_v < 0.02
+    assert sfb.sf_cache_state(eng.cache, 0) == (70, nxt)
+
+
+def test_half_stack_hidden_states_match_oracle(weights, kv, hist):
+    sfb = need_gpu()
+    H = synth.QWEN7B_HALF
+    ctx = 1024
+    say("[7b-half] engine")
+    e = sfb.Engine(H, weights, n_seqs=1, capacity=4096, k_max=K)
+    try:
+        nxt = int(hist[ctx])
+        _load_ctx(sfb, e.cache, kv, ctx, nxt, n_layers=H.n_layers)
+        d = hist[ctx + 1:ctx + 1 + K].astype(np.int32)
+        hid = torch.empty((K + 1, H.hidden), dtype=torch.int16, device="cuda")
+        sfb.sf_verify(e.cache, d[None], None, 0, dev_out=hid)
+        torch.cuda.synchronize()
+        # Hidden-state stacks commit all k+1 positions; the caller then rewinds.
+        assert sfb.sf_cache_state(e.cache, 0)[0] == ctx + K + 1
+        sfb.sf_rollback(e.cache, 0, ctx + 3)
+        assert sfb.sf_cache_state(e.cache, 0)[0] == ctx + 3
+        say("[7b-half] oracle")
+        r = oracle.verify(oracle.Model(H, weights), _oracle_cache(kv, ctx, nxt, H), d, K, commit=False)
+        xg = hid.cpu().view(torch.bfloat16).double()
+        xo = r["hidden"]
+        ng = xg / xg.pow(2).mean(-1, keepdim=True).sqrt()
+        no = xo / xo.pow(2).mean(-1, keepdim=True).sqrt()
+        err = (ng - no).abs().max().item()
+        say(f"[7b-half] max |d(x/rms x)| {err:.4g}")
+        assert err <= LOGIT_TOL
+    finally:
+        e.close()
