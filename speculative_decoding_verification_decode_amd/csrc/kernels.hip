@@ -43,34 +43,38 @@ __device__ __forceinline__ void store_split(uint16_t* base, size_t row_stride, i
 
 // Word 3 of a raw buffer resource on gfx9-family GPUs (gfx950 included).
 constexpr int kBufferWord3 = 0x00020000;
-// RMSNorm sum-of-squares partials (one per 16 columns) read per lane: hidden <= 64*16*4.
-constexpr int kSsqPerLane = 4;
-// Weight tiles per pipelined half-batch (single m tile).
+// RMSNorm sum-of-squares partials (one per 32 columns) read per lane: hidden <= 64*32*2.
+constexpr int kSsqPerLane = 2;
+// Weight tiles per pipelined half-batch.
 constexpr int kHalf = 8;
 // Cache policy of the weight stream: non-temporal (each weight byte is read once per pass).
 constexpr int kCacheStream = 2;
 
-// Element (n_local, m) of a 16 x (16*MT) accumulator tile stored in MFMA output order:
-// lane l of m-tile mt holds rows 4*(l/16)+r, column l%16.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Element (n_local, m) of a 32 x (32*MT) accumulator tile kept in 32x32 MFMA output order:
+// lane l, register r of m-tile mt holds n_local = 8*(r/4) + 4*(l/32) + r%4, m = mt*32 + l%32.
 __device__ __forceinline__ int tile_idx(int nl, int m) {
-  return (m >> 4) * 256 + ((((nl >> 2) << 4) + (m & 15)) << 2) + (nl & 3);
+  const int lane = (m & 31) + (((nl & 7) >> 2) << 5);
+  const int r = ((nl >> 3) << 2) + (nl & 3);
+  return (m >> 5) * 1024 + lane * 16 + r;
 }
 
 // ----------------------------------------------------------------------------------------------
-// Skinny GEMM: Y[m][n] = sum_k A[m][k] * W[n][k] for m < rows, where A has 2*rows rows
-// (hi parts, then lo parts) and Y[m] = acc[m] + acc[rows + m]; 2*rows <= 16*MT.
-// W is packed in 16x32 tiles, one 16-byte bf16x8 fragment per lane, so a wave's load of one
-// tile is one contiguous kilobyte.  Each wave streams its share of the k tiles of one
-// n block, all loads of a batch issued before the first MFMA.  Waves are combined in LDS;
-// with sp > 1 the workgroups of one n block are combined by the last one to finish, in
-// fixed order, so results do not depend on scheduling.
+// Skinny GEMM: Y[m][n] = sum_k A[m][k] * W[n][k] for m < rows.  A has 2*rows rows (bf16 hi
+// parts, then lo parts) and Y[m] = acc[m] + acc[rows + m]; 2*rows <= 32*MT.
+// W is pre-packed in tiles of 32 rows x 16 k, one 16-byte fragment per lane in the operand
+// order of v_mfma_f32_32x32x16_bf16, so one wave load of a tile reads one contiguous
+// kilobyte.  A workgroup owns one 32-row n block; its NW waves split the k tiles.  Each wave
+// keeps two 8-tile batches in flight (the next batch's weights and activations requested
+// before the current batch's MFMAs) and the waves' accumulators are added in wave order,
+// so results do not depend on scheduling.
 template <int EPI, int MT, int NW>
 __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
   constexpr int kThreads = NW * 64;
-  __shared__ float red[NW][MT * 256];
-  __shared__ float tile[MT * 256];
-  __shared__ float rscale[MT * 8 + NW];
-  __shared__ int last_flag;
+  constexpr int kRealRows = MT * 16;
+  __shared__ float tile[MT * 1024];
+  __shared__ float rscale[kRealRows + NW];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -79,11 +83,10 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
   const int kt0 = (int)(((long)g.kb * u) / U), kt1 = (int)(((long)g.kb * (u + 1)) / U);
 
   constexpr bool kScaled = (EPI == kEpiQkv || EPI == kEpiSwiglu || EPI == kEpiArgmax);
-  // Row scale of the folded RMSNorm.  Wave w owns rows w, w+8, ...; lane l sums parts
-  // l, l+64, l+128, l+192 in that order, then the wave reduces across lanes: the same
-  // order for a row whatever the number of rows.  The loads are issued here and summed
-  // after the weight stream, so they never delay it.
-  constexpr int kRealRows = MT * 8;
+  // Row scale of the folded RMSNorm.  Wave w owns rows w, w+NW, ...; lane l sums parts
+  // l, l+64 in that order, then the wave reduces across lanes: the same order for a row
+  // whatever the number of rows.  The loads are issued here and summed after the weight
+  // stream, so they never delay it.
   constexpr int kRowsPerWave = (kRealRows + NW - 1) / NW;
   float ssq_v[kRowsPerWave][kSsqPerLane];
   if constexpr (kScaled) {
@@ -101,45 +104,42 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
     }
   }
 
-  f32x4 acc[MT];
+  f32x16 acc[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x16){};
 
-  // Raw buffer loads: the hardware range check returns zeros for tiles at or past kt1
-  // without touching memory, so every batch issues all of its loads unconditionally.
+  // Raw buffer loads: the hardware range check returns zeros for tiles at or past kt1, and
+  // for activation rows past 2*rows, without touching memory, so every batch issues all of
+  // its loads unconditionally.
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(g.w + (size_t)nb * g.kb * 64), (short)0, kt1 * 1024, kBufferWord3);
   const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
       (void*)g.a, (short)0, 2 * kMaxRows * g.k * 2, kBufferWord3);
-  // Lanes whose activation row is past 2*rows read zeros without a memory access (below).
   const int ext_rows = 2 * g.rows;
-  const int a_lane = ((lane & 15) * g.k + (lane >> 4) * 8) * 2;
+  const int a_lane = ((lane & 31) * g.k + (lane >> 5) * 8) * 2;
 
-  if constexpr (MT <= 2) {
-    // Up to two m tiles: two 8-tile batches in flight, the next batch's weights and
-    // activations requested before the current batch's MFMAs, so a long k range streams
-    // continuously.
-    auto load = [&](int kt, u32x4 (&w)[kHalf], u32x4 (&a)[MT][kHalf]) {
+  auto load = [&](int kt, u32x4 (&w)[kHalf], u32x4 (&a)[MT][kHalf]) {
 #pragma unroll
-      for (int t = 0; t < kHalf; ++t)
-        w[t] = __builtin_amdgcn_raw_buffer_load_b128(wres, (kt + t) * 1024 + lane * 16, 0, kCacheStream);
+    for (int t = 0; t < kHalf; ++t)
+      w[t] = __builtin_amdgcn_raw_buffer_load_b128(wres, (kt + t) * 1024 + lane * 16, 0, kCacheStream);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const bool row_ok = mt * 16 + (lane & 15) < ext_rows;
+    for (int mt = 0; mt < MT; ++mt) {
+      const bool row_ok = mt * 32 + (lane & 31) < ext_rows;
 #pragma unroll
-        for (int t = 0; t < kHalf; ++t) {
-          const int off = (row_ok && kt + t < kt1) ? a_lane + (mt * 16 * g.k + (kt + t) * kTileK) * 2 : 0x7FFFFFF0;
-          a[mt][t] = __builtin_amdgcn_raw_buffer_load_b128(ares, off, 0, 0);
-        }
+      for (int t = 0; t < kHalf; ++t) {
+        const int off = (row_ok && kt + t < kt1) ? a_lane + (mt * 32 * g.k + (kt + t) * kTileK) * 2 : 0x7FFFFFF0;
+        a[mt][t] = __builtin_amdgcn_raw_buffer_load_b128(ares, off, 0, 0);
       }
-    };
-    auto mma = [&](const u32x4 (&w)[kHalf], const u32x4 (&a)[MT][kHalf]) {
+    }
+  };
+  auto mma = [&](const u32x4 (&w)[kHalf], const u32x4 (&a)[MT][kHalf]) {
 #pragma unroll
-      for (int t = 0; t < kHalf; ++t)
+    for (int t = 0; t < kHalf; ++t)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w[t]), as_bf16x8(a[mt][t]), acc[mt], 0, 0, 0);
-    };
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w[t]), as_bf16x8(a[mt][t]), acc[mt], 0, 0, 0);
+  };
+  {
     u32x4 w0[kHalf], w1[kHalf], a0[MT][kHalf], a1[MT][kHalf];
     load(kt0, w0, a0);
     for (int kt = kt0; kt < kt1; kt += 2 * kHalf) {
@@ -152,34 +152,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
       mma(w1, a1);
       __builtin_amdgcn_sched_barrier(0);
     }
-  } else {
-    for (int kt = kt0; kt < kt1; kt += kBatch) {
-      u32x4 w[kBatch];
-#pragma unroll
-      for (int t = 0; t < kBatch; ++t)
-        w[t] = __builtin_amdgcn_raw_buffer_load_b128(wres, (kt + t) * 1024 + lane * 16, 0, kCacheStream);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const bool row_ok = mt * 16 + (lane & 15) < ext_rows;
-        u32x4 a[kBatch];
-#pragma unroll
-        for (int t = 0; t < kBatch; ++t) {
-          const int off = (row_ok && kt + t < kt1) ? a_lane + (mt * 16 * g.k + (kt + t) * kTileK) * 2 : 0x7FFFFFF0;
-          a[t] = __builtin_amdgcn_raw_buffer_load_b128(ares, off, 0, 0);
-        }
-        // Keep every load of the batch ahead of the first MFMA (memory-level parallelism).
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int t = 0; t < kBatch; ++t)
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w[t]), as_bf16x8(a[t]), acc[mt], 0, 0, 0);
-      }
-    }
   }
-
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave][mt * 256 + lane * 4 + r] = acc[mt][r];
 
   if constexpr (kScaled) {
 #pragma unroll
@@ -193,34 +166,18 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
       if (lane == 0 && m < kRealRows) rscale[m] = (m < g.rows) ? 1.0f / sqrtf(t / (float)g.k + g.eps) : 0.f;
     }
   }
-  __syncthreads();
-  for (int e = tid; e < MT * 256; e += kThreads) {
-    float s = 0.f;
+  // Cross-wave sum in wave order.
 #pragma unroll
-    for (int w = 0; w < NW; ++w) s += red[w][e];
-    tile[e] = s;
-  }
-  __syncthreads();
-
-  if (g.sp > 1) {
-    float* mine = g.part + ((size_t)nb * g.sp + spi) * (MT * 256);
-    for (int e = tid; e < MT * 256; e += kThreads) mine[e] = tile[e];
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const int old = atomicAdd(&g.counters[nb], 1);
-      last_flag = (old == g.sp - 1);
+  for (int w = 0; w < NW; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float* t = &tile[mt * 1024 + lane * 16 + r];
+          *t = (w == 0) ? acc[mt][r] : *t + acc[mt][r];
+        }
     }
-    __syncthreads();
-    if (!last_flag) return;
-    __threadfence();
-    const float* all = g.part + (size_t)nb * g.sp * (MT * 256);
-    for (int e = tid; e < MT * 256; e += kThreads) {
-      float s = 0.f;
-      for (int q = 0; q < g.sp; ++q) s += __builtin_nontemporal_load(all + (size_t)q * (MT * 256) + e);
-      tile[e] = s;
-    }
-    if (tid == 0) g.counters[nb] = 0;
     __syncthreads();
   }
 
@@ -228,20 +185,20 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
   // Output (n_local, m) of real row m: hi-part row m plus lo-part row rows + m.
   auto val = [&](int nl, int m) { return tile[tile_idx(nl, m)] + tile[tile_idx(nl, g.rows + m)]; };
   if constexpr (EPI == kEpiQkv) {
-    // Packed rows of n block nb: 0..7 = head dims i0..i0+7, 8..15 = their RoPE partners i0+dh/2..
-    for (int it = tid; it < 8 * kRealRows; it += kThreads) {
-      const int p = it & 7, m = it >> 3;
+    // Packed rows of n block nb: 0..15 = head dims i0..i0+15, 16..31 = their RoPE partners.
+    for (int it = tid; it < 16 * kRealRows; it += kThreads) {
+      const int p = it & 15, m = it >> 4;
       if (m >= g.rows) continue;
-      const int half = g.dh >> 1, bph = g.dh >> 4;
+      const int half = g.dh >> 1, bph = g.dh >> 5;
       const int qb = g.nq * bph, kvb = g.nkv * bph;
       int sec, head, blk;
       if (nb < qb) { sec = 0; head = nb / bph; blk = nb - head * bph; }
       else if (nb < qb + kvb) { sec = 1; head = (nb - qb) / bph; blk = nb - qb - head * bph; }
       else { sec = 2; head = (nb - qb - kvb) / bph; blk = nb - qb - kvb - head * bph; }
-      const int i = blk * 8 + p;
+      const int i = blk * 16 + p;
       const float s = rscale[m];
-      const float y1 = val(p, m) * s + g.bias[nb * 16 + p];
-      const float y2 = val(p + 8, m) * s + g.bias[nb * 16 + p + 8];
+      const float y1 = val(p, m) * s + g.bias[nb * 32 + p];
+      const float y2 = val(p + 16, m) * s + g.bias[nb * 32 + p + 16];
       const int b = m / g.T, slot = m - b * g.T;
       const int pos = g.len[b] + slot;
       if (pos < g.cap) {
@@ -266,12 +223,12 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
       }
     }
   } else if constexpr (EPI == kEpiResid) {
-    float* sq = &red[0][0];
-    for (int e = tid; e < 16 * kRealRows; e += kThreads) {
-      const int nl = e & 15, m = e >> 4;
+    __shared__ float sq[32 * kRealRows];
+    for (int e = tid; e < 32 * kRealRows; e += kThreads) {
+      const int nl = e & 31, m = e >> 5;
       float v = 0.f;
       if (m < g.rows) {
-        const int n = nb * 16 + nl;
+        const int n = nb * 32 + nl;
         const size_t o = (size_t)m * g.n_out + n;
         v = g.x[o] + val(nl, m);
         g.x[o] = v;
@@ -284,30 +241,37 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
     if (tid < kRealRows && tid < g.rows) {
       float s = 0.f;
 #pragma unroll
-      for (int nl = 0; nl < 16; ++nl) s += sq[tid * 16 + nl];
+      for (int nl = 0; nl < 32; ++nl) s += sq[tid * 32 + nl];
       g.ssq_out[(size_t)tid * g.nb + nb] = s;
     }
   } else if constexpr (EPI == kEpiSwiglu) {
-    // Packed rows of n block nb: 0..7 = gate rows j0..j0+7, 8..15 = up rows j0..j0+7.
-    for (int it = tid; it < 8 * kRealRows; it += kThreads) {
-      const int p = it & 7, m = it >> 3;
+    // Packed rows of n block nb: 0..15 = gate rows j0..j0+15, 16..31 = up rows j0..j0+15.
+    for (int it = tid; it < 16 * kRealRows; it += kThreads) {
+      const int p = it & 15, m = it >> 4;
       if (m >= g.rows) continue;
       const float s = rscale[m];
       const float gt = val(p, m) * s;
-      const float up = val(p + 8, m) * s;
+      const float up = val(p + 16, m) * s;
       const float hv = gt / (1.0f + expf(-gt)) * up;
-      store_split(g.h, g.ffn, g.rows, m, nb * 8 + p, hv);
+      store_split(g.h, g.ffn, g.rows, m, nb * 16 + p, hv);
+    }
+  } else if constexpr (EPI == kEpiPartial) {
+    // Unscaled partial sums of this workgroup's k range: part[spi][m][n].
+    float* dst = g.part + (size_t)spi * g.rows * g.n_out;
+    for (int e = tid; e < 32 * kRealRows; e += kThreads) {
+      const int nl = e & 31, m = e >> 5;
+      if (m < g.rows) dst[(size_t)m * g.n_out + nb * 32 + nl] = val(nl, m);
     }
   } else if constexpr (EPI == kEpiArgmax) {
     const int m = tid;
     if (m < g.rows && m < kRealRows) {
       const float s = rscale[m];
       float best = -INFINITY;
-      int bi = nb * 16;
-      for (int nl = 0; nl < 16; ++nl) {
+      int bi = nb * 32;
+      for (int nl = 0; nl < 32; ++nl) {
         const float v = val(nl, m) * s;
-        if (g.logits) g.logits[(size_t)m * g.vocab + nb * 16 + nl] = v;
-        if (v > best) { best = v; bi = nb * 16 + nl; }
+        if (g.logits) g.logits[(size_t)m * g.vocab + nb * 32 + nl] = v;
+        if (v > best) { best = v; bi = nb * 32 + nl; }
       }
       g.amax[(size_t)m * g.nb + nb] = make_float2(best, __int_as_float(bi));
     }
@@ -316,23 +280,23 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
 
 template <int EPI, int NW>
 static hipError_t gemm_mt(const GemmArgs& g, hipStream_t s) {
-  const int mt = (2 * g.rows + 15) / 16;
+  const int mt = (2 * g.rows + 31) / 32;
   const dim3 grid(g.nb * g.sp), block(NW * 64);
   switch (mt) {
     case 1: k_gemm<EPI, 1, NW><<<grid, block, 0, s>>>(g); break;
     case 2: k_gemm<EPI, 2, NW><<<grid, block, 0, s>>>(g); break;
     case 3:
     case 4: k_gemm<EPI, 4, NW><<<grid, block, 0, s>>>(g); break;
-    case 5: case 6: case 7:
-    case 8: k_gemm<EPI, 8, NW><<<grid, block, 0, s>>>(g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+// More than two m tiles (prefill chunks) need the register file of 4-wave workgroups.
 template <int EPI>
 static hipError_t gemm_nw(const GemmArgs& g, hipStream_t s) {
-  return g.nw == 4 ? gemm_mt<EPI, 4>(g, s) : gemm_mt<EPI, 8>(g, s);
+  const bool wide = (2 * g.rows + 31) / 32 > 2;
+  return (g.nw == 4 || wide) ? gemm_mt<EPI, 4>(g, s) : gemm_mt<EPI, 8>(g, s);
 }
 
 hipError_t launch_gemm(int epi, const GemmArgs& g, hipStream_t s) {
@@ -341,13 +305,117 @@ hipError_t launch_gemm(int epi, const GemmArgs& g, hipStream_t s) {
     case kEpiResid: return gemm_nw<kEpiResid>(g, s);
     case kEpiSwiglu: return gemm_nw<kEpiSwiglu>(g, s);
     case kEpiArgmax: return gemm_nw<kEpiArgmax>(g, s);
+    case kEpiPartial: return gemm_nw<kEpiPartial>(g, s);
   }
   return hipErrorInvalidValue;
 }
 
 // ----------------------------------------------------------------------------------------------
+// Reductions of split-K partials, in split order, fused with the epilogue the undivided
+// GEMM would have run.
+
+// Row scale 1/sqrt(mean(x^2) + eps) from the per-32-column sums of squares, summed in the
+// same order as the GEMM prologue: lane l takes parts l, l+64, then a cross-lane tree.
+__device__ float row_scale(const float* ssq, int nparts, int k, float eps, int m, int lane) {
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < kSsqPerLane; ++i) {
+    const int p = lane + 64 * i;
+    t += (p < nparts) ? ssq[(size_t)m * nparts + p] : 0.f;
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) t += __shfl_xor(t, o);
+  return 1.0f / sqrtf(t / (float)k + eps);
+}
+
+// QKV: workgroup (row m, 512 output pairs).  Item (n block, pair p): rows p and p+16 of the
+// packed block are a RoPE pair (or two plain V dims).
+__global__ __launch_bounds__(256) void k_reduce_qkv(const GemmArgs g) {
+  __shared__ float sc;
+  const int m = blockIdx.y;
+  if (threadIdx.x < 64) {
+    const float v = row_scale(g.ssq_in, g.nparts_in, g.k, g.eps, m, threadIdx.x);
+    if (threadIdx.x == 0) sc = v;
+  }
+  __syncthreads();
+  const int item = blockIdx.x * 256 + threadIdx.x;
+  if (item >= g.nb * 16) return;
+  const int nb = item >> 4, p = item & 15;
+  const int n1 = nb * 32 + p, n2 = n1 + 16;
+  float a1 = 0.f, a2 = 0.f;
+  for (int q = 0; q < g.sp; ++q) {
+    const float* pq = g.part + ((size_t)q * g.rows + m) * g.n_out;
+    a1 += pq[n1];
+    a2 += pq[n2];
+  }
+  const float y1 = a1 * sc + g.bias[n1];
+  const float y2 = a2 * sc + g.bias[n2];
+  const int half = g.dh >> 1, bph = g.dh >> 5;
+  const int qb = g.nq * bph, kvb = g.nkv * bph;
+  int sec, head, blk;
+  if (nb < qb) { sec = 0; head = nb / bph; blk = nb - head * bph; }
+  else if (nb < qb + kvb) { sec = 1; head = (nb - qb) / bph; blk = nb - qb - head * bph; }
+  else { sec = 2; head = (nb - qb - kvb) / bph; blk = nb - qb - kvb - head * bph; }
+  const int i = blk * 16 + p;
+  const int b = m / g.T, slot = m - b * g.T;
+  const int pos = g.len[b] + slot;
+  if (pos >= g.cap) return;
+  if (sec == 2) {
+    uint16_t* dst = g.vc + (size_t)b * g.seq_stride + ((size_t)head * g.cap + pos) * g.dh;
+    dst[i] = f2bf(y1);
+    dst[i + half] = f2bf(y2);
+  } else {
+    const float2 cs = g.rope[(size_t)pos * half + i];
+    const float o1 = y1 * cs.x - y2 * cs.y;
+    const float o2 = y2 * cs.x + y1 * cs.y;
+    if (sec == 0) {
+      float* dst = g.q + ((size_t)m * g.nq + head) * g.dh;
+      dst[i] = o1;
+      dst[i + half] = o2;
+    } else {
+      uint16_t* dst = g.kc + (size_t)b * g.seq_stride + ((size_t)head * g.cap + pos) * g.dh;
+      dst[i] = f2bf(o1);
+      dst[i + half] = f2bf(o2);
+    }
+  }
+}
+
+// Residual: workgroup (row m, 256 columns).  x += sum of partials; next norm's input as
+// hi/lo bf16; sum of squares per 32-column block (a 32-lane tree, fixed order).
+__global__ __launch_bounds__(256) void k_reduce_resid(const GemmArgs g) {
+  const int m = blockIdx.y;
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  float v = 0.f;
+  if (n < g.n_out) {
+    float acc = 0.f;
+    for (int q = 0; q < g.sp; ++q) acc += g.part[((size_t)q * g.rows + m) * g.n_out + n];
+    const size_t o = (size_t)m * g.n_out + n;
+    v = g.x[o] + acc;
+    g.x[o] = v;
+    store_split(g.a_next, g.n_out, g.rows, m, n, v * g.gain_next[n]);
+    if (g.hidden) g.hidden[o] = f2bf(v);
+  }
+  float sq = v * v;
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) sq += __shfl_xor(sq, o);
+  if ((threadIdx.x & 31) == 0 && n < g.n_out) g.ssq_out[(size_t)m * (g.n_out / 32) + (n >> 5)] = sq;
+}
+
+hipError_t launch_reduce(int epi, const GemmArgs& g, hipStream_t s) {
+  if (epi == kEpiQkv) {
+    k_reduce_qkv<<<dim3((g.nb * 16 + 255) / 256, g.rows), 256, 0, s>>>(g);
+  } else if (epi == kEpiResid) {
+    k_reduce_resid<<<dim3((g.n_out + 255) / 256, g.rows), 256, 0, s>>>(g);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------------------------
 // Embedding: row r = (sequence b, slot i) takes [pending or stage.first, d_1..d_k, 0...][i],
-// writes the fp32 residual, bf16(x * ln1 gain) and per-16-column sums of squares.
+// writes the fp32 residual, x * ln1 gain as hi/lo bf16 rows, and per-32-column sums of
+// squares.  Thread t handles columns 8t..8t+7; four consecutive lanes form a 32-column block.
 __global__ __launch_bounds__(256) void k_embed(const EmbedArgs e) {
   const int r = blockIdx.x;
   const int b = r / e.T, slot = r - b * e.T;
@@ -360,18 +428,22 @@ __global__ __launch_bounds__(256) void k_embed(const EmbedArgs e) {
   }
   tok = min(max(tok, 0), e.V - 1);
   const uint16_t* src = e.embed + (size_t)tok * e.H;
-  const int nparts = e.H >> 4;
-  for (int blk = threadIdx.x; blk < nparts; blk += blockDim.x) {
+  const int nparts = e.H >> 5;
+  for (int c8 = threadIdx.x; c8 < (e.H >> 3); c8 += blockDim.x) {
+    const u32x4 u = *(const u32x4*)(src + c8 * 8);
+    const uint32_t wds[4] = {u.x, u.y, u.z, u.w};
     float s = 0.f;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const int col = blk * 16 + c;
-      const float v = bf2f(src[col]);
+    for (int j = 0; j < 8; ++j) {
+      const int col = c8 * 8 + j;
+      const float v = __uint_as_float(j & 1 ? (wds[j >> 1] & 0xFFFF0000u) : (wds[j >> 1] << 16));
       e.x[(size_t)r * e.H + col] = v;
       store_split(e.a, e.H, e.rows, r, col, v * e.gain[col]);
       s += v * v;
     }
-    e.ssq[(size_t)r * nparts + blk] = s;
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    if ((c8 & 3) == 0) e.ssq[(size_t)r * nparts + (c8 >> 2)] = s;
   }
 }
 
@@ -603,7 +675,23 @@ __global__ __launch_bounds__(256) void k_combine(const AttnArgs a) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) Ls += __shfl_xor(Ls, o);
   float o0 = 0.f, o1 = 0.f;
-  for (int j = 0; j < np; ++j) {
+  int j = 0;
+  for (; j + 8 <= np; j += 8) {
+    float v0[8], v1[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float* pj = base + (size_t)(j + u) * sstride;
+      v0[u] = pj[lane];
+      v1[u] = (DH > 64) ? pj[lane + 64] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float w = (j + u < 64) ? __shfl(w0, j + u) : __shfl(w1, j + u - 64);
+      o0 += w * v0[u];
+      o1 += w * v1[u];
+    }
+  }
+  for (; j < np; ++j) {
     const float w = (j < 64) ? __shfl(w0, j) : __shfl(w1, j - 64);
     const float* pj = base + (size_t)j * sstride;
     o0 += w * pj[lane];
@@ -635,39 +723,38 @@ hipError_t launch_attention(const AttnArgs& a, int dh, int B, hipStream_t s) {
 int attention_spans(int cap) { return (cap + kSpan - 1) / kSpan; }
 
 // ----------------------------------------------------------------------------------------------
-// Accept: per sequence, merge the LM head's per-tile (max, index) pairs into the greedy
-// choice at each of the T positions (largest value, lowest index on ties), count the
-// leading drafts that match, and commit.
+// Accept: per sequence, merge the LM head's per-block (max, index) pairs into the greedy
+// choice at each of the T positions (largest value, lowest index on ties; the merge is
+// order independent), count the leading drafts that match, and commit.  Wave w merges the
+// rows w, w+16, ... of the sequence.
+__device__ __forceinline__ void amax_merge(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+}
+
 __global__ __launch_bounds__(1024) void k_accept(const AcceptArgs a) {
-  __shared__ float sv[1024];
-  __shared__ int si[1024];
   __shared__ int tgt[kMaxRows];
   const int b = blockIdx.x, tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   if (a.has_head) {
-    for (int slot = 0; slot < a.T; ++slot) {
+    for (int slot = wave; slot < a.T; slot += 16) {
       const float2* row = a.amax + (size_t)(b * a.T + slot) * a.nparts;
       float bv = -INFINITY;
       int bi = 0x7FFFFFFF;
-      for (int p = tid; p < a.nparts; p += 1024) {
-        const float2 e = row[p];
-        const int ei = __float_as_int(e.y);
-        if (e.x > bv || (e.x == bv && ei < bi)) { bv = e.x; bi = ei; }
+      int p = lane;
+      for (; p + 7 * 64 < a.nparts; p += 8 * 64) {
+        float2 e[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) e[u] = row[p + u * 64];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) amax_merge(bv, bi, e[u].x, __float_as_int(e[u].y));
       }
-      sv[tid] = bv;
-      si[tid] = bi;
-      __syncthreads();
-      for (int w = 512; w > 0; w >>= 1) {
-        if (tid < w) {
-          const float ov = sv[tid + w];
-          const int oi = si[tid + w];
-          if (ov > sv[tid] || (ov == sv[tid] && oi < si[tid])) { sv[tid] = ov; si[tid] = oi; }
-        }
-        __syncthreads();
-      }
-      if (tid == 0) tgt[slot] = (si[0] == 0x7FFFFFFF) ? 0 : si[0];
-      __syncthreads();
+      for (; p < a.nparts; p += 64) amax_merge(bv, bi, row[p].x, __float_as_int(row[p].y));
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) amax_merge(bv, bi, __shfl_xor(bv, o), __shfl_xor(bi, o));
+      if (lane == 0) tgt[slot] = (bi == 0x7FFFFFFF) ? 0 : bi;
     }
   }
+  __syncthreads();
   if (tid == 0) {
     Stage* st = a.stage;
     const int flags = st->flags;
@@ -712,8 +799,8 @@ __global__ void k_pack(uint4* dst, const uint16_t* const* rowptr, int nb, int kb
   const int lane = (int)(idx & 63);
   const size_t t = idx >> 6;
   const int kt = (int)(t % kb), n_blk = (int)(t / kb);
-  const int row = n_blk * 16 + (lane & 15);
-  const int k0 = kt * kTileK + (lane >> 4) * 8;
+  const int row = n_blk * kTileN + (lane & 31);
+  const int k0 = kt * kTileK + (lane >> 5) * 8;
   dst[idx] = *(const uint4*)(rowptr[row] + k0);
 }
 

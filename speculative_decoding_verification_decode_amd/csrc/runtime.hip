@@ -83,13 +83,13 @@ struct sf_cache {
   Stage* stage_h = nullptr;
   float* x = nullptr;
   uint16_t *a_h = nullptr, *a_o = nullptr, *a_f = nullptr, *hidden = nullptr;
-  float *ssq = nullptr, *q = nullptr, *apart = nullptr, *gpart = nullptr;
+  float *ssq = nullptr, *q = nullptr, *apart = nullptr;
   float2* amax = nullptr;
   float2* rope = nullptr;
-  int* counters = nullptr;
   int32_t *res_d = nullptr, *res_h = nullptr, *dout_d = nullptr, *dout_h = nullptr;
-  int sp_qkv, sp_o, sp_gu, sp_d, sp_head;
   int nw_qkv, nw_o, nw_gu, nw_d, nw_head;
+  int sp_qkv, sp_o, sp_gu, sp_d, sp_head;
+  float* part = nullptr;
   hipGraphExec_t gx_verify = nullptr, gx_draft = nullptr;
   std::vector<int> len_h, next_h, len_hi;
   bool dirty = false;
@@ -98,25 +98,10 @@ struct sf_cache {
 };
 
 // ------------------------------------------------------------------------------------------
-// Work split of a GEMM with nb n-blocks and kb k-tiles: each wave takes at most kBatch tiles;
-// small GEMMs are spread over more workgroups (at least two tiles per wave).
-static int choose_sp(int nb, int kb, const char* env) {
-  // Cross-workgroup split-K needs device-scope fences (an L2 write-back per workgroup on
-  // this GPU), which cost far more than the parallelism gains: one workgroup per n block.
-  (void)nb;
-  (void)kb;
-  int sp = 1;
-  if (const char* v = getenv(env)) {
-    int o = atoi(v);
-    if (o >= 1 && o <= 64) sp = o;
-  }
-  return sp;
-}
-
-// Waves per GEMM workgroup: with few n blocks, 8 waves split each block's k range; with many,
-// 4-wave workgroups let three of them share a CU so one streams while another finishes.
-static int choose_nw(int nb, const char* env) {
-  int nw = nb >= 1024 ? 4 : 8;
+// Waves per GEMM workgroup: with many n blocks, 4-wave workgroups let several share a CU
+// so one streams while another finishes; short k ranges also take 4 waves.
+static int choose_nw(int nb, int kb, const char* env) {
+  int nw = (nb >= 1024 || kb < 256) ? 4 : 8;
   if (const char* v = getenv(env)) {
     int o = atoi(v);
     if (o == 4 || o == 8) nw = o;
@@ -124,12 +109,25 @@ static int choose_nw(int nb, const char* env) {
   return nw;
 }
 
+// Workgroups per n block.  Narrow projections have too few 32-row blocks to occupy the
+// GPU, so their k range is split over about 448 workgroups in total (each wave keeps at
+// least four 16-k tiles); the partial sums are reduced by a second small kernel.
+static int choose_sp(int nb, int kb, int nw, const char* env) {
+  int sp = (448 + nb / 2) / nb;
+  sp = std::max(1, std::min(sp, kb / (nw * 4)));
+  if (const char* v = getenv(env)) {
+    int o = atoi(v);
+    if (o >= 1 && o <= 64) sp = o;
+  }
+  return sp;
+}
+
 static sf_status check_desc(const sf_model_desc* d) {
   if (!d) return fail(SF_E_ARG, "desc is NULL");
   if (d->n_layers < 1 || d->hidden < 32 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->ffn < 32 || d->vocab < 16)
     return fail(SF_E_ARG, "non-positive dimension");
-  if (d->hidden % 32 || d->ffn % 32 || d->vocab % 16)
-    return fail(SF_E_ARG, "hidden and ffn must be multiples of 32, vocab of 16");
+  if (d->hidden % 32 || d->ffn % 32 || d->vocab % 32)
+    return fail(SF_E_ARG, "hidden, ffn and vocab must be multiples of 32");
   if (d->head_dim != 64 && d->head_dim != 128) return fail(SF_E_ARG, "head_dim must be 64 or 128");
   if (d->n_q_heads % d->n_kv_heads) return fail(SF_E_ARG, "n_kv_heads must divide n_q_heads");
   if ((d->n_q_heads * d->head_dim) % 32) return fail(SF_E_ARG, "n_q_heads*head_dim must be a multiple of 32");
@@ -161,10 +159,10 @@ extern "C" sf_status sf_model_create(const sf_model_desc* desc, const void* cons
   m->H = d.hidden; m->nq = d.n_q_heads; m->nkv = d.n_kv_heads; m->dh = d.head_dim;
   m->Q = d.n_q_heads * d.head_dim; m->KV = d.n_kv_heads * d.head_dim; m->F = d.ffn; m->V = d.vocab;
   m->L = d.n_layers;
-  m->nb_qkv = (m->Q + 2 * m->KV) / 16;
-  m->nb_h = m->H / 16;
-  m->nb_gu = m->F / 8;
-  m->nb_head = m->V / 16;
+  m->nb_qkv = (m->Q + 2 * m->KV) / kTileN;
+  m->nb_h = m->H / kTileN;
+  m->nb_gu = 2 * m->F / kTileN;
+  m->nb_head = m->V / kTileN;
 
   // Count and validate the weight table.
   const int per_layer = d.qkv_bias ? 12 : 9;
@@ -229,46 +227,47 @@ extern "C" sf_status sf_model_create(const sf_model_desc* desc, const void* cons
     const uint16_t* wu = W(idx++);
     const uint16_t* wd = W(idx++);
 
-    // QKV rows: n block -> (section, head, dims i0..i0+7 and their RoPE partners).
-    const int N = Q + 2 * KV, bph = dh / 16;
+    // QKV rows: 32-row block -> (section, head, dims i0..i0+15 and their RoPE partners
+    // i0+dh/2..i0+dh/2+15), so each rotated pair lands in one block.
+    const int N = Q + 2 * KV, bph = dh / 32;
     std::vector<const uint16_t*> rows(N), bias(N);
     for (int n = 0; n < N; ++n) {
-      const int nb = n / 16, nl = n % 16;
+      const int nb = n / 32, nl = n % 32;
       const int qb = m->nq * bph, kvb = m->nkv * bph;
       int head, blk;
       const uint16_t *wsrc, *bsrc;
       if (nb < qb) { head = nb / bph; blk = nb % bph; wsrc = wq; bsrc = bq; }
       else if (nb < qb + kvb) { head = (nb - qb) / bph; blk = (nb - qb) % bph; wsrc = wk; bsrc = bk; }
       else { head = (nb - qb - kvb) / bph; blk = (nb - qb - kvb) % bph; wsrc = wv; bsrc = bv; }
-      const int dim = blk * 8 + (nl % 8) + (nl >= 8 ? half : 0);
+      const int dim = blk * 16 + (nl % 16) + (nl >= 16 ? half : 0);
       const int r = head * dh + dim;
       rows[n] = wsrc + (size_t)r * H;
       bias[n] = bsrc ? bsrc + r : nullptr;
     }
     TRY(dalloc((void**)&Ly.wqkv, (size_t)N * H * 2));
-    TRY(with_table(rows, s, [&](const uint16_t* const* t) { return launch_pack(Ly.wqkv, t, N / 16, H / 32, s); }));
+    TRY(with_table(rows, s, [&](const uint16_t* const* t) { return launch_pack(Ly.wqkv, t, N / kTileN, H / kTileK, s); }));
     TRY(dalloc((void**)&Ly.bqkv, (size_t)N * 4));
     TRY(with_table(bias, s, [&](const uint16_t* const* t) { return launch_gather_f32(Ly.bqkv, t, N, s); }));
 
     std::vector<const uint16_t*> ro(H);
     for (int n = 0; n < H; ++n) ro[n] = wo + (size_t)n * Q;
     TRY(dalloc((void**)&Ly.wo, (size_t)H * Q * 2));
-    TRY(with_table(ro, s, [&](const uint16_t* const* t) { return launch_pack(Ly.wo, t, H / 16, Q / 32, s); }));
+    TRY(with_table(ro, s, [&](const uint16_t* const* t) { return launch_pack(Ly.wo, t, H / kTileN, Q / kTileK, s); }));
 
-    // gate/up rows: n block nb -> gate rows 8nb..8nb+7 then up rows 8nb..8nb+7.
+    // gate/up rows: 32-row block nb -> gate rows 16nb..16nb+15 then up rows 16nb..16nb+15.
     std::vector<const uint16_t*> rgu(2 * F);
     for (int n = 0; n < 2 * F; ++n) {
-      const int nb = n / 16, nl = n % 16;
-      const int j = nb * 8 + (nl % 8);
-      rgu[n] = (nl < 8 ? wg : wu) + (size_t)j * H;
+      const int nb = n / 32, nl = n % 32;
+      const int j = nb * 16 + (nl % 16);
+      rgu[n] = (nl < 16 ? wg : wu) + (size_t)j * H;
     }
     TRY(dalloc((void**)&Ly.wgu, (size_t)2 * F * H * 2));
-    TRY(with_table(rgu, s, [&](const uint16_t* const* t) { return launch_pack(Ly.wgu, t, 2 * F / 16, H / 32, s); }));
+    TRY(with_table(rgu, s, [&](const uint16_t* const* t) { return launch_pack(Ly.wgu, t, 2 * F / kTileN, H / kTileK, s); }));
 
     std::vector<const uint16_t*> rd(H);
     for (int n = 0; n < H; ++n) rd[n] = wd + (size_t)n * F;
     TRY(dalloc((void**)&Ly.wd, (size_t)H * F * 2));
-    TRY(with_table(rd, s, [&](const uint16_t* const* t) { return launch_pack(Ly.wd, t, H / 16, F / 32, s); }));
+    TRY(with_table(rd, s, [&](const uint16_t* const* t) { return launch_pack(Ly.wd, t, H / kTileN, F / kTileK, s); }));
 
     std::vector<const uint16_t*> g1(H), g2(H);
     for (int n = 0; n < H; ++n) { g1[n] = ln1 + n; g2[n] = ln2 + n; }
@@ -286,7 +285,7 @@ extern "C" sf_status sf_model_create(const sf_model_desc* desc, const void* cons
     TRY(dalloc((void**)&m->gfinal, (size_t)H * 4));
     TRY(with_table(gfv, s, [&](const uint16_t* const* t) { return launch_gather_f32(m->gfinal, t, H, s); }));
     TRY(dalloc((void**)&m->head, (size_t)V * H * 2));
-    TRY(with_table(rh, s, [&](const uint16_t* const* t) { return launch_pack(m->head, t, V / 16, H / 32, s); }));
+    TRY(with_table(rh, s, [&](const uint16_t* const* t) { return launch_pack(m->head, t, V / kTileN, H / kTileK, s); }));
   }
 #undef TRY
   *out = m;
@@ -300,6 +299,13 @@ extern "C" sf_status sf_model_free(sf_model* m) {
   if (m->own_stream) (void)hipStreamDestroy(m->stream);
   delete m;
   return SF_OK;
+}
+
+// A GEMM with epilogue `epi`, split over g.sp workgroups per block when g.sp > 1.
+static hipError_t launch_split_gemm(int epi, const GemmArgs& g, hipStream_t s) {
+  if (g.sp <= 1) return launch_gemm(epi, g, s);
+  hipError_t e = launch_gemm(kEpiPartial, g, s);
+  return e == hipSuccess ? launch_reduce(epi, g, s) : e;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -322,8 +328,8 @@ static hipError_t enqueue_forward(sf_cache* c, const Run& r) {
   if ((e = launch_embed(ea, s)) != hipSuccess) return e;
 
   GemmArgs base{};
-  base.rows = rows; base.part = c->gpart; base.counters = c->counters; base.ssq_in = c->ssq;
-  base.nparts_in = m->H / 16; base.eps = d.rms_eps; base.T = r.T; base.len = len; base.cap = c->cap;
+  base.rows = rows; base.ssq_in = c->ssq; base.part = c->part; base.sp = 1;
+  base.nparts_in = m->H / kTileN; base.eps = d.rms_eps; base.T = r.T; base.len = len; base.cap = c->cap;
   base.seq_stride = (long)c->seq_stride; base.rope = c->rope; base.nq = m->nq; base.nkv = m->nkv; base.dh = m->dh;
 
   AttnArgs aa{};
@@ -337,36 +343,41 @@ static hipError_t enqueue_forward(sf_cache* c, const Run& r) {
     uint16_t* vc = c->vpool + (size_t)l * c->layer_stride + kvoff;
 
     GemmArgs g = base;
-    g.w = Ly.wqkv; g.a = c->a_h; g.k = m->H; g.kb = m->H / 32; g.nb = m->nb_qkv; g.sp = c->sp_qkv; g.nw = c->nw_qkv;
+    g.w = Ly.wqkv; g.a = c->a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_qkv; g.nw = c->nw_qkv;
+    g.sp = c->sp_qkv; g.n_out = m->Q + 2 * m->KV;
     g.bias = Ly.bqkv; g.q = c->q; g.kc = kc; g.vc = vc;
-    if ((e = launch_gemm(kEpiQkv, g, s)) != hipSuccess) return e;
+    if ((e = launch_split_gemm(kEpiQkv, g, s)) != hipSuccess) return e;
 
     aa.kc = kc; aa.vc = vc;
     if ((e = launch_attention(aa, m->dh, r.B, s)) != hipSuccess) return e;
 
     g = base;
-    g.w = Ly.wo; g.a = c->a_o; g.k = m->Q; g.kb = m->Q / 32; g.nb = m->nb_h; g.sp = c->sp_o; g.nw = c->nw_o;
+    g.w = Ly.wo; g.a = c->a_o; g.k = m->Q; g.kb = m->Q / kTileK; g.nb = m->nb_h; g.nw = c->nw_o;
+    g.sp = c->sp_o;
     g.x = c->x; g.a_next = c->a_h; g.gain_next = Ly.g2; g.ssq_out = c->ssq; g.n_out = m->H;
-    if ((e = launch_gemm(kEpiResid, g, s)) != hipSuccess) return e;
+    if ((e = launch_split_gemm(kEpiResid, g, s)) != hipSuccess) return e;
 
     g = base;
-    g.w = Ly.wgu; g.a = c->a_h; g.k = m->H; g.kb = m->H / 32; g.nb = m->nb_gu; g.sp = c->sp_gu; g.nw = c->nw_gu;
+    g.w = Ly.wgu; g.a = c->a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_gu; g.nw = c->nw_gu;
+    g.sp = 1;
     g.h = c->a_f; g.ffn = m->F;
     if ((e = launch_gemm(kEpiSwiglu, g, s)) != hipSuccess) return e;
 
     const bool last = (l + 1 == m->L);
     g = base;
-    g.w = Ly.wd; g.a = c->a_f; g.k = m->F; g.kb = m->F / 32; g.nb = m->nb_h; g.sp = c->sp_d; g.nw = c->nw_d;
+    g.w = Ly.wd; g.a = c->a_f; g.k = m->F; g.kb = m->F / kTileK; g.nb = m->nb_h; g.nw = c->nw_d;
     g.x = c->x; g.a_next = c->a_h;
     g.gain_next = !last ? m->layers[l + 1].g1 : (d.has_head ? m->gfinal : m->ones);
     g.ssq_out = c->ssq; g.n_out = m->H;
     g.hidden = (last && !d.has_head) ? c->hidden : nullptr;
-    if ((e = launch_gemm(kEpiResid, g, s)) != hipSuccess) return e;
+    g.sp = c->sp_d;
+    if ((e = launch_split_gemm(kEpiResid, g, s)) != hipSuccess) return e;
   }
 
   if (d.has_head) {
     GemmArgs g = base;
-    g.w = m->head; g.a = c->a_h; g.k = m->H; g.kb = m->H / 32; g.nb = m->nb_head; g.sp = c->sp_head; g.nw = c->nw_head;
+    g.w = m->head; g.a = c->a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_head; g.nw = c->nw_head;
+    g.sp = 1;
     g.amax = c->amax; g.logits = r.logits; g.vocab = m->V;
     if ((e = launch_gemm(kEpiArgmax, g, s)) != hipSuccess) return e;
   }
@@ -419,16 +430,16 @@ extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacit
   c->seq_stride = (size_t)m->nkv * capacity * m->dh;
   c->layer_stride = c->seq_stride * n_seqs;
   c->len_h.assign(n_seqs, 0); c->next_h.assign(n_seqs, 0); c->len_hi.assign(n_seqs, 0);
-  c->sp_qkv = choose_sp(m->nb_qkv, m->H / 32, "SF_SP_QKV");
-  c->sp_o = choose_sp(m->nb_h, m->Q / 32, "SF_SP_O");
-  c->sp_gu = choose_sp(m->nb_gu, m->H / 32, "SF_SP_GU");
-  c->sp_d = choose_sp(m->nb_h, m->F / 32, "SF_SP_D");
-  c->sp_head = choose_sp(m->nb_head, m->H / 32, "SF_SP_HEAD");
-  c->nw_qkv = choose_nw(m->nb_qkv, "SF_NW_QKV");
-  c->nw_o = choose_nw(m->nb_h, "SF_NW_O");
-  c->nw_gu = choose_nw(m->nb_gu, "SF_NW_GU");
-  c->nw_d = choose_nw(m->nb_h, "SF_NW_D");
-  c->nw_head = choose_nw(m->nb_head, "SF_NW_HEAD");
+  c->nw_qkv = choose_nw(m->nb_qkv, m->H / kTileK, "SF_NW_QKV");
+  c->nw_o = choose_nw(m->nb_h, m->Q / kTileK, "SF_NW_O");
+  c->nw_gu = choose_nw(m->nb_gu, m->H / kTileK, "SF_NW_GU");
+  c->nw_d = choose_nw(m->nb_h, m->F / kTileK, "SF_NW_D");
+  c->nw_head = choose_nw(m->nb_head, m->H / kTileK, "SF_NW_HEAD");
+  c->sp_qkv = choose_sp(m->nb_qkv, m->H / kTileK, c->nw_qkv, "SF_SP_QKV");
+  c->sp_o = choose_sp(m->nb_h, m->Q / kTileK, c->nw_o, "SF_SP_O");
+  c->sp_gu = 1;
+  c->sp_d = choose_sp(m->nb_h, m->F / kTileK, c->nw_d, "SF_SP_D");
+  c->sp_head = 1;
 
   hipStream_t s = m->stream;
   auto bail = [&](sf_status st) { cache_release(c); return st; };
@@ -456,18 +467,15 @@ extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacit
   TRY(dalloc((void**)&c->a_o, 2 * R * m->Q * 2));
   TRY(dalloc((void**)&c->a_f, 2 * R * m->F * 2));
   TRY(dalloc((void**)&c->hidden, R * m->H * 2));
-  TRY(dalloc((void**)&c->ssq, R * (m->H / 16) * 4));
+  TRY(dalloc((void**)&c->ssq, R * (m->H / kTileN) * 4));
+  {
+    const size_t n_qkv = (size_t)m->Q + 2 * m->KV;
+    size_t pe = std::max({(size_t)c->sp_qkv * n_qkv, (size_t)c->sp_o * m->H, (size_t)c->sp_d * m->H});
+    TRY(dalloc((void**)&c->part, pe * R * 4));
+  }
   TRY(dalloc((void**)&c->q, R * m->Q * 4));
   TRY(dalloc((void**)&c->apart, R * m->nq * (size_t)c->nchunk * (m->dh + 2) * 4));
   TRY(dalloc((void**)&c->amax, R * m->nb_head * 8));
-  size_t gp = 0;
-  gp = std::max(gp, (size_t)m->nb_qkv * c->sp_qkv);
-  gp = std::max(gp, (size_t)m->nb_h * c->sp_o);
-  gp = std::max(gp, (size_t)m->nb_gu * c->sp_gu);
-  gp = std::max(gp, (size_t)m->nb_h * c->sp_d);
-  gp = std::max(gp, (size_t)m->nb_head * c->sp_head);
-  TRY(dalloc((void**)&c->gpart, gp * 4 * 256 * 4));
-  TRY(dalloc((void**)&c->counters, (size_t)std::max({m->nb_qkv, m->nb_gu, m->nb_head, m->nb_h}) * 4));
   TRY(dalloc((void**)&c->rope, (size_t)capacity * (m->dh / 2) * 8));
   TRY(dalloc((void**)&c->res_d, 4 * kMaxRows * 4));
   TRY(dalloc((void**)&c->dout_d, (size_t)n_seqs * kMaxDraftSteps * 4));
@@ -779,8 +787,8 @@ extern "C" sf_status sf_time_kernel(sf_cache* c, int32_t kernel, int32_t iters, 
   double L_total = 0;
   for (int b = 0; b < c->B; ++b) L_total += c->len_h[b] + c->T;
   GemmArgs base{};
-  base.rows = rows; base.part = c->gpart; base.counters = c->counters; base.ssq_in = c->ssq;
-  base.nparts_in = m->H / 16; base.eps = m->d.rms_eps; base.T = c->T; base.len = c->len; base.cap = c->cap;
+  base.rows = rows; base.ssq_in = c->ssq; base.part = c->part; base.sp = 1;
+  base.nparts_in = m->H / kTileN; base.eps = m->d.rms_eps; base.T = c->T; base.len = c->len; base.cap = c->cap;
   base.seq_stride = (long)c->seq_stride; base.rope = c->rope; base.nq = m->nq; base.nkv = m->nkv; base.dh = m->dh;
   double by = 0;
   auto launch = [&](int it) -> hipError_t {
@@ -791,10 +799,10 @@ extern "C" sf_status sf_time_kernel(sf_cache* c, int32_t kernel, int32_t iters, 
     GemmArgs g = base;
     switch (kernel) {
       case SF_KERNEL_QKV:
-        g.w = Ly.wqkv; g.a = c->a_h; g.k = m->H; g.kb = m->H / 32; g.nb = m->nb_qkv; g.sp = c->sp_qkv; g.nw = c->nw_qkv;
-        g.bias = Ly.bqkv; g.q = c->q; g.kc = kc; g.vc = vc;
-        by = (double)(m->Q + 2 * m->KV) * m->H * 2 + (double)rows * (m->H * 2 + m->Q * 4 + 2 * m->KV * 2);
-        return launch_gemm(kEpiQkv, g, s);
+        g.w = Ly.wqkv; g.a = c->a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_qkv; g.nw = c->nw_qkv;
+        g.bias = Ly.bqkv; g.q = c->q; g.kc = kc; g.vc = vc; g.sp = c->sp_qkv; g.n_out = m->Q + 2 * m->KV;
+        by = (double)(m->Q + 2 * m->KV) * m->H * 2 + (double)rows * (m->H * 4 + m->Q * 4 + 2 * m->KV * 2);
+        return launch_split_gemm(kEpiQkv, g, s);
       case SF_KERNEL_ATTENTION: {
         AttnArgs aa{};
         aa.q = c->q; aa.kc = kc; aa.vc = vc; aa.seq_stride = (long)c->seq_stride; aa.cap = c->cap; aa.len = c->len;
@@ -805,24 +813,24 @@ extern "C" sf_status sf_time_kernel(sf_cache* c, int32_t kernel, int32_t iters, 
         return launch_attention(aa, m->dh, c->B, s);
       }
       case SF_KERNEL_OPROJ:
-        g.w = Ly.wo; g.a = c->a_o; g.k = m->Q; g.kb = m->Q / 32; g.nb = m->nb_h; g.sp = c->sp_o; g.nw = c->nw_o;
-        g.x = c->x; g.a_next = c->a_h; g.gain_next = Ly.g2; g.ssq_out = c->ssq; g.n_out = m->H;
-        by = (double)m->H * m->Q * 2 + (double)rows * (m->Q * 2 + m->H * (4 + 4 + 2));
-        return launch_gemm(kEpiResid, g, s);
+        g.w = Ly.wo; g.a = c->a_o; g.k = m->Q; g.kb = m->Q / kTileK; g.nb = m->nb_h; g.nw = c->nw_o;
+        g.x = c->x; g.a_next = c->a_h; g.gain_next = Ly.g2; g.ssq_out = c->ssq; g.n_out = m->H; g.sp = c->sp_o;
+        by = (double)m->H * m->Q * 2 + (double)rows * (m->Q * 4 + m->H * (4 + 4 + 4));
+        return launch_split_gemm(kEpiResid, g, s);
       case SF_KERNEL_GATEUP:
-        g.w = Ly.wgu; g.a = c->a_h; g.k = m->H; g.kb = m->H / 32; g.nb = m->nb_gu; g.sp = c->sp_gu; g.nw = c->nw_gu;
-        g.h = c->a_f; g.ffn = m->F;
-        by = (double)2 * m->F * m->H * 2 + (double)rows * (m->H * 2 + m->F * 2);
+        g.w = Ly.wgu; g.a = c->a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_gu; g.nw = c->nw_gu;
+        g.h = c->a_f; g.ffn = m->F; g.sp = 1;
+        by = (double)2 * m->F * m->H * 2 + (double)rows * (m->H * 4 + m->F * 4);
         return launch_gemm(kEpiSwiglu, g, s);
       case SF_KERNEL_DOWN:
-        g.w = Ly.wd; g.a = c->a_f; g.k = m->F; g.kb = m->F / 32; g.nb = m->nb_h; g.sp = c->sp_d; g.nw = c->nw_d;
-        g.x = c->x; g.a_next = c->a_h; g.gain_next = Ly.g1; g.ssq_out = c->ssq; g.n_out = m->H;
-        by = (double)m->H * m->F * 2 + (double)rows * (m->F * 2 + m->H * (4 + 4 + 2));
-        return launch_gemm(kEpiResid, g, s);
+        g.w = Ly.wd; g.a = c->a_f; g.k = m->F; g.kb = m->F / kTileK; g.nb = m->nb_h; g.nw = c->nw_d;
+        g.x = c->x; g.a_next = c->a_h; g.gain_next = Ly.g1; g.ssq_out = c->ssq; g.n_out = m->H; g.sp = c->sp_d;
+        by = (double)m->H * m->F * 2 + (double)rows * (m->F * 4 + m->H * (4 + 4 + 4));
+        return launch_split_gemm(kEpiResid, g, s);
       default:
-        g.w = m->head; g.a = c->a_h; g.k = m->H; g.kb = m->H / 32; g.nb = m->nb_head; g.sp = c->sp_head; g.nw = c->nw_head;
-        g.amax = c->amax; g.vocab = m->V;
-        by = (double)m->V * m->H * 2 + (double)rows * (m->H * 2 + m->nb_head * 8);
+        g.w = m->head; g.a = c->a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_head; g.nw = c->nw_head;
+        g.amax = c->amax; g.vocab = m->V; g.sp = 1;
+        by = (double)m->V * m->H * 2 + (double)rows * (m->H * 4 + m->nb_head * 8);
         return launch_gemm(kEpiArgmax, g, s);
     }
   };

@@ -8,8 +8,8 @@
 namespace sf {
 
 constexpr int kWave = 64;
-constexpr int kTileN = 16;                    // output features per MFMA tile
-constexpr int kTileK = 32;                    // reduction depth per MFMA tile
+constexpr int kTileN = 32;                    // weight rows per packed tile (32x32x16 MFMA)
+constexpr int kTileK = 16;                    // reduction depth per packed tile
 constexpr int kBatch = 16;                    // weight tiles a wave loads before using them
 constexpr int kChunk = 64;                    // attention: KV positions per chunk (position aligned)
 constexpr int kMaxRows = 64;                  // rows (sequences x positions) per pass
@@ -34,15 +34,15 @@ struct Stage {
   int32_t draft[kMaxSeqs * kMaxK];
 };
 
-enum Epi { kEpiQkv = 0, kEpiResid = 1, kEpiSwiglu = 2, kEpiArgmax = 3 };
+enum Epi { kEpiQkv = 0, kEpiResid = 1, kEpiSwiglu = 2, kEpiArgmax = 3, kEpiPartial = 4 };
 
 struct GemmArgs {
-  const uint4* w;          // packed weight tiles [nb][kb][64 lanes] x 16 B
+  const uint4* w;          // packed weight tiles [nb][kb][64 lanes] x 16 B (32 rows x 16 k per tile)
   const uint16_t* a;       // bf16 activations [2*rows][k]: hi parts, then lo parts
-  int k, kb, nb, rows, sp; // in-features, k tiles, n blocks, valid rows, workgroups per n block
+  int k, kb, nb, rows;     // in-features, k tiles (k/16), 32-row n blocks, valid rows
+  int sp;                  // workgroups splitting each block's k range (>1: partials + reduce)
+  float* part;             // split partials [sp][rows][n_out] (kEpiPartial)
   int nw;                  // waves per workgroup: 4 or 8
-  float* part;             // split partials [nb][sp][mt*256]
-  int* counters;           // [nb], zero between launches
   // RMSNorm folded into the consumer: row scale = 1/sqrt(sum(ssq_in[r][*])/k + eps)
   const float* ssq_in;
   int nparts_in;
@@ -63,9 +63,9 @@ struct GemmArgs {
   float* x;                // residual [rows][n_out]
   uint16_t* a_next;        // x * gain_next as hi/lo bf16 rows [2*rows][n_out]
   const float* gain_next;  // [n_out]
-  float* ssq_out;          // [rows][nb]
+  float* ssq_out;          // [rows][nb]: sums of squares of x per 32 columns
   uint16_t* hidden;        // optional bf16(x) [rows][n_out]
-  int n_out;
+  int n_out;               // output features (also the partial buffer's row length)
   // kEpiSwiglu
   uint16_t* h;             // silu(gate)*up as hi/lo bf16 rows [2*rows][ffn]
   int ffn;
@@ -83,7 +83,7 @@ struct EmbedArgs {
   const float* gain;       // first layer's ln1
   float* x;
   uint16_t* a;             // x * gain as hi/lo bf16 rows [2*rows][H]
-  float* ssq;              // [rows][H/16]
+  float* ssq;              // [rows][H/32]
   int rows, T, H, V, kmax;
 };
 
@@ -114,6 +114,8 @@ struct AcceptArgs {
 
 // Launchers (kernels.hip).
 hipError_t launch_gemm(int epi, const GemmArgs& g, hipStream_t s);
+// Reduce kEpiPartial output of a split GEMM and apply epilogue `epi` (kEpiQkv or kEpiResid).
+hipError_t launch_reduce(int epi, const GemmArgs& g, hipStream_t s);
 hipError_t launch_embed(const EmbedArgs& e, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int dh, int B, hipStream_t s);
 int attention_spans(int cap);

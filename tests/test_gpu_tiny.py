@@ -229,12 +229,14 @@ def test_errors_leave_state_unchanged(pair):
     assert sfb.sf_cache_state(eng.cache, 0) == (100, st[1])
 
 
-def test_four_wave_workgroups_and_64_row_chunks(monkeypatch):
-    """Every GEMM with 4-wave workgroups (the choice for wide projections) and prefill
-    chunks of 64 rows: all row/pair items of the epilogues must be covered."""
+def test_four_wave_workgroups_split_k_and_64_row_chunks(monkeypatch):
+    """Every GEMM with 4-wave workgroups, QKV / O / down split over two workgroups per
+    block (partials + reduce kernels), and prefill chunks of 64 rows."""
     need_gpu()
     for v in ("SF_NW_QKV", "SF_NW_O", "SF_NW_GU", "SF_NW_D", "SF_NW_HEAD"):
         monkeypatch.setenv(v, "4")
+    for v in ("SF_SP_QKV", "SF_SP_O", "SF_SP_D"):
+        monkeypatch.setenv(v, "2")
     p = Pair(S, 1, capacity=128, k_max=4)
     try:
         for n in (64, 100):
