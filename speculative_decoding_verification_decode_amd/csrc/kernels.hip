@@ -313,6 +313,7 @@ hipError_t launch_gemm(int epi, const GemmArgs& g, hipStream_t s) {
 // ----------------------------------------------------------------------------------------------
 // Reductions of split-K partials, in split order, fused with the epilogue the undivided
 // GEMM would have run.
+constexpr int kMaxSplit = 8;
 
 // Row scale 1/sqrt(mean(x^2) + eps) from the per-32-column sums of squares, summed in the
 // same order as the GEMM prologue: lane l takes parts l, l+64, then a cross-lane tree.
@@ -342,12 +343,18 @@ __global__ __launch_bounds__(256) void k_reduce_qkv(const GemmArgs g) {
   if (item >= g.nb * 16) return;
   const int nb = item >> 4, p = item & 15;
   const int n1 = nb * 32 + p, n2 = n1 + 16;
-  float a1 = 0.f, a2 = 0.f;
-  for (int q = 0; q < g.sp; ++q) {
-    const float* pq = g.part + ((size_t)q * g.rows + m) * g.n_out;
-    a1 += pq[n1];
-    a2 += pq[n2];
+  // Partials of up to kMaxSplit splits, all loads issued before the (ordered) sum.
+  float p1[kMaxSplit], p2[kMaxSplit];
+#pragma unroll
+  for (int q = 0; q < kMaxSplit; ++q) {
+    const float* pq = g.part + ((size_t)min(q, g.sp - 1) * g.rows + m) * g.n_out;
+    p1[q] = pq[n1];
+    p2[q] = pq[n2];
   }
+  float a1 = 0.f, a2 = 0.f;
+#pragma unroll
+  for (int q = 0; q < kMaxSplit; ++q)
+    if (q < g.sp) { a1 += p1[q]; a2 += p2[q]; }
   const float y1 = a1 * sc + g.bias[n1];
   const float y2 = a2 * sc + g.bias[n2];
   const int half = g.dh >> 1, bph = g.dh >> 5;
@@ -387,8 +394,13 @@ __global__ __launch_bounds__(256) void k_reduce_resid(const GemmArgs g) {
   const int n = blockIdx.x * 256 + threadIdx.x;
   float v = 0.f;
   if (n < g.n_out) {
+    float pv[kMaxSplit];
+#pragma unroll
+    for (int q = 0; q < kMaxSplit; ++q) pv[q] = g.part[((size_t)min(q, g.sp - 1) * g.rows + m) * g.n_out + n];
     float acc = 0.f;
-    for (int q = 0; q < g.sp; ++q) acc += g.part[((size_t)q * g.rows + m) * g.n_out + n];
+#pragma unroll
+    for (int q = 0; q < kMaxSplit; ++q)
+      if (q < g.sp) acc += pv[q];
     const size_t o = (size_t)m * g.n_out + n;
     v = g.x[o] + acc;
     g.x[o] = v;
@@ -461,8 +473,10 @@ hipError_t launch_embed(const EmbedArgs& e, hipStream_t s) {
 // V transposed, P goes through LDS to change from the MFMA output layout to the input one.
 // Q and P enter the MFMAs as bf16 hi + lo pairs (two MFMAs each); K and V are the bf16 cache.
 // Spans are fixed by absolute position, so a row's result does not depend on the length.
-constexpr int kSpanChunks = 2;
+constexpr int kSpanChunks = 1;
 constexpr int kSpan = kSpanChunks * kChunk;
+// Spans a row can need at the largest cache capacity, held 64 per register slot in the merge.
+constexpr int kSpanSlots = (kMaxCapacity / kSpan + 63) / 64;
 
 template <int DH>
 __global__ __launch_bounds__(256) void k_attn(const AttnArgs a) {
@@ -487,21 +501,46 @@ __global__ __launch_bounds__(256) void k_attn(const AttnArgs a) {
   const int wrow0 = rg * 64 + wave * 16;         // first query row of this wave
   const bool active = wrow0 < nrows;
 
+  // K/V of a chunk: each thread loads kKvPerThread 16-byte pieces of K and of V, all
+  // issued before any is used (positions past the last row's are zero).
+  const uint16_t* kbase = a.kc + (size_t)b * a.seq_stride + (size_t)kvh * a.cap * DH;
+  const uint16_t* vbase = a.vc + (size_t)b * a.seq_stride + (size_t)kvh * a.cap * DH;
+  constexpr int kKvPerThread = kChunk * DH / 8 / 256;
+  u32x4 kreg[kKvPerThread], vreg[kKvPerThread];
+  auto load_kv = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < kKvPerThread; ++u) {
+      const int idx = tid + u * 256;
+      const int j = idx / (DH / 8), d8 = (idx - j * (DH / 8)) * 8;
+      const int pos = min(c0 + j, plast);
+      kreg[u] = *(const u32x4*)(kbase + (size_t)pos * DH + d8);
+      vreg[u] = *(const u32x4*)(vbase + (size_t)pos * DH + d8);
+      if (c0 + j > plast) { kreg[u] = (u32x4){0u, 0u, 0u, 0u}; vreg[u] = kreg[u]; }
+    }
+  };
+  load_kv(span0);
+
   // Q as the MFMA A operand: lane holds row wrow0 + l16, dims ks*32 + 8*g4 .. +8, as a
   // bf16 hi part (qa) and lo part (ql).
   bf16x8 qa[DH / 32], ql[DH / 32];
   {
     const int qr = wrow0 + l16;
     const bool ok = qr < nrows;
-    const int slot = ok ? qr / G : 0;
-    const int hh = kvh * G + (ok ? qr - slot * G : 0);
+    const int qc = min(qr, nrows - 1);
+    const int slot = qc / G;
+    const int hh = kvh * G + (qc - slot * G);
     const float* qp = a.q + ((size_t)(b * a.T + slot) * a.nq + hh) * DH;
+    float qv[DH / 32][8];
+#pragma unroll
+    for (int ks = 0; ks < DH / 32; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[ks][e] = qp[ks * 32 + g4 * 8 + e];
 #pragma unroll
     for (int ks = 0; ks < DH / 32; ++ks) {
       uint16_t t[8], tl[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float v = ok ? qp[ks * 32 + g4 * 8 + e] : 0.f;
+        const float v = ok ? qv[ks][e] : 0.f;
         t[e] = f2bf(v);
         tl[e] = f2bf(v - bf2f(t[e]));
       }
@@ -533,22 +572,18 @@ __global__ __launch_bounds__(256) void k_attn(const AttnArgs a) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) { mrun[r] = -INFINITY; lrun[r] = 0.f; }
 
-  const uint16_t* kbase = a.kc + (size_t)b * a.seq_stride + (size_t)kvh * a.cap * DH;
-  const uint16_t* vbase = a.vc + (size_t)b * a.seq_stride + (size_t)kvh * a.cap * DH;
 
   for (int ci = 0; ci < kSpanChunks; ++ci) {
     const int c0 = span0 + ci * kChunk;
     if (c0 > plast) break;
+    if (ci > 0) load_kv(c0);
     __syncthreads();
-    for (int idx = tid; idx < kChunk * DH / 8; idx += 256) {
+#pragma unroll
+    for (int u = 0; u < kKvPerThread; ++u) {
+      const int idx = tid + u * 256;
       const int j = idx / (DH / 8), d8 = (idx - j * (DH / 8)) * 8;
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (c0 + j <= plast) {
-        kv = *(const u32x4*)(kbase + (size_t)(c0 + j) * DH + d8);
-        vv = *(const u32x4*)(vbase + (size_t)(c0 + j) * DH + d8);
-      }
-      *(u32x4*)(&Kl[j * KP + d8]) = kv;
-      const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+      *(u32x4*)(&Kl[j * KP + d8]) = kreg[u];
+      const uint32_t vw[4] = {vreg[u].x, vreg[u].y, vreg[u].z, vreg[u].w};
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         Vt[(d8 + 2 * t) * VP + j] = (uint16_t)(vw[t] & 0xFFFFu);
@@ -663,39 +698,55 @@ __global__ __launch_bounds__(256) void k_combine(const AttnArgs a) {
   const size_t rstride = DH + 2;
   const size_t sstride = (size_t)nrows * rstride;
   const float* base = a.part + ((size_t)b * a.nkv + kvh) * a.nchunk * sstride + (size_t)qr * rstride;
-  float m0 = -INFINITY, m1 = -INFINITY, l0 = 0.f, l1 = 0.f;
-  if (lane < np) { m0 = base[lane * sstride + DH]; l0 = base[lane * sstride + DH + 1]; }
-  if (lane + 64 < np) { m1 = base[(lane + 64) * sstride + DH]; l1 = base[(lane + 64) * sstride + DH + 1]; }
-  float M = fmaxf(m0, m1);
+  // Lane l holds span l + 64*i of the row in slot i.
+  float ms[kSpanSlots], ws[kSpanSlots];
+  float M = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kSpanSlots; ++i) {
+    const int sp = lane + 64 * i;
+    ms[i] = (sp < np) ? base[sp * sstride + DH] : -INFINITY;
+    ws[i] = (sp < np) ? base[sp * sstride + DH + 1] : 0.f;
+    M = fmaxf(M, ms[i]);
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  const float w0 = (m0 == -INFINITY) ? 0.f : exp2f(m0 - M);
-  const float w1 = (m1 == -INFINITY) ? 0.f : exp2f(m1 - M);
-  float Ls = l0 * w0 + l1 * w1;
+  float Ls = 0.f;
+#pragma unroll
+  for (int i = 0; i < kSpanSlots; ++i) {
+    const float w = (ms[i] == -INFINITY) ? 0.f : exp2f(ms[i] - M);
+    Ls += ws[i] * w;   // slot order, then the cross-lane tree
+    ws[i] = w;
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) Ls += __shfl_xor(Ls, o);
   float o0 = 0.f, o1 = 0.f;
-  int j = 0;
-  for (; j + 8 <= np; j += 8) {
-    float v0[8], v1[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float* pj = base + (size_t)(j + u) * sstride;
-      v0[u] = pj[lane];
-      v1[u] = (DH > 64) ? pj[lane + 64] : 0.f;
-    }
+  for (int i = 0; i < kSpanSlots; ++i) {
+    const int j0 = 64 * i;
+    if (j0 >= np) break;
+    const int j1 = min(np, j0 + 64);
+    int j = j0;
+    for (; j + 8 <= j1; j += 8) {
+      float v0[8], v1[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float w = (j + u < 64) ? __shfl(w0, j + u) : __shfl(w1, j + u - 64);
-      o0 += w * v0[u];
-      o1 += w * v1[u];
+      for (int u = 0; u < 8; ++u) {
+        const float* pj = base + (size_t)(j + u) * sstride;
+        v0[u] = pj[lane];
+        v1[u] = (DH > 64) ? pj[lane + 64] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float w = __shfl(ws[i], j + u - j0);
+        o0 += w * v0[u];
+        o1 += w * v1[u];
+      }
     }
-  }
-  for (; j < np; ++j) {
-    const float w = (j < 64) ? __shfl(w0, j) : __shfl(w1, j - 64);
-    const float* pj = base + (size_t)j * sstride;
-    o0 += w * pj[lane];
-    if (DH > 64) o1 += w * pj[lane + 64];
+    for (; j < j1; ++j) {
+      const float w = __shfl(ws[i], j - j0);
+      const float* pj = base + (size_t)j * sstride;
+      o0 += w * pj[lane];
+      if (DH > 64) o1 += w * pj[lane + 64];
+    }
   }
   const float inv = 1.0f / Ls;
   const size_t qd = (size_t)a.nq * DH;

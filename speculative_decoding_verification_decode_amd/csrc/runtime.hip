@@ -117,9 +117,9 @@ static int choose_sp(int nb, int kb, int nw, const char* env) {
   sp = std::max(1, std::min(sp, kb / (nw * 4)));
   if (const char* v = getenv(env)) {
     int o = atoi(v);
-    if (o >= 1 && o <= 64) sp = o;
+    if (o >= 1) sp = o;
   }
-  return sp;
+  return std::min(sp, 8);  // the reduce kernels add at most eight partials
 }
 
 static sf_status check_desc(const sf_model_desc* d) {
@@ -423,7 +423,7 @@ extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacit
   if (!m || !out) return fail(SF_E_ARG, "model or out is NULL");
   if (k_max < 0 || k_max >= kMaxK) return fail(SF_E_ARG, "k_max must be in 0..15");
   if (n_seqs < 1 || n_seqs * (k_max + 1) > kMaxRows) return fail(SF_E_ARG, "n_seqs*(k_max+1) must be in 1..64");
-  if (capacity < k_max + 1 || capacity > 16384) return fail(SF_E_ARG, "capacity must be in k_max+1..16384");
+  if (capacity < k_max + 1 || capacity > kMaxCapacity) return fail(SF_E_ARG, "capacity must be in k_max+1..16384");
   sf_cache* c = new sf_cache();
   c->m = m; c->B = n_seqs; c->cap = capacity; c->kmax = k_max; c->T = k_max + 1;
   c->nchunk = attention_spans(capacity);

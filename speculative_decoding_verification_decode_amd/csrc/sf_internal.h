@@ -17,6 +17,7 @@ constexpr int kMaxSeqs = 64;
 constexpr int kMaxK = 16;                     // drafts per sequence (k_max <= 15, T <= 16)
 constexpr int kMaxDraftSteps = 256;
 constexpr int kPrefillChunk = 64;
+constexpr int kMaxCapacity = 16384;  // positions per sequence
 
 // Stage flags (device side).
 constexpr int kFlagNoCommit = 1;

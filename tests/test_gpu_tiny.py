@@ -264,3 +264,36 @@ def test_four_wave_workgroups_split_k_and_64_row_chunks(monkeypatch):
         assert (logits.double().cpu() - r["logits"]).abs().max().item() <= LOGIT_TOL
     finally:
         p.close()
+
+
+def test_largest_capacity_and_longest_draft():
+    """Capacity 16384 with K=15 drafts: the span merge sees up to 256 position spans.  Seeded
+    synthetic K/V fill contexts on both sides of the 64-, 128- and 192-span boundaries and
+    the last ones the capacity allows."""
+    need_gpu()
+    K, cap = 15, 16384
+    p = Pair(S, 1, capacity=cap, k_max=K)
+    try:
+        kb, vb = synth.synthetic_kv(S, cap - K - 1, synth.seeds(1)["kv"])
+        kd = torch.from_numpy(np.ascontiguousarray(kb).view(np.int16)).cuda()
+        vd = torch.from_numpy(np.ascontiguousarray(vb).view(np.int16)).cuda()
+        rng = np.random.default_rng(synth.seeds(1)["draft"])
+        for ctx in (4080, 4096, 8177, 12300, cap - K - 1):
+            say(f"[tiny/cap] ctx={ctx}")
+            nxt = int(rng.integers(0, S.vocab))
+            p.sfb.sf_kv_write(p.eng.cache, 0, kd, vd, ctx, kb.shape[2])
+            p.sfb.sf_set_next(p.eng.cache, 0, nxt)
+            d = rng.integers(0, S.vocab, size=(1, K)).astype(np.int32)
+            logits = torch.empty((K + 1, S.vocab), dtype=torch.float32, device="cuda")
+            acc, tgt = p.sfb.sf_verify(p.eng.cache, d, None, p.sfb.SF_DEBUG_LOGITS | p.sfb.SF_NO_COMMIT,
+                                       dev_out=logits)
+            torch.cuda.synchronize()
+            c = oracle.KVCache(S, ctx + K + 1)
+            c.load(kb, vb, ctx, next_token=nxt)
+            r = oracle.verify(p.model, c, d[0], K, commit=False)
+            err = (logits.double().cpu() - r["logits"]).abs().max().item()
+            say(f"[tiny/cap] ctx={ctx} max |dlogit| {err:.3g}")
+            assert err <= LOGIT_TOL
+            check_targets(tgt[0], r, K)
+    finally:
+        p.close()
