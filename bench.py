@@ -11,6 +11,7 @@ with SF_NO_COMMIT so each step verifies at exactly the nominal context.
 Prints one JSON line (see the field list at the end of main()).
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -23,10 +24,26 @@ HBM_PEAK_GBS = 8000.0
 K = 8
 CONTEXTS = (512, 2048, 8192)
 CAPACITY = 8192 + 16
+KERNEL_SRC = os.path.join(ROOT, "speculative_decoding_verification_decode_amd", "csrc", "kernels.hip")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gate_up_7b_k8_hbm_traffic.md")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def measured_traffic():
+    """HBM bytes per launch of the gate/up GEMM from the committed counter record, or None when
+    the kernel source has changed since the counters were taken."""
+    try:
+        rec = dict(l[2:].split(": ", 1) for l in open(TRAFFIC_RECORD).read().splitlines()
+                   if l.startswith("- ") and ": " in l)
+        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+        if rec.get("kernels.hip sha256", "").strip("` ") != src:
+            return None
+        return int(rec["traffic bytes per launch"].strip("` "))
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def main():
@@ -36,6 +53,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--kernel-iters", type=int, default=56)
+    ap.add_argument("--copy-calibrate", action="store_true",
+                    help="also run plain device copies of 1 GiB, so HBM byte counters can be scaled")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; --gpus above 1 is not supported "
@@ -144,6 +163,15 @@ def main():
     for kid, nm in names.items():
         us, by = sfb.sf_time_kernel(c512, kid, args.kernel_iters)
         kern[nm] = {"us": round(us, 3), "bytes": int(by), "GBps": round(by / us / 1e3, 1)}
+    if args.copy_calibrate:
+        # Plain copies of a known size (1 GiB read, 1 GiB written), for scaling byte counters.
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     layer_bytes = sum(kern[n]["bytes"] for n in ("qkv", "o_proj", "gate_up", "down"))
     # Algorithmic bytes of one verify: every layer's weights and activations once, the
     # LM head once, and K/V of positions 0..ctx+K read once per layer.
@@ -156,7 +184,7 @@ def main():
     g = kern["gate_up"]
     roofline = {"bound": "hbm", "kernel": "k_gemm<SWIGLU> (gate/up projection, 9 rows)",
                 "achieved": g["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(g["GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(g["GBps"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                 "launch_us": g["us"], "alg_bytes_per_launch": g["bytes"]}
 
     cpu = None
