@@ -219,3 +219,20 @@ def test_hidden_only_stack_is_prefix_of_full_stack():
     z = oracle.forward(oracle.Model(full, w0), oracle.KVCache(full, 8), toks, range(5))
     zh = oracle.rms_norm(xh, mf.get("final_norm"), full.rms_eps) @ mf.get("lm_head").T
     assert (z - zh).abs().max().item() < 1e-12
+
+
+def test_bf16_cache_holds_rounded_layer0_kv(tiny):
+    """Reading of the cache precision: K (after RoPE) and V are rounded to bf16 once on
+    append.  Layer 0's K/V depend only on the embedding and layer-0 weights, so a bf16
+    cache must hold exactly bf16(the float64 cache's layer-0 values)."""
+    S = synth.TINY
+    toks = synth.prompt_ids(S.vocab, 12, 91)
+    c16 = oracle.KVCache(S, 16)
+    c64 = oracle.KVCache(S, 16, dtype=F64)
+    oracle.forward(tiny, c16, toks, range(12))
+    oracle.forward(tiny, c64, toks, range(12))
+    for got, ref in ((c16.k[0, :, :12], c64.k[0, :, :12]), (c16.v[0, :, :12], c64.v[0, :, :12])):
+        want = oracle.round_bf16(ref).to(torch.bfloat16)
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+    # and a later layer differs from plain rounding (the rounded cache feeds attention)
+    assert not torch.equal(c16.k[1, :, :12].double(), oracle.round_bf16(c64.k[1, :, :12]))
