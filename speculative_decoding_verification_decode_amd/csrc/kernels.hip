@@ -11,54 +11,9 @@
 //   k_gemm<RESID>  down projection (split-K across workgroups, deterministic)
 // then k_gemm<ARGMAX> (LM head with per-tile argmax) and k_accept (argmax merge,
 // longest-prefix accept, commit).  The pass is captured once into a hipGraph.
-#include "sf_internal.h"
-
-#include <math.h>
+#include "device.h"
 
 namespace sf {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-
-// Round to nearest even (inputs are finite or inf; NaN stays NaN).
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-// Activations feeding an MFMA are carried as two bf16 values, hi = bf16(v) and
-// lo = bf16(v - hi) (about 16 significant bits), stored as rows r and rows + r of the
-// operand matrix; the weights are bf16 and the products accumulate in fp32.
-__device__ __forceinline__ void store_split(uint16_t* base, size_t row_stride, int rows, int r, int col, float v) {
-  const uint16_t hi = f2bf(v);
-  base[(size_t)r * row_stride + col] = hi;
-  base[(size_t)(rows + r) * row_stride + col] = f2bf(v - bf2f(hi));
-}
-
-// Word 3 of a raw buffer resource on gfx9-family GPUs (gfx950 included).
-constexpr int kBufferWord3 = 0x00020000;
-// RMSNorm sum-of-squares partials (one per 32 columns) read per lane: hidden <= 64*32*2.
-constexpr int kSsqPerLane = 2;
-// Weight tiles per pipelined half-batch.
-constexpr int kHalf = 8;
-// Cache policy of the weight stream: non-temporal (each weight byte is read once per pass).
-constexpr int kCacheStream = 2;
-
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-// Element (n_local, m) of a 32 x (32*MT) accumulator tile kept in 32x32 MFMA output order:
-// lane l, register r of m-tile mt holds n_local = 8*(r/4) + 4*(l/32) + r%4, m = mt*32 + l%32.
-__device__ __forceinline__ int tile_idx(int nl, int m) {
-  const int lane = (m & 31) + (((nl & 7) >> 2) << 5);
-  const int r = ((nl >> 3) << 2) + (nl & 3);
-  return (m >> 5) * 1024 + lane * 16 + r;
-}
 
 // ----------------------------------------------------------------------------------------------
 // Skinny GEMM: Y[m][n] = sum_k A[m][k] * W[n][k] for m < rows.  A has 2*rows rows (bf16 hi
@@ -464,294 +419,17 @@ hipError_t launch_embed(const EmbedArgs& e, hipStream_t s) {
   return hipGetLastError();
 }
 
-// ----------------------------------------------------------------------------------------------
-// Attention, phase 1 (MFMA).  Workgroup (span x, kv head, sequence x row group) takes up to 64
-// query rows of one KV head (slot-major: row = slot*G + head-in-group, G = nq/nkv) against
-// the span's positions [x*kSpan, (x+1)*kSpan), in chunks of 64 position-aligned keys.
-// Wave w owns query rows 16w..16w+15: S = Q K^T and O += P V are 16x16x32 bf16 MFMAs, the
-// softmax is the usual running (max, sum) per row in base 2.  K is staged in LDS row-major,
-// V transposed, P goes through LDS to change from the MFMA output layout to the input one.
-// Q and P enter the MFMAs as bf16 hi + lo pairs (two MFMAs each); K and V are the bf16 cache.
-// Spans are fixed by absolute position, so a row's result does not depend on the length.
-constexpr int kSpanChunks = 1;
-constexpr int kSpan = kSpanChunks * kChunk;
-// Spans a row can need at the largest cache capacity, held 64 per register slot in the merge.
-constexpr int kSpanSlots = (kMaxCapacity / kSpan + 63) / 64;
-
 template <int DH>
 __global__ __launch_bounds__(256) void k_attn(const AttnArgs a) {
-  constexpr int KP = DH + 8;        // K row pitch (bf16): 16-byte aligned, conflict-free b128 reads
-  constexpr int VP = kChunk + 8;    // V^T row pitch
-  constexpr int PP = kChunk + 8;    // P row pitch
-  __shared__ __attribute__((aligned(16))) uint16_t Kl[kChunk * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[DH * VP];
-  __shared__ __attribute__((aligned(16))) uint16_t Pl[4][2][16 * PP];   // [wave][hi, lo]
-
-  const int x = blockIdx.x, kvh = blockIdx.y;
-  const int G = a.nq / a.nkv, nrows = a.T * G;
-  const int ngroups = (nrows + 63) / 64;
-  const int b = blockIdx.z / ngroups, rg = blockIdx.z - b * ngroups;
-  const int L = a.len[b];
-  const int plast = L + a.T - 1;
-  const int span0 = x * kSpan;
-  if (span0 > plast) return;
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int l16 = lane & 15, g4 = lane >> 4;
-  const int wrow0 = rg * 64 + wave * 16;         // first query row of this wave
-  const bool active = wrow0 < nrows;
-
-  // K/V of a chunk: each thread loads kKvPerThread 16-byte pieces of K and of V, all
-  // issued before any is used (positions past the last row's are zero).
-  const uint16_t* kbase = a.kc + (size_t)b * a.seq_stride + (size_t)kvh * a.cap * DH;
-  const uint16_t* vbase = a.vc + (size_t)b * a.seq_stride + (size_t)kvh * a.cap * DH;
-  constexpr int kKvPerThread = kChunk * DH / 8 / 256;
-  u32x4 kreg[kKvPerThread], vreg[kKvPerThread];
-  auto load_kv = [&](int c0) {
-#pragma unroll
-    for (int u = 0; u < kKvPerThread; ++u) {
-      const int idx = tid + u * 256;
-      const int j = idx / (DH / 8), d8 = (idx - j * (DH / 8)) * 8;
-      const int pos = min(c0 + j, plast);
-      kreg[u] = *(const u32x4*)(kbase + (size_t)pos * DH + d8);
-      vreg[u] = *(const u32x4*)(vbase + (size_t)pos * DH + d8);
-      if (c0 + j > plast) { kreg[u] = (u32x4){0u, 0u, 0u, 0u}; vreg[u] = kreg[u]; }
-    }
-  };
-  load_kv(span0);
-
-  // Q as the MFMA A operand: lane holds row wrow0 + l16, dims ks*32 + 8*g4 .. +8, as a
-  // bf16 hi part (qa) and lo part (ql).
-  bf16x8 qa[DH / 32], ql[DH / 32];
-  {
-    const int qr = wrow0 + l16;
-    const bool ok = qr < nrows;
-    const int qc = min(qr, nrows - 1);
-    const int slot = qc / G;
-    const int hh = kvh * G + (qc - slot * G);
-    const float* qp = a.q + ((size_t)(b * a.T + slot) * a.nq + hh) * DH;
-    float qv[DH / 32][8];
-#pragma unroll
-    for (int ks = 0; ks < DH / 32; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qv[ks][e] = qp[ks * 32 + g4 * 8 + e];
-#pragma unroll
-    for (int ks = 0; ks < DH / 32; ++ks) {
-      uint16_t t[8], tl[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = ok ? qv[ks][e] : 0.f;
-        t[e] = f2bf(v);
-        tl[e] = f2bf(v - bf2f(t[e]));
-      }
-      u32x4 u, ul;
-      u.x = t[0] | ((uint32_t)t[1] << 16);
-      u.y = t[2] | ((uint32_t)t[3] << 16);
-      u.z = t[4] | ((uint32_t)t[5] << 16);
-      u.w = t[6] | ((uint32_t)t[7] << 16);
-      ul.x = tl[0] | ((uint32_t)tl[1] << 16);
-      ul.y = tl[2] | ((uint32_t)tl[3] << 16);
-      ul.z = tl[4] | ((uint32_t)tl[5] << 16);
-      ul.w = tl[6] | ((uint32_t)tl[7] << 16);
-      qa[ks] = as_bf16x8(u);
-      ql[ks] = as_bf16x8(ul);
-    }
-  }
-  // Positions of the 4 rows this lane holds in the MFMA output layout (rows 4*g4 + r).
-  int prow[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int qr = wrow0 + 4 * g4 + r;
-    prow[r] = (qr < nrows) ? L + qr / G : -1;
-  }
-
-  f32x4 o[DH / 16];
-#pragma unroll
-  for (int nt = 0; nt < DH / 16; ++nt) o[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float mrun[4], lrun[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) { mrun[r] = -INFINITY; lrun[r] = 0.f; }
-
-
-  for (int ci = 0; ci < kSpanChunks; ++ci) {
-    const int c0 = span0 + ci * kChunk;
-    if (c0 > plast) break;
-    if (ci > 0) load_kv(c0);
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < kKvPerThread; ++u) {
-      const int idx = tid + u * 256;
-      const int j = idx / (DH / 8), d8 = (idx - j * (DH / 8)) * 8;
-      *(u32x4*)(&Kl[j * KP + d8]) = kreg[u];
-      const uint32_t vw[4] = {vreg[u].x, vreg[u].y, vreg[u].z, vreg[u].w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        Vt[(d8 + 2 * t) * VP + j] = (uint16_t)(vw[t] & 0xFFFFu);
-        Vt[(d8 + 2 * t + 1) * VP + j] = (uint16_t)(vw[t] >> 16);
-      }
-    }
-    __syncthreads();
-    float alpha[4];
-    if (active) {
-      f32x4 sc[4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        sc[kt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < DH / 32; ++ks) {
-          const bf16x8 kb8 = as_bf16x8(*(const u32x4*)(&Kl[(kt * 16 + l16) * KP + ks * 32 + g4 * 8]));
-          sc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb8, sc[kt], 0, 0, 0);
-          sc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[ks], kb8, sc[kt], 0, 0, 0);
-        }
-      }
-      // Scale, causal mask, running softmax.  Lane holds rows 4*g4+r, keys kt*16 + l16.
-      float mloc[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float m = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const int kp = c0 + kt * 16 + l16;
-          float v = sc[kt][r] * a.scale_log2;
-          v = (kp <= prow[r]) ? v : -INFINITY;
-          sc[kt][r] = v;
-          m = fmaxf(m, v);
-        }
-        m = fmaxf(m, __shfl_xor(m, 1));
-        m = fmaxf(m, __shfl_xor(m, 2));
-        m = fmaxf(m, __shfl_xor(m, 4));
-        m = fmaxf(m, __shfl_xor(m, 8));
-        mloc[r] = m;
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float mnew = fmaxf(mrun[r], mloc[r]);
-        alpha[r] = (mnew == -INFINITY) ? 1.f : exp2f(mrun[r] - mnew);
-        float ls = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const float pv = (mnew == -INFINITY) ? 0.f : exp2f(sc[kt][r] - mnew);
-          sc[kt][r] = pv;
-          ls += pv;
-        }
-        ls += __shfl_xor(ls, 1);
-        ls += __shfl_xor(ls, 2);
-        ls += __shfl_xor(ls, 4);
-        ls += __shfl_xor(ls, 8);
-        lrun[r] = lrun[r] * alpha[r] + ls;
-        mrun[r] = mnew;
-      }
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint16_t hi = f2bf(sc[kt][r]);
-          Pl[wave][0][(4 * g4 + r) * PP + kt * 16 + l16] = hi;
-          Pl[wave][1][(4 * g4 + r) * PP + kt * 16 + l16] = f2bf(sc[kt][r] - bf2f(hi));
-        }
-    }
-    __syncthreads();
-    if (active) {
-#pragma unroll
-      for (int nt = 0; nt < DH / 16; ++nt) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[nt][r] *= alpha[r];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const u32x4 pa = *(const u32x4*)(&Pl[wave][0][l16 * PP + ks * 32 + g4 * 8]);
-          const u32x4 pl = *(const u32x4*)(&Pl[wave][1][l16 * PP + ks * 32 + g4 * 8]);
-          const bf16x8 vb = as_bf16x8(*(const u32x4*)(&Vt[(nt * 16 + l16) * VP + ks * 32 + g4 * 8]));
-          o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pa), vb, o[nt], 0, 0, 0);
-          o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pl), vb, o[nt], 0, 0, 0);
-        }
-      }
-    }
-  }
-  if (!active) return;
-  const size_t rstride = DH + 2;
-  float* pbase = a.part + (((size_t)b * a.nkv + kvh) * a.nchunk + x) * (size_t)nrows * rstride;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int qr = wrow0 + 4 * g4 + r;
-    if (qr >= nrows) continue;
-    float* pr = pbase + (size_t)qr * rstride;
-#pragma unroll
-    for (int nt = 0; nt < DH / 16; ++nt) pr[nt * 16 + l16] = o[nt][r];
-    if (l16 == 0) { pr[DH] = mrun[r]; pr[DH + 1] = lrun[r]; }
-  }
+  const int G = a.nq / a.nkv, ngroups = (a.T * G + 63) / 64;
+  attn_span<DH, false>(a, blockIdx.x, blockIdx.y, blockIdx.z / ngroups, blockIdx.z % ngroups);
 }
 
-// Attention, phase 2: one wave per (row, q head); merge spans 0..p/kSpan in order.  Span
-// maxima and sums are spread over lanes; the weighted sum of partial outputs runs over
-// spans in increasing order.
 template <int DH>
 __global__ __launch_bounds__(256) void k_combine(const AttnArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int item = blockIdx.x * 4 + wave;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= a.rows * a.nq) return;
-  const int r = item / a.nq, h = item - r * a.nq;
-  const int G = a.nq / a.nkv, nrows = a.T * G;
-  const int b = r / a.T, slot = r - b * a.T;
-  const int kvh = h / G, qr = slot * G + (h - kvh * G);
-  const int p = a.len[b] + slot;
-  const int np = p / kSpan + 1;
-  const size_t rstride = DH + 2;
-  const size_t sstride = (size_t)nrows * rstride;
-  const float* base = a.part + ((size_t)b * a.nkv + kvh) * a.nchunk * sstride + (size_t)qr * rstride;
-  // Lane l holds span l + 64*i of the row in slot i.
-  float ms[kSpanSlots], ws[kSpanSlots];
-  float M = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kSpanSlots; ++i) {
-    const int sp = lane + 64 * i;
-    ms[i] = (sp < np) ? base[sp * sstride + DH] : -INFINITY;
-    ws[i] = (sp < np) ? base[sp * sstride + DH + 1] : 0.f;
-    M = fmaxf(M, ms[i]);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  float Ls = 0.f;
-#pragma unroll
-  for (int i = 0; i < kSpanSlots; ++i) {
-    const float w = (ms[i] == -INFINITY) ? 0.f : exp2f(ms[i] - M);
-    Ls += ws[i] * w;   // slot order, then the cross-lane tree
-    ws[i] = w;
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) Ls += __shfl_xor(Ls, o);
-  float o0 = 0.f, o1 = 0.f;
-#pragma unroll
-  for (int i = 0; i < kSpanSlots; ++i) {
-    const int j0 = 64 * i;
-    if (j0 >= np) break;
-    const int j1 = min(np, j0 + 64);
-    int j = j0;
-    for (; j + 8 <= j1; j += 8) {
-      float v0[8], v1[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float* pj = base + (size_t)(j + u) * sstride;
-        v0[u] = pj[lane];
-        v1[u] = (DH > 64) ? pj[lane + 64] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float w = __shfl(ws[i], j + u - j0);
-        o0 += w * v0[u];
-        o1 += w * v1[u];
-      }
-    }
-    for (; j < j1; ++j) {
-      const float w = __shfl(ws[i], j - j0);
-      const float* pj = base + (size_t)j * sstride;
-      o0 += w * pj[lane];
-      if (DH > 64) o1 += w * pj[lane + 64];
-    }
-  }
-  const float inv = 1.0f / Ls;
-  const size_t qd = (size_t)a.nq * DH;
-  store_split(a.out, qd, a.rows, r, h * DH + lane, o0 * inv);
-  if (DH > 64) store_split(a.out, qd, a.rows, r, h * DH + lane + 64, o1 * inv);
+  combine_pair<DH, false>(a, item / a.nq, item % a.nq);
 }
 
 hipError_t launch_attention(const AttnArgs& a, int dh, int B, hipStream_t s) {
@@ -778,10 +456,6 @@ int attention_spans(int cap) { return (cap + kSpan - 1) / kSpan; }
 // choice at each of the T positions (largest value, lowest index on ties; the merge is
 // order independent), count the leading drafts that match, and commit.  Wave w merges the
 // rows w, w+16, ... of the sequence.
-__device__ __forceinline__ void amax_merge(float& bv, int& bi, float v, int i) {
-  if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
-}
-
 __global__ __launch_bounds__(1024) void k_accept(const AcceptArgs a) {
   __shared__ int tgt[kMaxRows];
   const int b = blockIdx.x, tid = threadIdx.x;
