@@ -40,13 +40,22 @@ __device__ __forceinline__ T ld(const T* p) {
 }
 
 // Activations feeding an MFMA are carried as two bf16 values, hi = bf16(v) and
-// lo = bf16(v - hi) (about 16 significant bits), stored as rows r and rows + r of the
-// operand matrix; the weights are bf16 and the products accumulate in fp32.
+// lo = bf16(v - hi) (about 16 significant bits), as operand rows r and rows + r; the weights
+// are bf16 and the products accumulate in fp32.
+//
+// Operand layout ("MFMA order"): for a matrix of ext = 2*rows operand rows and K columns,
+// the 8 bf16 values of row r, columns 16t + 8h .. 16t + 8h + 7 (tile t, k half h) are the
+// 16 bytes at index (t*2 + h)*ext + r.  One 32x32x16 MFMA's operand of a k tile is then
+// 2*ext consecutive 16-byte pieces, so a wave's load of it touches a few cache lines
+// instead of one line per row.
+__device__ __forceinline__ size_t act_index(int ext, int r, int col) {
+  return ((size_t)((col >> 4) * 2 + ((col >> 3) & 1)) * ext + r) * 8 + (col & 7);
+}
 template <bool kCoh = false>
-__device__ __forceinline__ void store_split(uint16_t* base, size_t row_stride, int rows, int r, int col, float v) {
+__device__ __forceinline__ void store_split(uint16_t* base, int rows, int r, int col, float v) {
   const uint16_t hi = f2bf(v);
-  st<kCoh>(base + (size_t)r * row_stride + col, hi);
-  st<kCoh>(base + (size_t)(rows + r) * row_stride + col, f2bf(v - bf2f(hi)));
+  st<kCoh>(base + act_index(2 * rows, r, col), hi);
+  st<kCoh>(base + act_index(2 * rows, rows + r, col), f2bf(v - bf2f(hi)));
 }
 
 // Word 3 of a raw buffer resource on gfx9-family GPUs (gfx950 included).
@@ -348,8 +357,8 @@ __device__ void combine_pair(const AttnArgs& a, int r, int h) {
   }
   const float inv = 1.0f / Ls;
   const size_t qd = (size_t)a.nq * DH;
-  store_split<kCoh>(a.out, qd, a.rows, r, h * DH + lane, o0 * inv);
-  if (DH > 64) store_split<kCoh>(a.out, qd, a.rows, r, h * DH + lane + 64, o1 * inv);
+  store_split<kCoh>(a.out, a.rows, r, h * DH + lane, o0 * inv);
+  if (DH > 64) store_split<kCoh>(a.out, a.rows, r, h * DH + lane + 64, o1 * inv);
 }
 
 __device__ __forceinline__ void amax_merge(float& bv, int& bi, float v, int i) {

@@ -24,7 +24,7 @@ namespace sf {
 // keeps two 8-tile batches in flight (the next batch's weights and activations requested
 // before the current batch's MFMAs) and the waves' accumulators are added in wave order,
 // so results do not depend on scheduling.
-template <int EPI, int MT, int NW>
+template <int EPI, int MT, int NW, int KH = kHalf>
 __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
   constexpr int kThreads = NW * 64;
   constexpr int kRealRows = MT * 16;
@@ -71,38 +71,38 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
   const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
       (void*)g.a, (short)0, 2 * kMaxRows * g.k * 2, kBufferWord3);
   const int ext_rows = 2 * g.rows;
-  const int a_lane = ((lane & 31) * g.k + (lane >> 5) * 8) * 2;
+  const int a_lane = ((lane >> 5) * ext_rows + (lane & 31)) * 16;   // operand (k half, row) of tile 0, m tile 0
 
-  auto load = [&](int kt, u32x4 (&w)[kHalf], u32x4 (&a)[MT][kHalf]) {
+  auto load = [&](int kt, u32x4 (&w)[KH], u32x4 (&a)[MT][KH]) {
 #pragma unroll
-    for (int t = 0; t < kHalf; ++t)
+    for (int t = 0; t < KH; ++t)
       w[t] = __builtin_amdgcn_raw_buffer_load_b128(wres, (kt + t) * 1024 + lane * 16, 0, kCacheStream);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const bool row_ok = mt * 32 + (lane & 31) < ext_rows;
 #pragma unroll
-      for (int t = 0; t < kHalf; ++t) {
-        const int off = (row_ok && kt + t < kt1) ? a_lane + (mt * 32 * g.k + (kt + t) * kTileK) * 2 : 0x7FFFFFF0;
+      for (int t = 0; t < KH; ++t) {
+        const int off = (row_ok && kt + t < kt1) ? a_lane + ((kt + t) * 2 * ext_rows + mt * 32) * 16 : 0x7FFFFFF0;
         a[mt][t] = __builtin_amdgcn_raw_buffer_load_b128(ares, off, 0, 0);
       }
     }
   };
-  auto mma = [&](const u32x4 (&w)[kHalf], const u32x4 (&a)[MT][kHalf]) {
+  auto mma = [&](const u32x4 (&w)[KH], const u32x4 (&a)[MT][KH]) {
 #pragma unroll
-    for (int t = 0; t < kHalf; ++t)
+    for (int t = 0; t < KH; ++t)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
         acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w[t]), as_bf16x8(a[mt][t]), acc[mt], 0, 0, 0);
   };
   {
-    u32x4 w0[kHalf], w1[kHalf], a0[MT][kHalf], a1[MT][kHalf];
+    u32x4 w0[KH], w1[KH], a0[MT][KH], a1[MT][KH];
     load(kt0, w0, a0);
-    for (int kt = kt0; kt < kt1; kt += 2 * kHalf) {
-      load(kt + kHalf, w1, a1);
+    for (int kt = kt0; kt < kt1; kt += 2 * KH) {
+      load(kt + KH, w1, a1);
       __builtin_amdgcn_sched_barrier(0);
       mma(w0, a0);
       __builtin_amdgcn_sched_barrier(0);
-      load(kt + 2 * kHalf, w0, a0);
+      load(kt + 2 * KH, w0, a0);
       __builtin_amdgcn_sched_barrier(0);
       mma(w1, a1);
       __builtin_amdgcn_sched_barrier(0);
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
         const size_t o = (size_t)m * g.n_out + n;
         v = g.x[o] + val(nl, m);
         g.x[o] = v;
-        store_split(g.a_next, g.n_out, g.rows, m, n, v * g.gain_next[n]);
+        store_split(g.a_next, g.rows, m, n, v * g.gain_next[n]);
         if (g.hidden) g.hidden[o] = f2bf(v);
       }
       sq[e] = v * v;
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
       const float gt = val(p, m) * s;
       const float up = val(p + 16, m) * s;
       const float hv = gt / (1.0f + expf(-gt)) * up;
-      store_split(g.h, g.ffn, g.rows, m, nb * 16 + p, hv);
+      store_split(g.h, g.rows, m, nb * 16 + p, hv);
     }
   } else if constexpr (EPI == kEpiPartial) {
     // Unscaled partial sums of this workgroup's k range: part[spi][m][n].
@@ -238,7 +238,10 @@ static hipError_t gemm_mt(const GemmArgs& g, hipStream_t s) {
   const int mt = (2 * g.rows + 31) / 32;
   const dim3 grid(g.nb * g.sp), block(NW * 64);
   switch (mt) {
-    case 1: k_gemm<EPI, 1, NW><<<grid, block, 0, s>>>(g); break;
+    case 1:
+      if (g.kh == 4) k_gemm<EPI, 1, NW, 4><<<grid, block, 0, s>>>(g);
+      else k_gemm<EPI, 1, NW><<<grid, block, 0, s>>>(g);
+      break;
     case 2: k_gemm<EPI, 2, NW><<<grid, block, 0, s>>>(g); break;
     case 3:
     case 4: k_gemm<EPI, 4, NW><<<grid, block, 0, s>>>(g); break;
@@ -359,7 +362,7 @@ __global__ __launch_bounds__(256) void k_reduce_resid(const GemmArgs g) {
     const size_t o = (size_t)m * g.n_out + n;
     v = g.x[o] + acc;
     g.x[o] = v;
-    store_split(g.a_next, g.n_out, g.rows, m, n, v * g.gain_next[n]);
+    store_split(g.a_next, g.rows, m, n, v * g.gain_next[n]);
     if (g.hidden) g.hidden[o] = f2bf(v);
   }
   float sq = v * v;
@@ -405,7 +408,7 @@ __global__ __launch_bounds__(256) void k_embed(const EmbedArgs e) {
       const int col = c8 * 8 + j;
       const float v = __uint_as_float(j & 1 ? (wds[j >> 1] & 0xFFFF0000u) : (wds[j >> 1] << 16));
       e.x[(size_t)r * e.H + col] = v;
-      store_split(e.a, e.H, e.rows, r, col, v * e.gain[col]);
+      store_split(e.a, e.rows, r, col, v * e.gain[col]);
       s += v * v;
     }
     s += __shfl_xor(s, 1);

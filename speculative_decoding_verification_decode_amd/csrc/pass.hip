@@ -87,7 +87,7 @@ __device__ f32x16 stream_block(const PassArgs& P, int gi, const uint4* wblk, int
   const __amdgpu_buffer_rsrc_t ares =
       __builtin_amdgcn_make_buffer_rsrc((void*)act, (short)0, ext_rows * k * 2, kBufferWord3);
   const bool row_ok = (lane & 31) < ext_rows;
-  const int a_lane = ((lane & 31) * k + (lane >> 5) * 8) * 2;
+  const int a_lane = ((lane >> 5) * ext_rows + (lane & 31)) * 16;   // operand (k half, row) of tile 0
   u32x4 w0[kPB], w1[kPB], a0[kPB], a1[kPB];
   auto loadw = [&](int kt, u32x4 (&w)[kPB]) {
 #pragma unroll
@@ -97,7 +97,7 @@ __device__ f32x16 stream_block(const PassArgs& P, int gi, const uint4* wblk, int
   auto loada = [&](int kt, u32x4 (&a)[kPB]) {
 #pragma unroll
     for (int t = 0; t < kPB; ++t) {
-      const int off = (row_ok && kt + t < kt1) ? a_lane + (kt + t) * kTileK * 2 : 0x7FFFFFF0;
+      const int off = (row_ok && kt + t < kt1) ? a_lane + (kt + t) * 2 * ext_rows * 16 : 0x7FFFFFF0;
       a[t] = __builtin_amdgcn_raw_buffer_load_b128(ares, off, 0, 0);
     }
   };
@@ -234,8 +234,8 @@ __device__ void item_embed(const PassArgs& P, int gi, int nb, int epoch) {
     const float* g1 = P.layers[0].g1;
     st<true>(P.x + (size_t)m * H + c, v0);
     st<true>(P.x + (size_t)m * H + c + 1, v1);
-    store_split<true>(P.a, H, R, m, c, v0 * g1[c]);
-    store_split<true>(P.a, H, R, m, c + 1, v1 * g1[c + 1]);
+    store_split<true>(P.a, R, m, c, v0 * g1[c]);
+    store_split<true>(P.a, R, m, c + 1, v1 * g1[c + 1]);
     s = v0 * v0 + v1 * v1;
   }
   s += __shfl_xor(s, 1);
@@ -383,7 +383,7 @@ __device__ void item_oproj(const PassArgs& P, PassLds& lds, int gi, int l, int n
       const size_t o = (size_t)m * H + n;
       v = xin[o] + tval(lds, R, nl, m);
       st<true>(xo + o, v);
-      store_split<true>(ao, H, R, m, n, v * Ly.g2[n]);
+      store_split<true>(ao, R, m, n, v * Ly.g2[n]);
     }
     lds.sq[e] = v * v;
   }
@@ -419,7 +419,7 @@ __device__ void item_gateup(const PassArgs& P, PassLds& lds, int gi, int l, int 
     const float gt = tval(lds, R, p, m) * s;
     const float up = tval(lds, R, p + 16, m) * s;
     const float hv = gt / (1.0f + expf(-gt)) * up;
-    store_split<true>(P.h + (size_t)l * 2 * kPassRows * P.F, P.F, R, m, nb * 16 + p, hv);
+    store_split<true>(P.h + (size_t)l * 2 * kPassRows * P.F, R, m, nb * 16 + p, hv);
   }
   publish(P, gi, epoch);
 }
@@ -469,7 +469,7 @@ __device__ void item_down(const PassArgs& P, PassLds& lds, int gi, int l, int nb
       const size_t o = (size_t)m * H + n;
       v = xin[o] + acc2;
       st<true>(xo + o, v);
-      store_split<true>(ao, H, R, m, n, v * Ly.gnext[n]);
+      store_split<true>(ao, R, m, n, v * Ly.gnext[n]);
       if (last_layer && P.hidden) P.hidden[o] = f2bf(v);
     }
     lds.sq[e] = v * v;

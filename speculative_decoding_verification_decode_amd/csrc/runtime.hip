@@ -92,6 +92,7 @@ struct sf_cache {
   int nw_qkv, nw_o, nw_gu, nw_d, nw_head;
   int sp_qkv, sp_o, sp_gu, sp_d, sp_head;
   float* part = nullptr;
+  int kh = 4;                      // GEMM: weight tiles per pipelined batch (one-tile row counts)
   // pass kernel
   bool pass_ok = false;       // buffers exist (the pass kernel serves passes of <= kPassRows rows)
   bool pass_on = false;       // chosen at allocation: SF_PASS=1 selects the pass kernel
@@ -110,10 +111,13 @@ struct sf_cache {
 };
 
 // ------------------------------------------------------------------------------------------
-// Waves per GEMM workgroup: with many n blocks, 4-wave workgroups let several share a CU
-// so one streams while another finishes; short k ranges also take 4 waves.
+// Waves per GEMM workgroup: four, so that up to five workgroups share a compute unit (the
+// kernel keeps about 100 registers per lane with 4-tile batches) and one streams while
+// another finishes.  8 is kept for experiments (SF_NW_*).
 static int choose_nw(int nb, int kb, const char* env) {
-  int nw = (nb >= 1024 || kb < 256) ? 4 : 8;
+  (void)nb;
+  (void)kb;
+  int nw = 4;
   if (const char* v = getenv(env)) {
     int o = atoi(v);
     if (o == 4 || o == 8) nw = o;
@@ -121,11 +125,13 @@ static int choose_nw(int nb, int kb, const char* env) {
   return nw;
 }
 
-// Workgroups per n block.  Narrow projections have too few 32-row blocks to occupy the
-// GPU, so their k range is split over about 448 workgroups in total (each wave keeps at
-// least four 16-k tiles); the partial sums are reduced by a second small kernel.
+// Workgroups per n block.  Narrow projections (O, down: 112 blocks at 7B) have too few
+// 32-row blocks to occupy the GPU, so their k range is split over about 256/nb workgroups
+// (each wave keeping at least four 16-k tiles); a second small kernel adds the partial sums.
+// Measured at the 7B verify shape: down 35.9 us with 2 splits vs 44.9 with 4, O 11.6 vs 12.6,
+// QKV (144 blocks) best unsplit.
 static int choose_sp(int nb, int kb, int nw, const char* env) {
-  int sp = (448 + nb / 2) / nb;
+  int sp = std::max(1, 256 / nb);
   sp = std::max(1, std::min(sp, kb / (nw * 4)));
   if (const char* v = getenv(env)) {
     int o = atoi(v);
@@ -331,6 +337,16 @@ static hipError_t launch_split_gemm(int epi, const GemmArgs& g, hipStream_t s) {
   return e == hipSuccess ? launch_reduce(epi, g, s) : e;
 }
 
+enum GemmKind { kGQkv = 0, kGO = 1, kGGateUp = 2, kGDown = 3, kGHead = 4 };
+
+// One GEMM of kind `kind` (with partials + reduce when g.sp > 1).
+static hipError_t run_gemm(const sf_cache* c, int kind, int layer, int epi, GemmArgs g, hipStream_t s) {
+  (void)kind;
+  (void)layer;
+  g.kh = c->kh;
+  return launch_split_gemm(epi, g, s);
+}
+
 // ------------------------------------------------------------------------------------------
 // Pass kernel arguments for a run of r.B sequences x r.T positions (r.B*r.T <= kPassRows).
 static PassArgs pass_args(sf_cache* c, const Run& r) {
@@ -414,7 +430,7 @@ static hipError_t enqueue_forward(sf_cache* c, const Run& r) {
     g.w = Ly.wqkv; g.a = c->a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_qkv; g.nw = c->nw_qkv;
     g.sp = c->sp_qkv; g.n_out = m->Q + 2 * m->KV;
     g.bias = Ly.bqkv; g.q = c->q; g.kc = kc; g.vc = vc;
-    if ((e = launch_split_gemm(kEpiQkv, g, s)) != hipSuccess) return e;
+    if ((e = run_gemm(c, kGQkv, l, kEpiQkv, g, s)) != hipSuccess) return e;
 
     aa.kc = kc; aa.vc = vc;
     if ((e = launch_attention(aa, m->dh, r.B, s)) != hipSuccess) return e;
@@ -423,13 +439,13 @@ static hipError_t enqueue_forward(sf_cache* c, const Run& r) {
     g.w = Ly.wo; g.a = c->a_o; g.k = m->Q; g.kb = m->Q / kTileK; g.nb = m->nb_h; g.nw = c->nw_o;
     g.sp = c->sp_o;
     g.x = c->x; g.a_next = c->a_h; g.gain_next = Ly.g2; g.ssq_out = c->ssq; g.n_out = m->H;
-    if ((e = launch_split_gemm(kEpiResid, g, s)) != hipSuccess) return e;
+    if ((e = run_gemm(c, kGO, l, kEpiResid, g, s)) != hipSuccess) return e;
 
     g = base;
     g.w = Ly.wgu; g.a = c->a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_gu; g.nw = c->nw_gu;
     g.sp = 1;
     g.h = c->a_f; g.ffn = m->F;
-    if ((e = launch_gemm(kEpiSwiglu, g, s)) != hipSuccess) return e;
+    if ((e = run_gemm(c, kGGateUp, l, kEpiSwiglu, g, s)) != hipSuccess) return e;
 
     const bool last = (l + 1 == m->L);
     g = base;
@@ -439,7 +455,7 @@ static hipError_t enqueue_forward(sf_cache* c, const Run& r) {
     g.ssq_out = c->ssq; g.n_out = m->H;
     g.hidden = (last && !d.has_head) ? c->hidden : nullptr;
     g.sp = c->sp_d;
-    if ((e = launch_split_gemm(kEpiResid, g, s)) != hipSuccess) return e;
+    if ((e = run_gemm(c, kGDown, l, kEpiResid, g, s)) != hipSuccess) return e;
   }
 
   if (d.has_head) {
@@ -447,7 +463,7 @@ static hipError_t enqueue_forward(sf_cache* c, const Run& r) {
     g.w = m->head; g.a = c->a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_head; g.nw = c->nw_head;
     g.sp = 1;
     g.amax = c->amax; g.logits = r.logits; g.vocab = m->V;
-    if ((e = launch_gemm(kEpiArgmax, g, s)) != hipSuccess) return e;
+    if ((e = run_gemm(c, kGHead, 0, kEpiArgmax, g, s)) != hipSuccess) return e;
   }
 
   AcceptArgs ac{};
@@ -508,6 +524,7 @@ extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacit
   c->sp_gu = 1;
   c->sp_d = choose_sp(m->nb_h, m->F / kTileK, c->nw_d, "SF_SP_D");
   c->sp_head = 1;
+  if (const char* v = getenv("SF_KH")) c->kh = (atoi(v) == 8) ? 8 : 4;
 
   hipStream_t s = m->stream;
   auto bail = [&](sf_status st) { cache_release(c); return st; };
@@ -979,7 +996,7 @@ extern "C" sf_status sf_time_kernel(sf_cache* c, int32_t kernel, int32_t iters, 
         g.w = Ly.wqkv; g.a = c->a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_qkv; g.nw = c->nw_qkv;
         g.bias = Ly.bqkv; g.q = c->q; g.kc = kc; g.vc = vc; g.sp = c->sp_qkv; g.n_out = m->Q + 2 * m->KV;
         by = (double)(m->Q + 2 * m->KV) * m->H * 2 + (double)rows * (m->H * 4 + m->Q * 4 + 2 * m->KV * 2);
-        return launch_split_gemm(kEpiQkv, g, s);
+        return run_gemm(c, kGQkv, l, kEpiQkv, g, s);
       case SF_KERNEL_ATTENTION: {
         AttnArgs aa{};
         aa.q = c->q; aa.kc = kc; aa.vc = vc; aa.seq_stride = (long)c->seq_stride; aa.cap = c->cap; aa.len = c->len;
@@ -993,22 +1010,22 @@ extern "C" sf_status sf_time_kernel(sf_cache* c, int32_t kernel, int32_t iters, 
         g.w = Ly.wo; g.a = c->a_o; g.k = m->Q; g.kb = m->Q / kTileK; g.nb = m->nb_h; g.nw = c->nw_o;
         g.x = c->x; g.a_next = c->a_h; g.gain_next = Ly.g2; g.ssq_out = c->ssq; g.n_out = m->H; g.sp = c->sp_o;
         by = (double)m->H * m->Q * 2 + (double)rows * (m->Q * 4 + m->H * (4 + 4 + 4));
-        return launch_split_gemm(kEpiResid, g, s);
+        return run_gemm(c, kGO, l, kEpiResid, g, s);
       case SF_KERNEL_GATEUP:
         g.w = Ly.wgu; g.a = c->a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_gu; g.nw = c->nw_gu;
         g.h = c->a_f; g.ffn = m->F; g.sp = 1;
         by = (double)2 * m->F * m->H * 2 + (double)rows * (m->H * 4 + m->F * 4);
-        return launch_gemm(kEpiSwiglu, g, s);
+        return run_gemm(c, kGGateUp, l, kEpiSwiglu, g, s);
       case SF_KERNEL_DOWN:
         g.w = Ly.wd; g.a = c->a_f; g.k = m->F; g.kb = m->F / kTileK; g.nb = m->nb_h; g.nw = c->nw_d;
         g.x = c->x; g.a_next = c->a_h; g.gain_next = Ly.g1; g.ssq_out = c->ssq; g.n_out = m->H; g.sp = c->sp_d;
         by = (double)m->H * m->F * 2 + (double)rows * (m->F * 4 + m->H * (4 + 4 + 4));
-        return launch_split_gemm(kEpiResid, g, s);
+        return run_gemm(c, kGDown, l, kEpiResid, g, s);
       default:
         g.w = m->head; g.a = c->a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_head; g.nw = c->nw_head;
         g.amax = c->amax; g.vocab = m->V; g.sp = 1;
         by = (double)m->V * m->H * 2 + (double)rows * (m->H * 4 + m->nb_head * 8);
-        return launch_gemm(kEpiArgmax, g, s);
+        return run_gemm(c, kGHead, 0, kEpiArgmax, g, s);
     }
   };
   hipError_t e = launch(0);  // warm-up

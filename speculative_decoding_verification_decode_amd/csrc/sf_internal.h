@@ -44,6 +44,7 @@ struct GemmArgs {
   int sp;                  // workgroups splitting each block's k range (>1: partials + reduce)
   float* part;             // split partials [sp][rows][n_out] (kEpiPartial)
   int nw;                  // waves per workgroup: 4 or 8
+  int kh;                  // weight tiles per pipelined batch (4 or 8) for single-tile row counts
   // RMSNorm folded into the consumer: row scale = 1/sqrt(sum(ssq_in[r][*])/k + eps)
   const float* ssq_in;
   int nparts_in;

@@ -230,9 +230,11 @@ def test_errors_leave_state_unchanged(pair):
 
 
 def test_four_wave_workgroups_split_k_and_64_row_chunks(monkeypatch):
-    """Every GEMM with 4-wave workgroups, QKV / O / down split over two workgroups per
-    block (partials + reduce kernels), and prefill chunks of 64 rows."""
+    """The GEMM kernels with 8-tile batches, every GEMM with 4-wave workgroups, QKV / O / down
+    split over two workgroups per block (partials + reduce kernels), and prefill chunks of 64
+    rows."""
     need_gpu()
+    monkeypatch.setenv("SF_KH", "8")     # 8-tile batches
     for v in ("SF_NW_QKV", "SF_NW_O", "SF_NW_GU", "SF_NW_D", "SF_NW_HEAD"):
         monkeypatch.setenv(v, "4")
     for v in ("SF_SP_QKV", "SF_SP_O", "SF_SP_D"):
