@@ -52,6 +52,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-batched", action="store_true", help="skip the 32-sequence batched verify line")
     ap.add_argument("--kernel-iters", type=int, default=56)
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="also run plain device copies of 1 GiB, so HBM byte counters can be scaled")
@@ -187,6 +188,42 @@ def main():
                 "frac": round(g["GBps"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                 "launch_us": g["us"], "alg_bytes_per_launch": g["bytes"]}
 
+    # Batched verify: 32 sequences x 9 positions in one pass, contexts drawn from U{256..8192}
+    # (one pool), each sequence's K/V a prefix of the same synthetic array.
+    batched = None
+    if not args.no_batched:
+        Bn = 32
+        rng = np.random.default_rng(synth.seeds(5)["contexts"])
+        bctx = rng.integers(256, max(CONTEXTS) + 1, size=Bn)
+        cb = sfb.sf_cache_alloc(model, Bn, CAPACITY, K)
+        kdev = torch.from_numpy(kbits.view(np.int16)).cuda()
+        vdev = torch.from_numpy(vbits.view(np.int16)).cuda()
+        for b in range(Bn):
+            sfb.sf_kv_write(cb, b, kdev, vdev, int(bctx[b]), max(CONTEXTS))
+            sfb.sf_set_next(cb, b, int(hist[int(bctx[b])]))
+        del kdev, vdev
+        bd = torch.from_numpy(rng.integers(0, S.vocab, size=(Bn, K)).astype(np.int32)).cuda()
+        for _ in range(2):
+            sfb.sf_verify_device(cb, bd, None, sfb.SF_NO_COMMIT)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        nb_ = max(3, args.steps // 2)
+        e0.record(stream)
+        for _ in range(nb_):
+            sfb.sf_verify_device(cb, bd, None, sfb.SF_NO_COMMIT)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        bms = e0.elapsed_time(e1) / nb_
+        w_bytes = S.n_layers * layer_bytes + kern["lm_head"]["bytes"]
+        kvb = float(sum(int(c) + K + 1 for c in bctx)) * 2 * S.kv_dim * 2 * S.n_layers
+        batched = {"sequences": Bn, "rows": Bn * (K + 1), "contexts": "U{256..8192}, mean %.0f" % bctx.mean(),
+                   "ms": round(bms, 4), "verify_tokens_per_s": round(Bn * (K + 1) / bms * 1e3, 1),
+                   "alg_GBps": round((w_bytes + kvb) / (bms * 1e-3) / 1e9, 1),
+                   "frac_peak": round((w_bytes + kvb) / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        sfb.sf_cache_free(cb)
+        log(f"batched: {batched}")
+
     cpu = None
     if not args.no_cpu:
         import oracle
@@ -231,6 +268,7 @@ def main():
         "per_context": {str(k): v for k, v in per_ctx.items()},
         "host_inclusive_verify_ms_ctx512": round(host_ms, 4),
         "kernels_at_verify_shape": kern,
+        "batched_32": batched,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

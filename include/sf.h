@@ -87,7 +87,8 @@ sf_status sf_model_free(sf_model* model);
  * fix 1, a pre-allocated fixed-size cache).  Every sequence starts with length 0
  * and pending token 0.  KV layout: [layer][seq][kv_head][position][head_dim] bf16;
  * K is stored after RoPE.
- * Limits: n_seqs * (k_max+1) <= 64, 0 <= k_max <= 15, capacity >= k_max+1. */
+ * Limits: 1 <= n_seqs <= 64, n_seqs * (k_max+1) <= 512, 0 <= k_max <= 15,
+ * k_max+1 <= capacity <= 16384. */
 sf_status sf_cache_alloc(sf_model* model, int32_t n_seqs, int32_t capacity, int32_t k_max,
                          sf_cache** out);
 sf_status sf_cache_free(sf_cache* cache);

@@ -177,11 +177,13 @@ def sf_prefill(cache, seq, tokens):
     return nxt.value
 
 
-def sf_verify(cache, draft, k=None, flags=0, n_seqs=1, k_max=None, dev_out=None):
+def sf_verify(cache, draft, k=None, flags=0, n_seqs=None, k_max=None, dev_out=None):
     """draft: int array [n_seqs][k_max].  Returns (accepted [n_seqs], target [n_seqs][k_max+1])."""
     d, dp = _i32(draft)
+    if n_seqs is None:
+        n_seqs = d.shape[0] if (d is not None and d.ndim == 2) else 1
     if k_max is None:
-        k_max = d.shape[-1] if d.ndim else 0
+        k_max = d.shape[-1] if (d is not None and d.ndim) else 0
     kk, kp = _i32(k)
     acc = np.zeros(n_seqs, dtype=np.int32)
     tgt = np.zeros((n_seqs, k_max + 1), dtype=np.int32)

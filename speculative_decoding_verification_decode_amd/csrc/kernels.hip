@@ -8,7 +8,8 @@
 //   k_gemm<RESID>  O projection; epilogue: residual add, next RMSNorm's gain and
 //                  sum-of-squares partials
 //   k_gemm<SWIGLU> gate/up projection; epilogue: row scale, silu(gate)*up
-//   k_gemm<RESID>  down projection (split-K across workgroups, deterministic)
+//   k_gemm<RESID>  down projection (k split across workgroups, reduced in split order by the
+//                  last workgroup to finish)
 // then k_gemm<ARGMAX> (LM head with per-tile argmax) and k_accept (argmax merge,
 // longest-prefix accept, commit).  The pass is captured once into a hipGraph.
 #include "device.h"
@@ -24,8 +25,16 @@ namespace sf {
 // keeps two 8-tile batches in flight (the next batch's weights and activations requested
 // before the current batch's MFMAs) and the waves' accumulators are added in wave order,
 // so results do not depend on scheduling.
-template <int EPI, int MT, int NW, int KH = kHalf>
+//
+// WIDE (more than 64 rows, batched verify): grid.y splits the rows into groups of 64; the
+// workgroup of group rg holds two hi m tiles (operand rows 64rg .. 64rg+63) and two lo m tiles
+// (rows + 64rg ..), so each weight tile feeds four MFMAs, and the groups of one block share
+// the block's weights through L2 (grid.x, a multiple of 8 here, keeps them on one XCD).  A
+// row's arithmetic is the same as in the compact layout: the per-row result does not depend
+// on the batch.
+template <int EPI, int MT, int NW, int KH = kHalf, bool WIDE = false>
 __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
+  static_assert(!WIDE || MT == 4, "wide row groups hold two hi and two lo m tiles");
   constexpr int kThreads = NW * 64;
   constexpr int kRealRows = MT * 16;
   __shared__ float tile[MT * 1024];
@@ -34,6 +43,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int nb = blockIdx.x / g.sp, spi = blockIdx.x - nb * g.sp;
+  const int rg = WIDE ? (int)blockIdx.y : 0, r0 = rg * 64;   // first real row of this workgroup
   const int U = g.sp * NW, u = spi * NW + wave;
   const int kt0 = (int)(((long)g.kb * u) / U), kt1 = (int)(((long)g.kb * (u + 1)) / U);
 
@@ -49,11 +59,11 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
         (void*)g.ssq_in, (short)0, g.rows * g.nparts_in * 4, kBufferWord3);
 #pragma unroll
     for (int j = 0; j < kRowsPerWave; ++j) {
-      const int m = wave + NW * j;
+      const int mr = r0 + wave + NW * j;
 #pragma unroll
       for (int i = 0; i < kSsqPerLane; ++i) {
         const int p = lane + 64 * i;
-        const int off = (m < g.rows && p < g.nparts_in) ? (m * g.nparts_in + p) * 4 : 0x7FFFFFF0;
+        const int off = (mr < g.rows && p < g.nparts_in) ? (mr * g.nparts_in + p) * 4 : 0x7FFFFFF0;
         ssq_v[j][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sres, off, 0, 0));
       }
     }
@@ -69,9 +79,22 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(g.w + (size_t)nb * g.kb * 64), (short)0, kt1 * 1024, kBufferWord3);
   const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)g.a, (short)0, 2 * kMaxRows * g.k * 2, kBufferWord3);
+      (void*)g.a, (short)0, 2 * g.rows * g.k * 2, kBufferWord3);
   const int ext_rows = 2 * g.rows;
   const int a_lane = ((lane >> 5) * ext_rows + (lane & 31)) * 16;   // operand (k half, row) of tile 0, m tile 0
+  // First operand row of m tile mt, and whether this lane's row of it is a real one.
+  int mt_row0[MT];
+  bool mt_ok[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    if (WIDE) {
+      mt_row0[mt] = (mt < 2) ? r0 + mt * 32 : g.rows + r0 + (mt - 2) * 32;
+      mt_ok[mt] = r0 + (mt & 1) * 32 + (lane & 31) < g.rows;
+    } else {
+      mt_row0[mt] = mt * 32;
+      mt_ok[mt] = mt * 32 + (lane & 31) < ext_rows;
+    }
+  }
 
   auto load = [&](int kt, u32x4 (&w)[KH], u32x4 (&a)[MT][KH]) {
 #pragma unroll
@@ -79,10 +102,9 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
       w[t] = __builtin_amdgcn_raw_buffer_load_b128(wres, (kt + t) * 1024 + lane * 16, 0, kCacheStream);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const bool row_ok = mt * 32 + (lane & 31) < ext_rows;
 #pragma unroll
       for (int t = 0; t < KH; ++t) {
-        const int off = (row_ok && kt + t < kt1) ? a_lane + ((kt + t) * 2 * ext_rows + mt * 32) * 16 : 0x7FFFFFF0;
+        const int off = (mt_ok[mt] && kt + t < kt1) ? a_lane + ((kt + t) * 2 * ext_rows + mt_row0[mt]) * 16 : 0x7FFFFFF0;
         a[mt][t] = __builtin_amdgcn_raw_buffer_load_b128(ares, off, 0, 0);
       }
     }
@@ -118,7 +140,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) t += __shfl_xor(t, o);
       const int m = wave + NW * j;
-      if (lane == 0 && m < kRealRows) rscale[m] = (m < g.rows) ? 1.0f / sqrtf(t / (float)g.k + g.eps) : 0.f;
+      if (lane == 0 && m < kRealRows) rscale[m] = (r0 + m < g.rows) ? 1.0f / sqrtf(t / (float)g.k + g.eps) : 0.f;
     }
   }
   // Cross-wave sum in wave order.
@@ -136,14 +158,50 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
     __syncthreads();
   }
 
+  // k split over g.sp workgroups per block: each stores its partial tile (agent-coherent,
+  // so the others see it without a cache flush) and counts its arrival on the block's
+  // counter; the one that brings the count to a multiple of sp adds the partials in split
+  // order and runs the epilogue.  The counters only grow, by sp per launch.
+  __shared__ int last_arrival;
+  const bool split = g.sp > 1;
+  float* const pblk = g.part + (size_t)nb * g.sp * g.rows * 32;   // [split][row][32]
+  // hi + lo of output (n_local nl, local row m) from this workgroup's tile
+  auto tval = [&](int nl, int m) {
+    return WIDE ? tile[tile_idx(nl, m)] + tile[tile_idx(nl, 64 + m)]
+                : tile[tile_idx(nl, m)] + tile[tile_idx(nl, g.rows + m)];
+  };
+  if (split) {
+    for (int e = tid; e < 32 * kRealRows; e += kThreads) {
+      const int nl = e & 31, m = e >> 5;
+      if (r0 + m < g.rows) st<true>(pblk + ((size_t)spi * g.rows + r0 + m) * 32 + nl, tval(nl, m));
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      const int old = __hip_atomic_fetch_add(g.counters + nb * gridDim.y + rg, 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+      last_arrival = ((old + 1) % g.sp) == 0;
+    }
+    __syncthreads();
+    if (!last_arrival) return;
+    asm volatile("" ::: "memory");
+  }
+
   // ------------------------------------------------------------------ epilogues
-  // Output (n_local, m) of real row m: hi-part row m plus lo-part row rows + m.
-  auto val = [&](int nl, int m) { return tile[tile_idx(nl, m)] + tile[tile_idx(nl, g.rows + m)]; };
+  // Output (n_local, m) of real row m: hi-part row m plus lo-part row rows + m (or the sum of
+  // the splits' partials).
+  auto val = [&](int nl, int m) {
+    if (!split) return tval(nl, m);
+    float s = 0.f;
+    for (int q = 0; q < g.sp; ++q) s += pblk[((size_t)q * g.rows + r0 + m) * 32 + nl];
+    return s;
+  };
   if constexpr (EPI == kEpiQkv) {
     // Packed rows of n block nb: 0..15 = head dims i0..i0+15, 16..31 = their RoPE partners.
     for (int it = tid; it < 16 * kRealRows; it += kThreads) {
-      const int p = it & 15, m = it >> 4;
-      if (m >= g.rows) continue;
+      const int p = it & 15, m = it >> 4, mr = r0 + m;
+      if (mr >= g.rows) continue;
       const int half = g.dh >> 1, bph = g.dh >> 5;
       const int qb = g.nq * bph, kvb = g.nkv * bph;
       int sec, head, blk;
@@ -154,7 +212,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
       const float s = rscale[m];
       const float y1 = val(p, m) * s + g.bias[nb * 32 + p];
       const float y2 = val(p + 16, m) * s + g.bias[nb * 32 + p + 16];
-      const int b = m / g.T, slot = m - b * g.T;
+      const int b = mr / g.T, slot = mr - b * g.T;
       const int pos = g.len[b] + slot;
       if (pos < g.cap) {
         if (sec == 2) {
@@ -166,7 +224,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
           const float o1 = y1 * cs.x - y2 * cs.y;
           const float o2 = y2 * cs.x + y1 * cs.y;
           if (sec == 0) {
-            float* dst = g.q + ((size_t)m * g.nq + head) * g.dh;
+            float* dst = g.q + ((size_t)mr * g.nq + head) * g.dh;
             dst[i] = o1;
             dst[i + half] = o2;
           } else {
@@ -180,55 +238,48 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
   } else if constexpr (EPI == kEpiResid) {
     __shared__ float sq[32 * kRealRows];
     for (int e = tid; e < 32 * kRealRows; e += kThreads) {
-      const int nl = e & 31, m = e >> 5;
+      const int nl = e & 31, m = e >> 5, mr = r0 + m;
       float v = 0.f;
-      if (m < g.rows) {
+      if (mr < g.rows) {
         const int n = nb * 32 + nl;
-        const size_t o = (size_t)m * g.n_out + n;
+        const size_t o = (size_t)mr * g.n_out + n;
         v = g.x[o] + val(nl, m);
         g.x[o] = v;
-        store_split(g.a_next, g.rows, m, n, v * g.gain_next[n]);
+        store_split(g.a_next, g.rows, mr, n, v * g.gain_next[n]);
         if (g.hidden) g.hidden[o] = f2bf(v);
       }
       sq[e] = v * v;
     }
     __syncthreads();
-    if (tid < kRealRows && tid < g.rows) {
+    if (tid < kRealRows && r0 + tid < g.rows) {
       float s = 0.f;
 #pragma unroll
       for (int nl = 0; nl < 32; ++nl) s += sq[tid * 32 + nl];
-      g.ssq_out[(size_t)tid * g.nb + nb] = s;
+      g.ssq_out[(size_t)(r0 + tid) * g.nb + nb] = s;
     }
   } else if constexpr (EPI == kEpiSwiglu) {
     // Packed rows of n block nb: 0..15 = gate rows j0..j0+15, 16..31 = up rows j0..j0+15.
     for (int it = tid; it < 16 * kRealRows; it += kThreads) {
-      const int p = it & 15, m = it >> 4;
-      if (m >= g.rows) continue;
+      const int p = it & 15, m = it >> 4, mr = r0 + m;
+      if (mr >= g.rows) continue;
       const float s = rscale[m];
       const float gt = val(p, m) * s;
       const float up = val(p + 16, m) * s;
       const float hv = gt / (1.0f + expf(-gt)) * up;
-      store_split(g.h, g.rows, m, nb * 16 + p, hv);
-    }
-  } else if constexpr (EPI == kEpiPartial) {
-    // Unscaled partial sums of this workgroup's k range: part[spi][m][n].
-    float* dst = g.part + (size_t)spi * g.rows * g.n_out;
-    for (int e = tid; e < 32 * kRealRows; e += kThreads) {
-      const int nl = e & 31, m = e >> 5;
-      if (m < g.rows) dst[(size_t)m * g.n_out + nb * 32 + nl] = val(nl, m);
+      store_split(g.h, g.rows, mr, nb * 16 + p, hv);
     }
   } else if constexpr (EPI == kEpiArgmax) {
-    const int m = tid;
-    if (m < g.rows && m < kRealRows) {
+    const int m = tid, mr = r0 + m;
+    if (m < kRealRows && mr < g.rows) {
       const float s = rscale[m];
       float best = -INFINITY;
       int bi = nb * 32;
       for (int nl = 0; nl < 32; ++nl) {
         const float v = val(nl, m) * s;
-        if (g.logits) g.logits[(size_t)m * g.vocab + nb * 32 + nl] = v;
+        if (g.logits) g.logits[(size_t)mr * g.vocab + nb * 32 + nl] = v;
         if (v > best) { best = v; bi = nb * 32 + nl; }
       }
-      g.amax[(size_t)m * g.nb + nb] = make_float2(best, __int_as_float(bi));
+      g.amax[(size_t)mr * g.nb + nb] = make_float2(best, __int_as_float(bi));
     }
   }
 }
@@ -237,6 +288,10 @@ template <int EPI, int NW>
 static hipError_t gemm_mt(const GemmArgs& g, hipStream_t s) {
   const int mt = (2 * g.rows + 31) / 32;
   const dim3 grid(g.nb * g.sp), block(NW * 64);
+  if (g.rows > 64) {
+    k_gemm<EPI, 4, 4, 4, true><<<dim3(g.nb * g.sp, (g.rows + 63) / 64), dim3(256), 0, s>>>(g);
+    return hipGetLastError();
+  }
   switch (mt) {
     case 1:
       if (g.kh == 4) k_gemm<EPI, 1, NW, 4><<<grid, block, 0, s>>>(g);
@@ -244,7 +299,7 @@ static hipError_t gemm_mt(const GemmArgs& g, hipStream_t s) {
       break;
     case 2: k_gemm<EPI, 2, NW><<<grid, block, 0, s>>>(g); break;
     case 3:
-    case 4: k_gemm<EPI, 4, NW><<<grid, block, 0, s>>>(g); break;
+    case 4: k_gemm<EPI, 4, NW, 4><<<grid, block, 0, s>>>(g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -263,123 +318,8 @@ hipError_t launch_gemm(int epi, const GemmArgs& g, hipStream_t s) {
     case kEpiResid: return gemm_nw<kEpiResid>(g, s);
     case kEpiSwiglu: return gemm_nw<kEpiSwiglu>(g, s);
     case kEpiArgmax: return gemm_nw<kEpiArgmax>(g, s);
-    case kEpiPartial: return gemm_nw<kEpiPartial>(g, s);
   }
   return hipErrorInvalidValue;
-}
-
-// ----------------------------------------------------------------------------------------------
-// Reductions of split-K partials, in split order, fused with the epilogue the undivided
-// GEMM would have run.
-constexpr int kMaxSplit = 8;
-
-// Row scale 1/sqrt(mean(x^2) + eps) from the per-32-column sums of squares, summed in the
-// same order as the GEMM prologue: lane l takes parts l, l+64, then a cross-lane tree.
-__device__ float row_scale(const float* ssq, int nparts, int k, float eps, int m, int lane) {
-  float t = 0.f;
-#pragma unroll
-  for (int i = 0; i < kSsqPerLane; ++i) {
-    const int p = lane + 64 * i;
-    t += (p < nparts) ? ssq[(size_t)m * nparts + p] : 0.f;
-  }
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) t += __shfl_xor(t, o);
-  return 1.0f / sqrtf(t / (float)k + eps);
-}
-
-// QKV: workgroup (row m, 512 output pairs).  Item (n block, pair p): rows p and p+16 of the
-// packed block are a RoPE pair (or two plain V dims).
-__global__ __launch_bounds__(256) void k_reduce_qkv(const GemmArgs g) {
-  __shared__ float sc;
-  const int m = blockIdx.y;
-  if (threadIdx.x < 64) {
-    const float v = row_scale(g.ssq_in, g.nparts_in, g.k, g.eps, m, threadIdx.x);
-    if (threadIdx.x == 0) sc = v;
-  }
-  __syncthreads();
-  const int item = blockIdx.x * 256 + threadIdx.x;
-  if (item >= g.nb * 16) return;
-  const int nb = item >> 4, p = item & 15;
-  const int n1 = nb * 32 + p, n2 = n1 + 16;
-  // Partials of up to kMaxSplit splits, all loads issued before the (ordered) sum.
-  float p1[kMaxSplit], p2[kMaxSplit];
-#pragma unroll
-  for (int q = 0; q < kMaxSplit; ++q) {
-    const float* pq = g.part + ((size_t)min(q, g.sp - 1) * g.rows + m) * g.n_out;
-    p1[q] = pq[n1];
-    p2[q] = pq[n2];
-  }
-  float a1 = 0.f, a2 = 0.f;
-#pragma unroll
-  for (int q = 0; q < kMaxSplit; ++q)
-    if (q < g.sp) { a1 += p1[q]; a2 += p2[q]; }
-  const float y1 = a1 * sc + g.bias[n1];
-  const float y2 = a2 * sc + g.bias[n2];
-  const int half = g.dh >> 1, bph = g.dh >> 5;
-  const int qb = g.nq * bph, kvb = g.nkv * bph;
-  int sec, head, blk;
-  if (nb < qb) { sec = 0; head = nb / bph; blk = nb - head * bph; }
-  else if (nb < qb + kvb) { sec = 1; head = (nb - qb) / bph; blk = nb - qb - head * bph; }
-  else { sec = 2; head = (nb - qb - kvb) / bph; blk = nb - qb - kvb - head * bph; }
-  const int i = blk * 16 + p;
-  const int b = m / g.T, slot = m - b * g.T;
-  const int pos = g.len[b] + slot;
-  if (pos >= g.cap) return;
-  if (sec == 2) {
-    uint16_t* dst = g.vc + (size_t)b * g.seq_stride + ((size_t)head * g.cap + pos) * g.dh;
-    dst[i] = f2bf(y1);
-    dst[i + half] = f2bf(y2);
-  } else {
-    const float2 cs = g.rope[(size_t)pos * half + i];
-    const float o1 = y1 * cs.x - y2 * cs.y;
-    const float o2 = y2 * cs.x + y1 * cs.y;
-    if (sec == 0) {
-      float* dst = g.q + ((size_t)m * g.nq + head) * g.dh;
-      dst[i] = o1;
-      dst[i + half] = o2;
-    } else {
-      uint16_t* dst = g.kc + (size_t)b * g.seq_stride + ((size_t)head * g.cap + pos) * g.dh;
-      dst[i] = f2bf(o1);
-      dst[i + half] = f2bf(o2);
-    }
-  }
-}
-
-// Residual: workgroup (row m, 256 columns).  x += sum of partials; next norm's input as
-// hi/lo bf16; sum of squares per 32-column block (a 32-lane tree, fixed order).
-__global__ __launch_bounds__(256) void k_reduce_resid(const GemmArgs g) {
-  const int m = blockIdx.y;
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  float v = 0.f;
-  if (n < g.n_out) {
-    float pv[kMaxSplit];
-#pragma unroll
-    for (int q = 0; q < kMaxSplit; ++q) pv[q] = g.part[((size_t)min(q, g.sp - 1) * g.rows + m) * g.n_out + n];
-    float acc = 0.f;
-#pragma unroll
-    for (int q = 0; q < kMaxSplit; ++q)
-      if (q < g.sp) acc += pv[q];
-    const size_t o = (size_t)m * g.n_out + n;
-    v = g.x[o] + acc;
-    g.x[o] = v;
-    store_split(g.a_next, g.rows, m, n, v * g.gain_next[n]);
-    if (g.hidden) g.hidden[o] = f2bf(v);
-  }
-  float sq = v * v;
-#pragma unroll
-  for (int o = 1; o < 32; o <<= 1) sq += __shfl_xor(sq, o);
-  if ((threadIdx.x & 31) == 0 && n < g.n_out) g.ssq_out[(size_t)m * (g.n_out / 32) + (n >> 5)] = sq;
-}
-
-hipError_t launch_reduce(int epi, const GemmArgs& g, hipStream_t s) {
-  if (epi == kEpiQkv) {
-    k_reduce_qkv<<<dim3((g.nb * 16 + 255) / 256, g.rows), 256, 0, s>>>(g);
-  } else if (epi == kEpiResid) {
-    k_reduce_resid<<<dim3((g.n_out + 255) / 256, g.rows), 256, 0, s>>>(g);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
 }
 
 // ----------------------------------------------------------------------------------------------
@@ -460,7 +400,7 @@ int attention_spans(int cap) { return (cap + kSpan - 1) / kSpan; }
 // order independent), count the leading drafts that match, and commit.  Wave w merges the
 // rows w, w+16, ... of the sequence.
 __global__ __launch_bounds__(1024) void k_accept(const AcceptArgs a) {
-  __shared__ int tgt[kMaxRows];
+  __shared__ int tgt[kMaxK];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   if (a.has_head) {

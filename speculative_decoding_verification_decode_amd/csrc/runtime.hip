@@ -93,6 +93,8 @@ struct sf_cache {
   int sp_qkv, sp_o, sp_gu, sp_d, sp_head;
   float* part = nullptr;
   int kh = 4;                      // GEMM: weight tiles per pipelined batch (one-tile row counts)
+  int* cnt = nullptr;              // k-split arrival counters [layer][QKV, O, down][block]
+  int cnt_stride = 0;
   // pass kernel
   bool pass_ok = false;       // buffers exist (the pass kernel serves passes of <= kPassRows rows)
   bool pass_on = false;       // chosen at allocation: SF_PASS=1 selects the pass kernel
@@ -127,7 +129,7 @@ static int choose_nw(int nb, int kb, const char* env) {
 
 // Workgroups per n block.  Narrow projections (O, down: 112 blocks at 7B) have too few
 // 32-row blocks to occupy the GPU, so their k range is split over about 256/nb workgroups
-// (each wave keeping at least four 16-k tiles); a second small kernel adds the partial sums.
+// (each wave keeping at least four 16-k tiles); the last to finish adds the partial sums.
 // Measured at the 7B verify shape: down 35.9 us with 2 splits vs 44.9 with 4, O 11.6 vs 12.6,
 // QKV (144 blocks) best unsplit.
 static int choose_sp(int nb, int kb, int nw, const char* env) {
@@ -137,7 +139,7 @@ static int choose_sp(int nb, int kb, int nw, const char* env) {
     int o = atoi(v);
     if (o >= 1) sp = o;
   }
-  return std::min(sp, 8);  // the reduce kernels add at most eight partials
+  return std::min(sp, 8);
 }
 
 static sf_status check_desc(const sf_model_desc* d) {
@@ -330,21 +332,18 @@ extern "C" sf_status sf_model_free(sf_model* m) {
   return SF_OK;
 }
 
-// A GEMM with epilogue `epi`, split over g.sp workgroups per block when g.sp > 1.
-static hipError_t launch_split_gemm(int epi, const GemmArgs& g, hipStream_t s) {
-  if (g.sp <= 1) return launch_gemm(epi, g, s);
-  hipError_t e = launch_gemm(kEpiPartial, g, s);
-  return e == hipSuccess ? launch_reduce(epi, g, s) : e;
-}
-
 enum GemmKind { kGQkv = 0, kGO = 1, kGGateUp = 2, kGDown = 3, kGHead = 4 };
 
-// One GEMM of kind `kind` (with partials + reduce when g.sp > 1).
+// One GEMM of kind `kind` in layer `layer`; a k split (g.sp > 1) uses the arrival counters
+// of that layer and kind.
 static hipError_t run_gemm(const sf_cache* c, int kind, int layer, int epi, GemmArgs g, hipStream_t s) {
-  (void)kind;
-  (void)layer;
   g.kh = c->kh;
-  return launch_split_gemm(epi, g, s);
+  if (g.sp > 1) {
+    if (kind == kGGateUp || kind == kGHead) return hipErrorInvalidValue;
+    const int slot = layer * 3 + (kind == kGQkv ? 0 : kind == kGO ? 1 : 2);
+    g.counters = c->cnt + (size_t)slot * c->cnt_stride;
+  }
+  return launch_gemm(epi, g, s);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -506,7 +505,8 @@ extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacit
                                     sf_cache** out) {
   if (!m || !out) return fail(SF_E_ARG, "model or out is NULL");
   if (k_max < 0 || k_max >= kMaxK) return fail(SF_E_ARG, "k_max must be in 0..15");
-  if (n_seqs < 1 || n_seqs * (k_max + 1) > kMaxRows) return fail(SF_E_ARG, "n_seqs*(k_max+1) must be in 1..64");
+  if (n_seqs < 1 || n_seqs > kMaxSeqs || n_seqs * (k_max + 1) > kMaxRows)
+    return fail(SF_E_ARG, "n_seqs must be in 1..64 and n_seqs*(k_max+1) in 1..512");
   if (capacity < k_max + 1 || capacity > kMaxCapacity) return fail(SF_E_ARG, "capacity must be in k_max+1..16384");
   sf_cache* c = new sf_cache();
   c->m = m; c->B = n_seqs; c->cap = capacity; c->kmax = k_max; c->T = k_max + 1;
@@ -540,7 +540,8 @@ extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacit
     sf_status st_ = (x);              \
     if (st_ != SF_OK) return bail(st_); \
   } while (0)
-  const size_t R = kMaxRows;
+  // Rows of the largest pass this cache runs: a verify (n_seqs x (k_max+1)) or a prefill chunk.
+  const size_t R = std::max(n_seqs * (k_max + 1), kPrefillChunk);
   const size_t pool = c->layer_stride * m->L * 2;
   TRY(dalloc((void**)&c->kpool, pool));
   TRY(dalloc((void**)&c->vpool, pool));
@@ -557,6 +558,8 @@ extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacit
     const size_t n_qkv = (size_t)m->Q + 2 * m->KV;
     size_t pe = std::max({(size_t)c->sp_qkv * n_qkv, (size_t)c->sp_o * m->H, (size_t)c->sp_d * m->H});
     TRY(dalloc((void**)&c->part, pe * R * 4));
+    c->cnt_stride = std::max(m->nb_qkv, m->nb_h) * (int)((R + 63) / 64);   // [block][64-row group]
+    TRY(dalloc((void**)&c->cnt, (size_t)m->L * 3 * c->cnt_stride * 4));
   }
   TRY(dalloc((void**)&c->q, R * m->Q * 4));
   TRY(dalloc((void**)&c->apart, R * m->nq * (size_t)c->nchunk * (m->dh + 2) * 4));

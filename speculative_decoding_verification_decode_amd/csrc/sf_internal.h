@@ -12,7 +12,7 @@ constexpr int kTileN = 32;                    // weight rows per packed tile (32
 constexpr int kTileK = 16;                    // reduction depth per packed tile
 constexpr int kBatch = 16;                    // weight tiles a wave loads before using them
 constexpr int kChunk = 64;                    // attention: KV positions per chunk (position aligned)
-constexpr int kMaxRows = 64;                  // rows (sequences x positions) per pass
+constexpr int kMaxRows = 512;                 // rows (sequences x positions) per pass
 constexpr int kMaxSeqs = 64;
 constexpr int kMaxK = 16;                     // drafts per sequence (k_max <= 15, T <= 16)
 constexpr int kMaxDraftSteps = 256;
@@ -35,14 +35,15 @@ struct Stage {
   int32_t draft[kMaxSeqs * kMaxK];
 };
 
-enum Epi { kEpiQkv = 0, kEpiResid = 1, kEpiSwiglu = 2, kEpiArgmax = 3, kEpiPartial = 4 };
+enum Epi { kEpiQkv = 0, kEpiResid = 1, kEpiSwiglu = 2, kEpiArgmax = 3 };
 
 struct GemmArgs {
   const uint4* w;          // packed weight tiles [nb][kb][64 lanes] x 16 B (32 rows x 16 k per tile)
   const uint16_t* a;       // bf16 activations [2*rows][k]: hi parts, then lo parts
   int k, kb, nb, rows;     // in-features, k tiles (k/16), 32-row n blocks, valid rows
-  int sp;                  // workgroups splitting each block's k range (>1: partials + reduce)
-  float* part;             // split partials [sp][rows][n_out] (kEpiPartial)
+  int sp;                  // workgroups splitting each block's k range
+  float* part;             // split partials [nb][sp][rows][32] (sp > 1)
+  int* counters;           // [nb] arrivals of the splits of each block (sp > 1); only grow
   int nw;                  // waves per workgroup: 4 or 8
   int kh;                  // weight tiles per pipelined batch (4 or 8) for single-tile row counts
   // RMSNorm folded into the consumer: row scale = 1/sqrt(sum(ssq_in[r][*])/k + eps)
@@ -116,8 +117,6 @@ struct AcceptArgs {
 
 // Launchers (kernels.hip).
 hipError_t launch_gemm(int epi, const GemmArgs& g, hipStream_t s);
-// Reduce kEpiPartial output of a split GEMM and apply epilogue `epi` (kEpiQkv or kEpiResid).
-hipError_t launch_reduce(int epi, const GemmArgs& g, hipStream_t s);
 hipError_t launch_embed(const EmbedArgs& e, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int dh, int B, hipStream_t s);
 int attention_spans(int cap);

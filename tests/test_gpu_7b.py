@@ -164,3 +164,50 @@ def test_half_stack_hidden_states_match_oracle(weights, kv, hist, mode):
         assert err <= LOGIT_TOL
     finally:
         e.close()
+
+
+def test_batched_32_sequences_matches_oracle_and_single_runs(weights, kv):
+    """32 sequences x 9 positions (288 rows, the row-grouped GEMM path) at contexts drawn
+    from U{256..8192}: two sequences against the oracle, and both bitwise equal to the same
+    sequence verified alone."""
+    sfb = need_gpu()
+    Bn = 32
+    rng = np.random.default_rng(synth.seeds(5)["contexts"])
+    ctx = rng.integers(256, 8192 + 1, size=Bn)
+    nxt = rng.integers(0, S.vocab, size=Bn)
+    drafts = rng.integers(0, S.vocab, size=(Bn, K)).astype(np.int32)
+    say(f"[7b-batched] contexts {ctx.min()}..{ctx.max()}")
+    eng = sfb.Engine(S, weights, n_seqs=Bn, capacity=CAP, k_max=K)
+    one = sfb.Engine(S, weights, n_seqs=1, capacity=CAP, k_max=K)
+    try:
+        kd = torch.from_numpy(np.ascontiguousarray(kv[0]).view(np.int16)).cuda()
+        vd = torch.from_numpy(np.ascontiguousarray(kv[1]).view(np.int16)).cuda()
+        for b in range(Bn):
+            sfb.sf_kv_write(eng.cache, b, kd, vd, int(ctx[b]), kv[0].shape[2])
+            sfb.sf_set_next(eng.cache, b, int(nxt[b]))
+        logits = torch.empty((Bn * (K + 1), S.vocab), dtype=torch.float32, device="cuda")
+        acc, tgt = sfb.sf_verify(eng.cache, drafts, None, sfb.SF_DEBUG_LOGITS | sfb.SF_NO_COMMIT, dev_out=logits)
+        acc_g, tgt_g = sfb.sf_verify(eng.cache, drafts, None, sfb.SF_NO_COMMIT)
+        torch.cuda.synchronize()
+        assert (acc_g == acc).all() and (tgt_g == tgt).all()
+        model = oracle.Model(S, weights)
+        one_logits = torch.empty((K + 1, S.vocab), dtype=torch.float32, device="cuda")
+        for b in (int(np.argmin(ctx)), int(np.argmax(ctx))):
+            sfb.sf_kv_write(one.cache, 0, kd, vd, int(ctx[b]), kv[0].shape[2])
+            sfb.sf_set_next(one.cache, 0, int(nxt[b]))
+            a1, t1 = sfb.sf_verify(one.cache, drafts[b:b + 1], None, sfb.SF_DEBUG_LOGITS | sfb.SF_NO_COMMIT,
+                                   dev_out=one_logits)
+            torch.cuda.synchronize()
+            assert torch.equal(one_logits.cpu(), logits.view(Bn, K + 1, S.vocab)[b].cpu()), f"sequence {b}"
+            assert a1[0] == acc[b] and (t1[0] == tgt[b]).all()
+            say(f"[7b-batched] seq {b} ctx {ctx[b]}: oracle")
+            r = oracle.verify(model, _oracle_cache(kv, int(ctx[b]), int(nxt[b])), drafts[b], K, commit=False)
+            err = (logits.view(Bn, K + 1, S.vocab)[b].double().cpu() - r["logits"]).abs().max().item()
+            say(f"[7b-batched] seq {b} max |dlogit| {err:.3g}")
+            assert err <= LOGIT_TOL
+            check_targets(tgt[b], r, K)
+            if accepted_decided(r, int(acc[b]), K):
+                assert acc[b] == r["accepted"]
+    finally:
+        eng.close()
+        one.close()

@@ -1,0 +1,77 @@
+"""GPU parity of the batched verify (many sequences in one pass, more than 64 rows), through
+the C ABI.
+
+Each sequence has its own length, pending token and drafts in one pool; the pass runs
+the row-grouped GEMM path.  Checks: every sequence against the float64 oracle (parity
+rule), and bitwise equality with the same sequence verified alone, since a row's
+arithmetic must not depend on the other rows of the batch.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import GAP, LOGIT_TOL, accepted_decided, check_targets, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+S = synth.TINY
+B, K, CAP = 16, 4, 512
+
+
+def _fill(sfb, eng, kv, ctx, nxt):
+    kb, vb = kv
+    kd = torch.from_numpy(np.ascontiguousarray(kb).view(np.int16)).cuda()
+    vd = torch.from_numpy(np.ascontiguousarray(vb).view(np.int16)).cuda()
+    for b, (c, t) in enumerate(zip(ctx, nxt)):
+        sfb.sf_kv_write(eng.cache, b, kd, vd, int(c), kb.shape[2])
+        sfb.sf_set_next(eng.cache, b, int(t))
+    torch.cuda.synchronize()
+
+
+def test_batched_tiny_matches_oracle_and_single_sequence_runs():
+    sfb = need_gpu()
+    sd = synth.seeds(5)
+    rng = np.random.default_rng(sd["contexts"])
+    ctx = rng.integers(40, CAP - K - 1, size=B)
+    nxt = rng.integers(0, S.vocab, size=B)
+    drafts = rng.integers(0, S.vocab, size=(B, K)).astype(np.int32)
+    ks = rng.integers(0, K + 1, size=B).astype(np.int32)
+    kv = synth.synthetic_kv(S, CAP, sd["kv"])
+    w = synth.model_weights(S, sd["weights"])
+    say(f"[batched] B={B} K={K} contexts {ctx.min()}..{ctx.max()}")
+    eng = sfb.Engine(S, w, n_seqs=B, capacity=CAP, k_max=K)
+    one = sfb.Engine(S, w, n_seqs=1, capacity=CAP, k_max=K)
+    try:
+        _fill(sfb, eng, kv, ctx, nxt)
+        logits = torch.empty((B * (K + 1), S.vocab), dtype=torch.float32, device="cuda")
+        acc, tgt = sfb.sf_verify(eng.cache, drafts, ks, sfb.SF_DEBUG_LOGITS | sfb.SF_NO_COMMIT, dev_out=logits)
+        acc_g, tgt_g = sfb.sf_verify(eng.cache, drafts, ks, 0)   # graph replay, commits
+        torch.cuda.synchronize()
+        assert (acc_g == acc).all() and (tgt_g == tgt).all()
+        lg = logits.double().cpu().view(B, K + 1, S.vocab)
+        model = oracle.Model(S, w)
+        one_logits = torch.empty((K + 1, S.vocab), dtype=torch.float32, device="cuda")
+        worst = 0.0
+        for b in range(B):
+            c = oracle.KVCache(S, int(ctx[b]) + K + 1)
+            c.load(kv[0], kv[1], int(ctx[b]), next_token=int(nxt[b]))
+            r = oracle.verify(model, c, drafts[b], int(ks[b]), commit=True)
+            worst = max(worst, (lg[b] - r["logits"]).abs().max().item())
+            check_targets(tgt[b], r, K)
+            if accepted_decided(r, int(acc[b]), int(ks[b])):
+                assert acc[b] == r["accepted"]
+                assert sfb.sf_cache_state(eng.cache, b) == (c.length, c.next_token)
+            # the same sequence alone
+            _fill(sfb, one, kv, [ctx[b]], [nxt[b]])
+            a1, t1 = sfb.sf_verify(one.cache, drafts[b:b + 1], ks[b:b + 1], sfb.SF_DEBUG_LOGITS | sfb.SF_NO_COMMIT,
+                                   dev_out=one_logits)
+            torch.cuda.synchronize()
+            assert a1[0] == acc[b] and (t1[0] == tgt[b]).all()
+            assert torch.equal(one_logits.cpu(), logits.view(B, K + 1, S.vocab)[b].cpu()), f"sequence {b}"
+        say(f"[batched] max |dlogit| vs oracle over {B} sequences: {worst:.3g}")
+        assert worst <= LOGIT_TOL
+    finally:
+        eng.close()
+        one.close()
