@@ -45,11 +45,11 @@ __device__ __forceinline__ T ld(const T* p) {
 //
 // Operand layout ("MFMA order"): for a matrix of ext = 2*rows operand rows and K columns,
 // the 8 bf16 values of row r, columns 16t + 8h .. 16t + 8h + 7 (tile t, k half h) are the
-// 16 bytes at index (t*2 + h)*ext + r.  One 32x32x16 MFMA's operand of a k tile is then
-// 2*ext consecutive 16-byte pieces, so a wave's load of it touches a few cache lines
-// instead of one line per row.
+// 16 bytes at index t*act_tile_pieces(ext) + h*ext + r.  One 32x32x16 MFMA's operand of a k
+// tile is then 2*ext consecutive 16-byte pieces, so a wave's load of it touches a few cache
+// lines instead of one line per row; each tile starts on a 128-byte line.
 __device__ __forceinline__ size_t act_index(int ext, int r, int col) {
-  return ((size_t)((col >> 4) * 2 + ((col >> 3) & 1)) * ext + r) * 8 + (col & 7);
+  return ((size_t)(col >> 4) * act_tile_pieces(ext) + ((col >> 3) & 1) * ext + r) * 8 + (col & 7);
 }
 template <bool kCoh = false>
 __device__ __forceinline__ void store_split(uint16_t* base, int rows, int r, int col, float v) {

@@ -79,8 +79,9 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(g.w + (size_t)nb * g.kb * 64), (short)0, kt1 * 1024, kBufferWord3);
   const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)g.a, (short)0, 2 * g.rows * g.k * 2, kBufferWord3);
+      (void*)g.a, (short)0, (int)act_bytes(2 * g.rows, g.k), kBufferWord3);
   const int ext_rows = 2 * g.rows;
+  const int tsp = act_tile_pieces(ext_rows);
   const int a_lane = ((lane >> 5) * ext_rows + (lane & 31)) * 16;   // operand (k half, row) of tile 0, m tile 0
   // First operand row of m tile mt, and whether this lane's row of it is a real one.
   int mt_row0[MT];
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
       for (int t = 0; t < KH; ++t) {
-        const int off = (mt_ok[mt] && kt + t < kt1) ? a_lane + ((kt + t) * 2 * ext_rows + mt_row0[mt]) * 16 : 0x7FFFFFF0;
+        const int off = (mt_ok[mt] && kt + t < kt1) ? a_lane + ((kt + t) * tsp + mt_row0[mt]) * 16 : 0x7FFFFFF0;
         a[mt][t] = __builtin_amdgcn_raw_buffer_load_b128(ares, off, 0, 0);
       }
     }

@@ -71,12 +71,15 @@ struct Layout {
   // Flag of 32-column block nb of x[l] (the embedding for l = 0, else the down reduction).
   __device__ int xflag(int l) const { return l == 0 ? 0 : lbase(l - 1) + P.off_down; }
   __device__ int xstride(int l) const { return l == 0 ? 1 : P.sp_d; }
+  // Flag of QKV block nb / O block nb of layer l (the split-0 item's index).
+  __device__ int qkv_flag(int l, int nb) const { return lbase(l) + nb * P.sp_q; }
+  __device__ int o_flag(int l, int nb) const { return lbase(l) + P.off_o + nb * P.sp_o; }
   __device__ int head_base() const { return P.nb_h + P.L * P.per_layer; }
 };
 
 // ---------------------------------------------------------------------------------------------
 // One wave's share of a weight block: tiles [kt0, kt1) of the packed 32-row block `wblk`
-// against activation rows [0, ext_rows) of `act` ([2R][k] bf16 hi/lo rows).  The first two
+// against activation rows [0, ext_rows) of `act` (bf16 hi/lo operand rows in MFMA order).  The first two
 // batches of weight tiles are requested before `wait` runs; the activations only after it.
 template <typename Wait>
 __device__ f32x16 stream_block(const PassArgs& P, int gi, const uint4* wblk, int kt0, int kt1, const uint16_t* act,
@@ -85,7 +88,8 @@ __device__ f32x16 stream_block(const PassArgs& P, int gi, const uint4* wblk, int
   const __amdgpu_buffer_rsrc_t wres =
       __builtin_amdgcn_make_buffer_rsrc((void*)wblk, (short)0, kt1 * 1024, kBufferWord3);
   const __amdgpu_buffer_rsrc_t ares =
-      __builtin_amdgcn_make_buffer_rsrc((void*)act, (short)0, ext_rows * k * 2, kBufferWord3);
+      __builtin_amdgcn_make_buffer_rsrc((void*)act, (short)0, (int)act_bytes(ext_rows, k), kBufferWord3);
+  const int tsp = act_tile_pieces(ext_rows);
   const bool row_ok = (lane & 31) < ext_rows;
   const int a_lane = ((lane >> 5) * ext_rows + (lane & 31)) * 16;   // operand (k half, row) of tile 0
   u32x4 w0[kPB], w1[kPB], a0[kPB], a1[kPB];
@@ -97,7 +101,7 @@ __device__ f32x16 stream_block(const PassArgs& P, int gi, const uint4* wblk, int
   auto loada = [&](int kt, u32x4 (&a)[kPB]) {
 #pragma unroll
     for (int t = 0; t < kPB; ++t) {
-      const int off = (row_ok && kt + t < kt1) ? a_lane + (kt + t) * 2 * ext_rows * 16 : 0x7FFFFFF0;
+      const int off = (row_ok && kt + t < kt1) ? a_lane + (kt + t) * tsp * 16 : 0x7FFFFFF0;
       a[t] = __builtin_amdgcn_raw_buffer_load_b128(ares, off, 0, 0);
     }
   };
@@ -132,9 +136,12 @@ __device__ f32x16 stream_block(const PassArgs& P, int gi, const uint4* wblk, int
 
 struct PassLds {
   float tile[1024];      // 32 x 32 accumulator tile in MFMA output order
+  float val[kPassRows * 32];   // block outputs [row][32] (hi + lo, summed over k splits)
   float rscale[kPassRows];
   float sq[32 * kPassRows];
   int last;
+  int next_item;
+  int epoch;
 };
 
 // Sum of the four waves' accumulators, in wave order, into lds.tile.
@@ -192,6 +199,44 @@ __device__ __forceinline__ float tval(const PassLds& lds, int R, int nl, int m) 
   return lds.tile[tile_idx(nl, m)] + lds.tile[tile_idx(nl, R + m)];
 }
 
+// Block outputs into lds.val, summing k splits: with sp > 1 each split stores its values to
+// part ([split][row][32] for this block, written through) and counts its arrival; only the
+// split that brings the count to a multiple of sp continues, after adding the partials in
+// split order.  Returns false for the others.
+__device__ bool block_values(const PassArgs& P, PassLds& lds, float* part, int sp, int sidx, int* counter) {
+  const int tid = threadIdx.x, R = P.R;
+  for (int e = tid; e < 32 * kPassRows; e += kPassThreads) {
+    const int nl = e & 31, m = e >> 5;
+    if (m < R) {
+      const float v = tval(lds, R, nl, m);
+      lds.val[e] = v;
+      if (sp > 1) st<true>(part + ((size_t)sidx * kPassRows + m) * 32 + nl, v);
+    }
+  }
+  if (sp > 1) {
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      lds.last = ((old + 1) % sp) == 0;
+    }
+    __syncthreads();
+    if (!lds.last) return false;
+    compiler_fence();
+    for (int e = tid; e < 32 * kPassRows; e += kPassThreads) {
+      const int m = e >> 5;
+      if (m < R) {
+        float acc = 0.f;
+        for (int q = 0; q < sp; ++q) acc += part[(size_t)q * kPassRows * 32 + e];
+        lds.val[e] = acc;
+      }
+    }
+  }
+  __syncthreads();
+  return true;
+}
+
 // Packed (value, index) key whose unsigned maximum is the largest value, lowest index first.
 __device__ __forceinline__ unsigned long long amax_key(float v, int idx) {
   uint32_t u = __float_as_uint(v + 0.0f);   // -0 -> +0
@@ -246,13 +291,14 @@ __device__ void item_embed(const PassArgs& P, int gi, int nb, int epoch) {
   publish(P, gi, epoch);
 }
 
-// QKV block nb of layer l: bias, RoPE, q and the K/V append at positions len + slot.
-__device__ void item_qkv(const PassArgs& P, PassLds& lds, int gi, int l, int nb, int epoch) {
+// QKV block nb of layer l, k split sidx of sp_q: bias, RoPE, q and the K/V append at positions
+// len + slot (by the split that completes the block).
+__device__ void item_qkv(const PassArgs& P, PassLds& lds, int gi, int l, int nb, int sidx, int epoch) {
   const Layout Lo{P};
-  const int wave = wave_id(), H = P.H, R = P.R;
+  const int wave = wave_id(), H = P.H, R = P.R, sp = P.sp_q;
   const PassLayer& Ly = P.layers[l];
   int kt0, kt1;
-  wave_range(P.kb_h, wave, 4, kt0, kt1);
+  wave_range(P.kb_h, sidx * 4 + wave, 4 * sp, kt0, kt1);
   const int xs = Lo.xstride(l);
   SsqRegs sr;
   const f32x16 acc = stream_block(P, gi, Ly.wqkv + (size_t)nb * P.kb_h * 64, kt0, kt1, P.a + (size_t)l * 2 * kPassRows * H,
@@ -262,6 +308,8 @@ __device__ void item_qkv(const PassArgs& P, PassLds& lds, int gi, int l, int nb,
                                   });
   row_scales(lds, sr, H, P.eps, R);
   reduce_waves(lds, acc);
+  float* part = P.qpart + (((size_t)l * P.nb_qkv + nb) * sp) * kPassRows * 32;
+  if (!block_values(P, lds, part, sp, sidx, P.dcount + ((size_t)l * 3 + 0) * P.cnt_stride + nb)) return;
   const int tid = threadIdx.x, p = tid & 15, m = tid >> 4;
   if (m < R) {
     const int dh = P.dh, half = dh >> 1, bph = dh >> 5;
@@ -272,8 +320,8 @@ __device__ void item_qkv(const PassArgs& P, PassLds& lds, int gi, int l, int nb,
     else { sec = 2; head = (nb - qb - kvb) / bph; blk = nb - qb - kvb - head * bph; }
     const int i = blk * 16 + p;
     const float s = lds.rscale[m];
-    const float y1 = tval(lds, R, p, m) * s + Ly.bqkv[nb * 32 + p];
-    const float y2 = tval(lds, R, p + 16, m) * s + Ly.bqkv[nb * 32 + p + 16];
+    const float y1 = lds.val[m * 32 + p] * s + Ly.bqkv[nb * 32 + p];
+    const float y2 = lds.val[m * 32 + p + 16] * s + Ly.bqkv[nb * 32 + p + 16];
     const int b = m / P.T, slot = m - b * P.T;
     const int pos = P.len[b] + slot;
     if (pos < P.cap) {
@@ -296,7 +344,7 @@ __device__ void item_qkv(const PassArgs& P, PassLds& lds, int gi, int l, int nb,
       }
     }
   }
-  publish(P, gi, epoch);
+  publish(P, Lo.qkv_flag(l, nb), epoch);
 }
 
 __device__ AttnArgs attn_args(const PassArgs& P, int l) {
@@ -329,10 +377,10 @@ __device__ void item_attn(const PassArgs& P, int gi, int l, int i, int epoch) {
   rest /= P.ngroups;
   const int b = rest % P.B, kvh = rest / P.B;
   const int G = P.nq / P.nkv, bph = DH / 32;
-  const int base = Lo.lbase(l);
-  wait_flags(P, base + kvh * G * bph, G * bph, 1, epoch);                             // q heads of the group
-  wait_flags(P, base + P.nq * bph + kvh * bph, bph, 1, epoch);                        // k head
-  wait_flags(P, base + (P.nq + P.nkv) * bph + kvh * bph, bph, 1, epoch);              // v head
+  const int sq = P.sp_q;
+  wait_flags(P, Lo.qkv_flag(l, kvh * G * bph), G * bph, sq, epoch);                   // q heads of the group
+  wait_flags(P, Lo.qkv_flag(l, P.nq * bph + kvh * bph), bph, sq, epoch);              // k head
+  wait_flags(P, Lo.qkv_flag(l, (P.nq + P.nkv) * bph + kvh * bph), bph, sq, epoch);    // v head
   mark(P, gi, 1);
   const AttnArgs aa = attn_args(P, l);
   const int plast = P.len[b] + P.T - 1;
@@ -357,13 +405,14 @@ __device__ void item_comb(const PassArgs& P, int gi, int l, int c, int epoch) {
   publish(P, gi, epoch);
 }
 
-// O projection block nb: x_mid = x + o W^T, x_mid * ln2 as hi/lo, sums of squares.
-__device__ void item_oproj(const PassArgs& P, PassLds& lds, int gi, int l, int nb, int epoch) {
+// O projection block nb, k split sidx of sp_o: x_mid = x + o W^T, x_mid * ln2 as hi/lo, sums of
+// squares (by the split that completes the block).
+__device__ void item_oproj(const PassArgs& P, PassLds& lds, int gi, int l, int nb, int sidx, int epoch) {
   const Layout Lo{P};
-  const int wave = wave_id(), H = P.H, R = P.R;
+  const int wave = wave_id(), H = P.H, R = P.R, sp = P.sp_o;
   const PassLayer& Ly = P.layers[l];
   int kt0, kt1;
-  wave_range(P.kb_q, wave, 4, kt0, kt1);
+  wave_range(P.kb_q, sidx * 4 + wave, 4 * sp, kt0, kt1);
   const f32x16 acc = stream_block(P, gi, Ly.wo + (size_t)nb * P.kb_q * 64, kt0, kt1, P.o + (size_t)l * 2 * kPassRows * P.Q,
                                   P.Q, 2 * R, [&] {
                                     const int hh0 = kt0 * kTileK / P.dh, hh1 = (kt1 * kTileK - 1) / P.dh;
@@ -371,6 +420,8 @@ __device__ void item_oproj(const PassArgs& P, PassLds& lds, int gi, int l, int n
                                     wait_flags(P, Lo.lbase(l) + P.off_comb + c0, c1 - c0, 1, epoch);
                                   });
   reduce_waves(lds, acc);
+  float* part = P.opart + (((size_t)l * P.nb_h + nb) * sp) * kPassRows * 32;
+  if (!block_values(P, lds, part, sp, sidx, P.dcount + ((size_t)l * 3 + 1) * P.cnt_stride + nb)) return;
   const int tid = threadIdx.x;
   const float* xin = P.x + (size_t)l * kPassRows * H;
   float* xo = P.xm + (size_t)l * kPassRows * H;
@@ -381,7 +432,7 @@ __device__ void item_oproj(const PassArgs& P, PassLds& lds, int gi, int l, int n
     if (m < R) {
       const int n = nb * 32 + nl;
       const size_t o = (size_t)m * H + n;
-      v = xin[o] + tval(lds, R, nl, m);
+      v = xin[o] + lds.val[e];
       st<true>(xo + o, v);
       store_split<true>(ao, R, m, n, v * Ly.g2[n]);
     }
@@ -394,7 +445,7 @@ __device__ void item_oproj(const PassArgs& P, PassLds& lds, int gi, int l, int n
     for (int nl = 0; nl < 32; ++nl) s += lds.sq[tid * 32 + nl];
     st<true>(P.ssqm + ((size_t)l * kPassRows + tid) * P.nb_h + nb, s);
   }
-  publish(P, gi, epoch);
+  publish(P, Lo.o_flag(l, nb), epoch);
 }
 
 // gate/up block nb: h = silu(gate) * up for 16 ffn columns, as hi/lo.
@@ -404,11 +455,10 @@ __device__ void item_gateup(const PassArgs& P, PassLds& lds, int gi, int l, int 
   const PassLayer& Ly = P.layers[l];
   int kt0, kt1;
   wave_range(P.kb_h, wave, 4, kt0, kt1);
-  const int obase = Lo.lbase(l) + P.off_o;
   SsqRegs sr;
   const f32x16 acc = stream_block(P, gi, Ly.wgu + (size_t)nb * P.kb_h * 64, kt0, kt1, P.am + (size_t)l * 2 * kPassRows * H,
                                   H, 2 * R, [&] {
-                                    wait_flags(P, obase, P.nb_h, 1, epoch);
+                                    wait_flags(P, Lo.o_flag(l, 0), P.nb_h, P.sp_o, epoch);
                                     sr = ssq_load(P.ssqm + (size_t)l * kPassRows * P.nb_h, P.nb_h, R);
                                   });
   row_scales(lds, sr, H, P.eps, R);
@@ -439,22 +489,8 @@ __device__ void item_down(const PassArgs& P, PassLds& lds, int gi, int l, int nb
                                   });
   reduce_waves(lds, acc);
   const int tid = threadIdx.x;
-  float* part = P.dpart + (size_t)l * sp * kPassRows * H;
-  for (int e = tid; e < 32 * kPassRows; e += kPassThreads) {
-    const int nl = e & 31, m = e >> 5;
-    if (m < R) st<true>(part + ((size_t)sidx * kPassRows + m) * H + nb * 32 + nl, tval(lds, R, nl, m));
-  }
-  compiler_fence();
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(P.dcount + (size_t)l * P.nb_h + nb, 1, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-    lds.last = ((old + 1) % sp) == 0;
-  }
-  __syncthreads();
-  if (!lds.last) return;
-  compiler_fence();
+  float* part = P.dpart + (((size_t)l * P.nb_h + nb) * sp) * kPassRows * 32;
+  if (!block_values(P, lds, part, sp, sidx, P.dcount + ((size_t)l * 3 + 2) * P.cnt_stride + nb)) return;
   const bool last_layer = (l + 1 == P.L);
   const float* xin = P.xm + (size_t)l * kPassRows * H;
   float* xo = P.x + (size_t)(l + 1) * kPassRows * H;
@@ -464,10 +500,8 @@ __device__ void item_down(const PassArgs& P, PassLds& lds, int gi, int l, int nb
     float v = 0.f;
     if (m < R) {
       const int n = nb * 32 + nl;
-      float acc2 = 0.f;
-      for (int q = 0; q < sp; ++q) acc2 += part[((size_t)q * kPassRows + m) * H + n];
       const size_t o = (size_t)m * H + n;
-      v = xin[o] + acc2;
+      v = xin[o] + lds.val[e];
       st<true>(xo + o, v);
       store_split<true>(ao, R, m, n, v * Ly.gnext[n]);
       if (last_layer && P.hidden) P.hidden[o] = f2bf(v);
@@ -524,6 +558,14 @@ __device__ void item_final(const PassArgs& P, int epoch) {
   const Layout Lo{P};
   __shared__ int tgt[kPassRows];
   const int tid = threadIdx.x, R = P.R;
+  if (tid == 0) {
+    int spins = 0;
+    while (ld<true>(P.checkin) < (int)gridDim.x) {
+      if (++spins > kSpinLimit) { st<true>(P.abort_flag, 1); break; }
+      if ((spins & 63) == 0 && ld<true>(P.abort_flag) != 0) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
   if (P.has_head) {
     if (tid == 0) {
       int spins = 0;
@@ -574,6 +616,8 @@ __device__ void item_final(const PassArgs& P, int epoch) {
     }
     P.result[kResultStatus] = ld<true>(P.abort_flag);
     st<true>(P.hcount, 0);
+    st<true>(P.checkin, 0);
+    st<true>(P.queue + ((epoch + 1) & 1), 0);   // the next pass takes items from the other slot
     st<true>(P.epoch, epoch + 1);
   }
   if (tid < R) st<true>(P.amax + tid, 0ull);
@@ -585,12 +629,33 @@ __device__ void run_item(const PassArgs& P, PassLds& lds, int gi, int epoch);
 template <int DH>
 __global__ __launch_bounds__(kPassThreads, 2) void k_pass(const PassArgs P) {
   __shared__ PassLds lds;
-  const int epoch = ld<true>(P.epoch);
-  for (int gi = blockIdx.x; gi < P.n_items; gi += gridDim.x) {
+  // Every workgroup reads the epoch and then checks in; the final item advances the epoch only
+  // after all have checked in, so a workgroup that starts late still sees this pass's epoch
+  // (and takes items from this pass's counter).
+  if (threadIdx.x == 0) {
+    lds.epoch = ld<true>(P.epoch);
+    __hip_atomic_fetch_add(P.checkin, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  const int epoch = lds.epoch;
+  // Items are taken from a counter in list order (one counter per epoch parity; the final item
+  // clears the other one for the next pass).  The next index is requested when an item starts,
+  // so its latency is hidden by the item.  A workgroup's next item always comes after its
+  // current one, so the lowest unfinished item is always being run: no deadlock.
+  int* queue = P.queue + (epoch & 1);
+  if (threadIdx.x == 0) lds.next_item = __hip_atomic_fetch_add(queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  int gi = lds.next_item;
+  while (gi < P.n_items) {
+    int nxt = 0;
+    if (threadIdx.x == 0) nxt = __hip_atomic_fetch_add(queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     mark(P, gi, 0);
     run_item<DH>(P, lds, gi, epoch);
     __syncthreads();  // LDS of this item is free for the next
     mark(P, gi, 3);
+    if (threadIdx.x == 0) lds.next_item = nxt;
+    __syncthreads();
+    gi = lds.next_item;
   }
 }
 
@@ -606,10 +671,10 @@ __device__ void run_item(const PassArgs& P, PassLds& lds, int gi, int epoch) {
     const int l = j / per_layer;
     if (l < P.L) {
       const int r = j - l * per_layer;
-      if (r < P.off_attn) item_qkv(P, lds, gi, l, r, epoch);
+      if (r < P.off_attn) item_qkv(P, lds, gi, l, r / P.sp_q, r % P.sp_q, epoch);
       else if (r < P.off_comb) item_attn<DH>(P, gi, l, r - P.off_attn, epoch);
       else if (r < P.off_o) item_comb<DH>(P, gi, l, r - P.off_comb, epoch);
-      else if (r < P.off_gu) item_oproj(P, lds, gi, l, r - P.off_o, epoch);
+      else if (r < P.off_gu) item_oproj(P, lds, gi, l, (r - P.off_o) / P.sp_o, (r - P.off_o) % P.sp_o, epoch);
       else if (r < P.off_down) item_gateup(P, lds, gi, l, r - P.off_gu, epoch);
       else {
         const int d = r - P.off_down;

@@ -98,11 +98,13 @@ struct sf_cache {
   // pass kernel
   bool pass_ok = false;       // buffers exist (the pass kernel serves passes of <= kPassRows rows)
   bool pass_on = false;       // chosen at allocation: SF_PASS=1 selects the pass kernel
-  int grid = 0, sp_pass = 1, attn_a = 1;
+  int grid = 0, psp_q = 1, psp_o = 1, sp_pass = 1, attn_a = 1;
   float *px = nullptr, *pxm = nullptr, *pssq = nullptr, *pssqm = nullptr, *pq = nullptr, *pdpart = nullptr;
+  float *pqpart = nullptr, *popart = nullptr;
   uint16_t *pa = nullptr, *pam = nullptr, *po = nullptr, *ph = nullptr;
   unsigned long long* pamax = nullptr;
-  int *pflags = nullptr, *pdcount = nullptr, *psync = nullptr;  // psync: hcount, epoch, abort
+  int *pflags = nullptr, *pdcount = nullptr, *psync = nullptr;  // psync: hcount, epoch, abort, checkin, queue[2]
+  int pcnt_stride = 0;
   unsigned long long* ptrace = nullptr;  // per-item timeline (diagnostics, SF_PASS_TRACE)
   int trace_items = 0;
   hipGraphExec_t gx_verify = nullptr, gx_draft = nullptr;
@@ -356,7 +358,7 @@ static PassArgs pass_args(sf_cache* c, const Run& r) {
   P.has_head = d.has_head;
   P.nb_qkv = m->nb_qkv; P.nb_h = m->nb_h; P.nb_gu = m->nb_gu; P.nb_head = m->nb_head;
   P.kb_h = m->H / kTileK; P.kb_q = m->Q / kTileK; P.kb_f = m->F / kTileK;
-  P.sp_d = c->sp_pass;
+  P.sp_q = c->psp_q; P.sp_o = c->psp_o; P.sp_d = c->sp_pass;
   P.eps = d.rms_eps;
   P.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)m->dh));
   P.embed = m->embed; P.layers = m->dlayers; P.head = m->head;
@@ -365,21 +367,25 @@ static PassArgs pass_args(sf_cache* c, const Run& r) {
   P.kpool = c->kpool + (size_t)r.seq0 * c->seq_stride; P.vpool = c->vpool + (size_t)r.seq0 * c->seq_stride;
   P.rope = c->rope; P.len = c->len + r.seq0; P.next = c->next + r.seq0; P.stage = c->stage_d;
   P.x = c->px; P.xm = c->pxm; P.a = c->pa; P.am = c->pam; P.ssq = c->pssq; P.ssqm = c->pssqm; P.q = c->pq;
-  P.o = c->po; P.h = c->ph; P.dpart = c->pdpart; P.apart = c->apart; P.amax = c->pamax;
+  P.o = c->po; P.h = c->ph; P.qpart = c->pqpart; P.opart = c->popart; P.dpart = c->pdpart;
+  P.apart = c->apart; P.amax = c->pamax;
   P.logits = r.logits; P.hidden = d.has_head ? nullptr : c->hidden; P.result = c->res_d;
   P.draft_out = r.draft_mode ? c->dout_d : nullptr;
   P.flags = c->pflags; P.dcount = c->pdcount; P.hcount = c->psync; P.epoch = c->psync + 1;
   P.abort_flag = c->psync + 2;
+  P.queue = c->psync + 4;
+  P.checkin = c->psync + 3;
+  P.cnt_stride = c->pcnt_stride;
   P.trace = c->ptrace;
   const int G = m->nq / m->nkv;
   P.attn_a = c->attn_a;
   P.ngroups = (r.T * G + 63) / 64;
   const int n_attn = m->nkv * r.B * P.ngroups * P.attn_a;
   const int n_comb = (m->nq * P.R + 3) / 4;
-  P.off_attn = m->nb_qkv;
+  P.off_attn = m->nb_qkv * P.sp_q;
   P.off_comb = P.off_attn + n_attn;
   P.off_o = P.off_comb + n_comb;
-  P.off_gu = P.off_o + m->nb_h;
+  P.off_gu = P.off_o + m->nb_h * P.sp_o;
   P.off_down = P.off_gu + m->nb_gu;
   P.per_layer = P.off_down + m->nb_h * P.sp_d;
   P.n_items = m->nb_h + m->L * P.per_layer + (d.has_head ? m->nb_head : 0) + 1;
@@ -549,9 +555,9 @@ extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacit
   TRY(dalloc((void**)&c->next, n_seqs * 4));
   TRY(dalloc((void**)&c->stage_d, sizeof(Stage)));
   TRY(dalloc((void**)&c->x, R * m->H * 4));
-  TRY(dalloc((void**)&c->a_h, 2 * R * m->H * 2));
-  TRY(dalloc((void**)&c->a_o, 2 * R * m->Q * 2));
-  TRY(dalloc((void**)&c->a_f, 2 * R * m->F * 2));
+  TRY(dalloc((void**)&c->a_h, act_bytes(2 * (int)R, m->H)));
+  TRY(dalloc((void**)&c->a_o, act_bytes(2 * (int)R, m->Q)));
+  TRY(dalloc((void**)&c->a_f, act_bytes(2 * (int)R, m->F)));
   TRY(dalloc((void**)&c->hidden, R * m->H * 2));
   TRY(dalloc((void**)&c->ssq, R * (m->H / kTileN) * 4));
   {
@@ -585,11 +591,18 @@ extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacit
     if (const char* v = getenv("SF_PASS_WPC")) wpc = std::max(1, std::min(2, atoi(v)));
     c->grid = cus * wpc;
     const int L = m->L, H = m->H, nbh = m->nb_h;
-    // Down projection k split: about two items per workgroup, each wave keeping >= 8 tiles.
-    int sp = std::max(1, (2 * c->grid + nbh / 2) / nbh);
-    sp = std::min(sp, std::max(1, (m->F / kTileK) / 32));
-    if (const char* v = getenv("SF_PASS_SPD")) sp = std::max(1, std::min(atoi(v), std::max(1, (m->F / kTileK) / 4)));
+    // k splits: the down projection gets about two items per workgroup, QKV and O about one
+    // (short items keep the attention chain short); each wave keeps >= 8 tiles.
+    auto split = [&](int nb, int kb, int per_wg, const char* env) {
+      int sp = std::max(1, (per_wg * c->grid + nb / 2) / nb);
+      sp = std::min(sp, std::max(1, kb / 32));
+      if (const char* v = getenv(env)) sp = std::max(1, std::min(atoi(v), std::max(1, kb / 4)));
+      return sp;
+    };
+    const int sp = split(nbh, m->F / kTileK, 2, "SF_PASS_SPD");
     c->sp_pass = sp;
+    c->psp_q = split(m->nb_qkv, m->H / kTileK, 1, "SF_PASS_SPQ");
+    c->psp_o = split(nbh, m->Q / kTileK, 1, "SF_PASS_SPO");
     c->attn_a = std::min(32, c->nchunk);
     if (const char* v = getenv("SF_PASS_ATTN")) c->attn_a = std::max(1, std::min(atoi(v), c->nchunk));
     const size_t P16 = kPassRows, P32 = 2 * kPassRows;
@@ -602,10 +615,13 @@ extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacit
     TRY(dalloc((void**)&c->pq, L * P16 * m->Q * 4));
     TRY(dalloc((void**)&c->po, L * P32 * m->Q * 2));
     TRY(dalloc((void**)&c->ph, L * P32 * m->F * 2));
-    TRY(dalloc((void**)&c->pdpart, (size_t)L * sp * P16 * H * 4));
+    TRY(dalloc((void**)&c->pqpart, (size_t)L * m->nb_qkv * c->psp_q * P16 * 32 * 4));
+    TRY(dalloc((void**)&c->popart, (size_t)L * nbh * c->psp_o * P16 * 32 * 4));
+    TRY(dalloc((void**)&c->pdpart, (size_t)L * nbh * sp * P16 * 32 * 4));
     TRY(dalloc((void**)&c->pamax, P16 * 8));
-    TRY(dalloc((void**)&c->pdcount, (size_t)L * nbh * 4));
-    TRY(dalloc((void**)&c->psync, 16));
+    c->pcnt_stride = std::max(m->nb_qkv, nbh);
+    TRY(dalloc((void**)&c->pdcount, (size_t)L * 3 * c->pcnt_stride * 4));
+    TRY(dalloc((void**)&c->psync, 32));
     int n_max = 0;
     for (int T : {c->T, 1}) {
       if (n_seqs * T > kPassRows) continue;
@@ -616,7 +632,7 @@ extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacit
       TRY(dalloc((void**)&c->ptrace, (size_t)std::max(n_max, 1) * 32));
       c->trace_items = n_max;
     }
-    const int sync0[4] = {0, 1, 0, 0};  // head counter, epoch (flags start at 0, the first pass is 1), abort
+    const int sync0[4] = {0, 1, 0, 0};  // head counter, epoch (flags start at 0, the first pass is 1), abort, check-ins
     hipError_t e = hipMemcpyAsync(c->psync, sync0, sizeof(sync0), hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return bail(fail(SF_E_HIP, std::string("pass state: ") + hipGetErrorString(e)));

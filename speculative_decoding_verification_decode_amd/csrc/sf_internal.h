@@ -19,6 +19,12 @@ constexpr int kMaxDraftSteps = 256;
 constexpr int kPrefillChunk = 64;
 constexpr int kMaxCapacity = 16384;  // positions per sequence
 
+// GEMM activation operand layout with `ext` operand rows: for each 16-column k tile, the 2*ext
+// 16-byte pieces (k half, row) are contiguous, padded to whole 128-byte lines so that no cache
+// line holds pieces of two tiles (a consumer of a k range never touches a neighbouring tile).
+__host__ __device__ constexpr int act_tile_pieces(int ext) { return (2 * ext + 7) & ~7; }
+__host__ __device__ constexpr size_t act_bytes(int ext, int k) { return (size_t)(k / 16) * act_tile_pieces(ext) * 16; }
+
 // Stage flags (device side).
 constexpr int kFlagNoCommit = 1;
 constexpr int kFlagForce = 2;
@@ -155,7 +161,7 @@ struct PassArgs {
   int L, H, Q, F, V, nq, nkv, dh, has_head;
   int nb_qkv, nb_h, nb_gu, nb_head;   // 32-row weight blocks
   int kb_h, kb_q, kb_f;               // 16-k tiles of hidden, q width, ffn
-  int sp_d;                           // down projection: workgroups per block (k split)
+  int sp_q, sp_o, sp_d;               // k splits of QKV, O and down blocks
   float eps, scale_log2;
   const uint16_t* embed;
   const PassLayer* layers;
@@ -177,7 +183,9 @@ struct PassArgs {
   float* q;         // [L][kPassRows][Q]
   uint16_t* o;      // [L][2*kPassRows][Q]
   uint16_t* h;      // [L][2*kPassRows][F]
-  float* dpart;     // [L][sp_d][kPassRows][H]
+  float* qpart;     // k-split partials [L][nb_qkv][sp_q][kPassRows][32]
+  float* opart;     // [L][nb_h][sp_o][kPassRows][32]
+  float* dpart;     // [L][nb_h][sp_d][kPassRows][32]
   float* apart;     // attention span partials, reused by every layer (read coherently)
   unsigned long long* amax;  // [kPassRows] packed (value, index) maxima of the LM head
   float* logits;    // optional fp32 [R][V]
@@ -186,7 +194,10 @@ struct PassArgs {
   int32_t* draft_out;
   // synchronisation
   int* flags;       // per item: epoch of the pass that finished it
-  int* dcount;      // [L][nb_h] arrivals of down-projection splits (grows by sp_d per pass)
+  int* dcount;      // [L][QKV, O, down][cnt_stride] arrivals of k splits (grow by sp per pass)
+  int cnt_stride;
+  int* queue;       // [2] work-item counters, one per epoch parity
+  int* checkin;     // workgroups that have read this pass's epoch
   int* hcount;      // finished LM-head items of this pass
   int* epoch;       // pass counter (read at kernel start, advanced by the final item)
   int* abort_flag;  // set when a wait gives up; sticky
