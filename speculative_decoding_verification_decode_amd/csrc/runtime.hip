@@ -99,6 +99,7 @@ struct sf_cache {
   bool pass_ok = false;       // buffers exist (the pass kernel serves passes of <= kPassRows rows)
   bool pass_on = false;       // chosen at allocation: SF_PASS=1 selects the pass kernel
   int grid = 0, psp_q = 1, psp_o = 1, sp_pass = 1, attn_a = 1;
+  bool prefetch_o = true;   // warm the O projection's weights into L2 during attention
   float *px = nullptr, *pxm = nullptr, *pssq = nullptr, *pssqm = nullptr, *pq = nullptr, *pdpart = nullptr;
   float *pqpart = nullptr, *popart = nullptr;
   uint16_t *pa = nullptr, *pam = nullptr, *po = nullptr, *ph = nullptr;
@@ -424,7 +425,7 @@ static hipError_t enqueue_forward(sf_cache* c, const Run& r) {
   AttnArgs aa{};
   aa.q = c->q; aa.seq_stride = (long)c->seq_stride; aa.cap = c->cap; aa.len = len; aa.T = r.T; aa.nq = m->nq;
   aa.nkv = m->nkv; aa.nchunk = c->nchunk; aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)m->dh));
-  aa.part = c->apart; aa.out = c->a_o; aa.rows = rows;
+  aa.part = c->apart; aa.out = c->a_o; aa.rows = rows; aa.dh = m->dh;
 
   for (int l = 0; l < m->L; ++l) {
     const Layer& Ly = m->layers[l];
@@ -438,6 +439,7 @@ static hipError_t enqueue_forward(sf_cache* c, const Run& r) {
     if ((e = run_gemm(c, kGQkv, l, kEpiQkv, g, s)) != hipSuccess) return e;
 
     aa.kc = kc; aa.vc = vc;
+    if (c->prefetch_o && c->nchunk * m->nkv >= kPrefetchGroups) { aa.pf_w = Ly.wo; aa.pf_nb = m->nb_h; aa.pf_kb = m->Q / kTileK; aa.pf_sp = c->sp_o; }
     if ((e = launch_attention(aa, m->dh, r.B, s)) != hipSuccess) return e;
 
     g = base;
@@ -531,6 +533,7 @@ extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacit
   c->sp_d = choose_sp(m->nb_h, m->F / kTileK, c->nw_d, "SF_SP_D");
   c->sp_head = 1;
   if (const char* v = getenv("SF_KH")) c->kh = (atoi(v) == 8) ? 8 : 4;
+  if (const char* v = getenv("SF_PREFETCH")) c->prefetch_o = atoi(v) != 0;
 
   hipStream_t s = m->stream;
   auto bail = [&](sf_status st) { cache_release(c); return st; };
@@ -1021,7 +1024,7 @@ extern "C" sf_status sf_time_kernel(sf_cache* c, int32_t kernel, int32_t iters, 
         aa.q = c->q; aa.kc = kc; aa.vc = vc; aa.seq_stride = (long)c->seq_stride; aa.cap = c->cap; aa.len = c->len;
         aa.T = c->T; aa.nq = m->nq; aa.nkv = m->nkv; aa.nchunk = c->nchunk;
         aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)m->dh));
-        aa.part = c->apart; aa.out = c->a_o; aa.rows = rows;
+        aa.part = c->apart; aa.out = c->a_o; aa.rows = rows; aa.dh = m->dh;
         by = L_total * 2.0 * m->KV * 2 + (double)rows * (m->Q * 4 + m->Q * 2);
         return launch_attention(aa, m->dh, c->B, s);
       }
