@@ -15,11 +15,29 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// Round to nearest even (inputs are finite or inf; NaN stays NaN).
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// Round to nearest even: gfx950's v_cvt_pk_bf16_f32 (one instruction instead of four).
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// Lane permutations inside a 16-lane DPP row (no LDS traffic, unlike __shfl_xor).
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+// Max and sum over the 16 lanes of a DPP row, every lane receiving the result: partners
+// lane^1, lane^2 (quad permutes), then the mirrored half-row and row, which pair each
+// group with a lane of the group it has not met yet -- the grouping of an xor tree.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  return fmaxf(v, dpp<kDppMirror>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  return v + dpp<kDppMirror>(v);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -128,10 +146,9 @@ __device__ void attn_span(const AttnArgs& a, int x, int kvh, int b, int rg) {
       if (c0 + j > plast) { kreg[u] = (u32x4){0u, 0u, 0u, 0u}; vreg[u] = kreg[u]; }
     }
   };
-  load_kv(span0);
-
   // Q as the MFMA A operand: lane holds row wrow0 + l16, dims ks*32 + 8*g4 .. +8, as a
-  // bf16 hi part (qa) and lo part (ql).
+  // bf16 hi part (qa) and lo part (ql).  The Q loads go out first and are converted while
+  // the K/V loads are still in flight.
   bf16x8 qa[DH / 32], ql[DH / 32];
   {
     const int qr = wrow0 + l16;
@@ -145,6 +162,8 @@ __device__ void attn_span(const AttnArgs& a, int x, int kvh, int b, int rg) {
     for (int ks = 0; ks < DH / 32; ++ks)
 #pragma unroll
       for (int e = 0; e < 8; ++e) qv[ks][e] = qp[ks * 32 + g4 * 8 + e];
+    load_kv(span0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < DH / 32; ++ks) {
       uint16_t t[8], tl[8];
@@ -163,9 +182,12 @@ __device__ void attn_span(const AttnArgs& a, int x, int kvh, int b, int rg) {
       ul.y = tl[2] | ((uint32_t)tl[3] << 16);
       ul.z = tl[4] | ((uint32_t)tl[5] << 16);
       ul.w = tl[6] | ((uint32_t)tl[7] << 16);
+      // Keep the conversion here, ahead of the K/V wait, rather than next to its first use.
+      asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w), "+v"(ul.x), "+v"(ul.y), "+v"(ul.z), "+v"(ul.w));
       qa[ks] = as_bf16x8(u);
       ql[ks] = as_bf16x8(ul);
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
   // Positions of the 4 rows this lane holds in the MFMA output layout (rows 4*g4 + r).
   int prow[4];
@@ -227,11 +249,7 @@ __device__ void attn_span(const AttnArgs& a, int x, int kvh, int b, int rg) {
           sc[kt][r] = v;
           m = fmaxf(m, v);
         }
-        m = fmaxf(m, __shfl_xor(m, 1));
-        m = fmaxf(m, __shfl_xor(m, 2));
-        m = fmaxf(m, __shfl_xor(m, 4));
-        m = fmaxf(m, __shfl_xor(m, 8));
-        mloc[r] = m;
+        mloc[r] = row16_max(m);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -244,11 +262,7 @@ __device__ void attn_span(const AttnArgs& a, int x, int kvh, int b, int rg) {
           sc[kt][r] = pv;
           ls += pv;
         }
-        ls += __shfl_xor(ls, 1);
-        ls += __shfl_xor(ls, 2);
-        ls += __shfl_xor(ls, 4);
-        ls += __shfl_xor(ls, 8);
-        lrun[r] = lrun[r] * alpha[r] + ls;
+        lrun[r] = lrun[r] * alpha[r] + row16_sum(ls);
         mrun[r] = mnew;
       }
 #pragma unroll
