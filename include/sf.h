@@ -202,17 +202,16 @@ sf_status sf_sync(sf_cache* cache);
 #define SF_KERNEL_GATEUP     3
 #define SF_KERNEL_DOWN       4
 #define SF_KERNEL_LMHEAD     5
-/* The whole verify pass as captured (a replay of the verify graph with commit off).
- * When n_seqs*(k_max+1) <= 16 this is the single persistent pass kernel. */
-#define SF_KERNEL_PASS       6
+/* The whole verify pass as captured (a replay of the verify graph with commit off). */
+#define SF_KERNEL_VERIFY     6
 
 /* sf_time_kernel: launch one kernel of the verify pass `iters` times back to back
  * on the library stream between two HIP events and return the mean time per
  * launch in microseconds (host *avg_us) and the algorithmic bytes one launch
  * must move (host *bytes: weights once, activations once, KV once; for
- * SF_KERNEL_PASS: every weight once, K/V of positions 0..len+k_max read once per
+ * SF_KERNEL_VERIFY: every weight once, K/V of positions 0..len+k_max read once per
  * layer and the new positions written once).
- * Overwrites scratch and the staged drafts (SF_KERNEL_PASS stages k = 0 with commit
+ * Overwrites scratch and the staged drafts (SF_KERNEL_VERIFY stages k = 0 with commit
  * off), so call it between passes only. */
 sf_status sf_time_kernel(sf_cache* cache, int32_t kernel, int32_t iters, float* avg_us,
                          double* bytes);

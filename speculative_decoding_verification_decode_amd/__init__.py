@@ -34,7 +34,7 @@ SF_KERNEL_OPROJ = 2
 SF_KERNEL_GATEUP = 3
 SF_KERNEL_DOWN = 4
 SF_KERNEL_LMHEAD = 5
-SF_KERNEL_PASS = 6
+SF_KERNEL_VERIFY = 6
 
 _NAMES = {SF_E_ARG: "SF_E_ARG", SF_E_CAPACITY: "SF_E_CAPACITY", SF_E_STATE: "SF_E_STATE",
           SF_E_HIP: "SF_E_HIP", SF_E_NOMEM: "SF_E_NOMEM"}

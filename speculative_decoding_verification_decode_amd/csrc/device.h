@@ -1,5 +1,5 @@
-// Device code shared by the standalone kernels (kernels.hip) and the persistent pass
-// kernel (pass.hip): bf16 helpers, coherent store/load helpers, and the attention span and
+// Device helpers of the verify kernels: bf16 conversion, DPP row reductions, coherent
+// store/load helpers, the MFMA-order activation layout, and the attention span and
 // span-merge bodies.
 #pragma once
 
@@ -44,8 +44,8 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 
 // Stores and loads of data that other workgroups of the same kernel read.  With kCoh the
 // access is agent-coherent (a relaxed agent-scope atomic: the store is written through to
-// memory and the load is served coherently), which is what the persistent pass kernel
-// needs between its work items; without it these are ordinary accesses.
+// memory and the load is served coherently), as the split-K partials of the GEMM need;
+// without it these are ordinary accesses.
 template <bool kCoh, typename T>
 __device__ __forceinline__ void st(T* p, T v) {
   if constexpr (kCoh) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -64,7 +64,6 @@ struct sf_model {
   float* gfinal = nullptr;
   float* ones = nullptr;
   uint4* head = nullptr;
-  PassLayer* dlayers = nullptr;  // per-layer pointer table for the pass kernel
   DevAllocs mem;
 };
 
@@ -95,19 +94,7 @@ struct sf_cache {
   int kh = 4;                      // GEMM: weight tiles per pipelined batch (one-tile row counts)
   int* cnt = nullptr;              // k-split arrival counters [layer][QKV, O, down][block]
   int cnt_stride = 0;
-  // pass kernel
-  bool pass_ok = false;       // buffers exist (the pass kernel serves passes of <= kPassRows rows)
-  bool pass_on = false;       // chosen at allocation: SF_PASS=1 selects the pass kernel
-  int grid = 0, psp_q = 1, psp_o = 1, sp_pass = 1, attn_a = 1;
   bool prefetch_o = true;   // warm the O projection's weights into L2 during attention
-  float *px = nullptr, *pxm = nullptr, *pssq = nullptr, *pssqm = nullptr, *pq = nullptr, *pdpart = nullptr;
-  float *pqpart = nullptr, *popart = nullptr;
-  uint16_t *pa = nullptr, *pam = nullptr, *po = nullptr, *ph = nullptr;
-  unsigned long long* pamax = nullptr;
-  int *pflags = nullptr, *pdcount = nullptr, *psync = nullptr;  // psync: hcount, epoch, abort, checkin, queue[2]
-  int pcnt_stride = 0;
-  unsigned long long* ptrace = nullptr;  // per-item timeline (diagnostics, SF_PASS_TRACE)
-  int trace_items = 0;
   hipGraphExec_t gx_verify = nullptr, gx_draft = nullptr;
   std::vector<int> len_h, next_h, len_hi;
   bool dirty = false;
@@ -310,17 +297,6 @@ extern "C" sf_status sf_model_create(const sf_model_desc* desc, const void* cons
     TRY(dalloc((void**)&m->head, (size_t)V * H * 2));
     TRY(with_table(rh, s, [&](const uint16_t* const* t) { return launch_pack(m->head, t, V / kTileN, H / kTileK, s); }));
   }
-  {
-    std::vector<PassLayer> tab(d.n_layers);
-    for (int l = 0; l < d.n_layers; ++l) {
-      const Layer& Ly = m->layers[l];
-      tab[l] = PassLayer{Ly.wqkv, Ly.wo, Ly.wgu, Ly.wd, Ly.bqkv, Ly.g1, Ly.g2,
-                         l + 1 < d.n_layers ? m->layers[l + 1].g1 : (d.has_head ? m->gfinal : m->ones)};
-    }
-    TRY(dalloc((void**)&m->dlayers, tab.size() * sizeof(PassLayer)));
-    hipError_t e = hipMemcpy(m->dlayers, tab.data(), tab.size() * sizeof(PassLayer), hipMemcpyHostToDevice);
-    if (e != hipSuccess) return cleanup(fail(SF_E_HIP, std::string("layer table: ") + hipGetErrorString(e)));
-  }
 #undef TRY
   *out = m;
   return SF_OK;
@@ -350,53 +326,6 @@ static hipError_t run_gemm(const sf_cache* c, int kind, int layer, int epi, Gemm
 }
 
 // ------------------------------------------------------------------------------------------
-// Pass kernel arguments for a run of r.B sequences x r.T positions (r.B*r.T <= kPassRows).
-static PassArgs pass_args(sf_cache* c, const Run& r) {
-  sf_model* m = c->m;
-  const sf_model_desc& d = m->d;
-  PassArgs P{};
-  P.L = m->L; P.H = m->H; P.Q = m->Q; P.F = m->F; P.V = m->V; P.nq = m->nq; P.nkv = m->nkv; P.dh = m->dh;
-  P.has_head = d.has_head;
-  P.nb_qkv = m->nb_qkv; P.nb_h = m->nb_h; P.nb_gu = m->nb_gu; P.nb_head = m->nb_head;
-  P.kb_h = m->H / kTileK; P.kb_q = m->Q / kTileK; P.kb_f = m->F / kTileK;
-  P.sp_q = c->psp_q; P.sp_o = c->psp_o; P.sp_d = c->sp_pass;
-  P.eps = d.rms_eps;
-  P.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)m->dh));
-  P.embed = m->embed; P.layers = m->dlayers; P.head = m->head;
-  P.B = r.B; P.T = r.T; P.R = r.B * r.T; P.cap = c->cap; P.kmax = r.kmax; P.nchunk = c->nchunk;
-  P.seq_stride = (long)c->seq_stride; P.layer_stride = (long)c->layer_stride;
-  P.kpool = c->kpool + (size_t)r.seq0 * c->seq_stride; P.vpool = c->vpool + (size_t)r.seq0 * c->seq_stride;
-  P.rope = c->rope; P.len = c->len + r.seq0; P.next = c->next + r.seq0; P.stage = c->stage_d;
-  P.x = c->px; P.xm = c->pxm; P.a = c->pa; P.am = c->pam; P.ssq = c->pssq; P.ssqm = c->pssqm; P.q = c->pq;
-  P.o = c->po; P.h = c->ph; P.qpart = c->pqpart; P.opart = c->popart; P.dpart = c->pdpart;
-  P.apart = c->apart; P.amax = c->pamax;
-  P.logits = r.logits; P.hidden = d.has_head ? nullptr : c->hidden; P.result = c->res_d;
-  P.draft_out = r.draft_mode ? c->dout_d : nullptr;
-  P.flags = c->pflags; P.dcount = c->pdcount; P.hcount = c->psync; P.epoch = c->psync + 1;
-  P.abort_flag = c->psync + 2;
-  P.queue = c->psync + 4;
-  P.checkin = c->psync + 3;
-  P.cnt_stride = c->pcnt_stride;
-  P.trace = c->ptrace;
-  const int G = m->nq / m->nkv;
-  P.attn_a = c->attn_a;
-  P.ngroups = (r.T * G + 63) / 64;
-  const int n_attn = m->nkv * r.B * P.ngroups * P.attn_a;
-  const int n_comb = (m->nq * P.R + 3) / 4;
-  P.off_attn = m->nb_qkv * P.sp_q;
-  P.off_comb = P.off_attn + n_attn;
-  P.off_o = P.off_comb + n_comb;
-  P.off_gu = P.off_o + m->nb_h * P.sp_o;
-  P.off_down = P.off_gu + m->nb_gu;
-  P.per_layer = P.off_down + m->nb_h * P.sp_d;
-  P.n_items = m->nb_h + m->L * P.per_layer + (d.has_head ? m->nb_head : 0) + 1;
-  return P;
-}
-
-static bool use_pass(const sf_cache* c, const Run& r) {
-  return c->pass_ok && c->pass_on && !r.prefill && r.seq0 == 0 && r.B * r.T <= kPassRows;
-}
-
 // ------------------------------------------------------------------------------------------
 // One forward pass (embed .. accept) enqueued on the model stream.  Used both eagerly and
 // under stream capture, so it must not allocate or synchronise.
@@ -409,7 +338,6 @@ static hipError_t enqueue_forward(sf_cache* c, const Run& r) {
   int32_t* next = c->next + r.seq0;
   const size_t kvoff = (size_t)r.seq0 * c->seq_stride;
   hipError_t e;
-  if (use_pass(c, r)) return launch_pass(pass_args(c, r), c->grid, s);
 
   EmbedArgs ea{};
   ea.embed = m->embed; ea.stage = c->stage_d; ea.len = len; ea.next = next; ea.gain = m->layers[0].g1;
@@ -583,66 +511,6 @@ extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacit
     if (e != hipSuccess) return bail(fail(SF_E_NOMEM, std::string("hipHostMalloc: ") + hipGetErrorString(e)));
     memset(c->stage_h, 0, sizeof(Stage));
   }
-  if (n_seqs <= kPassRows) {
-    // Pass kernel: per-layer activation buffers for up to kPassRows rows, flags, counters.
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-      return bail(fail(SF_E_HIP, "cannot read the compute unit count"));
-    // Workgroups per compute unit (all must be resident at once: the kernel is limited to
-    // two per CU by its register and LDS use).
-    int wpc = 2;
-    if (const char* v = getenv("SF_PASS_WPC")) wpc = std::max(1, std::min(2, atoi(v)));
-    c->grid = cus * wpc;
-    const int L = m->L, H = m->H, nbh = m->nb_h;
-    // k splits: the down projection gets about two items per workgroup, QKV and O about one
-    // (short items keep the attention chain short); each wave keeps >= 8 tiles.
-    auto split = [&](int nb, int kb, int per_wg, const char* env) {
-      int sp = std::max(1, (per_wg * c->grid + nb / 2) / nb);
-      sp = std::min(sp, std::max(1, kb / 32));
-      if (const char* v = getenv(env)) sp = std::max(1, std::min(atoi(v), std::max(1, kb / 4)));
-      return sp;
-    };
-    const int sp = split(nbh, m->F / kTileK, 2, "SF_PASS_SPD");
-    c->sp_pass = sp;
-    c->psp_q = split(m->nb_qkv, m->H / kTileK, 1, "SF_PASS_SPQ");
-    c->psp_o = split(nbh, m->Q / kTileK, 1, "SF_PASS_SPO");
-    c->attn_a = std::min(32, c->nchunk);
-    if (const char* v = getenv("SF_PASS_ATTN")) c->attn_a = std::max(1, std::min(atoi(v), c->nchunk));
-    const size_t P16 = kPassRows, P32 = 2 * kPassRows;
-    TRY(dalloc((void**)&c->px, (L + 1) * P16 * H * 4));
-    TRY(dalloc((void**)&c->pxm, L * P16 * H * 4));
-    TRY(dalloc((void**)&c->pa, (L + 1) * P32 * H * 2));
-    TRY(dalloc((void**)&c->pam, L * P32 * H * 2));
-    TRY(dalloc((void**)&c->pssq, (L + 1) * P16 * nbh * 4));
-    TRY(dalloc((void**)&c->pssqm, L * P16 * nbh * 4));
-    TRY(dalloc((void**)&c->pq, L * P16 * m->Q * 4));
-    TRY(dalloc((void**)&c->po, L * P32 * m->Q * 2));
-    TRY(dalloc((void**)&c->ph, L * P32 * m->F * 2));
-    TRY(dalloc((void**)&c->pqpart, (size_t)L * m->nb_qkv * c->psp_q * P16 * 32 * 4));
-    TRY(dalloc((void**)&c->popart, (size_t)L * nbh * c->psp_o * P16 * 32 * 4));
-    TRY(dalloc((void**)&c->pdpart, (size_t)L * nbh * sp * P16 * 32 * 4));
-    TRY(dalloc((void**)&c->pamax, P16 * 8));
-    c->pcnt_stride = std::max(m->nb_qkv, nbh);
-    TRY(dalloc((void**)&c->pdcount, (size_t)L * 3 * c->pcnt_stride * 4));
-    TRY(dalloc((void**)&c->psync, 32));
-    int n_max = 0;
-    for (int T : {c->T, 1}) {
-      if (n_seqs * T > kPassRows) continue;
-      n_max = std::max(n_max, pass_args(c, Run{n_seqs, T, 0, k_max, nullptr, false, false}).n_items);
-    }
-    TRY(dalloc((void**)&c->pflags, (size_t)std::max(n_max, 1) * 4));
-    if (getenv("SF_PASS_TRACE")) {
-      TRY(dalloc((void**)&c->ptrace, (size_t)std::max(n_max, 1) * 32));
-      c->trace_items = n_max;
-    }
-    const int sync0[4] = {0, 1, 0, 0};  // head counter, epoch (flags start at 0, the first pass is 1), abort, check-ins
-    hipError_t e = hipMemcpyAsync(c->psync, sync0, sizeof(sync0), hipMemcpyHostToDevice, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
-    if (e != hipSuccess) return bail(fail(SF_E_HIP, std::string("pass state: ") + hipGetErrorString(e)));
-    c->pass_ok = true;
-    const char* v = getenv("SF_PASS");
-    c->pass_on = (v && v[0] == '1');
-  }
   {
     hipError_t e = launch_rope_table(c->rope, capacity, m->dh / 2, (double)m->d.rope_base, s);
     if (e == hipSuccess) e = hipEventCreate(&c->ev0);
@@ -664,19 +532,11 @@ extern "C" sf_status sf_cache_free(sf_cache* c) {
   return SF_OK;
 }
 
-// The pass kernel's report of a dependency wait that gave up (res_h must be current).
-static sf_status pass_status(sf_cache* c) {
-  if (c->pass_ok && c->res_h[kResultStatus] != 0)
-    return fail(SF_E_HIP, "pass kernel: a dependency wait timed out; the cache state is undefined");
-  return SF_OK;
-}
-
 // Refresh the host copies of length / pending token from the device.
 static sf_status refresh(sf_cache* c) {
   hipStream_t s = c->m->stream;
   HIPCHK(hipStreamSynchronize(s));
   HIPCHK(hipMemcpy(c->res_h, c->res_d, 4 * kMaxRows * 4, hipMemcpyDeviceToHost));
-  if (sf_status st = pass_status(c)) return st;
   HIPCHK(hipMemcpy(c->res_h, c->len, c->B * 4, hipMemcpyDeviceToHost));
   for (int b = 0; b < c->B; ++b) c->len_h[b] = c->res_h[b];
   HIPCHK(hipMemcpy(c->res_h, c->next, c->B * 4, hipMemcpyDeviceToHost));
@@ -684,24 +544,6 @@ static sf_status refresh(sf_cache* c) {
   c->len_hi = c->len_h;
   c->dirty = false;
   return SF_OK;
-}
-
-// Diagnostics: with SF_PASS_TRACE=<file>, each host-synchronised verify writes the pass
-// kernel's per-item (start, end) timestamps to <file> and the item layout to <file>.json.
-static void dump_trace(sf_cache* c) {
-  const char* path = getenv("SF_PASS_TRACE");
-  if (!path || !c->ptrace) return;
-  const PassArgs P = pass_args(c, Run{c->B, c->T, 0, c->kmax, nullptr, false, false});
-  std::vector<unsigned long long> h((size_t)P.n_items * 4);
-  if (hipMemcpy(h.data(), c->ptrace, h.size() * 8, hipMemcpyDeviceToHost) != hipSuccess) return;
-  if (FILE* f = fopen(path, "wb")) { fwrite(h.data(), 8, h.size(), f); fclose(f); }
-  const std::string js = std::string(path) + ".json";
-  if (FILE* f = fopen(js.c_str(), "w")) {
-    fprintf(f, "{\"n_items\": %d, \"nb_h\": %d, \"L\": %d, \"per_layer\": %d, \"off_attn\": %d, \"off_comb\": %d, "
-            "\"off_o\": %d, \"off_gu\": %d, \"off_down\": %d, \"nb_head\": %d, \"grid\": %d}\n",
-            P.n_items, P.nb_h, P.L, P.per_layer, P.off_attn, P.off_comb, P.off_o, P.off_gu, P.off_down, P.nb_head, c->grid);
-    fclose(f);
-  }
 }
 
 static size_t stage_bytes(int B, int kmax) { return offsetof(Stage, draft) + (size_t)B * std::max(kmax, 1) * 4; }
@@ -748,8 +590,6 @@ extern "C" sf_status sf_verify(sf_cache* c, const int32_t* draft, const int32_t*
   if (!m->d.has_head && dev_out)
     HIPCHK(hipMemcpyAsync(dev_out, c->hidden, (size_t)c->B * c->T * m->H * 2, hipMemcpyDeviceToDevice, s));
   HIPCHK(hipStreamSynchronize(s));
-  if (sf_status st = pass_status(c)) return st;
-  if (c->ptrace) dump_trace(c);
   for (int b = 0; b < c->B; ++b) {
     const int M = c->res_h[b];
     if (accepted) accepted[b] = M;
@@ -890,7 +730,6 @@ extern "C" sf_status sf_draft_step(sf_cache* c, int32_t n_steps, int32_t* tokens
   HIPCHK(hipMemcpyAsync(c->dout_h, c->dout_d, (size_t)c->B * kMaxDraftSteps * 4, hipMemcpyDeviceToHost, s));
   HIPCHK(hipMemcpyAsync(c->res_h, c->res_d, 4 * kMaxRows * 4, hipMemcpyDeviceToHost, s));
   HIPCHK(hipStreamSynchronize(s));
-  if (sf_status st = pass_status(c)) return st;
   for (int b = 0; b < c->B; ++b) {
     for (int i = 0; i < n_steps; ++i)
       if (tokens) tokens[b * n_steps + i] = c->dout_h[b * kMaxDraftSteps + i];
@@ -962,7 +801,7 @@ extern "C" sf_status sf_time_kernel(sf_cache* c, int32_t kernel, int32_t iters, 
   if (!c || !avg_us) return fail(SF_E_ARG, "NULL argument");
   if (iters < 1 || iters > 100000) return fail(SF_E_ARG, "iters out of range");
   sf_model* m = c->m;
-  if (kernel < SF_KERNEL_QKV || kernel > SF_KERNEL_PASS) return fail(SF_E_ARG, "unknown kernel");
+  if (kernel < SF_KERNEL_QKV || kernel > SF_KERNEL_VERIFY) return fail(SF_E_ARG, "unknown kernel");
   if (kernel == SF_KERNEL_LMHEAD && !m->d.has_head) return fail(SF_E_ARG, "no LM head");
   if (c->dirty) {
     if (sf_status st = refresh(c)) return st;
@@ -973,7 +812,7 @@ extern "C" sf_status sf_time_kernel(sf_cache* c, int32_t kernel, int32_t iters, 
   const int rows = c->B * c->T;
   double L_total = 0;
   for (int b = 0; b < c->B; ++b) L_total += c->len_h[b] + c->T;
-  if (kernel == SF_KERNEL_PASS) {
+  if (kernel == SF_KERNEL_VERIFY) {
     Stage* st = c->stage_h;
     st->flags = kFlagNoCommit;
     st->kmax = c->kmax;
@@ -988,7 +827,6 @@ extern "C" sf_status sf_time_kernel(sf_cache* c, int32_t kernel, int32_t iters, 
     float ms = 0.f;
     HIPCHK(hipEventElapsedTime(&ms, c->ev0, c->ev1));
     HIPCHK(hipMemcpy(c->res_h, c->res_d, 4 * kMaxRows * 4, hipMemcpyDeviceToHost));
-    if (sf_status st2 = pass_status(c)) return st2;
     *avg_us = ms * 1000.f / iters;
     if (bytes) {
       const double kvdim = (double)m->KV;

@@ -146,75 +146,3 @@ hipError_t launch_copy_kv(uint16_t* pool, uint16_t* src, long pool_layer_stride,
                           int dh, int n_layers, int n_pos, int src_positions, int to_pool, hipStream_t s);
 
 }  // namespace sf
-
-namespace sf {
-
-// ----------------------------------------------------------------------------------------------
-// Persistent pass kernel (pass.hip): the whole forward pass of at most kPassRows rows as one
-// launch.  Work items are numbered in dependency order and dealt round-robin to one
-// workgroup per compute unit; every item waits only for earlier items through per-item done
-// flags tagged with the pass epoch.
-constexpr int kPassRows = 16;  // 2*rows hi/lo operand rows fill one 32-wide MFMA tile
-// Slot of the result buffer (4*kMaxRows ints) where the pass kernel reports a timed-out wait.
-constexpr int kResultStatus = 4 * kMaxRows - 1;
-
-struct PassLayer {
-  const uint4 *wqkv, *wo, *wgu, *wd;  // packed weight tiles
-  const float *bqkv, *g1, *g2;        // packed q/k/v bias, RMSNorm gains
-  const float* gnext;                 // gain applied to this layer's output (next ln1, final norm, or ones)
-};
-
-struct PassArgs {
-  // shape
-  int L, H, Q, F, V, nq, nkv, dh, has_head;
-  int nb_qkv, nb_h, nb_gu, nb_head;   // 32-row weight blocks
-  int kb_h, kb_q, kb_f;               // 16-k tiles of hidden, q width, ffn
-  int sp_q, sp_o, sp_d;               // k splits of QKV, O and down blocks
-  float eps, scale_log2;
-  const uint16_t* embed;
-  const PassLayer* layers;
-  const uint4* head;
-  // sequences and cache
-  int B, T, R, cap, kmax, nchunk;
-  long seq_stride, layer_stride;      // elements
-  uint16_t *kpool, *vpool;
-  const float2* rope;
-  int32_t *len, *next;
-  Stage* stage;
-  // per-layer activations (each written once per pass); row stride = the feature width
-  float* x;         // [L+1][kPassRows][H]   layer inputs; x[L] feeds the head
-  float* xm;        // [L][kPassRows][H]     after attention
-  uint16_t* a;      // [L+1][2*kPassRows][H] x * gain as hi/lo rows
-  uint16_t* am;     // [L][2*kPassRows][H]
-  float* ssq;       // [L+1][kPassRows][H/32]
-  float* ssqm;      // [L][kPassRows][H/32]
-  float* q;         // [L][kPassRows][Q]
-  uint16_t* o;      // [L][2*kPassRows][Q]
-  uint16_t* h;      // [L][2*kPassRows][F]
-  float* qpart;     // k-split partials [L][nb_qkv][sp_q][kPassRows][32]
-  float* opart;     // [L][nb_h][sp_o][kPassRows][32]
-  float* dpart;     // [L][nb_h][sp_d][kPassRows][32]
-  float* apart;     // attention span partials, reused by every layer (read coherently)
-  unsigned long long* amax;  // [kPassRows] packed (value, index) maxima of the LM head
-  float* logits;    // optional fp32 [R][V]
-  uint16_t* hidden; // optional bf16 [R][H] (stacks without a head)
-  int32_t* result;  // accepted[B], target[B][T], status
-  int32_t* draft_out;
-  // synchronisation
-  int* flags;       // per item: epoch of the pass that finished it
-  int* dcount;      // [L][QKV, O, down][cnt_stride] arrivals of k splits (grow by sp per pass)
-  int cnt_stride;
-  int* queue;       // [2] work-item counters, one per epoch parity
-  int* checkin;     // workgroups that have read this pass's epoch
-  int* hcount;      // finished LM-head items of this pass
-  int* epoch;       // pass counter (read at kernel start, advanced by the final item)
-  int* abort_flag;  // set when a wait gives up; sticky
-  // item layout
-  int n_items, per_layer, off_attn, off_comb, off_o, off_gu, off_down;
-  int attn_a, ngroups;                // attention items per (kv head, sequence, row group); row groups
-  unsigned long long* trace;          // optional [n_items][2]: item start / end (s_memrealtime ticks)
-};
-
-hipError_t launch_pass(const PassArgs& p, int grid, hipStream_t s);
-
-}  // namespace sf

@@ -19,28 +19,6 @@ def say(*a):
     sys.stdout.flush()
 
 
-MODES = ["kernels", "pass"]   # kernel-per-step path, and the persistent pass kernel
-
-
-class mode_env:
-    """Sets SF_PASS while an engine is created: the cache picks its path at allocation."""
-
-    def __init__(self, mode):
-        self.mode = mode
-
-    def __enter__(self):
-        import os
-        self.old = os.environ.get("SF_PASS")
-        os.environ["SF_PASS"] = "1" if self.mode == "pass" else "0"
-
-    def __exit__(self, *exc):
-        import os
-        if self.old is None:
-            os.environ.pop("SF_PASS", None)
-        else:
-            os.environ["SF_PASS"] = self.old
-
-
 def need_gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
@@ -72,14 +50,13 @@ def accepted_decided(res_o, M_gpu, K):
 class Pair:
     """An oracle model/cache and a GPU engine with the same weights and state."""
 
-    def __init__(self, shape, seed_cfg, capacity, k_max, n_seqs=1, mode="kernels"):
+    def __init__(self, shape, seed_cfg, capacity, k_max, n_seqs=1):
         sfb = need_gpu()
         self.sfb = sfb
         self.shape = shape
         w = synth.model_weights(shape, synth.seeds(seed_cfg)["weights"])
         self.model = oracle.Model(shape, w, cache=True)
-        with mode_env(mode):
-            self.eng = sfb.Engine(shape, w, n_seqs=n_seqs, capacity=capacity, k_max=k_max)
+        self.eng = sfb.Engine(shape, w, n_seqs=n_seqs, capacity=capacity, k_max=k_max)
         self.K = k_max
         self.cap = capacity
 

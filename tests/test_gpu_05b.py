@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import GAP, MODES, mode_env, need_gpu, say
+from gpu_util import GAP, need_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -26,13 +26,12 @@ def weights():
     return synth.model_weights(S, synth.seeds(2)["weights"])
 
 
-@pytest.fixture(scope="module", params=MODES)
-def setup(request, weights):
+@pytest.fixture(scope="module")
+def setup(weights):
     sfb = need_gpu()
     model = oracle.Model(S, weights, cache=True)
-    say(f"[0.5b] engine ({request.param})")
-    with mode_env(request.param):
-        eng = sfb.Engine(S, weights, n_seqs=1, capacity=2048, k_max=8)
+    say("[0.5b] engine")
+    eng = sfb.Engine(S, weights, n_seqs=1, capacity=2048, k_max=8)
     yield sfb, model, eng
     eng.close()
 

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import GAP, LOGIT_TOL, MODES, accepted_decided, check_targets, mode_env, need_gpu, say
+from gpu_util import GAP, LOGIT_TOL, accepted_decided, check_targets, need_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -42,12 +42,11 @@ def hist():
     return synth.lookup_history(S.vocab, 8193, synth.seeds(4)["prompt"])
 
 
-@pytest.fixture(scope="module", params=MODES)
-def eng(request, weights):
+@pytest.fixture(scope="module")
+def eng(weights):
     sfb = need_gpu()
-    say(f"[7b] packing weights ({request.param})")
-    with mode_env(request.param):
-        e = sfb.Engine(S, weights, n_seqs=1, capacity=CAP, k_max=K)
+    say("[7b] packing weights")
+    e = sfb.Engine(S, weights, n_seqs=1, capacity=CAP, k_max=K)
     yield e
     e.close()
 
@@ -134,14 +133,12 @@ def test_prefill_two_chunks_matches_oracle(eng, weights):
     assert sfb.sf_cache_state(eng.cache, 0) == (70, nxt)
 
 
-@pytest.mark.parametrize("mode", MODES)
-def test_half_stack_hidden_states_match_oracle(weights, kv, hist, mode):
+def test_half_stack_hidden_states_match_oracle(weights, kv, hist):
     sfb = need_gpu()
     H = synth.QWEN7B_HALF
     ctx = 1024
-    say(f"[7b-half] engine ({mode})")
-    with mode_env(mode):
-        e = sfb.Engine(H, weights, n_seqs=1, capacity=4096, k_max=K)
+    say("[7b-half] engine")
+    e = sfb.Engine(H, weights, n_seqs=1, capacity=4096, k_max=K)
     try:
         nxt = int(hist[ctx])
         _load_ctx(sfb, e.cache, kv, ctx, nxt, n_layers=H.n_layers)

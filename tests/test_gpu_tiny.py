@@ -11,18 +11,18 @@ import torch
 
 import oracle
 import synth
-from gpu_util import GAP, LOGIT_TOL, MODES, Pair, accepted_decided, check_targets, need_gpu, say
+from gpu_util import GAP, LOGIT_TOL, Pair, accepted_decided, check_targets, need_gpu, say
 
 pytestmark = pytest.mark.gpu
 
 S = synth.TINY
 
 
-@pytest.fixture(scope="module", params=MODES)
-def pair(request):
+@pytest.fixture(scope="module")
+def pair():
     need_gpu()
-    say(f"[tiny] building engine ({request.param})")
-    p = Pair(S, 1, capacity=128, k_max=4, mode=request.param)
+    say("[tiny] building engine")
+    p = Pair(S, 1, capacity=128, k_max=4)
     yield p
     p.close()
 
@@ -268,14 +268,13 @@ def test_four_wave_workgroups_split_k_and_64_row_chunks(monkeypatch):
         p.close()
 
 
-@pytest.mark.parametrize("mode", MODES)
-def test_largest_capacity_and_longest_draft(mode):
+def test_largest_capacity_and_longest_draft():
     """Capacity 16384 with K=15 drafts: the span merge sees up to 256 position spans.  Seeded
     synthetic K/V fill contexts on both sides of the 64-, 128- and 192-span boundaries and
     the last ones the capacity allows."""
     need_gpu()
     K, cap = 15, 16384
-    p = Pair(S, 1, capacity=cap, k_max=K, mode=mode)
+    p = Pair(S, 1, capacity=cap, k_max=K)
     try:
         kb, vb = synth.synthetic_kv(S, cap - K - 1, synth.seeds(1)["kv"])
         kd = torch.from_numpy(np.ascontiguousarray(kb).view(np.int16)).cuda()
