@@ -37,7 +37,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
   static_assert(!WIDE || MT == 4, "wide row groups hold two hi and two lo m tiles");
   constexpr int kThreads = NW * 64;
   constexpr int kRealRows = MT * 16;
-  __shared__ float tile[MT * 1024];
+  __shared__ float tile[NW][MT * 1024];
   __shared__ float rscale[kRealRows + NW];
 
   const int tid = threadIdx.x;
@@ -150,20 +150,21 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
     }
   }
 
-  // Cross-wave sum in wave order.
+  // Cross-wave sum in wave order: every wave stores its accumulators, then each thread adds
+  // the NW images of its share of the outputs into wave 0's image.
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    if (wave == w) {
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+    for (int r = 0; r < 16; ++r) tile[wave][mt * 1024 + lane * 16 + r] = acc[mt][r];
+  __syncthreads();
+  for (int e = tid; e < MT * 1024; e += kThreads) {
+    float v = tile[0][e];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float* t = &tile[mt * 1024 + lane * 16 + r];
-          *t = (w == 0) ? acc[mt][r] : *t + acc[mt][r];
-        }
-    }
-    __syncthreads();
+    for (int w = 1; w < NW; ++w) v += tile[w][e];
+    tile[0][e] = v;
   }
+  __syncthreads();
+  const float* img = tile[0];
 
   // k split over g.sp workgroups per block: each stores its partial tile (agent-coherent,
   // so the others see it without a cache flush) and counts its arrival on the block's
@@ -174,8 +175,8 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
   float* const pblk = g.part + (size_t)nb * g.sp * g.rows * 32;   // [split][row][32]
   // hi + lo of output (n_local nl, local row m) from this workgroup's tile
   auto tval = [&](int nl, int m) {
-    return WIDE ? tile[tile_idx(nl, m)] + tile[tile_idx(nl, 64 + m)]
-                : tile[tile_idx(nl, m)] + tile[tile_idx(nl, g.rows + m)];
+    return WIDE ? img[tile_idx(nl, m)] + img[tile_idx(nl, 64 + m)]
+                : img[tile_idx(nl, m)] + img[tile_idx(nl, g.rows + m)];
   };
   if (split) {
     for (int e = tid; e < 32 * kRealRows; e += kThreads) {
