@@ -16,6 +16,99 @@
 
 namespace sf {
 
+// Epilogues of one 32-row n block for real rows r0 .. r0+kRealRows-1: val(nl, m) is output
+// (n_local nl, local row m) before the row scale; rscale holds the folded RMSNorm's row scales.
+// Called by every thread of the workgroup.
+template <int EPI, int kRealRows, int kThreads, typename Val>
+__device__ void gemm_epilogue(const GemmArgs& g, int nb, int r0, const float* rscale, Val val) {
+  const int tid = threadIdx.x;
+  if constexpr (EPI == kEpiQkv) {
+    // Packed rows of n block nb: 0..15 = head dims i0..i0+15, 16..31 = their RoPE partners.
+    for (int it = tid; it < 16 * kRealRows; it += kThreads) {
+      const int p = it & 15, m = it >> 4, mr = r0 + m;
+      if (mr >= g.rows) continue;
+      const int half = g.dh >> 1, bph = g.dh >> 5;
+      const int qb = g.nq * bph, kvb = g.nkv * bph;
+      int sec, head, blk;
+      if (nb < qb) { sec = 0; head = nb / bph; blk = nb - head * bph; }
+      else if (nb < qb + kvb) { sec = 1; head = (nb - qb) / bph; blk = nb - qb - head * bph; }
+      else { sec = 2; head = (nb - qb - kvb) / bph; blk = nb - qb - kvb - head * bph; }
+      const int i = blk * 16 + p;
+      const float s = rscale[m];
+      const float y1 = val(p, m) * s + g.bias[nb * 32 + p];
+      const float y2 = val(p + 16, m) * s + g.bias[nb * 32 + p + 16];
+      const int b = mr / g.T, slot = mr - b * g.T;
+      const int pos = g.len[b] + slot;
+      if (pos < g.cap) {
+        if (sec == 2) {
+          uint16_t* dst = g.vc + (size_t)b * g.seq_stride + ((size_t)head * g.cap + pos) * g.dh;
+          dst[i] = f2bf(y1);
+          dst[i + half] = f2bf(y2);
+        } else {
+          const float2 cs = g.rope[(size_t)pos * half + i];
+          const float o1 = y1 * cs.x - y2 * cs.y;
+          const float o2 = y2 * cs.x + y1 * cs.y;
+          if (sec == 0) {
+            float* dst = g.q + ((size_t)mr * g.nq + head) * g.dh;
+            dst[i] = o1;
+            dst[i + half] = o2;
+          } else {
+            uint16_t* dst = g.kc + (size_t)b * g.seq_stride + ((size_t)head * g.cap + pos) * g.dh;
+            dst[i] = f2bf(o1);
+            dst[i + half] = f2bf(o2);
+          }
+        }
+      }
+    }
+  } else if constexpr (EPI == kEpiResid) {
+    __shared__ float sq[32 * kRealRows];
+    for (int e = tid; e < 32 * kRealRows; e += kThreads) {
+      const int nl = e & 31, m = e >> 5, mr = r0 + m;
+      float v = 0.f;
+      if (mr < g.rows) {
+        const int n = nb * 32 + nl;
+        const size_t o = (size_t)mr * g.n_out + n;
+        v = g.x[o] + val(nl, m);
+        g.x[o] = v;
+        store_split(g.a_next, g.rows, mr, n, v * g.gain_next[n]);
+        if (g.hidden) g.hidden[o] = f2bf(v);
+      }
+      sq[e] = v * v;
+    }
+    __syncthreads();
+    if (tid < kRealRows && r0 + tid < g.rows) {
+      float s = 0.f;
+#pragma unroll
+      for (int nl = 0; nl < 32; ++nl) s += sq[tid * 32 + nl];
+      g.ssq_out[(size_t)(r0 + tid) * g.nb + nb] = s;
+    }
+  } else if constexpr (EPI == kEpiSwiglu) {
+    // Packed rows of n block nb: 0..15 = gate rows j0..j0+15, 16..31 = up rows j0..j0+15.
+    for (int it = tid; it < 16 * kRealRows; it += kThreads) {
+      const int p = it & 15, m = it >> 4, mr = r0 + m;
+      if (mr >= g.rows) continue;
+      const float s = rscale[m];
+      const float gt = val(p, m) * s;
+      const float up = val(p + 16, m) * s;
+      const float hv = gt / (1.0f + expf(-gt)) * up;
+      store_split(g.h, g.rows, mr, nb * 16 + p, hv);
+    }
+  } else if constexpr (EPI == kEpiArgmax) {
+    const int m = tid, mr = r0 + m;
+    if (m < kRealRows && mr < g.rows) {
+      const float s = rscale[m];
+      float best = -INFINITY;
+      int bi = nb * 32;
+      for (int nl = 0; nl < 32; ++nl) {
+        const float v = val(nl, m) * s;
+        if (g.logits) g.logits[(size_t)mr * g.vocab + nb * 32 + nl] = v;
+        if (v > best) { best = v; bi = nb * 32 + nl; }
+      }
+      g.amax[(size_t)mr * g.nb + nb] = make_float2(best, __int_as_float(bi));
+    }
+  }
+}
+
 // ----------------------------------------------------------------------------------------------
 // Skinny GEMM: Y[m][n] = sum_k A[m][k] * W[n][k] for m < rows.  A has 2*rows rows (bf16 hi
 // parts, then lo parts) and Y[m] = acc[m] + acc[rows + m]; 2*rows <= 32*MT.
@@ -26,12 +119,11 @@ namespace sf {
 // before the current batch's MFMAs) and the waves' accumulators are added in wave order,
 // so results do not depend on scheduling.
 //
-// WIDE (more than 64 rows, batched verify): grid.y splits the rows into groups of 64; the
+// WIDE (more than 64 rows, batched verify): the rows are split into groups of 64; the
 // workgroup of group rg holds two hi m tiles (operand rows 64rg .. 64rg+63) and two lo m tiles
 // (rows + 64rg ..), so each weight tile feeds four MFMAs, and the groups of one block share
-// the block's weights through L2 (grid.x, a multiple of 8 here, keeps them on one XCD).  A
-// row's arithmetic is the same as in the compact layout: the per-row result does not depend
-// on the batch.
+// the block's weights through L2 (see the index mapping below).  A row's arithmetic is the
+// same as in the compact layout: the per-row result does not depend on the batch.
 template <int EPI, int MT, int NW, int KH = kHalf, bool WIDE = false>
 __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
   static_assert(!WIDE || MT == 4, "wide row groups hold two hi and two lo m tiles");
@@ -42,8 +134,20 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int nb = blockIdx.x / g.sp, spi = blockIdx.x - nb * g.sp;
-  const int rg = WIDE ? (int)blockIdx.y : 0, r0 = rg * 64;   // first real row of this workgroup
+  // WIDE: workgroup (block split bs, row group rg) has linear index ((bs/8)*G + rg)*8 + bs%8
+  // (G row groups).  Workgroups go to the 8 XCDs round-robin by index, so the G row groups of
+  // one block split run on the same XCD and are dispatched close together: the block's
+  // weights come from HBM once and from that XCD's L2 for the other row groups.
+  const int G = WIDE ? (g.rows + 63) / 64 : 1;
+  int bs = blockIdx.x, rg = 0;
+  if (WIDE) {
+    const int q = blockIdx.x >> 3;
+    rg = q % G;
+    bs = (q / G) * 8 + (blockIdx.x & 7);
+    if (bs >= g.nb * g.sp) return;   // padding of the last group of 8 block splits
+  }
+  const int nb = bs / g.sp, spi = bs - nb * g.sp;
+  const int r0 = rg * 64;   // first real row of this workgroup
   const int U = g.sp * NW, u = spi * NW + wave;
   const int kt0 = (int)(((long)g.kb * u) / U), kt1 = (int)(((long)g.kb * (u + 1)) / U);
 
@@ -187,7 +291,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
-      const int old = __hip_atomic_fetch_add(g.counters + nb * gridDim.y + rg, 1, __ATOMIC_RELAXED,
+      const int old = __hip_atomic_fetch_add(g.counters + nb * G + rg, 1, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
       last_arrival = ((old + 1) % g.sp) == 0;
     }
@@ -205,90 +309,203 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
     for (int q = 0; q < g.sp; ++q) s += pblk[((size_t)q * g.rows + r0 + m) * 32 + nl];
     return s;
   };
-  if constexpr (EPI == kEpiQkv) {
-    // Packed rows of n block nb: 0..15 = head dims i0..i0+15, 16..31 = their RoPE partners.
-    for (int it = tid; it < 16 * kRealRows; it += kThreads) {
-      const int p = it & 15, m = it >> 4, mr = r0 + m;
-      if (mr >= g.rows) continue;
-      const int half = g.dh >> 1, bph = g.dh >> 5;
-      const int qb = g.nq * bph, kvb = g.nkv * bph;
-      int sec, head, blk;
-      if (nb < qb) { sec = 0; head = nb / bph; blk = nb - head * bph; }
-      else if (nb < qb + kvb) { sec = 1; head = (nb - qb) / bph; blk = nb - qb - head * bph; }
-      else { sec = 2; head = (nb - qb - kvb) / bph; blk = nb - qb - kvb - head * bph; }
-      const int i = blk * 16 + p;
-      const float s = rscale[m];
-      const float y1 = val(p, m) * s + g.bias[nb * 32 + p];
-      const float y2 = val(p + 16, m) * s + g.bias[nb * 32 + p + 16];
-      const int b = mr / g.T, slot = mr - b * g.T;
-      const int pos = g.len[b] + slot;
-      if (pos < g.cap) {
-        if (sec == 2) {
-          uint16_t* dst = g.vc + (size_t)b * g.seq_stride + ((size_t)head * g.cap + pos) * g.dh;
-          dst[i] = f2bf(y1);
-          dst[i + half] = f2bf(y2);
-        } else {
-          const float2 cs = g.rope[(size_t)pos * half + i];
-          const float o1 = y1 * cs.x - y2 * cs.y;
-          const float o2 = y2 * cs.x + y1 * cs.y;
-          if (sec == 0) {
-            float* dst = g.q + ((size_t)mr * g.nq + head) * g.dh;
-            dst[i] = o1;
-            dst[i + half] = o2;
-          } else {
-            uint16_t* dst = g.kc + (size_t)b * g.seq_stride + ((size_t)head * g.cap + pos) * g.dh;
-            dst[i] = f2bf(o1);
-            dst[i + half] = f2bf(o2);
-          }
-        }
+  gemm_epilogue<EPI, kRealRows, kThreads>(g, nb, r0, rscale, val);
+}
+
+// ----------------------------------------------------------------------------------------------
+// Batched GEMM (more than 64 rows).  The per-output arithmetic is k_gemm's: wave w of split spi
+// accumulates k tiles [kb*u/U, kb*(u+1)/U) (u = 4*spi + w, U = 4*sp) in one MFMA chain per
+// output tile, the waves' sums are added in wave order and the splits' in split order, so a
+// row's result does not depend on the batch.  What changes is the work per wave: four 32-row
+// weight blocks x four m tiles (hi and lo parts of 64 real rows), 16 MFMAs per k tile against
+// 8 KB of operands, where the row-group mode of k_gemm does 4 MFMAs per 5 KB.  Operands stream
+// through a per-wave ring of kStages stages in LDS, filled by buffer loads that write LDS
+// directly, kStages-1 k tiles ahead of the MFMAs; a wave reads only its own ring, so the loop
+// needs no barrier, only a wait on its own loads.
+template <int EPI, int kStages>
+__global__ __launch_bounds__(256) void k_gemm_b(const GemmArgs g) {
+  constexpr int NW = 4, kThreads = 256, kRealRows = 64, kBlocks = 4, MT = 4;
+  constexpr int kLoads = kBlocks + MT;   // buffer loads per stage and wave
+  __shared__ __attribute__((aligned(16))) u32x4 ring[NW][kStages][kLoads][64];
+  __shared__ float rscale[kRealRows + NW];
+  __shared__ int last_arrival;
+  static_assert(sizeof(ring) >= NW * MT * 1024 * sizeof(float), "the ring holds the cross-wave images");
+  static_assert(kLoads == 8, "the stage read below is written for 4 weight + 4 operand fragments");
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  // Workgroup (group split gs, row group rg) has linear index ((gs/8)*G + rg)*8 + gs%8: the G
+  // row groups of one group of weight blocks run on the same XCD (workgroups go to the XCDs
+  // round-robin by index) and close together in time, so the weights come from HBM once.
+  const int G = (g.rows + 63) / 64, ngroups = g.nb / kBlocks;
+  const int q = blockIdx.x >> 3;
+  const int rg = q % G;
+  const int gs = (q / G) * 8 + (blockIdx.x & 7);
+  if (gs >= ngroups * g.sp) return;   // padding of the last group of 8
+  const int bgrp = gs / g.sp, spi = gs - bgrp * g.sp;
+  const int nb0 = bgrp * kBlocks, r0 = rg * 64;
+  const int U = g.sp * NW, u = spi * NW + wave;
+  const int kt0 = (int)(((long)g.kb * u) / U), kt1 = (int)(((long)g.kb * (u + 1)) / U);
+
+  constexpr bool kScaled = (EPI == kEpiQkv || EPI == kEpiSwiglu || EPI == kEpiArgmax);
+  constexpr int kRowsPerWave = kRealRows / NW;
+  float ssq_v[kRowsPerWave][kSsqPerLane];
+  if constexpr (kScaled) {
+    const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)g.ssq_in, (short)0, g.rows * g.nparts_in * 4, kBufferWord3);
+#pragma unroll
+    for (int j = 0; j < kRowsPerWave; ++j) {
+      const int mr = r0 + wave + NW * j;
+#pragma unroll
+      for (int i = 0; i < kSsqPerLane; ++i) {
+        const int p = lane + 64 * i;
+        const int off = (mr < g.rows && p < g.nparts_in) ? (mr * g.nparts_in + p) * 4 : 0x7FFFFFF0;
+        ssq_v[j][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sres, off, 0, 0));
       }
     }
-  } else if constexpr (EPI == kEpiResid) {
-    __shared__ float sq[32 * kRealRows];
-    for (int e = tid; e < 32 * kRealRows; e += kThreads) {
-      const int nl = e & 31, m = e >> 5, mr = r0 + m;
-      float v = 0.f;
-      if (mr < g.rows) {
-        const int n = nb * 32 + nl;
-        const size_t o = (size_t)mr * g.n_out + n;
-        v = g.x[o] + val(nl, m);
-        g.x[o] = v;
-        store_split(g.a_next, g.rows, mr, n, v * g.gain_next[n]);
-        if (g.hidden) g.hidden[o] = f2bf(v);
-      }
-      sq[e] = v * v;
+  }
+
+  __amdgpu_buffer_rsrc_t wres[kBlocks];
+#pragma unroll
+  for (int j = 0; j < kBlocks; ++j)
+    wres[j] = __builtin_amdgcn_make_buffer_rsrc((void*)(g.w + (size_t)(nb0 + j) * g.kb * 64), (short)0, kt1 * 1024,
+                                                kBufferWord3);
+  const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)g.a, (short)0, (int)act_bytes(2 * g.rows, g.k), kBufferWord3);
+  const int ext_rows = 2 * g.rows;
+  const int tsp = act_tile_pieces(ext_rows);
+  const int a_lane = ((lane >> 5) * ext_rows + (lane & 31)) * 16;
+  int mt_row0[MT];
+  bool mt_ok[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    mt_row0[mt] = (mt < 2 ? 0 : g.rows) + r0 + (mt & 1) * 32;
+    mt_ok[mt] = r0 + (mt & 1) * 32 + (lane & 31) < g.rows;
+  }
+  // Stage sg <- k tile kt: the four weight tiles, then the four operand tiles.  Lanes whose
+  // source is out of range (tiles at or past kt1, rows past the batch) read zeros.
+  auto issue = [&](int kt, int sg) {
+#pragma unroll
+    for (int j = 0; j < kBlocks; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wres[j], (__attribute__((address_space(3))) void*)&ring[wave][sg][j][0],
+                                               16, kt * 1024 + lane * 16, 0, 0, 0);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int off = (mt_ok[mt] && kt < kt1) ? a_lane + (kt * tsp + mt_row0[mt]) * 16 : 0x7FFFFFF0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ares, (__attribute__((address_space(3))) void*)&ring[wave][sg][kBlocks + mt][0],
+                                               16, off, 0, 0, 0);
+    }
+  };
+
+  f32x16 acc[kBlocks][MT];
+#pragma unroll
+  for (int j = 0; j < kBlocks; ++j)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[j][mt] = (f32x16){};
+
+#pragma unroll
+  for (int i = 0; i < kStages - 1; ++i) issue(kt0 + i, i);
+  if constexpr (kScaled) {
+#pragma unroll
+    for (int j = 0; j < kRowsPerWave; ++j) {
+      float t = 0.f;
+#pragma unroll
+      for (int i = 0; i < kSsqPerLane; ++i) t += ssq_v[j][i];
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) t += __shfl_xor(t, o);
+      const int m = wave + NW * j;
+      if (lane == 0) rscale[m] = (r0 + m < g.rows) ? 1.0f / sqrtf(t / (float)g.k + g.eps) : 0.f;
+    }
+  }
+  // vmcnt encoding of s_waitcnt (expcnt and lgkmcnt left at their maxima): at most
+  // (kStages-1) stages of loads outstanding, i.e. the oldest stage has landed in LDS.
+  constexpr int kWait = (kStages - 1) * kLoads;
+  constexpr int kWaitImm = (kWait & 15) | ((kWait >> 4) << 14) | (7 << 4) | (15 << 8);
+  int stage = 0;
+  for (int kt = kt0; kt < kt1; ++kt) {
+    issue(kt + kStages - 1, stage == 0 ? kStages - 1 : stage - 1);
+    __builtin_amdgcn_s_waitcnt(kWaitImm);
+    __builtin_amdgcn_sched_barrier(0);
+    // The stage's eight fragments.  Read in asm: the compiler cannot tell which ring slots the
+    // in-flight LDS-writing loads target and would otherwise wait for all of them here.
+    u32x4 w[kBlocks], a[MT];
+    const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) u32x4*)&ring[wave][stage][0][lane];
+    asm volatile(
+        "ds_read_b128 %0, %8\n"
+        "ds_read_b128 %1, %8 offset:1024\n"
+        "ds_read_b128 %2, %8 offset:2048\n"
+        "ds_read_b128 %3, %8 offset:3072\n"
+        "ds_read_b128 %4, %8 offset:4096\n"
+        "ds_read_b128 %5, %8 offset:5120\n"
+        "ds_read_b128 %6, %8 offset:6144\n"
+        "ds_read_b128 %7, %8 offset:7168\n"
+        "s_waitcnt lgkmcnt(0)"
+        // early-clobber: no fragment may share a register with the address the later reads use
+        : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+        : "v"(lds));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kBlocks; ++j)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[j][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w[j]), as_bf16x8(a[mt]), acc[j][mt], 0, 0, 0);
+    stage = (stage + 1 == kStages) ? 0 : stage + 1;
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // the loads past kt1 (zeros) land before the ring is reused
+  __syncthreads();
+
+  // Per weight block: the waves' images in the ring, summed in wave order into wave 0's.
+  float* const red = reinterpret_cast<float*>(&ring[0][0][0][0]);
+  const bool split = g.sp > 1;
+#pragma unroll
+  for (int j = 0; j < kBlocks; ++j) {   // unrolled: acc[j] must stay in registers
+    const int nb = nb0 + j;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[wave * MT * 1024 + mt * 1024 + lane * 16 + r] = acc[j][mt][r];
+    __syncthreads();
+    for (int e = tid; e < MT * 1024; e += kThreads) {
+      float v = red[e];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) v += red[w * MT * 1024 + e];
+      red[e] = v;
     }
     __syncthreads();
-    if (tid < kRealRows && r0 + tid < g.rows) {
-      float s = 0.f;
-#pragma unroll
-      for (int nl = 0; nl < 32; ++nl) s += sq[tid * 32 + nl];
-      g.ssq_out[(size_t)(r0 + tid) * g.nb + nb] = s;
-    }
-  } else if constexpr (EPI == kEpiSwiglu) {
-    // Packed rows of n block nb: 0..15 = gate rows j0..j0+15, 16..31 = up rows j0..j0+15.
-    for (int it = tid; it < 16 * kRealRows; it += kThreads) {
-      const int p = it & 15, m = it >> 4, mr = r0 + m;
-      if (mr >= g.rows) continue;
-      const float s = rscale[m];
-      const float gt = val(p, m) * s;
-      const float up = val(p + 16, m) * s;
-      const float hv = gt / (1.0f + expf(-gt)) * up;
-      store_split(g.h, g.rows, mr, nb * 16 + p, hv);
-    }
-  } else if constexpr (EPI == kEpiArgmax) {
-    const int m = tid, mr = r0 + m;
-    if (m < kRealRows && mr < g.rows) {
-      const float s = rscale[m];
-      float best = -INFINITY;
-      int bi = nb * 32;
-      for (int nl = 0; nl < 32; ++nl) {
-        const float v = val(nl, m) * s;
-        if (g.logits) g.logits[(size_t)mr * g.vocab + nb * 32 + nl] = v;
-        if (v > best) { best = v; bi = nb * 32 + nl; }
+    auto tval = [&](int nl, int m) { return red[tile_idx(nl, m)] + red[tile_idx(nl, 64 + m)]; };
+    if (split) {
+      float* const pblk = g.part + (size_t)nb * g.sp * g.rows * 32;
+      for (int e = tid; e < 32 * kRealRows; e += kThreads) {
+        const int nl = e & 31, m = e >> 5;
+        if (r0 + m < g.rows) st<true>(pblk + ((size_t)spi * g.rows + r0 + m) * 32 + nl, tval(nl, m));
       }
-      g.amax[(size_t)mr * g.nb + nb] = make_float2(best, __int_as_float(bi));
+    } else {
+      gemm_epilogue<EPI, kRealRows, kThreads>(g, nb, r0, rscale, tval);
     }
+    __syncthreads();
+  }
+  if (!split) return;
+  // k split: as in k_gemm, the last of the sp workgroups of this group of blocks and row group
+  // adds the partials in split order and runs the epilogues.
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(g.counters + nb0 * G + rg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_arrival = ((old + 1) % g.sp) == 0;
+  }
+  __syncthreads();
+  if (!last_arrival) return;
+  asm volatile("" ::: "memory");
+  for (int j = 0; j < kBlocks; ++j) {
+    const float* const pblk = g.part + (size_t)(nb0 + j) * g.sp * g.rows * 32;
+    auto val = [&](int nl, int m) {
+      float s = 0.f;
+      for (int q2 = 0; q2 < g.sp; ++q2) s += pblk[((size_t)q2 * g.rows + r0 + m) * 32 + nl];
+      return s;
+    };
+    gemm_epilogue<EPI, kRealRows, kThreads>(g, nb0 + j, r0, rscale, val);
+    __syncthreads();
   }
 }
 
@@ -297,7 +514,14 @@ static hipError_t gemm_mt(const GemmArgs& g, hipStream_t s) {
   const int mt = (2 * g.rows + 31) / 32;
   const dim3 grid(g.nb * g.sp), block(NW * 64);
   if (g.rows > 64) {
-    k_gemm<EPI, 4, 4, 4, true><<<dim3(g.nb * g.sp, (g.rows + 63) / 64), dim3(256), 0, s>>>(g);
+    const int G = (g.rows + 63) / 64;
+    if (g.nb % 4 == 0) {
+      const int ngs = (g.nb / 4) * g.sp;
+      k_gemm_b<EPI, 4><<<dim3(((ngs + 7) / 8) * 8 * G), dim3(256), 0, s>>>(g);
+    } else {
+      const int nbs = g.nb * g.sp;
+      k_gemm<EPI, 4, 4, 4, true><<<dim3(((nbs + 7) / 8) * 8 * G), dim3(256), 0, s>>>(g);
+    }
     return hipGetLastError();
   }
   switch (mt) {
