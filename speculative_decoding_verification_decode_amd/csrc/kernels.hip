@@ -318,19 +318,15 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
 // output tile, the waves' sums are added in wave order and the splits' in split order, so a
 // row's result does not depend on the batch.  What changes is the work per wave: four 32-row
 // weight blocks x four m tiles (hi and lo parts of 64 real rows), 16 MFMAs per k tile against
-// 8 KB of operands, where the row-group mode of k_gemm does 4 MFMAs per 5 KB.  Operands stream
-// through a per-wave ring of kStages stages in LDS, filled by buffer loads that write LDS
-// directly, kStages-1 k tiles ahead of the MFMAs; a wave reads only its own ring, so the loop
-// needs no barrier, only a wait on its own loads.
+// 8 KB of operands, where the row-group mode of k_gemm does 4 MFMAs per 5 KB.  With the
+// 256 accumulators in AGPRs, the VGPRs hold a ring of kStages k tiles of operands (32 registers
+// each), loaded kStages-1 tiles ahead of the MFMAs that use them.
 template <int EPI, int kStages>
 __global__ __launch_bounds__(256) void k_gemm_b(const GemmArgs g) {
   constexpr int NW = 4, kThreads = 256, kRealRows = 64, kBlocks = 4, MT = 4;
-  constexpr int kLoads = kBlocks + MT;   // buffer loads per stage and wave
-  __shared__ __attribute__((aligned(16))) u32x4 ring[NW][kStages][kLoads][64];
+  __shared__ float red[NW * MT * 1024];   // cross-wave images of one weight block
   __shared__ float rscale[kRealRows + NW];
   __shared__ int last_arrival;
-  static_assert(sizeof(ring) >= NW * MT * 1024 * sizeof(float), "the ring holds the cross-wave images");
-  static_assert(kLoads == 8, "the stage read below is written for 4 weight + 4 operand fragments");
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -382,18 +378,15 @@ __global__ __launch_bounds__(256) void k_gemm_b(const GemmArgs g) {
     mt_row0[mt] = (mt < 2 ? 0 : g.rows) + r0 + (mt & 1) * 32;
     mt_ok[mt] = r0 + (mt & 1) * 32 + (lane & 31) < g.rows;
   }
-  // Stage sg <- k tile kt: the four weight tiles, then the four operand tiles.  Lanes whose
-  // source is out of range (tiles at or past kt1, rows past the batch) read zeros.
-  auto issue = [&](int kt, int sg) {
+  // One k tile of operands: the four weight fragments, then the four operand fragments.
+  // Lanes whose source is out of range (tiles at or past kt1, rows past the batch) read zeros.
+  auto load = [&](int kt, u32x4 (&f)[kBlocks + MT]) {
 #pragma unroll
-    for (int j = 0; j < kBlocks; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wres[j], (__attribute__((address_space(3))) void*)&ring[wave][sg][j][0],
-                                               16, kt * 1024 + lane * 16, 0, 0, 0);
+    for (int j = 0; j < kBlocks; ++j) f[j] = __builtin_amdgcn_raw_buffer_load_b128(wres[j], kt * 1024 + lane * 16, 0, 0);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int off = (mt_ok[mt] && kt < kt1) ? a_lane + (kt * tsp + mt_row0[mt]) * 16 : 0x7FFFFFF0;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ares, (__attribute__((address_space(3))) void*)&ring[wave][sg][kBlocks + mt][0],
-                                               16, off, 0, 0, 0);
+      f[kBlocks + mt] = __builtin_amdgcn_raw_buffer_load_b128(ares, off, 0, 0);
     }
   };
 
@@ -403,8 +396,9 @@ __global__ __launch_bounds__(256) void k_gemm_b(const GemmArgs g) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[j][mt] = (f32x16){};
 
+  u32x4 ring[kStages][kBlocks + MT];
 #pragma unroll
-  for (int i = 0; i < kStages - 1; ++i) issue(kt0 + i, i);
+  for (int i = 0; i < kStages - 1; ++i) load(kt0 + i, ring[i]);
   if constexpr (kScaled) {
 #pragma unroll
     for (int j = 0; j < kRowsPerWave; ++j) {
@@ -417,45 +411,25 @@ __global__ __launch_bounds__(256) void k_gemm_b(const GemmArgs g) {
       if (lane == 0) rscale[m] = (r0 + m < g.rows) ? 1.0f / sqrtf(t / (float)g.k + g.eps) : 0.f;
     }
   }
-  // vmcnt encoding of s_waitcnt (expcnt and lgkmcnt left at their maxima): at most
-  // (kStages-1) stages of loads outstanding, i.e. the oldest stage has landed in LDS.
-  constexpr int kWait = (kStages - 1) * kLoads;
-  constexpr int kWaitImm = (kWait & 15) | ((kWait >> 4) << 14) | (7 << 4) | (15 << 8);
-  int stage = 0;
-  for (int kt = kt0; kt < kt1; ++kt) {
-    issue(kt + kStages - 1, stage == 0 ? kStages - 1 : stage - 1);
-    __builtin_amdgcn_s_waitcnt(kWaitImm);
-    __builtin_amdgcn_sched_barrier(0);
-    // The stage's eight fragments.  Read in asm: the compiler cannot tell which ring slots the
-    // in-flight LDS-writing loads target and would otherwise wait for all of them here.
-    u32x4 w[kBlocks], a[MT];
-    const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) u32x4*)&ring[wave][stage][0][lane];
-    asm volatile(
-        "ds_read_b128 %0, %8\n"
-        "ds_read_b128 %1, %8 offset:1024\n"
-        "ds_read_b128 %2, %8 offset:2048\n"
-        "ds_read_b128 %3, %8 offset:3072\n"
-        "ds_read_b128 %4, %8 offset:4096\n"
-        "ds_read_b128 %5, %8 offset:5120\n"
-        "ds_read_b128 %6, %8 offset:6144\n"
-        "ds_read_b128 %7, %8 offset:7168\n"
-        "s_waitcnt lgkmcnt(0)"
-        // early-clobber: no fragment may share a register with the address the later reads use
-        : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
-        : "v"(lds));
-    __builtin_amdgcn_sched_barrier(0);
+  auto mma = [&](const u32x4 (&f)[kBlocks + MT]) {
 #pragma unroll
     for (int j = 0; j < kBlocks; ++j)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        acc[j][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w[j]), as_bf16x8(a[mt]), acc[j][mt], 0, 0, 0);
-    stage = (stage + 1 == kStages) ? 0 : stage + 1;
+        acc[j][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(f[j]), as_bf16x8(f[kBlocks + mt]), acc[j][mt], 0,
+                                                              0, 0);
+  };
+  // Unrolled by kStages so that every ring slot is a fixed set of registers.
+  for (int kt = kt0; kt < kt1; kt += kStages) {
+#pragma unroll
+    for (int s = 0; s < kStages; ++s) {
+      load(kt + s + kStages - 1, ring[(s + kStages - 1) % kStages]);
+      if (kt + s < kt1) mma(ring[s]);
+    }
   }
-  __builtin_amdgcn_s_waitcnt(0);   // the loads past kt1 (zeros) land before the ring is reused
   __syncthreads();
 
-  // Per weight block: the waves' images in the ring, summed in wave order into wave 0's.
-  float* const red = reinterpret_cast<float*>(&ring[0][0][0][0]);
+  // Per weight block: the waves' images in LDS, summed in wave order into wave 0's.
   const bool split = g.sp > 1;
 #pragma unroll
   for (int j = 0; j < kBlocks; ++j) {   // unrolled: acc[j] must stay in registers
