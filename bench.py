@@ -24,7 +24,9 @@ HBM_PEAK_GBS = 8000.0
 K = 8
 CONTEXTS = (512, 2048, 8192)
 CAPACITY = 8192 + 16
-KERNEL_SRC = os.path.join(ROOT, "speculative_decoding_verification_decode_amd", "csrc", "kernels.hip")
+# Device sources of the GEMM kernel whose counters the traffic record holds.
+KERNEL_SRCS = [os.path.join(ROOT, "speculative_decoding_verification_decode_amd", "csrc", f)
+               for f in ("kernels.hip", "device.h", "sf_internal.h")]
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gate_up_7b_k8_hbm_traffic.md")
 
 
@@ -38,8 +40,10 @@ def measured_traffic():
     try:
         rec = dict(l[2:].split(": ", 1) for l in open(TRAFFIC_RECORD).read().splitlines()
                    if l.startswith("- ") and ": " in l)
-        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-        if rec.get("kernels.hip sha256", "").strip("` ") != src:
+        h = hashlib.sha256()
+        for f in KERNEL_SRCS:
+            h.update(open(f, "rb").read())
+        if rec.get("device sources sha256", "").strip("` ") != h.hexdigest():
             return None
         return int(rec["traffic bytes per launch"].strip("` "))
     except (OSError, KeyError, ValueError):

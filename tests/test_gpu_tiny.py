@@ -269,9 +269,9 @@ def test_four_wave_workgroups_split_k_and_64_row_chunks(monkeypatch):
 
 
 def test_largest_capacity_and_longest_draft():
-    """Capacity 16384 with K=15 drafts: the span merge sees up to 256 position spans.  Seeded
-    synthetic K/V fill contexts on both sides of the 64-, 128- and 192-span boundaries and
-    the last ones the capacity allows."""
+    """Capacity 16384 with K=15 drafts: the span merge sees up to 256 position spans (four
+    register slots of 64).  Seeded synthetic K/V fill contexts on both sides of the 64-,
+    128- and 192-span boundaries and the last ones the capacity allows."""
     need_gpu()
     K, cap = 15, 16384
     p = Pair(S, 1, capacity=cap, k_max=K)
