@@ -324,7 +324,11 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
 template <int EPI, int kStages>
 __global__ __launch_bounds__(256) void k_gemm_b(const GemmArgs g) {
   constexpr int NW = 4, kThreads = 256, kRealRows = 64, kBlocks = 4, MT = 4;
-  __shared__ float red[NW * MT * 1024];   // cross-wave images of one weight block
+  // Cross-wave images of one weight block: wave w's accumulator register r of m tile mt, lane l
+  // at red[w][(mt*16 + r)*kRedPitch + l].  Consecutive lanes hit consecutive banks when the
+  // images are written, and the odd pitch spreads the epilogue's reads over the banks.
+  constexpr int kRedPitch = 65, kRedWave = MT * 16 * kRedPitch;
+  __shared__ float red[NW * kRedWave];
   __shared__ float rscale[kRealRows + NW];
   __shared__ int last_arrival;
 
@@ -437,16 +441,21 @@ __global__ __launch_bounds__(256) void k_gemm_b(const GemmArgs g) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) red[wave * MT * 1024 + mt * 1024 + lane * 16 + r] = acc[j][mt][r];
+      for (int r = 0; r < 16; ++r) red[wave * kRedWave + (mt * 16 + r) * kRedPitch + lane] = acc[j][mt][r];
     __syncthreads();
-    for (int e = tid; e < MT * 1024; e += kThreads) {
+    for (int e = tid; e < kRedWave; e += kThreads) {
       float v = red[e];
 #pragma unroll
-      for (int w = 1; w < NW; ++w) v += red[w * MT * 1024 + e];
+      for (int w = 1; w < NW; ++w) v += red[w * kRedWave + e];
       red[e] = v;
     }
     __syncthreads();
-    auto tval = [&](int nl, int m) { return red[tile_idx(nl, m)] + red[tile_idx(nl, 64 + m)]; };
+    // Output (n_local nl, operand row e) in 32x32 MFMA output order: lane (e & 31) + 32*((nl&7)>>2),
+    // register 4*(nl>>3) + (nl&3) of m tile e >> 5.
+    auto at = [&](int nl, int e) {
+      return red[((e >> 5) * 16 + ((nl >> 3) << 2) + (nl & 3)) * kRedPitch + (e & 31) + (((nl & 7) >> 2) << 5)];
+    };
+    auto tval = [&](int nl, int m) { return at(nl, m) + at(nl, 64 + m); };
     if (split) {
       float* const pblk = g.part + (size_t)nb * g.sp * g.rows * 32;
       for (int e = tid; e < 32 * kRealRows; e += kThreads) {
