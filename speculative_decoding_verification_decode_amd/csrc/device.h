@@ -96,10 +96,11 @@ __device__ __forceinline__ int tile_idx(int nl, int m) {
 }
 
 // ----------------------------------------------------------------------------------------------
-// Attention, phase 1 (MFMA).  Workgroup (span x, kv head, sequence x row group) takes up to 64
+// Attention, phase 1 (MFMA).  Workgroup (x0, kv head, sequence x row group) takes up to 64
 // query rows of one KV head (slot-major: row = slot*G + head-in-group, G = nq/nkv) against
-// the span's positions [x*kSpan, (x+1)*kSpan), in chunks of 64 position-aligned keys; each
-// chunk's K/V loads are issued while the previous chunk is computed.  One chunk per span:
+// spans x0, x0 + xstep, ... (positions [x*kSpan, (x+1)*kSpan)), each in chunks of 64
+// position-aligned keys, writing one partial per span; each chunk's K/V loads are issued
+// while the previous chunk is computed.  One chunk per span:
 // four-chunk spans (smaller partials, fewer workgroups) measured 0.27 ms slower per 7B verify
 // at contexts 512 and 2048 (each chunk is about 3 us of latency-bound work) and only 2% faster
 // at 8192.
@@ -114,7 +115,7 @@ constexpr int kSpan = kSpanChunks * kChunk;
 constexpr int kSpanSlots = (kMaxCapacity / kSpan + 63) / 64;
 
 template <int DH, bool kCoh>
-__device__ void attn_span(const AttnArgs& a, int x, int kvh, int b, int rg) {
+__device__ void attn_spans(const AttnArgs& a, int x0, int xstep, int kvh, int b, int rg) {
   constexpr int KP = DH + 8;        // K row pitch (bf16): 16-byte aligned, conflict-free b128 reads
   constexpr int VP = kChunk + 8;    // V^T row pitch
   constexpr int PP = kChunk + 8;    // P row pitch
@@ -125,7 +126,7 @@ __device__ void attn_span(const AttnArgs& a, int x, int kvh, int b, int rg) {
   const int G = a.nq / a.nkv, nrows = a.T * G;
   const int L = a.len[b];
   const int plast = L + a.T - 1;
-  const int span0 = x * kSpan;
+  int x = x0, span0 = x * kSpan;
   if (span0 > plast) return;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -201,112 +202,121 @@ __device__ void attn_span(const AttnArgs& a, int x, int kvh, int b, int rg) {
     prow[r] = (qr < nrows) ? L + qr / G : -1;
   }
 
-  f32x4 o[DH / 16];
+  for (;;) {   // spans x0, x0 + xstep, ... up to the last position
+    f32x4 o[DH / 16];
 #pragma unroll
-  for (int nt = 0; nt < DH / 16; ++nt) o[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float mrun[4], lrun[4];
+    for (int nt = 0; nt < DH / 16; ++nt) o[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    float mrun[4], lrun[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) { mrun[r] = -INFINITY; lrun[r] = 0.f; }
+    for (int r = 0; r < 4; ++r) { mrun[r] = -INFINITY; lrun[r] = 0.f; }
 
-
-  for (int ci = 0; ci < kSpanChunks; ++ci) {
-    const int c0 = span0 + ci * kChunk;
-    if (c0 > plast) break;
-    __syncthreads();   // every wave is done with the previous chunk's K and V
+    for (int ci = 0; ci < kSpanChunks; ++ci) {
+      const int c0 = span0 + ci * kChunk;
+      if (c0 > plast) break;
+      __syncthreads();   // every wave is done with the previous chunk's K and V
 #pragma unroll
-    for (int u = 0; u < kKvPerThread; ++u) {
-      const int idx = tid + u * 256;
-      const int j = idx / (DH / 8), d8 = (idx - j * (DH / 8)) * 8;
-      *(u32x4*)(&Kl[j * KP + d8]) = kreg[u];
-      const uint32_t vw[4] = {vreg[u].x, vreg[u].y, vreg[u].z, vreg[u].w};
+      for (int u = 0; u < kKvPerThread; ++u) {
+        const int idx = tid + u * 256;
+        const int j = idx / (DH / 8), d8 = (idx - j * (DH / 8)) * 8;
+        *(u32x4*)(&Kl[j * KP + d8]) = kreg[u];
+        const uint32_t vw[4] = {vreg[u].x, vreg[u].y, vreg[u].z, vreg[u].w};
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        Vt[(d8 + 2 * t) * VP + j] = (uint16_t)(vw[t] & 0xFFFFu);
-        Vt[(d8 + 2 * t + 1) * VP + j] = (uint16_t)(vw[t] >> 16);
-      }
-    }
-    // The next chunk's K/V loads go out now and land while this chunk is computed.
-    if (ci + 1 < kSpanChunks && c0 + kChunk <= plast) load_kv(c0 + kChunk);
-    __syncthreads();
-    float alpha[4];
-    if (active) {
-      f32x4 sc[4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        sc[kt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < DH / 32; ++ks) {
-          const bf16x8 kb8 = as_bf16x8(*(const u32x4*)(&Kl[(kt * 16 + l16) * KP + ks * 32 + g4 * 8]));
-          sc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb8, sc[kt], 0, 0, 0);
-          sc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[ks], kb8, sc[kt], 0, 0, 0);
+        for (int t = 0; t < 4; ++t) {
+          Vt[(d8 + 2 * t) * VP + j] = (uint16_t)(vw[t] & 0xFFFFu);
+          Vt[(d8 + 2 * t + 1) * VP + j] = (uint16_t)(vw[t] >> 16);
         }
       }
-      // Scale, causal mask, running softmax.  Lane holds rows 4*g4+r, keys kt*16 + l16.
-      float mloc[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float m = -INFINITY;
+      // The next chunk's K/V loads (this span's next chunk, else the first chunk of this
+      // workgroup's next span) go out now and land while this chunk is computed.
+      {
+        const int nc = (ci + 1 < kSpanChunks && c0 + kChunk <= plast) ? c0 + kChunk : (x + xstep) * kSpan;
+        if (nc <= plast) load_kv(nc);
+      }
+      __syncthreads();
+      float alpha[4];
+      if (active) {
+        f32x4 sc[4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-          const int kp = c0 + kt * 16 + l16;
-          float v = sc[kt][r] * a.scale_log2;
-          v = (kp <= prow[r]) ? v : -INFINITY;
-          sc[kt][r] = v;
-          m = fmaxf(m, v);
+          sc[kt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < DH / 32; ++ks) {
+            const bf16x8 kb8 = as_bf16x8(*(const u32x4*)(&Kl[(kt * 16 + l16) * KP + ks * 32 + g4 * 8]));
+            sc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb8, sc[kt], 0, 0, 0);
+            sc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[ks], kb8, sc[kt], 0, 0, 0);
+          }
         }
-        mloc[r] = row16_max(m);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float mnew = fmaxf(mrun[r], mloc[r]);
-        alpha[r] = (mnew == -INFINITY) ? 1.f : exp2f(mrun[r] - mnew);
-        float ls = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const float pv = (mnew == -INFINITY) ? 0.f : exp2f(sc[kt][r] - mnew);
-          sc[kt][r] = pv;
-          ls += pv;
-        }
-        lrun[r] = lrun[r] * alpha[r] + row16_sum(ls);
-        mrun[r] = mnew;
-      }
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+        // Scale, causal mask, running softmax.  Lane holds rows 4*g4+r, keys kt*16 + l16.
+        float mloc[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const uint16_t hi = f2bf(sc[kt][r]);
-          Pl[wave][0][(4 * g4 + r) * PP + kt * 16 + l16] = hi;
-          Pl[wave][1][(4 * g4 + r) * PP + kt * 16 + l16] = f2bf(sc[kt][r] - bf2f(hi));
+          float m = -INFINITY;
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt) {
+            const int kp = c0 + kt * 16 + l16;
+            float v = sc[kt][r] * a.scale_log2;
+            v = (kp <= prow[r]) ? v : -INFINITY;
+            sc[kt][r] = v;
+            m = fmaxf(m, v);
+          }
+          mloc[r] = row16_max(m);
         }
-    }
-    __syncthreads();
-    if (active) {
 #pragma unroll
-      for (int nt = 0; nt < DH / 16; ++nt) {
+        for (int r = 0; r < 4; ++r) {
+          const float mnew = fmaxf(mrun[r], mloc[r]);
+          alpha[r] = (mnew == -INFINITY) ? 1.f : exp2f(mrun[r] - mnew);
+          float ls = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[nt][r] *= alpha[r];
+          for (int kt = 0; kt < 4; ++kt) {
+            const float pv = (mnew == -INFINITY) ? 0.f : exp2f(sc[kt][r] - mnew);
+            sc[kt][r] = pv;
+            ls += pv;
+          }
+          lrun[r] = lrun[r] * alpha[r] + row16_sum(ls);
+          mrun[r] = mnew;
+        }
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const u32x4 pa = *(const u32x4*)(&Pl[wave][0][l16 * PP + ks * 32 + g4 * 8]);
-          const u32x4 pl = *(const u32x4*)(&Pl[wave][1][l16 * PP + ks * 32 + g4 * 8]);
-          const bf16x8 vb = as_bf16x8(*(const u32x4*)(&Vt[(nt * 16 + l16) * VP + ks * 32 + g4 * 8]));
-          o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pa), vb, o[nt], 0, 0, 0);
-          o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pl), vb, o[nt], 0, 0, 0);
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint16_t hi = f2bf(sc[kt][r]);
+            Pl[wave][0][(4 * g4 + r) * PP + kt * 16 + l16] = hi;
+            Pl[wave][1][(4 * g4 + r) * PP + kt * 16 + l16] = f2bf(sc[kt][r] - bf2f(hi));
+          }
+      }
+      __syncthreads();
+      if (active) {
+#pragma unroll
+        for (int nt = 0; nt < DH / 16; ++nt) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[nt][r] *= alpha[r];
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const u32x4 pa = *(const u32x4*)(&Pl[wave][0][l16 * PP + ks * 32 + g4 * 8]);
+            const u32x4 pl = *(const u32x4*)(&Pl[wave][1][l16 * PP + ks * 32 + g4 * 8]);
+            const bf16x8 vb = as_bf16x8(*(const u32x4*)(&Vt[(nt * 16 + l16) * VP + ks * 32 + g4 * 8]));
+            o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pa), vb, o[nt], 0, 0, 0);
+            o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pl), vb, o[nt], 0, 0, 0);
+          }
         }
       }
     }
-  }
-  if (!active) return;
-  const size_t rstride = DH + 2;
-  float* pbase = a.part + (((size_t)b * a.nkv + kvh) * a.nchunk + x) * (size_t)nrows * rstride;
+    if (active) {
+      const size_t rstride = DH + 2;
+      float* pbase = a.part + (((size_t)b * a.nkv + kvh) * a.nchunk + x) * (size_t)nrows * rstride;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int qr = wrow0 + 4 * g4 + r;
-    if (qr >= nrows) continue;
-    float* pr = pbase + (size_t)qr * rstride;
+      for (int r = 0; r < 4; ++r) {
+        const int qr = wrow0 + 4 * g4 + r;
+        if (qr >= nrows) continue;
+        float* pr = pbase + (size_t)qr * rstride;
 #pragma unroll
-    for (int nt = 0; nt < DH / 16; ++nt) st<kCoh>(pr + nt * 16 + l16, o[nt][r]);
-    if (l16 == 0) { st<kCoh>(pr + DH, mrun[r]); st<kCoh>(pr + DH + 1, lrun[r]); }
+        for (int nt = 0; nt < DH / 16; ++nt) st<kCoh>(pr + nt * 16 + l16, o[nt][r]);
+        if (l16 == 0) { st<kCoh>(pr + DH, mrun[r]); st<kCoh>(pr + DH + 1, lrun[r]); }
+      }
+    }
+    x += xstep;
+    span0 = x * kSpan;
+    if (span0 > plast) break;
   }
 }
 

@@ -14,6 +14,8 @@
 // longest-prefix accept, commit).  The pass is captured once into a hipGraph.
 #include "device.h"
 
+#include <algorithm>
+
 namespace sf {
 
 // Epilogues of one 32-row n block for real rows r0 .. r0+kRealRows-1: val(nl, m) is output
@@ -627,7 +629,7 @@ __global__ __launch_bounds__(256) void k_attn(const AttnArgs a, int B) {
     if (lin < g0 + kPrefetchGroups) prefetch_chunks(a, B, lin, g0);
     return;
   }
-  attn_span<DH, false>(a, blockIdx.x, blockIdx.y, blockIdx.z / ngroups, blockIdx.z % ngroups);
+  attn_spans<DH, false>(a, blockIdx.x, gridDim.x, blockIdx.y, blockIdx.z / ngroups, blockIdx.z % ngroups);
 }
 
 template <int DH>
@@ -640,15 +642,20 @@ __global__ __launch_bounds__(256) void k_combine(const AttnArgs a) {
 hipError_t launch_attention(const AttnArgs& a, int dh, int B, hipStream_t s) {
   const int G = a.nq / a.nkv;
   const int ngroups = (a.T * G + 63) / 64;
-  const dim3 grid(a.nchunk, a.nkv, B * ngroups + (a.pf_w ? 1 : 0));
-  if (a.pf_w && a.nchunk * a.nkv < kPrefetchGroups) return hipErrorInvalidValue;   // slice too small
+  // Workgroups along the spans: all of them when the grid stays within about eight
+  // workgroups per CU, else fewer, each taking every nx-th span (its next span's K/V loads
+  // overlap the current span's compute).  A span's partial does not depend on the choice.
+  const int nx = std::min(a.nchunk, std::max(1, kAttnWorkgroups / (a.nkv * B * ngroups)));
+  AttnArgs aw = a;
+  if (aw.pf_w && nx * a.nkv < kPrefetchGroups) aw.pf_w = nullptr;   // warm-up slice too small
+  const dim3 grid(nx, a.nkv, B * ngroups + (aw.pf_w ? 1 : 0));
   const int ncomb = (a.rows * a.nq + 3) / 4;
   if (dh == 128) {
-    k_attn<128><<<grid, 256, 0, s>>>(a, B);
-    k_combine<128><<<ncomb, 256, 0, s>>>(a);
+    k_attn<128><<<grid, 256, 0, s>>>(aw, B);
+    k_combine<128><<<ncomb, 256, 0, s>>>(aw);
   } else if (dh == 64) {
-    k_attn<64><<<grid, 256, 0, s>>>(a, B);
-    k_combine<64><<<ncomb, 256, 0, s>>>(a);
+    k_attn<64><<<grid, 256, 0, s>>>(aw, B);
+    k_combine<64><<<ncomb, 256, 0, s>>>(aw);
   } else {
     return hipErrorInvalidValue;
   }

@@ -115,8 +115,10 @@ struct AttnArgs {
   int pf_nb, pf_kb, pf_sp;
   int dh;
 };
-// Workgroups of the attention grid's warm-up slice (needs spans * kv heads >= this).
+// Workgroups of the attention grid's warm-up slice (needs span workgroups * kv heads >= this).
 constexpr int kPrefetchGroups = 64;
+// Target number of attention workgroups (a few per CU): beyond it, a workgroup takes several spans.
+constexpr int kAttnWorkgroups = 2048;
 
 struct AcceptArgs {
   const float2* amax;      // [rows][nparts]
