@@ -46,6 +46,7 @@ typedef int32_t sf_status;
 
 typedef struct sf_model sf_model;   /* opaque, library-owned */
 typedef struct sf_cache sf_cache;   /* opaque, library-owned */
+typedef struct sf_round sf_round;   /* opaque, library-owned */
 
 /* Decoder shape (Qwen2.5 decoder layer: pre-norm RMSNorm, rotate-half RoPE,
  * grouped-query attention, SwiGLU FFN, optional q/k/v biases). */
@@ -171,6 +172,35 @@ sf_status sf_cache_state(sf_cache* cache, int32_t seq, int32_t* length, int32_t*
  * Errors: SF_E_STATE (hidden-state stack), SF_E_ARG (n_steps < 1 or > 4096),
  * SF_E_CAPACITY (length + n_steps > capacity). */
 sf_status sf_draft_step(sf_cache* cache, int32_t n_steps, int32_t* tokens);
+
+/* sf_round_create: a device-resident speculative round over a drafter cache `drafter` and a
+ * verifier cache `verifier` holding the same sequences ([ShardFlow] "Speculative Decoding: The
+ * Idea": a small model guesses k tokens, the large one checks them in one pass and the agreed
+ * prefix is committed; "CUDA Graphs: What They Are and Why They Helped": the whole round is one
+ * captured graph, with no host round trip between its steps).  One round, for every sequence:
+ *   1. k greedy drafter steps (as sf_draft_step) from the shared pending token;
+ *   2. one verifier pass over [pending, d_1..d_k] (as sf_verify), accepting M drafts and
+ *      committing length += M+1, pending = target[M];
+ *   3. the drafter rewound in place to the committed stream ([ShardFlow] "Why It Kept
+ *      Breaking", fix 4): length L+M+1 and pending target[M]; when all k drafts were accepted
+ *      it first feeds its last draft d_k (one non-committing step counted afterwards).
+ * Both models must share one stream (the stream given to sf_model_create), both stacks need
+ * an LM head and the same vocabulary, the caches the same n_seqs, and 1 <= k <= the
+ * verifier's k_max.  The round object holds the graph and 2*n_seqs ints of device scratch;
+ * it does not own the caches, which must outlive it.
+ * Errors: SF_E_ARG, SF_E_STATE (a stack without a head), SF_E_NOMEM, SF_E_HIP. */
+sf_status sf_round_create(sf_cache* drafter, sf_cache* verifier, int32_t k, sf_round** out);
+
+/* sf_round_run: enqueue n_rounds rounds (graph replays) without waiting.  Before the first,
+ * every sequence's drafter and verifier must be at the same point (equal length and pending
+ * token, e.g. after the same sf_prefill on both).  Afterwards the verifier's last results are
+ * at sf_results_device(verifier) and sf_cache_state reads either cache's position.
+ * Errors: SF_E_ARG, SF_E_STATE (caches not at the same point), SF_E_CAPACITY (n_rounds*(k+1)
+ * more positions, plus one verify, might not fit a cache). */
+sf_status sf_round_run(sf_round* round, int32_t n_rounds);
+
+/* sf_round_free: waits for the stream, then releases the round (not the caches). */
+sf_status sf_round_free(sf_round* round);
 
 /* sf_ngram_propose: prompt-lookup drafter ([Sangama] "Speculative decoding:
  * correct, but slower (for now)": if the last 2-4 tokens appeared earlier, guess

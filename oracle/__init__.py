@@ -44,6 +44,7 @@ from .spec import (
     rollback,
     set_next,
     speculative_decode,
+    model_draft_round,
 )
 from .ngram import propose
 
@@ -51,5 +52,5 @@ __all__ = [
     "Model", "KVCache", "round_bf16", "rms_norm", "rope_angles", "rope", "silu", "swiglu",
     "causal_gqa_attention", "forward", "argmax_lowest", "top_gap", "accept_prefix", "verify",
     "prefill", "greedy_decode", "greedy_continuation", "rollback", "set_next",
-    "speculative_decode", "propose",
+    "speculative_decode", "model_draft_round", "propose",
 ]

@@ -139,3 +139,37 @@ def speculative_decode(model, cache, n_tokens, draft_fn, K):
         r = verify(model, cache, d, k)
         emitted.extend([first] + [int(t) for t in d[:r["accepted"]]])
     return emitted[:n_tokens]
+
+
+def model_draft_round(drafter, dcache, verifier, vcache, K):
+    """One speculative round with a model drafter (ShardFlow, "Speculative Decoding: The Idea":
+    a small model guesses K tokens, the large one checks them in one pass and the agreed prefix
+    is committed).  Both caches start at the same length L and pending token.
+
+    The drafter takes K greedy single-token steps (d_1..d_K), the verifier verifies them and
+    commits M+1 tokens, and the drafter's cache is rewound in place to the committed stream
+    (ShardFlow, "Why It Kept Breaking", fix 4).  Reading taken where the pages leave it open:
+    after M < K accepted drafts, the drafter's cache already holds positions L..L+M of the
+    committed stream, so its length becomes L+M+1; after all K, it has not yet consumed d_K,
+    so it takes one more step (feeding d_K at L+K) first.  Either way its pending token becomes
+    the verifier's.  Returns verify()'s result dict for the verifier plus "draft" and
+    "draft_gap" (the drafter's top-1/top-2 gap at each of its K choices).
+    """
+    if dcache.length != vcache.length or dcache.next_token != vcache.next_token:
+        raise ValueError("drafter and verifier caches are not at the same point")
+    L = dcache.length
+    d, gaps = [], []
+    for _ in range(K):
+        rd = verify(drafter, dcache, [], 0)
+        d.append(dcache.next_token)
+        gaps.append(float(rd["gap"][0]))
+    r = verify(verifier, vcache, d, K)
+    M = r["accepted"]
+    if M < K:
+        rollback(dcache, L + M + 1)
+    else:
+        verify(drafter, dcache, [], 0)
+    set_next(dcache, vcache.next_token)
+    r["draft"] = d
+    r["draft_gap"] = gaps
+    return r

@@ -80,6 +80,9 @@ def lib():
             "sf_set_next": [_P, _I, _I],
             "sf_cache_state": [_P, _I, _PI, _PI],
             "sf_draft_step": [_P, _I, _PI],
+            "sf_round_create": [_P, _P, _I, ctypes.POINTER(_P)],
+            "sf_round_run": [_P, _I],
+            "sf_round_free": [_P],
             "sf_ngram_propose": [_PI, _I, _I, _I, _I, _PI],
             "sf_kv_write": [_P, _I, _P, _P, _I, _I],
             "sf_kv_read": [_P, _I, _P, _P, _I, _I],
@@ -222,6 +225,20 @@ def sf_draft_step(cache, n_steps, n_seqs=1):
     return out
 
 
+def sf_round_create(drafter_cache, verifier_cache, k):
+    out = _P()
+    _check(lib().sf_round_create(drafter_cache, verifier_cache, k, ctypes.byref(out)))
+    return out
+
+
+def sf_round_run(round_, n_rounds=1):
+    _check(lib().sf_round_run(round_, n_rounds))
+
+
+def sf_round_free(round_):
+    _check(lib().sf_round_free(round_))
+
+
 def sf_ngram_propose(hist, min_n=2, max_n=4, k_max=8):
     h, hp = _i32(hist)
     out = np.zeros(max(k_max, 1), dtype=np.int32)
@@ -263,11 +280,12 @@ def upload_weights(weights, desc, device="cuda"):
 
 
 class Engine:
-    """A model plus one cache on a dedicated torch stream."""
+    """A model plus one cache on a torch stream (a new one unless `stream` is given: engines
+    that take part in one speculative round share a stream)."""
 
-    def __init__(self, shape, weights, n_seqs=1, capacity=128, k_max=4, keep_weights=False):
+    def __init__(self, shape, weights, n_seqs=1, capacity=128, k_max=4, keep_weights=False, stream=None):
         import torch
-        self.stream = torch.cuda.Stream()
+        self.stream = stream if stream is not None else torch.cuda.Stream()
         self.desc = desc_from_shape(shape)
         self.n_seqs, self.capacity, self.k_max = n_seqs, capacity, k_max
         tensors, ptrs = upload_weights(weights, self.desc)

@@ -799,6 +799,66 @@ __global__ void k_stage_device(Stage* st, const int32_t* draft, const int32_t* k
   for (int i = t; i < B * kmax; i += blockDim.x) st->draft[i] = draft[i];
 }
 
+// ----------------------------------------------------------------------------------------------
+// Round bookkeeping ([ShardFlow] "Speculative Decoding: The Idea": the drafter guesses k tokens,
+// the verifier checks them in one pass and the agreed prefix is committed; the drafter is then
+// rewound in place to the committed stream, "Why It Kept Breaking", fix 4).  Thread b owns
+// sequence b.
+//   begin:     remember the verifier's length; the drafter commits each step; the verifier
+//              takes k drafts.
+//   stage:     the drafter's k step outputs become the verifier's drafts.
+//   reconcile: with M accepted and L the old length: M < k: the drafter's K/V of positions
+//              L .. L+M is right, so its length becomes L+M+1 and its pending token the
+//              verifier's target[M].  M = k: its last draft d_k was never fed to it, so the
+//              next (non-committing) step feeds d_k at L+k and finish counts it.
+//   finish:    the drafter's length takes the catch-up step; its pending token is the
+//              verifier's.
+__global__ void k_round(const RoundArgs a, int phase) {
+  const int b = threadIdx.x;
+  if (phase == kRoundBegin) {
+    if (b == 0) {
+      a.dstage->flags = 0;
+      a.dstage->kmax = 0;
+      a.vstage->flags = 0;
+      a.vstage->kmax = a.vkmax;
+    }
+    if (b < a.B) {
+      a.scratch[b] = a.vlen[b];
+      a.dstage->k[b] = 0;
+      a.dstage->step[b] = 0;
+      a.vstage->k[b] = a.k;
+    }
+  } else if (phase == kRoundStage) {
+    if (b < a.B)
+      for (int j = 0; j < a.vkmax; ++j) a.vstage->draft[b * a.vkmax + j] = (j < a.k) ? a.dout[b * kMaxDraftSteps + j] : 0;
+  } else if (phase == kRoundReconcile) {
+    if (b == 0) a.dstage->flags = kFlagNoCommit;
+    if (b < a.B) {
+      const int M = a.vres[b], L = a.scratch[b];
+      if (M < a.k) {
+        a.dlen[b] = L + M + 1;
+        a.dnext[b] = a.vres[a.B + b * a.vT + M];
+        a.scratch[a.B + b] = 0;
+      } else {
+        a.scratch[a.B + b] = 1;
+      }
+    }
+  } else {
+    if (b == 0) a.dstage->flags = 0;
+    if (b < a.B) {
+      a.dlen[b] += a.scratch[a.B + b];
+      a.dnext[b] = a.vnext[b];
+    }
+  }
+}
+
+hipError_t launch_round(const RoundArgs& r, int phase, hipStream_t s) {
+  if (r.B < 1 || r.B > kMaxSeqs || r.k < 1 || r.k > r.vkmax || r.vkmax >= kMaxK || r.k >= kMaxDraftSteps)
+    return hipErrorInvalidValue;
+  k_round<<<1, kMaxSeqs, 0, s>>>(r, phase);
+  return hipGetLastError();
+}
+
 hipError_t launch_stage_device(Stage* stage, const int32_t* draft, const int32_t* k, int B, int kmax,
                                int flags, hipStream_t s) {
   k_stage_device<<<1, 256, 0, s>>>(stage, draft, k, B, kmax, flags);

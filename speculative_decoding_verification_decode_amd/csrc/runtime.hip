@@ -740,6 +740,105 @@ extern "C" sf_status sf_draft_step(sf_cache* c, int32_t n_steps, int32_t* tokens
   return SF_OK;
 }
 
+// ------------------------------------------------------------------------------------------
+// Device-resident speculative round: drafter steps, verify, accept and the drafter's rewind,
+// captured once into one graph over two caches that share a stream.
+struct sf_round {
+  sf_cache* d = nullptr;
+  sf_cache* v = nullptr;
+  int k = 0;
+  int32_t* scratch = nullptr;
+  hipGraphExec_t gx = nullptr;
+};
+
+static void round_release(sf_round* r) {
+  if (r->gx) (void)hipGraphExecDestroy(r->gx);
+  if (r->scratch) (void)hipFree(r->scratch);
+  delete r;
+}
+
+extern "C" sf_status sf_round_create(sf_cache* d, sf_cache* v, int32_t k, sf_round** out) {
+  if (!d || !v || !out) return fail(SF_E_ARG, "NULL argument");
+  *out = nullptr;
+  if (d == v) return fail(SF_E_ARG, "drafter and verifier must be different caches");
+  if (!d->m->d.has_head || !v->m->d.has_head || !d->gx_draft)
+    return fail(SF_E_STATE, "both stacks need an LM head");
+  if (d->B != v->B) return fail(SF_E_ARG, "drafter and verifier must hold the same number of sequences");
+  if (d->m->stream != v->m->stream) return fail(SF_E_ARG, "drafter and verifier models must share one stream");
+  if (d->m->V != v->m->V) return fail(SF_E_ARG, "drafter and verifier must share the vocabulary");
+  if (k < 1 || k > v->kmax) return fail(SF_E_ARG, "k must be in 1..verifier k_max");
+  sf_round* r = new sf_round();
+  r->d = d;
+  r->v = v;
+  r->k = k;
+  hipError_t e = hipMalloc((void**)&r->scratch, (size_t)2 * d->B * 4);
+  if (e != hipSuccess) {
+    round_release(r);
+    return fail(SF_E_NOMEM, std::string("hipMalloc: ") + hipGetErrorString(e));
+  }
+  RoundArgs a{};
+  a.dstage = d->stage_d; a.vstage = v->stage_d; a.dlen = d->len; a.dnext = d->next; a.vlen = v->len;
+  a.vnext = v->next; a.dout = d->dout_d; a.vres = v->res_d; a.scratch = r->scratch;
+  a.B = d->B; a.k = k; a.vkmax = v->kmax; a.vT = v->T;
+  const Run draft{d->B, 1, 0, 0, nullptr, true, false};
+  const Run verify{v->B, v->T, 0, v->kmax, nullptr, false, false};
+  hipStream_t s = d->m->stream;
+  hipGraph_t graph = nullptr;
+  e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+  if (e == hipSuccess) {
+    hipError_t c = launch_round(a, kRoundBegin, s);
+    for (int i = 0; i < k && c == hipSuccess; ++i) c = enqueue_forward(d, draft);
+    if (c == hipSuccess) c = launch_round(a, kRoundStage, s);
+    if (c == hipSuccess) c = enqueue_forward(v, verify);
+    if (c == hipSuccess) c = launch_round(a, kRoundReconcile, s);
+    if (c == hipSuccess) c = enqueue_forward(d, draft);   // catch-up step, commit off
+    if (c == hipSuccess) c = launch_round(a, kRoundFinish, s);
+    const hipError_t ce = hipStreamEndCapture(s, &graph);
+    e = (c != hipSuccess) ? c : ce;
+  }
+  if (e == hipSuccess) e = hipGraphInstantiate(&r->gx, graph, nullptr, nullptr, 0);
+  if (graph) (void)hipGraphDestroy(graph);
+  if (e != hipSuccess) {
+    round_release(r);
+    return fail(SF_E_HIP, std::string("round capture: ") + hipGetErrorString(e));
+  }
+  *out = r;
+  return SF_OK;
+}
+
+extern "C" sf_status sf_round_run(sf_round* r, int32_t n_rounds) {
+  if (!r) return fail(SF_E_ARG, "round is NULL");
+  if (n_rounds < 1 || n_rounds > 1 << 20) return fail(SF_E_ARG, "n_rounds out of range");
+  sf_cache* d = r->d;
+  sf_cache* v = r->v;
+  if (d->dirty)
+    if (sf_status st = refresh(d)) return st;
+  if (v->dirty)
+    if (sf_status st = refresh(v)) return st;
+  const long grow = (long)n_rounds * (r->k + 1);
+  for (int b = 0; b < d->B; ++b) {
+    if (d->len_h[b] != v->len_h[b] || d->next_h[b] != v->next_h[b])
+      return fail(SF_E_STATE, "sequence " + std::to_string(b) + ": drafter and verifier are not at the same point");
+    if (v->len_h[b] + grow + v->T > v->cap || d->len_h[b] + grow + v->T > d->cap)
+      return fail(SF_E_CAPACITY, "sequence " + std::to_string(b) + ": the rounds may exceed a capacity");
+  }
+  hipStream_t s = d->m->stream;
+  for (int i = 0; i < n_rounds; ++i) HIPCHK(hipGraphLaunch(r->gx, s));
+  for (int b = 0; b < d->B; ++b) {
+    d->len_hi[b] += (int)grow;
+    v->len_hi[b] += (int)grow;
+  }
+  d->dirty = v->dirty = true;
+  return SF_OK;
+}
+
+extern "C" sf_status sf_round_free(sf_round* r) {
+  if (!r) return fail(SF_E_ARG, "round is NULL");
+  (void)hipStreamSynchronize(r->d->m->stream);
+  round_release(r);
+  return SF_OK;
+}
+
 extern "C" int32_t sf_ngram_propose(const int32_t* hist, int32_t n_hist, int32_t min_n, int32_t max_n,
                                     int32_t k_max, int32_t* out) {
   if ((!hist && n_hist > 0) || n_hist < 0 || min_n < 1 || max_n < min_n || k_max < 0 || (!out && k_max > 0))

@@ -142,6 +142,21 @@ hipError_t launch_gather_f32(float* dst, const uint16_t* const* eltptr, int n, h
 hipError_t launch_rope_table(float2* rope, int cap, int half, double base, hipStream_t s);
 hipError_t launch_set_state(int32_t* len, int32_t* next, int seq, int new_len, int new_next, int which,
                             hipStream_t s);
+// Device-resident speculative round (drafter cache d, verifier cache v, both of B sequences
+// in step): the bookkeeping kernels that run between the captured passes.
+enum RoundPhase { kRoundBegin = 0, kRoundStage = 1, kRoundReconcile = 2, kRoundFinish = 3 };
+struct RoundArgs {
+  Stage* dstage;           // drafter staging block (draft-step flags, step counters)
+  Stage* vstage;           // verifier staging block (k and the drafts)
+  int32_t *dlen, *dnext;   // drafter length / pending token
+  const int32_t* vlen;     // verifier length / pending token
+  const int32_t* vnext;
+  const int32_t* dout;     // drafter's step outputs [B][kMaxDraftSteps]
+  const int32_t* vres;     // verifier results: accepted[B], target[B][vT]
+  int32_t* scratch;        // [B] verifier length before the verify, [B] catch-up flag
+  int B, k, vkmax, vT;
+};
+hipError_t launch_round(const RoundArgs& r, int phase, hipStream_t s);
 hipError_t launch_stage_device(Stage* stage, const int32_t* draft, const int32_t* k, int B, int kmax,
                                int flags, hipStream_t s);
 hipError_t launch_copy_kv(uint16_t* pool, uint16_t* src, long pool_layer_stride, int nkv, int cap,

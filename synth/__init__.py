@@ -22,10 +22,12 @@ from .gen import (
     batch_contexts,
     rejected_suffix,
     seeds,
+    with_head_gain,
+    near_copy,
 )
 
 __all__ = [
     "Shape", "TINY", "QWEN05B", "QWEN7B", "QWEN7B_HALF", "SHAPES", "tensor_names", "tensor_shape",
     "bf16_normal", "model_weights", "prompt_ids", "corrupt_draft", "synthetic_kv", "lookup_history",
-    "batch_contexts", "rejected_suffix", "seeds",
+    "batch_contexts", "rejected_suffix", "seeds", "with_head_gain", "near_copy",
 ]

@@ -86,6 +86,28 @@ def model_weights(shape, seed, names=None, threads=None):
     return out
 
 
+def with_head_gain(weights, gain):
+    """A copy of `weights` whose final RMSNorm gain is bf16(gain) everywhere: every logit is
+    scaled by the gain, which widens the spread between the top choices (random-init stacks
+    otherwise have logits far flatter than a trained model's)."""
+    out = dict(weights)
+    out["final_norm"] = np.full_like(weights["final_norm"], _f32_to_bf16_bits(np.array([gain], np.float32))[0])
+    return out
+
+
+def near_copy(weights, other, eps):
+    """A stack close to `weights`: every projection becomes bf16(w + eps * o), o the same
+    tensor of `other`; embeddings, norms and the head are shared.  Used as a drafter that
+    agrees with the target often but not always."""
+    def f32(u):
+        return (u.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    out = dict(weights)
+    for name, w in weights.items():
+        if name.split(".")[-1] in ("wq", "wk", "wv", "wo", "wg", "wu", "wd"):
+            out[name] = _f32_to_bf16_bits(f32(w) + np.float32(eps) * f32(other[name]))
+    return out
+
+
 def prompt_ids(vocab, n, seed):
     """n token ids uniform in [0, vocab)."""
     rng = np.random.Generator(np.random.PCG64(seed))

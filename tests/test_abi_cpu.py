@@ -98,6 +98,9 @@ def test_null_handles_are_rejected():
     assert L.sf_cache_free(null) == sfb.SF_E_ARG
     assert L.sf_model_free(null) == sfb.SF_E_ARG
     assert L.sf_sync(null) == sfb.SF_E_ARG
+    assert L.sf_round_create(null, null, 1, ctypes.byref(ctypes.c_void_p())) == sfb.SF_E_ARG
+    assert L.sf_round_run(null, 1) == sfb.SF_E_ARG
+    assert L.sf_round_free(null) == sfb.SF_E_ARG
     assert "NULL" in sfb.sf_last_error()
 
 

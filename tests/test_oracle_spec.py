@@ -236,3 +236,79 @@ def test_bf16_cache_holds_rounded_layer0_kv(tiny):
         assert torch.equal(got.view(torch.int16), want.view(torch.int16))
     # and a later layer differs from plain rounding (the rounded cache feeds attention)
     assert not torch.equal(c16.k[1, :, :12].double(), oracle.round_bf16(c64.k[1, :, :12]))
+
+
+# ---------------------------------------------------------------- model-drafter rounds
+
+def _round_pair(drafter, verifier, seed=21, n=20):
+    prompt = synth.prompt_ids(verifier.shape.vocab, n, seed)
+    dc, vc = oracle.KVCache(drafter.shape, 160), oracle.KVCache(verifier.shape, 160)
+    oracle.prefill(drafter, dc, prompt)
+    oracle.prefill(verifier, vc, prompt)
+    oracle.set_next(dc, vc.next_token)   # the verifier's choice after the prompt is the stream's
+    return dc, vc
+
+
+def _emit(drafter, verifier, K, rounds, seed=21):
+    """Stream committed by `rounds` model-drafter rounds, and the per-round accepted counts."""
+    dc, vc = _round_pair(drafter, verifier, seed)
+    out, accepted = [], []
+    for _ in range(rounds):
+        first = vc.next_token
+        r = oracle.model_draft_round(drafter, dc, verifier, vc, K)
+        out += [first] + [int(t) for t in r["draft"][:r["accepted"]]]
+        accepted.append(r["accepted"])
+        assert dc.length == vc.length and dc.next_token == vc.next_token
+    return out, accepted, dc, vc
+
+
+def test_model_draft_round_with_itself_accepts_everything_and_equals_greedy(tiny):
+    K = 4
+    out, accepted, _, _ = _emit(tiny, tiny, K, 5)
+    assert accepted == [K] * 5
+    _, vc = _round_pair(tiny, tiny)
+    assert out == oracle.greedy_decode(tiny, vc, len(out))
+
+
+def test_model_draft_round_with_another_drafter_equals_greedy():
+    drafter = oracle.Model(synth.TINY, synth.model_weights(synth.TINY, synth.seeds(2)["weights"]), cache=True)
+    verifier = oracle.Model(synth.TINY, synth.model_weights(synth.TINY, synth.seeds(1)["weights"]), cache=True)
+    out, accepted, dc, _ = _emit(drafter, verifier, 4, 6)
+    _, vc = _round_pair(drafter, verifier)
+    assert out == oracle.greedy_decode(verifier, vc, len(out))
+    # The rewound drafter cache holds exactly the committed stream: its next greedy token
+    # equals that of a fresh drafter cache that consumed the same stream.
+    fresh = oracle.KVCache(synth.TINY, 160)
+    prompt = synth.prompt_ids(synth.TINY.vocab, 20, 21)
+    oracle.prefill(drafter, fresh, [int(t) for t in prompt] + out)
+    oracle.set_next(fresh, dc.next_token)
+    assert fresh.length == dc.length
+    ra = oracle.verify(drafter, dc.copy(), [], 0, commit=False)
+    rb = oracle.verify(drafter, fresh, [], 0, commit=False)
+    assert (ra["logits"] - rb["logits"]).abs().max().item() < 1e-6
+
+
+def test_model_draft_round_with_a_near_copy_drafter_takes_both_branches_and_equals_greedy():
+    """A drafter close to the verifier (each projection w + 0.05 o, head gain 32): rounds
+    that reject part of the draft and rounds that accept all of it both occur, and the
+    committed stream is still the verifier's greedy one."""
+    wv = synth.with_head_gain(synth.model_weights(synth.TINY, synth.seeds(1)["weights"]), 32.0)
+    wd = synth.near_copy(wv, synth.model_weights(synth.TINY, synth.seeds(2)["weights"]), 0.05)
+    verifier = oracle.Model(synth.TINY, wv, cache=True)
+    drafter = oracle.Model(synth.TINY, wd, cache=True)
+    out, accepted, _, _ = _emit(drafter, verifier, 4, 8)
+    assert 4 in accepted and min(accepted) < 4
+    _, vc = _round_pair(drafter, verifier)
+    assert out == oracle.greedy_decode(verifier, vc, len(out))
+
+
+def test_head_gain_scales_every_logit():
+    """The final RMSNorm gain multiplies the head's input, so a gain of 32 (a power of two:
+    exact through bf16 rounding) scales every logit by exactly 32."""
+    w1 = synth.model_weights(synth.TINY, synth.seeds(1)["weights"])
+    prompt = synth.prompt_ids(synth.TINY.vocab, 12, 5)
+    z = []
+    for w in (w1, synth.with_head_gain(w1, 32.0)):
+        c = oracle.KVCache(synth.TINY, 16)
+        z.append(oracle.prefill(oracle.Model(synth.TINY, w, cache=True), c, prompt))
+    assert (z[1] - 32.0 * z[0]).abs().max().item() <= 1e-9 * z[1].abs().max().item()
