@@ -57,6 +57,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-batched", action="store_true", help="skip the 32-sequence batched verify line")
+    ap.add_argument("--no-round", action="store_true", help="skip the device-resident draft+verify round line")
     ap.add_argument("--kernel-iters", type=int, default=56)
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="also run plain device copies of 1 GiB, so HBM byte counters can be scaled")
@@ -228,6 +229,57 @@ def main():
         sfb.sf_cache_free(cb)
         log(f"batched: {batched}")
 
+    # Device-resident speculative round: a Qwen2.5-0.5B-shape drafter (tied head) and this
+    # 7B-shape verifier on one stream, both prefilled with the same 512-token prompt; each
+    # round is one graph replay (8 drafter steps, the 9-position verify, accept, the drafter's
+    # rewind and catch-up step).  Random-init stacks rarely agree, so the measured acceptance
+    # is near zero: ms per round is the cost of a round, committed tokens/s what these
+    # weights yield.
+    spec_round = None
+    if not args.no_round:
+        SD = synth.QWEN05B
+        sr = synth.seeds(6)
+        wd = synth.model_weights(SD, sr["weights"])
+        dtensors, dptrs = sfb.upload_weights(wd, sfb.desc_from_shape(SD))
+        torch.cuda.synchronize()
+        dmodel = sfb.sf_model_create(sfb.desc_from_shape(SD), dptrs, stream.cuda_stream)
+        del dtensors, dptrs, wd
+        torch.cuda.synchronize()
+        n_rounds = max(4, args.steps)
+        rcap = 512 + (n_rounds + 2) * (K + 1) + K + 1
+        vcache = sfb.sf_cache_alloc(model, 1, rcap, K)
+        dcache = sfb.sf_cache_alloc(dmodel, 1, rcap, 0)
+        prompt = synth.prompt_ids(SD.vocab, 512, sr["prompt"])
+        nxt = sfb.sf_prefill(vcache, 0, prompt)
+        sfb.sf_prefill(dcache, 0, prompt)
+        sfb.sf_set_next(dcache, 0, nxt)
+        rnd = sfb.sf_round_create(dcache, vcache, K)
+        sfb.sf_round_run(rnd, 1)                      # warm-up round
+        L0, _ = sfb.sf_cache_state(vcache, 0)
+        sfb.sf_sync(dcache)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        sfb.sf_round_run(rnd, n_rounds)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rwall = time.perf_counter() - t0
+        rms = e0.elapsed_time(e1) / n_rounds
+        L1, _ = sfb.sf_cache_state(vcache, 0)
+        committed = L1 - L0
+        spec_round = {"drafter": "qwen2.5-0.5b-shape, random-init bf16", "verifier": "this model", "K": K,
+                      "prompt": 512, "rounds": n_rounds, "contexts": f"{L0}..{L1}",
+                      "ms_per_round": round(rms, 4), "committed_tokens": committed,
+                      "mean_accepted": round(committed / n_rounds - 1, 3),
+                      "committed_tokens_per_s": round(committed / (rms * n_rounds) * 1e3, 1),
+                      "wall_ms_per_round": round(rwall * 1e3 / n_rounds, 4)}
+        sfb.sf_round_free(rnd)
+        sfb.sf_cache_free(dcache)
+        sfb.sf_cache_free(vcache)
+        sfb.sf_model_free(dmodel)
+        log(f"round: {spec_round}")
+
     cpu = None
     if not args.no_cpu:
         import oracle
@@ -273,6 +325,7 @@ def main():
         "host_inclusive_verify_ms_ctx512": round(host_ms, 4),
         "kernels_at_verify_shape": kern,
         "batched_32": batched,
+        "device_round_0.5b_drafter": spec_round,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

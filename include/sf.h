@@ -185,7 +185,9 @@ sf_status sf_draft_step(sf_cache* cache, int32_t n_steps, int32_t* tokens);
  *      Breaking", fix 4): length L+M+1 and pending target[M]; when all k drafts were accepted
  *      it first feeds its last draft d_k (one non-committing step counted afterwards).
  * Both models must share one stream (the stream given to sf_model_create), both stacks need
- * an LM head and the same vocabulary, the caches the same n_seqs, and 1 <= k <= the
+ * an LM head, the drafter's vocabulary may not exceed the verifier's (shared token ids; a
+ * verifier token beyond the drafter's table, a padding row that a trained head never picks,
+ * embeds as the drafter's last row), the caches hold the same n_seqs, and 1 <= k <= the
  * verifier's k_max.  The round object holds the graph and 2*n_seqs ints of device scratch;
  * it does not own the caches, which must outlive it.
  * Errors: SF_E_ARG, SF_E_STATE (a stack without a head), SF_E_NOMEM, SF_E_HIP. */

@@ -765,7 +765,7 @@ extern "C" sf_status sf_round_create(sf_cache* d, sf_cache* v, int32_t k, sf_rou
     return fail(SF_E_STATE, "both stacks need an LM head");
   if (d->B != v->B) return fail(SF_E_ARG, "drafter and verifier must hold the same number of sequences");
   if (d->m->stream != v->m->stream) return fail(SF_E_ARG, "drafter and verifier models must share one stream");
-  if (d->m->V != v->m->V) return fail(SF_E_ARG, "drafter and verifier must share the vocabulary");
+  if (d->m->V > v->m->V) return fail(SF_E_ARG, "the drafter's vocabulary must not exceed the verifier's");
   if (k < 1 || k > v->kmax) return fail(SF_E_ARG, "k must be in 1..verifier k_max");
   sf_round* r = new sf_round();
   r->d = d;
