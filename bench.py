@@ -58,6 +58,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-batched", action="store_true", help="skip the 32-sequence batched verify line")
     ap.add_argument("--no-round", action="store_true", help="skip the device-resident draft+verify round line")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill (time to first token) line")
     ap.add_argument("--kernel-iters", type=int, default=56)
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="also run plain device copies of 1 GiB, so HBM byte counters can be scaled")
@@ -229,6 +230,33 @@ def main():
         sfb.sf_cache_free(cb)
         log(f"batched: {batched}")
 
+    # Prefill (time to first token): prompts of 512 and 2048 seeded ids from an empty cache,
+    # in passes of up to 512 positions, host-inclusive (sf_prefill returns the next token).
+    # Work per prompt: 2 flops per weight per position (layers and head) plus the causal
+    # attention's QK^T and PV, 4*dh flops per (query head, position pair).
+    prefill = None
+    if not args.no_prefill:
+        pc = sfb.sf_cache_alloc(model, 1, 2048 + 16, K)
+        q_dim, kv_dim = S.n_q_heads * S.head_dim, S.n_kv_heads * S.head_dim
+        params_layers = S.n_layers * (S.hidden * (q_dim + 2 * kv_dim) + q_dim * S.hidden + 3 * S.hidden * S.ffn)
+        prefill = {}
+        for n in (512, 2048):
+            prompt = synth.prompt_ids(S.vocab, n, synth.seeds(7)["prompt"])
+            sfb.sf_prefill(pc, 0, prompt[:64])
+            best = 1e9
+            for _ in range(3):
+                t0 = time.perf_counter()
+                sfb.sf_prefill(pc, 0, prompt)
+                best = min(best, time.perf_counter() - t0)
+            flops = 2.0 * n * (params_layers + S.vocab * S.hidden) + \
+                S.n_layers * S.n_q_heads * 4.0 * S.head_dim * n * (n + 1) / 2
+            prefill[str(n)] = {"ms": round(best * 1e3, 3), "prompt_tokens_per_s": round(n / best, 1),
+                               "tflops": round(flops / best / 1e12, 1),
+                               "frac_bf16_dense_peak": round(flops / best / 1e12 / 2500.0, 4)}
+        prefill["pass_positions"] = 512
+        sfb.sf_cache_free(pc)
+        log(f"prefill: {prefill}")
+
     # Device-resident speculative round: a Qwen2.5-0.5B-shape drafter (tied head) and this
     # 7B-shape verifier on one stream, both prefilled with the same 512-token prompt; each
     # round is one graph replay (8 drafter steps, the 9-position verify, accept, the drafter's
@@ -326,6 +354,7 @@ def main():
         "kernels_at_verify_shape": kern,
         "batched_32": batched,
         "device_round_0.5b_drafter": spec_round,
+        "prefill_ttft": prefill,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -88,6 +88,7 @@ sf_status sf_model_free(sf_model* model);
  * fix 1, a pre-allocated fixed-size cache).  Every sequence starts with length 0
  * and pending token 0.  KV layout: [layer][seq][kv_head][position][head_dim] bf16;
  * K is stored after RoPE.
+ * Scratch is sized for passes of max(n_seqs*(k_max+1), prefill pass size) rows.
  * Limits: 1 <= n_seqs <= 64, n_seqs * (k_max+1) <= 512, 0 <= k_max <= 15,
  * k_max+1 <= capacity <= 16384. */
 sf_status sf_cache_alloc(sf_model* model, int32_t n_seqs, int32_t capacity, int32_t k_max,
@@ -98,7 +99,12 @@ sf_status sf_cache_free(sf_cache* cache);
  * (any previous content of that sequence is discarded) and commit all of them.
  * Afterwards length = n and the pending token is the greedy choice after the
  * last prompt token, returned in *next_token (host, may be NULL; hidden-state
- * stacks return 0).  Runs in chunks of up to 64 positions, not graph-captured.
+ * stacks return 0).  [Sangama] "What made it faster", item 4, splits long prompts into
+ * 64-token pieces so that pipeline stages work on different pieces at once; on one GPU
+ * there is no pipeline to fill, so up to eight such pieces (512 positions) go through
+ * one pass together, which lets each weight byte serve 512 rows.  Not graph-captured.  The pass size (1..512) can be lowered for a cache by setting
+ * SF_PREFILL_CHUNK in the environment before sf_cache_alloc; results are bit-identical
+ * for any pass size.
  * Errors: SF_E_ARG (token id outside [0,V), n < 1), SF_E_CAPACITY (n > capacity). */
 sf_status sf_prefill(sf_cache* cache, int32_t seq, const int32_t* tokens, int32_t n,
                      int32_t* next_token);

@@ -670,7 +670,7 @@ int attention_spans(int cap) { return (cap + kSpan - 1) / kSpan; }
 // order independent), count the leading drafts that match, and commit.  Wave w merges the
 // rows w, w+16, ... of the sequence.
 __global__ __launch_bounds__(1024) void k_accept(const AcceptArgs a) {
-  __shared__ int tgt[kMaxK];
+  __shared__ int tgt[kMaxRows];   // one per slot: up to k_max+1 in a verify, a whole prefill chunk
   const int b = blockIdx.x, tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   if (a.has_head) {
@@ -724,6 +724,7 @@ __global__ __launch_bounds__(1024) void k_accept(const AcceptArgs a) {
 }
 
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t s) {
+  if (a.T < 1 || a.T > kMaxRows) return hipErrorInvalidValue;
   k_accept<<<a.B, 1024, 0, s>>>(a);
   return hipGetLastError();
 }

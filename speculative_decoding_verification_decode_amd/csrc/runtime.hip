@@ -77,6 +77,7 @@ struct Run {
 struct sf_cache {
   sf_model* m;
   int B, cap, kmax, T, nchunk;
+  int pchunk = kPrefillChunk;       // prompt positions per prefill pass
   size_t layer_stride, seq_stride;  // elements
   uint16_t *kpool = nullptr, *vpool = nullptr;
   int32_t *len = nullptr, *next = nullptr;
@@ -478,7 +479,9 @@ extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacit
     if (st_ != SF_OK) return bail(st_); \
   } while (0)
   // Rows of the largest pass this cache runs: a verify (n_seqs x (k_max+1)) or a prefill chunk.
-  const size_t R = std::max(n_seqs * (k_max + 1), kPrefillChunk);
+  c->pchunk = kPrefillChunk;
+  if (const char* v = getenv("SF_PREFILL_CHUNK")) c->pchunk = std::min(std::max(atoi(v), 1), kMaxRows);
+  const size_t R = std::max(n_seqs * (k_max + 1), c->pchunk);
   const size_t pool = c->layer_stride * m->L * 2;
   TRY(dalloc((void**)&c->kpool, pool));
   TRY(dalloc((void**)&c->vpool, pool));
@@ -648,8 +651,8 @@ extern "C" sf_status sf_prefill(sf_cache* c, int32_t seq, const int32_t* tokens,
   hipStream_t s = m->stream;
   HIPCHK(launch_set_state(c->len, c->next, seq, 0, 0, 1, s));
   int last_cnt = 1;
-  for (int j0 = 0; j0 < n; j0 += kPrefillChunk) {
-    const int cnt = std::min(kPrefillChunk, n - j0);
+  for (int j0 = 0; j0 < n; j0 += c->pchunk) {
+    const int cnt = std::min(c->pchunk, n - j0);
     Stage* st = c->stage_h;
     st->flags = kFlagForce | kFlagFirst;
     st->kmax = cnt - 1;

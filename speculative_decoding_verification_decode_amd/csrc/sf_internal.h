@@ -16,7 +16,8 @@ constexpr int kMaxRows = 512;                 // rows (sequences x positions) pe
 constexpr int kMaxSeqs = 64;
 constexpr int kMaxK = 16;                     // drafts per sequence (k_max <= 15, T <= 16)
 constexpr int kMaxDraftSteps = 256;
-constexpr int kPrefillChunk = 64;
+constexpr int kPrefillChunk = 512;            // default prompt positions per prefill pass
+static_assert(kPrefillChunk <= kMaxRows, "a prefill chunk is one pass");
 constexpr int kMaxCapacity = 16384;  // positions per sequence
 
 // GEMM activation operand layout with `ext` operand rows: for each 16-column k tile, the 2*ext

@@ -107,7 +107,10 @@ def test_full_stack_verify_matches_oracle(eng, weights, kv, hist, ctx):
         assert sfb.sf_cache_state(eng.cache, 0) == (ctx + r2["accepted"] + 1, int(r2["target"][r2["accepted"]]))
 
 
-def test_prefill_two_chunks_matches_oracle(eng, weights):
+def test_prefill_one_and_two_passes_match_oracle(eng, weights, monkeypatch):
+    """A 70-token prompt as one 70-row pass (the batched GEMM kernel) and as passes of 64 + 6
+    rows (the single-group kernel) writes bit-identical K/V, within 0.02 relative of the
+    oracle's cache."""
     sfb = need_gpu()
     prompt = synth.prompt_ids(S.vocab, 70, 4242)
     say("[7b] prefill 70")
@@ -116,7 +119,17 @@ def test_prefill_two_chunks_matches_oracle(eng, weights):
     kg = torch.zeros(shape, dtype=torch.int16, device="cuda")
     vg = torch.zeros_like(kg)
     sfb.sf_kv_read(eng.cache, 0, kg, vg, 70, 70)
-    torch.cuda.synchronize()
+    monkeypatch.setenv("SF_PREFILL_CHUNK", "64")
+    c64 = sfb.sf_cache_alloc(eng.model, 1, 80, K)
+    try:
+        assert sfb.sf_prefill(c64, 0, prompt) == nxt
+        k64 = torch.zeros_like(kg)
+        v64 = torch.zeros_like(kg)
+        sfb.sf_kv_read(c64, 0, k64, v64, 70, 70)
+        torch.cuda.synchronize()
+        assert torch.equal(kg, k64) and torch.equal(vg, v64)
+    finally:
+        sfb.sf_cache_free(c64)
     c = oracle.KVCache(S, 80)
     z = oracle.prefill(oracle.Model(S, weights), c, prompt)
     gap = oracle.top_gap(z[-1:])[0].item()

@@ -49,6 +49,47 @@ def test_prefill_matches_oracle(pair):
         assert sfb.sf_cache_state(eng.cache, 0) == (n, nxt)
 
 
+def _kv(sfb, cache, n, cap):
+    shape = (S.n_layers, S.n_kv_heads, cap, S.head_dim)
+    kg = torch.zeros(shape, dtype=torch.int16, device="cuda")
+    vg = torch.zeros_like(kg)
+    sfb.sf_kv_read(cache, 0, kg, vg, n, cap)
+    torch.cuda.synchronize()
+    return kg.cpu()[:, :, :n], vg.cpu()[:, :, :n]
+
+
+def test_prefill_chunk_sizes_agree_bitwise_and_match_oracle(monkeypatch):
+    """A 1100-token prompt in passes of 512 positions (the default: 512 + 512 + 76) and of 64
+    (18 passes) writes bit-identical K/V and picks the same next token: every GEMM splits k
+    the same way at any row count and attention spans are fixed by absolute position.  Both
+    match the oracle's cache within 0.02."""
+    sfb = need_gpu()
+    n, cap = 1100, 1152
+    p = Pair(S, 1, capacity=cap, k_max=4)
+    monkeypatch.setenv("SF_PREFILL_CHUNK", "64")
+    c64 = sfb.sf_cache_alloc(p.eng.model, 1, cap, 4)
+    try:
+        prompt = synth.prompt_ids(S.vocab, n, 4100)
+        say(f"[tiny] prefill {n} in passes of 512 and of 64")
+        nxt = sfb.sf_prefill(p.eng.cache, 0, prompt)
+        nxt64 = sfb.sf_prefill(c64, 0, prompt)
+        assert nxt == nxt64
+        ka, va = _kv(sfb, p.eng.cache, n, cap)
+        kb, vb = _kv(sfb, c64, n, cap)
+        assert torch.equal(ka, kb) and torch.equal(va, vb)
+        c = oracle.KVCache(S, cap)
+        z = oracle.prefill(p.model, c, prompt)
+        if oracle.top_gap(z[-1:])[0].item() > GAP:
+            assert nxt == c.next_token
+        assert (ka.view(torch.bfloat16).double() - c.k[:, :, :n].double()).abs().max().item() <= 0.02
+        assert (va.view(torch.bfloat16).double() - c.v[:, :, :n].double()).abs().max().item() <= 0.02
+        assert sfb.sf_cache_state(p.eng.cache, 0) == (n, nxt)
+        assert sfb.sf_cache_state(c64, 0) == (n, nxt)
+    finally:
+        sfb.sf_cache_free(c64)
+        p.close()
+
+
 def test_c1_lockstep_16_steps(pair):
     """The tiny workload end to end: eager debug pass (logits), graph pass (accepted,
     targets), and the oracle, step by step; both sides are then forced to the oracle's
@@ -234,6 +275,7 @@ def test_four_wave_workgroups_split_k_and_64_row_chunks(monkeypatch):
     split over two workgroups per block (partials + reduce kernels), and prefill chunks of 64
     rows."""
     need_gpu()
+    monkeypatch.setenv("SF_PREFILL_CHUNK", "64")
     monkeypatch.setenv("SF_KH", "8")     # 8-tile batches
     for v in ("SF_NW_QKV", "SF_NW_O", "SF_NW_GU", "SF_NW_D", "SF_NW_HEAD"):
         monkeypatch.setenv(v, "4")
