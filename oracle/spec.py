@@ -102,6 +102,42 @@ def rollback(cache, pos):
     cache.length = int(pos)
 
 
+def snapshot(cache, T):
+    """The state one pass of T positions overwrites: committed length, pending token, and the
+    cache's K/V rows at positions [length, length + T) (clipped to the capacity).  [Sangama]
+    "Speculative decoding: correct, but slower (for now)": every worker saves its state
+    before the guesses are checked."""
+    L = cache.length
+    hi = min(L + T, cache.capacity)
+    return {"length": L, "next_token": cache.next_token,
+            "k": cache.k[:, :, L:hi].clone(), "v": cache.v[:, :, L:hi].clone()}
+
+
+def restore(cache, snap):
+    """Put a snapshot back: its K/V rows at its length, then its length and pending token."""
+    L = snap["length"]
+    n = snap["k"].shape[2]
+    cache.k[:, :, L:L + n] = snap["k"]
+    cache.v[:, :, L:L + n] = snap["v"]
+    cache.length = L
+    cache.next_token = snap["next_token"]
+
+
+def snapshot_verify(model, cache, draft, k):
+    """One verify with the snapshot form of rollback (same page and section as snapshot()):
+    save the state, check the k drafts (the pass commits as verify() does), and when some
+    were rejected restore the snapshot and replay only the accepted drafts, a pass over the
+    pending token and d_1..d_M whose last target is the new pending token.  Returns the
+    checking pass's result dict."""
+    snap = snapshot(cache, k + 1)
+    res = verify(model, cache, draft, k)
+    M = res["accepted"]
+    if M < k:
+        restore(cache, snap)
+        verify(model, cache, [int(t) for t in draft[:M]], M, force_accept=True)
+    return res
+
+
 def set_next(cache, token):
     cache.next_token = int(token)
 

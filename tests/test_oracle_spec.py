@@ -312,3 +312,55 @@ def test_head_gain_scales_every_logit():
         c = oracle.KVCache(synth.TINY, 16)
         z.append(oracle.prefill(oracle.Model(synth.TINY, w, cache=True), c, prompt))
     assert (z[1] - 32.0 * z[0]).abs().max().item() <= 1e-9 * z[1].abs().max().item()
+
+
+# ---------------------------------------------------------------- snapshot rollback
+
+def _corrupted_rounds(model, cache, K, rounds, seed):
+    """Per round: the model's own K-token continuation with one seeded corruption."""
+    rng = np.random.default_rng(seed)
+    for _ in range(rounds):
+        d, _ = synth.corrupt_draft(oracle.greedy_continuation(model, cache, K), model.shape.vocab, rng)
+        yield d
+
+
+def test_snapshot_restore_returns_every_byte(tiny):
+    """Save, a committing verify that writes K+1 K/V rows, restore: the whole cache (both
+    arrays, every position), the length and the pending token are as before."""
+    K = 4
+    c = oracle.KVCache(synth.TINY, 64)
+    oracle.prefill(tiny, c, synth.prompt_ids(synth.TINY.vocab, 20, 21))
+    before = c.copy()
+    snap = oracle.snapshot(c, K + 1)
+    oracle.verify(tiny, c, [1, 2, 3, 4], K)
+    assert c.length > before.length and not torch.equal(c.k, before.k)
+    oracle.restore(c, snap)
+    assert torch.equal(c.k, before.k) and torch.equal(c.v, before.v)
+    assert (c.length, c.next_token) == (before.length, before.next_token)
+
+
+def test_snapshot_verify_equals_in_place_verify_and_greedy(tiny):
+    """Rounds with the snapshot form of rollback (save, check, restore, replay the accepted
+    drafts) reach the same length, pending token and committed K/V as the in-place form
+    (commit M+1, leave the rest stale), and their committed stream is plain greedy decoding."""
+    K = 4
+    prompt = synth.prompt_ids(synth.TINY.vocab, 20, 21)
+    a, b = oracle.KVCache(synth.TINY, 96), oracle.KVCache(synth.TINY, 96)
+    oracle.prefill(tiny, a, prompt)
+    oracle.prefill(tiny, b, prompt)
+    stream, accepted = [], []
+    for d in _corrupted_rounds(tiny, a, K, 8, 5):
+        first = a.next_token
+        ra = oracle.verify(tiny, a, d, K)
+        rb = oracle.snapshot_verify(tiny, b, d, K)
+        assert ra["accepted"] == rb["accepted"]
+        assert (a.length, a.next_token) == (b.length, b.next_token)
+        n = a.length
+        assert (a.k[:, :, :n].double() - b.k[:, :, :n].double()).abs().max().item() == 0.0
+        assert (a.v[:, :, :n].double() - b.v[:, :, :n].double()).abs().max().item() == 0.0
+        stream += [first] + [int(t) for t in d[:ra["accepted"]]]
+        accepted.append(ra["accepted"])
+    assert min(accepted) < K                      # the restore-and-replay branch ran
+    g = oracle.KVCache(synth.TINY, 96)
+    oracle.prefill(tiny, g, prompt)
+    assert stream == oracle.greedy_decode(tiny, g, len(stream))
