@@ -151,6 +151,27 @@ def main():
         ms = e0.elapsed_time(e1) / n
         per_ctx[ctx] = {"ms": round(ms, 4), "verify_tokens_per_s": round((K + 1) / ms * 1e3, 1)}
 
+    # Snapshot form of rollback at context 512: saving and restoring the state one pass
+    # overwrites (length, pending token, 9 K/V rows of every layer), timed with HIP events;
+    # a rejected round then pays one replay pass, a verify-shaped pass of the same graph.
+    csnap = caches[CONTEXTS[0]]
+    nsn = 50
+    tsn = {}
+    for nm, fn in (("save", sfb.sf_snapshot_save), ("restore", sfb.sf_snapshot_restore)):
+        fn(csnap)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(nsn):
+            fn(csnap)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        tsn[nm] = e0.elapsed_time(e1) * 1e3 / nsn
+    snapshot_rb = {"save_us": round(tsn["save"], 2), "restore_us": round(tsn["restore"], 2),
+                   "replay_pass_ms": per_ctx[CONTEXTS[0]]["ms"],
+                   "bytes_each_way": 2 * S.n_layers * S.n_kv_heads * (K + 1) * S.head_dim * 2,
+                   "in_place_rewind": "index write, no pass"}
+
     # Host-inclusive latency of one synchronous verify (H2D drafts, replay, D2H results).
     c512 = caches[CONTEXTS[0]]
     hd = drafts[CONTEXTS[0]].cpu().numpy()[None]
@@ -355,6 +376,7 @@ def main():
         "batched_32": batched,
         "device_round_0.5b_drafter": spec_round,
         "prefill_ttft": prefill,
+        "snapshot_rollback_ctx512": snapshot_rb,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

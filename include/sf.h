@@ -162,6 +162,21 @@ sf_status sf_results_device(sf_cache* cache, int32_t** dev_accepted, int32_t** d
  * Errors: SF_E_ARG (bad seq), SF_E_STATE (pos > length or pos < 0). */
 sf_status sf_rollback(sf_cache* cache, int32_t seq, int32_t pos);
 
+/* sf_snapshot_save: record, for every sequence, its length, pending token and the K/V
+ * rows of every layer at positions [length, length+k_max+1): the state one verify pass
+ * overwrites.  sf_snapshot_restore puts all of it back.  Together with a replay of the
+ * accepted drafts (sf_verify with SF_FORCE_ACCEPT and k = accepted count) this is the
+ * pages' other rollback ([Sangama] "Speculative decoding: correct, but slower (for now)":
+ * each worker saves a snapshot of its state before checking the guesses and, when some
+ * were wrong, restores it and replays only the accepted tokens locally), the form needed by
+ * stacks whose state cannot be rewound by an index.  For this attention-only stack it
+ * reaches bit-identical state to sf_rollback's index rewind at the cost of the replay
+ * pass.  Both calls are enqueued on the model stream without waiting; restore marks the
+ * host view of the state stale.  One snapshot per cache; a save replaces the previous one.
+ * Errors: SF_E_ARG (NULL), SF_E_STATE (restore before any save), SF_E_HIP. */
+sf_status sf_snapshot_save(sf_cache* cache);
+sf_status sf_snapshot_restore(sf_cache* cache);
+
 /* sf_set_next: set the pending token of `seq` (the token the next pass places at
  * position `length`).  Errors: SF_E_ARG (bad seq or token outside [0,V)). */
 sf_status sf_set_next(sf_cache* cache, int32_t seq, int32_t token);

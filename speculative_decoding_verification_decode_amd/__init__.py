@@ -78,6 +78,8 @@ def lib():
             "sf_results_device": [_P, ctypes.POINTER(_P), ctypes.POINTER(_P)],
             "sf_rollback": [_P, _I, _I],
             "sf_set_next": [_P, _I, _I],
+            "sf_snapshot_save": [_P],
+            "sf_snapshot_restore": [_P],
             "sf_cache_state": [_P, _I, _PI, _PI],
             "sf_draft_step": [_P, _I, _PI],
             "sf_round_create": [_P, _P, _I, ctypes.POINTER(_P)],
@@ -207,6 +209,14 @@ def sf_results_device(cache):
 
 def sf_rollback(cache, seq, pos):
     _check(lib().sf_rollback(cache, seq, pos))
+
+
+def sf_snapshot_save(cache):
+    _check(lib().sf_snapshot_save(cache))
+
+
+def sf_snapshot_restore(cache):
+    _check(lib().sf_snapshot_restore(cache))
 
 
 def sf_set_next(cache, seq, token):

@@ -789,6 +789,54 @@ hipError_t launch_set_state(int32_t* len, int32_t* next, int seq, int new_len, i
   return hipGetLastError();
 }
 
+// Snapshot save (copy the live rows out, record length and pending token) or restore (copy
+// the saved rows back at the saved length, then reinstate length and pending token).  One
+// 16-byte unit of K and of V per thread and step; positions past the capacity are skipped.
+__global__ __launch_bounds__(256) void k_snapshot(const SnapArgs a, int save) {
+  const int units = a.dh / 8;
+  const size_t total = (size_t)a.L * a.B * a.nkv * a.T * units;
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    size_t t = idx / units;
+    const int u = (int)(idx - t * units);
+    const int slot = (int)(t % a.T);
+    t /= a.T;
+    const int h = (int)(t % a.nkv);
+    t /= a.nkv;
+    const int b = (int)(t % a.B);
+    const int l = (int)(t / a.B);
+    const int pos = (save ? a.len[b] : a.slen[b]) + slot;
+    if (pos >= a.cap) continue;
+    const size_t po = (size_t)l * a.layer_stride + (size_t)b * a.seq_stride + ((size_t)h * a.cap + pos) * a.dh + u * 8;
+    const size_t so = ((((size_t)l * a.B + b) * a.nkv + h) * a.T + slot) * a.dh + u * 8;
+    if (save) {
+      *(uint4*)(a.sk + so) = *(const uint4*)(a.kpool + po);
+      *(uint4*)(a.sv + so) = *(const uint4*)(a.vpool + po);
+    } else {
+      *(uint4*)(a.kpool + po) = *(const uint4*)(a.sk + so);
+      *(uint4*)(a.vpool + po) = *(const uint4*)(a.sv + so);
+    }
+  }
+  if (blockIdx.x == 0)
+    for (int b = threadIdx.x; b < a.B; b += blockDim.x) {
+      if (save) {
+        a.slen[b] = a.len[b];
+        a.snext[b] = a.next[b];
+      } else {
+        a.len[b] = a.slen[b];
+        a.next[b] = a.snext[b];
+      }
+    }
+}
+
+hipError_t launch_snapshot(const SnapArgs& a, int save, hipStream_t s) {
+  if (a.L < 1 || a.B < 1 || a.nkv < 1 || a.T < 1 || a.dh % 8) return hipErrorInvalidValue;
+  const size_t units = (size_t)a.L * a.B * a.nkv * a.T * (a.dh / 8);
+  const int grid = (int)std::min<size_t>((units + 255) / 256, 1024);
+  k_snapshot<<<grid, 256, 0, s>>>(a, save);
+  return hipGetLastError();
+}
+
 // Device-resident drafts -> fixed staging block (draft [B][kmax], k [B] or all kmax).
 __global__ void k_stage_device(Stage* st, const int32_t* draft, const int32_t* k, int B, int kmax, int flags) {
   const int t = threadIdx.x;

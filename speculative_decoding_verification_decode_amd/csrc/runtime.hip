@@ -97,6 +97,9 @@ struct sf_cache {
   int cnt_stride = 0;
   bool prefetch_o = true;   // warm the O projection's weights into L2 during attention
   hipGraphExec_t gx_verify = nullptr, gx_draft = nullptr;
+  uint16_t *snap_k = nullptr, *snap_v = nullptr;   // state snapshot: K/V rows [len, len+T)
+  int32_t *snap_len = nullptr, *snap_next = nullptr;
+  bool snap_valid = false;
   std::vector<int> len_h, next_h, len_hi;
   bool dirty = false;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
@@ -508,6 +511,13 @@ extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacit
   TRY(dalloc((void**)&c->res_d, 4 * kMaxRows * 4));
   TRY(dalloc((void**)&c->dout_d, (size_t)n_seqs * kMaxDraftSteps * 4));
   {
+    const size_t snap = (size_t)m->L * n_seqs * m->nkv * c->T * m->dh * 2;
+    TRY(dalloc((void**)&c->snap_k, snap));
+    TRY(dalloc((void**)&c->snap_v, snap));
+    TRY(dalloc((void**)&c->snap_len, n_seqs * 4));
+    TRY(dalloc((void**)&c->snap_next, n_seqs * 4));
+  }
+  {
     hipError_t e = hipHostMalloc((void**)&c->stage_h, sizeof(Stage), hipHostMallocDefault);
     if (e == hipSuccess) e = hipHostMalloc((void**)&c->res_h, 4 * kMaxRows * 4, hipHostMallocDefault);
     if (e == hipSuccess) e = hipHostMalloc((void**)&c->dout_h, (size_t)n_seqs * kMaxDraftSteps * 4, hipHostMallocDefault);
@@ -675,6 +685,33 @@ extern "C" sf_status sf_prefill(sf_cache* c, int32_t seq, const int32_t* tokens,
     c->next_h[seq] = nxt;
   }
   if (next_token) *next_token = nxt;
+  return SF_OK;
+}
+
+static SnapArgs snap_args(sf_cache* c) {
+  sf_model* m = c->m;
+  SnapArgs a{};
+  a.kpool = c->kpool; a.vpool = c->vpool; a.sk = c->snap_k; a.sv = c->snap_v;
+  a.len = c->len; a.next = c->next; a.slen = c->snap_len; a.snext = c->snap_next;
+  a.layer_stride = (long)c->layer_stride; a.seq_stride = (long)c->seq_stride;
+  a.L = m->L; a.B = c->B; a.nkv = m->nkv; a.cap = c->cap; a.dh = m->dh; a.T = c->T;
+  return a;
+}
+
+extern "C" sf_status sf_snapshot_save(sf_cache* c) {
+  if (!c) return fail(SF_E_ARG, "cache is NULL");
+  const hipError_t e = launch_snapshot(snap_args(c), 1, c->m->stream);
+  if (e != hipSuccess) return fail(SF_E_HIP, std::string("snapshot save: ") + hipGetErrorString(e));
+  c->snap_valid = true;
+  return SF_OK;
+}
+
+extern "C" sf_status sf_snapshot_restore(sf_cache* c) {
+  if (!c) return fail(SF_E_ARG, "cache is NULL");
+  if (!c->snap_valid) return fail(SF_E_STATE, "no snapshot has been saved on this cache");
+  const hipError_t e = launch_snapshot(snap_args(c), 0, c->m->stream);
+  if (e != hipSuccess) return fail(SF_E_HIP, std::string("snapshot restore: ") + hipGetErrorString(e));
+  c->dirty = true;
   return SF_OK;
 }
 

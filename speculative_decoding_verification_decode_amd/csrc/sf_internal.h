@@ -162,5 +162,16 @@ hipError_t launch_stage_device(Stage* stage, const int32_t* draft, const int32_t
                                int flags, hipStream_t s);
 hipError_t launch_copy_kv(uint16_t* pool, uint16_t* src, long pool_layer_stride, int nkv, int cap,
                           int dh, int n_layers, int n_pos, int src_positions, int to_pool, hipStream_t s);
+// State snapshot of every sequence: (length, pending token) and the K/V rows at positions
+// [length, length+T) of every layer, the rows one pass of T positions writes.
+struct SnapArgs {
+  uint16_t *kpool, *vpool;   // [layer][seq][kv head][position][dh]
+  uint16_t *sk, *sv;         // [layer][seq][kv head][T][dh]
+  int32_t *len, *next;       // live state [B]
+  int32_t *slen, *snext;     // saved state [B]
+  long layer_stride, seq_stride;
+  int L, B, nkv, cap, dh, T;
+};
+hipError_t launch_snapshot(const SnapArgs& a, int save, hipStream_t s);
 
 }  // namespace sf

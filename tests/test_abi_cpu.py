@@ -101,6 +101,8 @@ def test_null_handles_are_rejected():
     assert L.sf_round_create(null, null, 1, ctypes.byref(ctypes.c_void_p())) == sfb.SF_E_ARG
     assert L.sf_round_run(null, 1) == sfb.SF_E_ARG
     assert L.sf_round_free(null) == sfb.SF_E_ARG
+    assert L.sf_snapshot_save(null) == sfb.SF_E_ARG
+    assert L.sf_snapshot_restore(null) == sfb.SF_E_ARG
     assert "NULL" in sfb.sf_last_error()
 
 
