@@ -50,10 +50,11 @@ from .spec import (
     snapshot_verify,
 )
 from .ngram import propose
+from . import nf4
 
 __all__ = [
     "Model", "KVCache", "round_bf16", "rms_norm", "rope_angles", "rope", "silu", "swiglu",
     "causal_gqa_attention", "forward", "argmax_lowest", "top_gap", "accept_prefix", "verify",
     "prefill", "greedy_decode", "greedy_continuation", "rollback", "set_next",
-    "speculative_decode", "model_draft_round", "snapshot", "restore", "snapshot_verify", "propose",
+    "speculative_decode", "model_draft_round", "snapshot", "restore", "snapshot_verify", "propose", "nf4",
 ]

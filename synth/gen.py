@@ -108,6 +108,62 @@ def near_copy(weights, other, eps):
     return out
 
 
+NF4_QUANTIZED = ("wq", "wk", "wv", "wo", "wg", "wu", "wd")
+
+
+def nf4_tensor(shape, seed, name, threads=None, pool=None):
+    """Synthetic NF4 projection [rows][n_in] with the statistics of a quantized bf16(0.02 z)
+    matrix: codes uint8 [rows][n_in / 2] (two per byte, even input in the low nibble), each
+    code uniform over the 16 levels (NF4 levels bound equal-probability bins of a normal
+    weight), and scales as bf16 bits [rows][n_in / 64]: 0.02 times the largest |z| of 64
+    standard normals, drawn by inverting that maximum's distribution function."""
+    from scipy.special import ndtri
+    rows, n_in = int(shape[0]), int(shape[1])
+    codes = np.empty(rows * n_in // 2, dtype=np.uint8)
+    scales = np.empty(rows * n_in // 64, dtype=np.uint16)
+    nc = (codes.size + CHUNK - 1) // CHUNK
+    ns = (scales.size + CHUNK - 1) // CHUNK
+
+    def fill(c):
+        if c < nc:
+            lo, hi = c * CHUNK, min(codes.size, (c + 1) * CHUNK)
+            codes[lo:hi] = _stream(seed, name + "/codes", c).integers(0, 256, hi - lo, dtype=np.uint8)
+        else:
+            c -= nc
+            lo, hi = c * CHUNK, min(scales.size, (c + 1) * CHUNK)
+            u = _stream(seed, name + "/scales", c).random(hi - lo)
+            m = ndtri(0.5 * (1.0 + u ** (1.0 / 64.0)))
+            scales[lo:hi] = _f32_to_bf16_bits((WEIGHT_STD * m).astype(np.float32))
+
+    if nc + ns <= 1:
+        for c in range(nc + ns):
+            fill(c)
+    elif pool is not None:
+        list(pool.map(fill, range(nc + ns)))
+    else:
+        with ThreadPoolExecutor(_threads(threads)) as p:
+            list(p.map(fill, range(nc + ns)))
+    return codes.reshape(rows, n_in // 2), scales.reshape(rows, n_in // 64)
+
+
+def nf4_model_weights(shape, seed, names=None, threads=None):
+    """All weights of `shape` with the projections (q, k, v, o, gate, up, down) in NF4 as
+    (codes, scales) pairs from nf4_tensor; embeddings, norms, biases and the head as in
+    model_weights."""
+    names = tensor_names(shape) if names is None else names
+    out = {}
+    with ThreadPoolExecutor(_threads(threads)) as pool:
+        for name in names:
+            shp = tensor_shape(shape, name)
+            if name.split(".")[-1] in NF4_QUANTIZED:
+                out[name] = nf4_tensor(shp, seed, name, pool=pool)
+            elif name.endswith("ln1") or name.endswith("ln2") or name == "final_norm":
+                out[name] = np.full(shp, BF16_ONE, dtype=np.uint16)
+            else:
+                out[name] = bf16_normal(shp, WEIGHT_STD, seed, name, pool=pool)
+    return out
+
+
 def prompt_ids(vocab, n, seed):
     """n token ids uniform in [0, vocab)."""
     rng = np.random.Generator(np.random.PCG64(seed))

@@ -63,7 +63,13 @@ QWEN7B = Shape("qwen2.5-7b", n_layers=28, hidden=3584, n_q_heads=28, n_kv_heads=
 # First half of the 7B stack (embedding + layers 0..13), emitting hidden states.
 QWEN7B_HALF = replace(QWEN7B, name="qwen2.5-7b-half", n_layers=14, has_head=False)
 
-SHAPES = {s.name: s for s in (TINY, QWEN05B, QWEN7B, QWEN7B_HALF)}
+# Qwen2.5-14B dimensions (NF4 verifier; untied head).
+QWEN14B = Shape("qwen2.5-14b", n_layers=48, hidden=5120, n_q_heads=40, n_kv_heads=8, head_dim=128,
+                ffn=13824, vocab=152064, rope_base=1e6)
+# Two layers of the 14B stack with its full embedding and head: every kernel at its real shape.
+QWEN14B_2L = replace(QWEN14B, name="qwen2.5-14b-2l", n_layers=2)
+
+SHAPES = {s.name: s for s in (TINY, QWEN05B, QWEN7B, QWEN7B_HALF, QWEN14B, QWEN14B_2L)}
 
 
 def tensor_names(shape):
