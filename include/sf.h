@@ -20,7 +20,7 @@
  *     or written during the call.  "device" pointers are HIP device memory owned
  *     by the caller.  Everything else (packed weights, KV pool, scratch,
  *     counters, captured graphs) is owned by the library.
- *   - The library allocates device memory only in sf_model_create and
+ *   - The library allocates device memory only in sf_model_create(_nf4) and
  *     sf_cache_alloc; every later call reuses fixed addresses, so captured graph
  *     replays stay valid ([ShardFlow] "Why It Kept Breaking (and How I Fixed
  *     It)": captured addresses must not change; fixes 1 and 2).
@@ -80,6 +80,30 @@ typedef struct sf_model_desc {
  * Errors: SF_E_ARG for unsupported shapes, SF_E_NOMEM, SF_E_HIP. */
 sf_status sf_model_create(const sf_model_desc* desc, const void* const* weights, void* stream,
                           sf_model** out);
+
+/* sf_model_create_nf4: as sf_model_create, with the seven projections of every layer (wq,
+ * wk, wv, wo, wg, wu, wd) in 4-bit NormalFloat ([ShardFlow] "The Numbers": the 14.7B model
+ * run with 4-bit NF4 quantization).  Each projection takes two consecutive entries of
+ * `weights` in place of one:
+ *   codes   device uint8 [out][in/2]: the 4-bit code of input k of a row in byte k/2, the
+ *           even input in the low nibble;
+ *   scales  device bf16 [out][in/64]: one scale per 64 consecutive inputs of a row.
+ * The weight of code c in block b is level[c] * scale[b], level[] the table sf_nf4_levels
+ * returns.  Embedding, norms, biases and the LM head stay bf16.  The library packs each
+ * 32-row x 64-input block as 1 KB of codes in MFMA operand order plus the 32 row scales and
+ * turns codes into bf16 levels inside the GEMM (weights are read once per pass at about
+ * 0.53 bytes per weight).  Needs hidden, ffn and n_q_heads*head_dim to be multiples of 64;
+ * caches of an NF4 model run passes of at most 64 rows (n_seqs*(k_max+1) <= 64, prefill
+ * passes of 64 positions).  Errors as sf_model_create. */
+sf_status sf_model_create_nf4(const sf_model_desc* desc, const void* const* weights, void* stream,
+                              sf_model** out);
+
+/* sf_nf4_levels: the 16 NF4 levels the library decodes codes 0..15 to (host float out[16]):
+ * quantiles of the standard normal distribution at evenly spaced probabilities, 8 positive
+ * and 7 negative plus an exact zero, normalised to [-1, 1] (the QLoRA paper's 4-bit
+ * NormalFloat), each rounded to bf16.  Callers quantize with this table.  Errors: SF_E_ARG. */
+sf_status sf_nf4_levels(float* out);
+
 sf_status sf_model_free(sf_model* model);
 
 /* sf_cache_alloc: static KV pool for n_seqs sequences of `capacity` positions

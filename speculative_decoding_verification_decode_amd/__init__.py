@@ -79,6 +79,8 @@ def lib():
             "sf_rollback": [_P, _I, _I],
             "sf_set_next": [_P, _I, _I],
             "sf_snapshot_save": [_P],
+            "sf_model_create_nf4": [ctypes.POINTER(sf_model_desc), ctypes.POINTER(_P), _P, ctypes.POINTER(_P)],
+            "sf_nf4_levels": [ctypes.POINTER(ctypes.c_float)],
             "sf_snapshot_restore": [_P],
             "sf_cache_state": [_P, _I, _PI, _PI],
             "sf_draft_step": [_P, _I, _PI],
@@ -137,15 +139,18 @@ def desc_from_shape(shape):
                          int(shape.has_head), int(shape.tied_head), int(shape.qkv_bias))
 
 
-def weight_order(desc):
-    """Tensor names in the order sf_model_create expects them."""
+def weight_order(desc, nf4=False):
+    """Tensor names in the order sf_model_create expects them; with nf4, each projection
+    appears twice (its codes, then its scales), as sf_model_create_nf4 expects."""
+    def proj(n):
+        return [n, n] if nf4 else [n]
     names = ["embed"]
     for i in range(desc.n_layers):
         p = f"l{i}."
-        names += [p + "ln1", p + "wq"] + ([p + "bq"] if desc.qkv_bias else [])
-        names += [p + "wk"] + ([p + "bk"] if desc.qkv_bias else [])
-        names += [p + "wv"] + ([p + "bv"] if desc.qkv_bias else [])
-        names += [p + "wo", p + "ln2", p + "wg", p + "wu", p + "wd"]
+        names += [p + "ln1"] + proj(p + "wq") + ([p + "bq"] if desc.qkv_bias else [])
+        names += proj(p + "wk") + ([p + "bk"] if desc.qkv_bias else [])
+        names += proj(p + "wv") + ([p + "bv"] if desc.qkv_bias else [])
+        names += proj(p + "wo") + [p + "ln2"] + proj(p + "wg") + proj(p + "wu") + proj(p + "wd")
     if desc.has_head:
         names += ["final_norm"] + ([] if desc.tied_head else ["lm_head"])
     return names
@@ -158,6 +163,20 @@ def sf_model_create(desc, weight_ptrs, stream=None):
     arr = (_P * len(weight_ptrs))(*[int(p) for p in weight_ptrs])
     out = _P()
     _check(lib().sf_model_create(ctypes.byref(desc), arr, _ptr(stream), ctypes.byref(out)))
+    return out
+
+
+def sf_model_create_nf4(desc, weight_ptrs, stream=None):
+    """weight_ptrs: device addresses in weight_order(desc, nf4=True).  Returns the model handle."""
+    arr = (_P * len(weight_ptrs))(*[int(p) for p in weight_ptrs])
+    out = _P()
+    _check(lib().sf_model_create_nf4(ctypes.byref(desc), arr, _ptr(stream), ctypes.byref(out)))
+    return out
+
+
+def sf_nf4_levels():
+    out = np.zeros(16, dtype=np.float32)
+    _check(lib().sf_nf4_levels(out.ctypes.data_as(ctypes.POINTER(ctypes.c_float))))
     return out
 
 
@@ -279,13 +298,27 @@ def sf_time_kernel(cache, kernel, iters):
 
 # ------------------------------------------------------------------ torch conveniences
 
+def is_nf4(weights):
+    """True if the projections come as (codes, scales) pairs."""
+    return isinstance(weights.get("l0.wq"), tuple)
+
+
 def upload_weights(weights, desc, device="cuda"):
-    """Copy bf16 bit arrays (numpy uint16, by name) to the device; returns (tensors, pointers)."""
+    """Copy bf16 bit arrays (numpy uint16, by name) and, for NF4 projections, their (codes
+    uint8, scales uint16) pairs to the device; returns (tensors, pointers) in weight_order."""
     import torch
-    tensors = []
-    for name in weight_order(desc):
-        a = np.ascontiguousarray(weights[name])
-        tensors.append(torch.from_numpy(a.view(np.int16)).to(device))
+    nf4 = is_nf4(weights)
+    tensors, seen = [], {}
+    for name in weight_order(desc, nf4):
+        w = weights[name]
+        if isinstance(w, tuple):
+            i = seen.get(name, 0)
+            seen[name] = i + 1
+            a = np.ascontiguousarray(w[i])
+            a = a.view(np.int16) if a.dtype == np.uint16 else a
+        else:
+            a = np.ascontiguousarray(w).view(np.int16)
+        tensors.append(torch.from_numpy(a).to(device))
     return tensors, [t.data_ptr() for t in tensors]
 
 
@@ -300,7 +333,8 @@ class Engine:
         self.n_seqs, self.capacity, self.k_max = n_seqs, capacity, k_max
         tensors, ptrs = upload_weights(weights, self.desc)
         torch.cuda.synchronize()
-        self.model = sf_model_create(self.desc, ptrs, self.stream.cuda_stream)
+        create = sf_model_create_nf4 if is_nf4(weights) else sf_model_create
+        self.model = create(self.desc, ptrs, self.stream.cuda_stream)
         self._weights = tensors if keep_weights else None
         del tensors
         self.cache = sf_cache_alloc(self.model, n_seqs, capacity, k_max)

@@ -78,8 +78,8 @@ __device__ __forceinline__ void store_split(uint16_t* base, int rows, int r, int
 
 // Word 3 of a raw buffer resource on gfx9-family GPUs (gfx950 included).
 constexpr int kBufferWord3 = 0x00020000;
-// RMSNorm sum-of-squares partials (one per 32 columns) read per lane: hidden <= 64*32*2.
-constexpr int kSsqPerLane = 2;
+// RMSNorm sum-of-squares partials (one per 32 columns) read per lane: hidden <= 64*32*3.
+constexpr int kSsqPerLane = 3;
 // Weight tiles per pipelined half-batch.
 constexpr int kHalf = 8;
 // Cache policy of the weight stream: non-temporal (each weight byte is read once per pass).

@@ -315,6 +315,281 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
 }
 
 // ----------------------------------------------------------------------------------------------
+// NF4 skinny GEMM: Y[m][n] = sum_b scale[n][b] * sum_{k in block b} level[code[n][k]] * A[m][k]
+// for m < rows <= 64, blocks of 64 inputs.  Packed weights, per 32-row block and 64-input
+// block, 1088 bytes: 1 KB of codes (lane l: row l%32, inputs 8*(l/32) .. +8 of each of the
+// four 16-input k tiles, one dword per tile whose byte j holds the codes of inputs j and j+4)
+// then the 32 rows' scales as bf16.  A wave turns a tile's dword into the 8 bf16 levels of a
+// v_mfma_f32_32x32x16_bf16 operand with byte permutes (no memory lookups), runs the block's
+// four k tiles into a block accumulator with the activations as the A operand (so a lane's
+// 16 outputs share its weight row and its block scale), and adds scale * block accumulator.
+// Everything after the k loop (cross-wave sum in wave order, k split by last arrival,
+// epilogues) is k_gemm's, with the accumulator image transposed.
+
+// Byte tables for v_perm_b32: dword q holds byte `hi` of levels 4q .. 4q+3.
+constexpr uint32_t nf4_bytes(int q, int hi) {
+  uint32_t v = 0;
+  for (int e = 0; e < 4; ++e) v |= (uint32_t)((kNf4Bits[4 * q + e] >> (8 * hi)) & 0xFF) << (8 * e);
+  return v;
+}
+
+// Codes dword c (byte j = code of input j | code of input j+4 << 4) -> bf16x8 levels of
+// inputs 0..7.  Per group of four codes: the low three bits select a byte from the 8-entry
+// half tables, bit 3 picks the half (0x00 / 0xFF byte masks from the permute's constant
+// selectors 12 and 13), and two more permutes interleave low and high bytes.
+__device__ __forceinline__ u32x4 nf4_levels8(uint32_t c, const uint32_t (&tl)[4], const uint32_t (&th)[4]) {
+  const uint32_t sa = c & 0x07070707u;
+  const uint32_t sb = (c >> 4) & 0x07070707u;
+  const uint32_t ma = __builtin_amdgcn_perm(0u, 0u, ((c >> 3) & 0x01010101u) | 0x0C0C0C0Cu);
+  const uint32_t mb = __builtin_amdgcn_perm(0u, 0u, ((c >> 7) & 0x01010101u) | 0x0C0C0C0Cu);
+  auto pick = [](uint32_t m, uint32_t x, uint32_t y) { return (x & m) | (y & ~m); };
+  const uint32_t la = pick(ma, __builtin_amdgcn_perm(tl[3], tl[2], sa), __builtin_amdgcn_perm(tl[1], tl[0], sa));
+  const uint32_t ha = pick(ma, __builtin_amdgcn_perm(th[3], th[2], sa), __builtin_amdgcn_perm(th[1], th[0], sa));
+  const uint32_t lb = pick(mb, __builtin_amdgcn_perm(tl[3], tl[2], sb), __builtin_amdgcn_perm(tl[1], tl[0], sb));
+  const uint32_t hb = pick(mb, __builtin_amdgcn_perm(th[3], th[2], sb), __builtin_amdgcn_perm(th[1], th[0], sb));
+  u32x4 o;
+  o.x = __builtin_amdgcn_perm(ha, la, 0x05010400u);
+  o.y = __builtin_amdgcn_perm(ha, la, 0x07030602u);
+  o.z = __builtin_amdgcn_perm(hb, lb, 0x05010400u);
+  o.w = __builtin_amdgcn_perm(hb, lb, 0x07030602u);
+  return o;
+}
+
+// Position of output (n_local nl, operand row m) in the transposed accumulator image: lane
+// nl + 32*((m%8)/4), register 4*((m%32)/8) + m%4 of m tile m/32.
+__device__ __forceinline__ int tile_idx_t(int nl, int m) {
+  const int ml = m & 31;
+  return (m >> 5) * 1024 + ((nl & 31) + (((ml >> 2) & 1) << 5)) * 16 + ((ml >> 3) << 2) + (ml & 3);
+}
+
+template <int EPI, int MT, int NW, int KB>
+__global__ __launch_bounds__(NW * 64) void k_gemm_nf4(const GemmArgs g) {
+  constexpr int kThreads = NW * 64;
+  constexpr int kRealRows = MT * 16;
+  __shared__ float tile[NW][MT * 1024];
+  __shared__ float rscale[kRealRows + NW];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int nb = blockIdx.x / g.sp, spi = blockIdx.x - nb * g.sp;
+  const int nblk = g.kb / 4;                                   // 64-input blocks
+  const int U = g.sp * NW, u = spi * NW + wave;
+  const int b0 = (int)(((long)nblk * u) / U), b1 = (int)(((long)nblk * (u + 1)) / U);
+
+  constexpr bool kScaled = (EPI == kEpiQkv || EPI == kEpiSwiglu || EPI == kEpiArgmax);
+  constexpr int kRowsPerWave = (kRealRows + NW - 1) / NW;
+  float ssq_v[kRowsPerWave][kSsqPerLane];
+  if constexpr (kScaled) {
+    const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)g.ssq_in, (short)0, g.rows * g.nparts_in * 4, kBufferWord3);
+#pragma unroll
+    for (int j = 0; j < kRowsPerWave; ++j) {
+      const int mr = wave + NW * j;
+#pragma unroll
+      for (int i = 0; i < kSsqPerLane; ++i) {
+        const int p = lane + 64 * i;
+        const int off = (mr < g.rows && p < g.nparts_in) ? (mr * g.nparts_in + p) * 4 : 0x7FFFFFF0;
+        ssq_v[j][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sres, off, 0, 0));
+      }
+    }
+  }
+  auto row_scales = [&]() {
+    if constexpr (kScaled) {
+#pragma unroll
+      for (int j = 0; j < kRowsPerWave; ++j) {
+        float t = 0.f;
+#pragma unroll
+        for (int i = 0; i < kSsqPerLane; ++i) t += ssq_v[j][i];
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) t += __shfl_xor(t, o);
+        const int m = wave + NW * j;
+        if (lane == 0 && m < kRealRows) rscale[m] = (m < g.rows) ? 1.0f / sqrtf(t / (float)g.k + g.eps) : 0.f;
+      }
+    }
+  };
+
+  const uint32_t tl[4] = {nf4_bytes(0, 0), nf4_bytes(1, 0), nf4_bytes(2, 0), nf4_bytes(3, 0)};
+  const uint32_t th[4] = {nf4_bytes(0, 1), nf4_bytes(1, 1), nf4_bytes(2, 1), nf4_bytes(3, 1)};
+
+  f32x16 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x16){};
+
+  // Buffer range checks return zeros for blocks at or past b1 and for operand rows past
+  // 2*rows, so every batch issues all of its loads.
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const uint8_t*)g.w + (size_t)nb * nblk * kNf4BlockBytes), (short)0, b1 * kNf4BlockBytes,
+      kBufferWord3);
+  const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)g.a, (short)0, (int)act_bytes(2 * g.rows, g.k), kBufferWord3);
+  const int ext_rows = 2 * g.rows;
+  const int tsp = act_tile_pieces(ext_rows);
+  const int a_lane = ((lane >> 5) * ext_rows + (lane & 31)) * 16;
+  bool mt_ok[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) mt_ok[mt] = mt * 32 + (lane & 31) < ext_rows;
+
+  struct Stage {
+    u32x4 c[KB];
+    uint16_t s[KB];
+    u32x4 a[KB][MT][4];
+  };
+  auto load = [&](int b, Stage& st) {
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      const int bo = (b + i) * kNf4BlockBytes;
+      st.c[i] = __builtin_amdgcn_raw_buffer_load_b128(wres, bo + lane * 16, 0, kCacheStream);
+      st.s[i] = __builtin_amdgcn_raw_buffer_load_b16(wres, bo + 1024 + (lane & 31) * 2, 0, kCacheStream);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int kt = (b + i) * 4 + t;
+          const int off = (mt_ok[mt] && b + i < b1) ? a_lane + (kt * tsp + mt * 32) * 16 : 0x7FFFFFF0;
+          st.a[i][mt][t] = __builtin_amdgcn_raw_buffer_load_b128(ares, off, 0, 0);
+        }
+    }
+  };
+  auto mma = [&](const Stage& st) {
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      f32x16 part[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) part[mt] = (f32x16){};
+      const uint32_t cw[4] = {st.c[i].x, st.c[i].y, st.c[i].z, st.c[i].w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16x8 w = as_bf16x8(nf4_levels8(cw[t], tl, th));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          part[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(st.a[i][mt][t]), w, part[mt], 0, 0, 0);
+      }
+      const float sc = __uint_as_float((uint32_t)st.s[i] << 16);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mt][r] = fmaf(sc, part[mt][r], acc[mt][r]);
+    }
+  };
+  {
+    Stage s0, s1;
+    load(b0, s0);
+    __builtin_amdgcn_sched_barrier(0);
+    row_scales();
+    __builtin_amdgcn_sched_barrier(0);
+    for (int b = b0; b < b1; b += 2 * KB) {
+      load(b + KB, s1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(s0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(b + 2 * KB, s0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(s1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) tile[wave][mt * 1024 + lane * 16 + r] = acc[mt][r];
+  __syncthreads();
+  for (int e = tid; e < MT * 1024; e += kThreads) {
+    float v = tile[0][e];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v += tile[w][e];
+    tile[0][e] = v;
+  }
+  __syncthreads();
+  const float* img = tile[0];
+
+  __shared__ int last_arrival;
+  const bool split = g.sp > 1;
+  float* const pblk = g.part + (size_t)nb * g.sp * g.rows * 32;   // [split][row][32]
+  auto tval = [&](int nl, int m) { return img[tile_idx_t(nl, m)] + img[tile_idx_t(nl, g.rows + m)]; };
+  if (split) {
+    for (int e = tid; e < 32 * kRealRows; e += kThreads) {
+      const int nl = e & 31, m = e >> 5;
+      if (m < g.rows) st<true>(pblk + ((size_t)spi * g.rows + m) * 32 + nl, tval(nl, m));
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      const int old = __hip_atomic_fetch_add(g.counters + nb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last_arrival = ((old + 1) % g.sp) == 0;
+    }
+    __syncthreads();
+    if (!last_arrival) return;
+    asm volatile("" ::: "memory");
+  }
+  auto val = [&](int nl, int m) {
+    if (!split) return tval(nl, m);
+    float s = 0.f;
+    for (int q = 0; q < g.sp; ++q) s += pblk[((size_t)q * g.rows + m) * 32 + nl];
+    return s;
+  };
+  gemm_epilogue<EPI, kRealRows, kThreads>(g, nb, 0, rscale, val);
+}
+
+template <int EPI>
+static hipError_t gemm_nf4(const GemmArgs& g, hipStream_t s) {
+  if (g.rows < 1 || g.rows > 64 || g.kb % 4) return hipErrorInvalidValue;
+  const int mt = (2 * g.rows + 31) / 32;
+  const dim3 grid(g.nb * g.sp), block(256);
+  switch (mt) {
+    case 1: k_gemm_nf4<EPI, 1, 4, 2><<<grid, block, 0, s>>>(g); break;
+    case 2: k_gemm_nf4<EPI, 2, 4, 1><<<grid, block, 0, s>>>(g); break;
+    default: k_gemm_nf4<EPI, 4, 4, 1><<<grid, block, 0, s>>>(g); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_nf4(int epi, const GemmArgs& g, hipStream_t s) {
+  switch (epi) {
+    case kEpiQkv: return gemm_nf4<kEpiQkv>(g, s);
+    case kEpiResid: return gemm_nf4<kEpiResid>(g, s);
+    case kEpiSwiglu: return gemm_nf4<kEpiSwiglu>(g, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// Pack NF4 projections: block (32-row block nb, 64-input block b) of 1088 bytes from row
+// pointer tables (rows [0, N): codes, two per byte, even input in the low nibble; rows
+// [N, 2N): bf16 scales per 64 inputs).  One thread per lane of a block.
+__global__ void k_pack_nf4(uint8_t* dst, const uint8_t* const* rowptr, int N, int nb, int nblk) {
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)nb * nblk * 64) return;
+  const int lane = (int)(idx & 63);
+  const size_t blk = idx >> 6;
+  const int b = (int)(blk % nblk), n_blk = (int)(blk / nblk);
+  const int row = n_blk * kTileN + (lane & 31);
+  const uint8_t* codes = rowptr[row];
+  uint32_t out[4];
+  for (int t = 0; t < 4; ++t) {
+    const int k0 = b * kNf4Block + t * 16 + (lane >> 5) * 8;
+    uint32_t v = 0;
+    for (int j = 0; j < 4; ++j) {
+      const int ka = k0 + j, kb = k0 + j + 4;
+      const uint32_t ca = (codes[ka >> 1] >> (4 * (ka & 1))) & 0xF;
+      const uint32_t cb = (codes[kb >> 1] >> (4 * (kb & 1))) & 0xF;
+      v |= (ca | (cb << 4)) << (8 * j);
+    }
+    out[t] = v;
+  }
+  uint8_t* d = dst + blk * kNf4BlockBytes;
+  *(uint4*)(d + lane * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+  if (lane < 32) ((uint16_t*)(d + 1024))[lane] = ((const uint16_t*)rowptr[N + row])[b];
+}
+
+hipError_t launch_pack_nf4(uint8_t* dst, const uint8_t* const* rowptr, int N, int nblk, hipStream_t s) {
+  if (N % kTileN || nblk < 1) return hipErrorInvalidValue;
+  const size_t total = (size_t)(N / kTileN) * nblk * 64;
+  k_pack_nf4<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(dst, rowptr, N, N / kTileN, nblk);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------------------------
 // Batched GEMM (more than 64 rows).  The per-output arithmetic is k_gemm's: wave w of split spi
 // accumulates k tiles [kb*u/U, kb*(u+1)/U) (u = 4*spi + w, U = 4*sp) in one MFMA chain per
 // output tile, the waves' sums are added in wave order and the splits' in split order, so a

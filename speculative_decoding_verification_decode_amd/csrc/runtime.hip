@@ -59,6 +59,7 @@ struct sf_model {
   bool own_stream = false;
   int H, Q, KV, F, V, dh, nq, nkv, L;
   int nb_qkv, nb_h, nb_gu, nb_head;
+  bool nf4 = false;                // projections packed as NF4 blocks (embedding and head bf16)
   uint16_t* embed = nullptr;
   std::vector<Layer> layers;
   float* gfinal = nullptr;
@@ -145,7 +146,7 @@ static sf_status check_desc(const sf_model_desc* d) {
   if (d->head_dim != 64 && d->head_dim != 128) return fail(SF_E_ARG, "head_dim must be 64 or 128");
   if (d->n_q_heads % d->n_kv_heads) return fail(SF_E_ARG, "n_kv_heads must divide n_q_heads");
   if ((d->n_q_heads * d->head_dim) % 32) return fail(SF_E_ARG, "n_q_heads*head_dim must be a multiple of 32");
-  if (d->hidden > 4096) return fail(SF_E_ARG, "hidden must be <= 4096");
+  if (d->hidden > 6144) return fail(SF_E_ARG, "hidden must be <= 6144");
   if (!(d->rms_eps >= 0.f) || !(d->rope_base > 1.f)) return fail(SF_E_ARG, "bad rms_eps or rope_base");
   return SF_OK;
 }
@@ -163,11 +164,20 @@ static sf_status with_table(const std::vector<const uint16_t*>& tab, hipStream_t
   return SF_OK;
 }
 
-extern "C" sf_status sf_model_create(const sf_model_desc* desc, const void* const* weights, void* stream,
-                                     sf_model** out) {
+// Bytes of one projection of n outputs and k inputs as stored: bf16, or NF4 codes (half a
+// byte per weight) plus one bf16 scale per 64 inputs.
+static double proj_bytes(const sf_model* m, double n, double k) {
+  return m->nf4 ? n * k * 0.5 + n * (k / kNf4Block) * 2 : n * k * 2;
+}
+
+static sf_status create_model(const sf_model_desc* desc, const void* const* weights, void* stream,
+                              sf_model** out, bool nf4) {
   if (sf_status st = check_desc(desc)) return st;
   if (!weights || !out) return fail(SF_E_ARG, "weights or out is NULL");
+  if (nf4 && (desc->hidden % kNf4Block || desc->ffn % kNf4Block || (desc->n_q_heads * desc->head_dim) % kNf4Block))
+    return fail(SF_E_ARG, "NF4 needs hidden, ffn and n_q_heads*head_dim to be multiples of 64");
   sf_model* m = new sf_model();
+  m->nf4 = nf4;
   m->d = *desc;
   const sf_model_desc& d = *desc;
   m->H = d.hidden; m->nq = d.n_q_heads; m->nkv = d.n_kv_heads; m->dh = d.head_dim;
@@ -179,7 +189,7 @@ extern "C" sf_status sf_model_create(const sf_model_desc* desc, const void* cons
   m->nb_head = m->V / kTileN;
 
   // Count and validate the weight table.
-  const int per_layer = d.qkv_bias ? 12 : 9;
+  const int per_layer = (d.qkv_bias ? 12 : 9) + (nf4 ? 7 : 0);   // NF4: codes + scales per projection
   const int n_tensors = 1 + d.n_layers * per_layer + (d.has_head ? 1 + (d.tied_head ? 0 : 1) : 0);
   for (int i = 0; i < n_tensors; ++i)
     if (!weights[i]) { delete m; return fail(SF_E_ARG, "weight pointer " + std::to_string(i) + " is NULL"); }
@@ -200,6 +210,22 @@ extern "C" sf_status sf_model_create(const sf_model_desc* desc, const void* cons
   hipStream_t s = m->stream;
   const int H = m->H, Q = m->Q, KV = m->KV, F = m->F, V = m->V, dh = m->dh, half = dh / 2;
   auto W = [&](int i) { return (const uint16_t*)weights[i]; };
+  // A projection's source: bf16 rows, or NF4 codes (two per byte) and bf16 scales per 64.
+  struct Proj {
+    const uint16_t* w = nullptr;
+    const uint8_t* codes = nullptr;
+    const uint16_t* scales = nullptr;
+  };
+  auto P = [&](int& i) {
+    Proj p;
+    if (nf4) {
+      p.codes = (const uint8_t*)weights[i++];
+      p.scales = (const uint16_t*)weights[i++];
+    } else {
+      p.w = (const uint16_t*)weights[i++];
+    }
+    return p;
+  };
 
   auto dalloc = [&](void** p, size_t bytes) -> sf_status {
     hipError_t e = m->mem.alloc(p, bytes);
@@ -211,6 +237,27 @@ extern "C" sf_status sf_model_create(const sf_model_desc* desc, const void* cons
     sf_status st_ = (x);                 \
     if (st_ != SF_OK) return cleanup(st_); \
   } while (0)
+  // Pack projection rows (row n of the packed matrix = source row src_row[n] of proj[n]) with
+  // k inputs into library-owned tiles.
+  auto pack = [&](uint4** dst, const std::vector<const Proj*>& proj, const std::vector<int>& src_row, int k) -> sf_status {
+    const int N = (int)src_row.size();
+    if (!nf4) {
+      std::vector<const uint16_t*> rows(N);
+      for (int n = 0; n < N; ++n) rows[n] = proj[n]->w + (size_t)src_row[n] * k;
+      if (sf_status st = dalloc((void**)dst, (size_t)N * k * 2)) return st;
+      return with_table(rows, s, [&](const uint16_t* const* t) { return launch_pack(*dst, t, N / kTileN, k / kTileK, s); });
+    }
+    // NF4: a table of 2N row addresses, codes then scales, handed over as one pointer array.
+    std::vector<const uint16_t*> rows(2 * N);
+    for (int n = 0; n < N; ++n) {
+      rows[n] = (const uint16_t*)(proj[n]->codes + (size_t)src_row[n] * (k / 2));
+      rows[N + n] = proj[n]->scales + (size_t)src_row[n] * (k / kNf4Block);
+    }
+    if (sf_status st = dalloc((void**)dst, (size_t)(N / kTileN) * (k / kNf4Block) * kNf4BlockBytes)) return st;
+    return with_table(rows, s, [&](const uint16_t* const* t) {
+      return launch_pack_nf4((uint8_t*)*dst, (const uint8_t* const*)t, N, k / kNf4Block, s);
+    });
+  };
 
   TRY(dalloc((void**)&m->embed, (size_t)V * H * 2));
   {
@@ -229,59 +276,57 @@ extern "C" sf_status sf_model_create(const sf_model_desc* desc, const void* cons
   for (int l = 0; l < d.n_layers; ++l) {
     Layer& Ly = m->layers[l];
     const uint16_t* ln1 = W(idx++);
-    const uint16_t* wq = W(idx++);
+    const Proj wq = P(idx);
     const uint16_t* bq = d.qkv_bias ? W(idx++) : nullptr;
-    const uint16_t* wk = W(idx++);
+    const Proj wk = P(idx);
     const uint16_t* bk = d.qkv_bias ? W(idx++) : nullptr;
-    const uint16_t* wv = W(idx++);
+    const Proj wv = P(idx);
     const uint16_t* bv = d.qkv_bias ? W(idx++) : nullptr;
-    const uint16_t* wo = W(idx++);
+    const Proj wo = P(idx);
     const uint16_t* ln2 = W(idx++);
-    const uint16_t* wg = W(idx++);
-    const uint16_t* wu = W(idx++);
-    const uint16_t* wd = W(idx++);
+    const Proj wg = P(idx);
+    const Proj wu = P(idx);
+    const Proj wd = P(idx);
 
     // QKV rows: 32-row block -> (section, head, dims i0..i0+15 and their RoPE partners
     // i0+dh/2..i0+dh/2+15), so each rotated pair lands in one block.
     const int N = Q + 2 * KV, bph = dh / 32;
-    std::vector<const uint16_t*> rows(N), bias(N);
+    std::vector<const Proj*> pq(N);
+    std::vector<int> rq(N);
+    std::vector<const uint16_t*> bias(N);
     for (int n = 0; n < N; ++n) {
       const int nb = n / 32, nl = n % 32;
       const int qb = m->nq * bph, kvb = m->nkv * bph;
       int head, blk;
-      const uint16_t *wsrc, *bsrc;
-      if (nb < qb) { head = nb / bph; blk = nb % bph; wsrc = wq; bsrc = bq; }
-      else if (nb < qb + kvb) { head = (nb - qb) / bph; blk = (nb - qb) % bph; wsrc = wk; bsrc = bk; }
-      else { head = (nb - qb - kvb) / bph; blk = (nb - qb - kvb) % bph; wsrc = wv; bsrc = bv; }
+      const Proj* wsrc;
+      const uint16_t* bsrc;
+      if (nb < qb) { head = nb / bph; blk = nb % bph; wsrc = &wq; bsrc = bq; }
+      else if (nb < qb + kvb) { head = (nb - qb) / bph; blk = (nb - qb) % bph; wsrc = &wk; bsrc = bk; }
+      else { head = (nb - qb - kvb) / bph; blk = (nb - qb - kvb) % bph; wsrc = &wv; bsrc = bv; }
       const int dim = blk * 16 + (nl % 16) + (nl >= 16 ? half : 0);
       const int r = head * dh + dim;
-      rows[n] = wsrc + (size_t)r * H;
+      pq[n] = wsrc;
+      rq[n] = r;
       bias[n] = bsrc ? bsrc + r : nullptr;
     }
-    TRY(dalloc((void**)&Ly.wqkv, (size_t)N * H * 2));
-    TRY(with_table(rows, s, [&](const uint16_t* const* t) { return launch_pack(Ly.wqkv, t, N / kTileN, H / kTileK, s); }));
+    TRY(pack(&Ly.wqkv, pq, rq, H));
     TRY(dalloc((void**)&Ly.bqkv, (size_t)N * 4));
     TRY(with_table(bias, s, [&](const uint16_t* const* t) { return launch_gather_f32(Ly.bqkv, t, N, s); }));
 
-    std::vector<const uint16_t*> ro(H);
-    for (int n = 0; n < H; ++n) ro[n] = wo + (size_t)n * Q;
-    TRY(dalloc((void**)&Ly.wo, (size_t)H * Q * 2));
-    TRY(with_table(ro, s, [&](const uint16_t* const* t) { return launch_pack(Ly.wo, t, H / kTileN, Q / kTileK, s); }));
+    std::vector<int> ident(H);
+    for (int n = 0; n < H; ++n) ident[n] = n;
+    TRY(pack(&Ly.wo, std::vector<const Proj*>(H, &wo), ident, Q));
 
     // gate/up rows: 32-row block nb -> gate rows 16nb..16nb+15 then up rows 16nb..16nb+15.
-    std::vector<const uint16_t*> rgu(2 * F);
+    std::vector<const Proj*> pgu(2 * F);
+    std::vector<int> rgu(2 * F);
     for (int n = 0; n < 2 * F; ++n) {
       const int nb = n / 32, nl = n % 32;
-      const int j = nb * 16 + (nl % 16);
-      rgu[n] = (nl < 16 ? wg : wu) + (size_t)j * H;
+      pgu[n] = nl < 16 ? &wg : &wu;
+      rgu[n] = nb * 16 + (nl % 16);
     }
-    TRY(dalloc((void**)&Ly.wgu, (size_t)2 * F * H * 2));
-    TRY(with_table(rgu, s, [&](const uint16_t* const* t) { return launch_pack(Ly.wgu, t, 2 * F / kTileN, H / kTileK, s); }));
-
-    std::vector<const uint16_t*> rd(H);
-    for (int n = 0; n < H; ++n) rd[n] = wd + (size_t)n * F;
-    TRY(dalloc((void**)&Ly.wd, (size_t)H * F * 2));
-    TRY(with_table(rd, s, [&](const uint16_t* const* t) { return launch_pack(Ly.wd, t, H / kTileN, F / kTileK, s); }));
+    TRY(pack(&Ly.wgu, pgu, rgu, H));
+    TRY(pack(&Ly.wd, std::vector<const Proj*>(H, &wd), ident, F));
 
     std::vector<const uint16_t*> g1(H), g2(H);
     for (int n = 0; n < H; ++n) { g1[n] = ln1 + n; g2[n] = ln2 + n; }
@@ -306,6 +351,25 @@ extern "C" sf_status sf_model_create(const sf_model_desc* desc, const void* cons
   return SF_OK;
 }
 
+extern "C" sf_status sf_model_create(const sf_model_desc* desc, const void* const* weights, void* stream,
+                                     sf_model** out) {
+  return create_model(desc, weights, stream, out, false);
+}
+
+extern "C" sf_status sf_model_create_nf4(const sf_model_desc* desc, const void* const* weights, void* stream,
+                                         sf_model** out) {
+  return create_model(desc, weights, stream, out, true);
+}
+
+extern "C" sf_status sf_nf4_levels(float* out) {
+  if (!out) return fail(SF_E_ARG, "out is NULL");
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t u = (uint32_t)kNf4Bits[i] << 16;
+    memcpy(&out[i], &u, 4);
+  }
+  return SF_OK;
+}
+
 extern "C" sf_status sf_model_free(sf_model* m) {
   if (!m) return fail(SF_E_ARG, "model is NULL");
   (void)hipStreamSynchronize(m->stream);
@@ -326,6 +390,7 @@ static hipError_t run_gemm(const sf_cache* c, int kind, int layer, int epi, Gemm
     const int slot = layer * 3 + (kind == kGQkv ? 0 : kind == kGO ? 1 : 2);
     g.counters = c->cnt + (size_t)slot * c->cnt_stride;
   }
+  if (c->m->nf4 && kind != kGHead) return launch_gemm_nf4(epi, g, s);
   return launch_gemm(epi, g, s);
 }
 
@@ -448,6 +513,8 @@ extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacit
   if (n_seqs < 1 || n_seqs > kMaxSeqs || n_seqs * (k_max + 1) > kMaxRows)
     return fail(SF_E_ARG, "n_seqs must be in 1..64 and n_seqs*(k_max+1) in 1..512");
   if (capacity < k_max + 1 || capacity > kMaxCapacity) return fail(SF_E_ARG, "capacity must be in k_max+1..16384");
+  if (m->nf4 && n_seqs * (k_max + 1) > kNf4MaxRows)
+    return fail(SF_E_ARG, "an NF4 model runs passes of at most 64 rows: n_seqs*(k_max+1) <= 64");
   sf_cache* c = new sf_cache();
   c->m = m; c->B = n_seqs; c->cap = capacity; c->kmax = k_max; c->T = k_max + 1;
   c->nchunk = attention_spans(capacity);
@@ -484,6 +551,7 @@ extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacit
   // Rows of the largest pass this cache runs: a verify (n_seqs x (k_max+1)) or a prefill chunk.
   c->pchunk = kPrefillChunk;
   if (const char* v = getenv("SF_PREFILL_CHUNK")) c->pchunk = std::min(std::max(atoi(v), 1), kMaxRows);
+  if (m->nf4) c->pchunk = std::min(c->pchunk, kNf4MaxRows);
   const size_t R = std::max(n_seqs * (k_max + 1), c->pchunk);
   const size_t pool = c->layer_stride * m->L * 2;
   TRY(dalloc((void**)&c->kpool, pool));
@@ -969,8 +1037,8 @@ extern "C" sf_status sf_time_kernel(sf_cache* c, int32_t kernel, int32_t iters, 
     *avg_us = ms * 1000.f / iters;
     if (bytes) {
       const double kvdim = (double)m->KV;
-      double w = (double)m->L * ((double)(m->Q + 2 * m->KV) * m->H + (double)m->H * m->Q + 2.0 * m->F * m->H +
-                                 (double)m->H * m->F) * 2;
+      double w = (double)m->L * (proj_bytes(m, m->Q + 2 * m->KV, m->H) + proj_bytes(m, m->H, m->Q) +
+                                 proj_bytes(m, 2.0 * m->F, m->H) + proj_bytes(m, m->H, m->F));
       w += (double)m->L * ((m->Q + 2 * m->KV) + 2.0 * m->H) * 2;  // q/k/v biases and norm gains (bf16)
       if (m->d.has_head) w += ((double)m->V * m->H + m->H) * 2;
       w += (double)rows * m->H * 2;                                  // embedding rows
@@ -994,7 +1062,7 @@ extern "C" sf_status sf_time_kernel(sf_cache* c, int32_t kernel, int32_t iters, 
       case SF_KERNEL_QKV:
         g.w = Ly.wqkv; g.a = c->a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_qkv; g.nw = c->nw_qkv;
         g.bias = Ly.bqkv; g.q = c->q; g.kc = kc; g.vc = vc; g.sp = c->sp_qkv; g.n_out = m->Q + 2 * m->KV;
-        by = (double)(m->Q + 2 * m->KV) * m->H * 2 + (double)rows * (m->H * 4 + m->Q * 4 + 2 * m->KV * 2);
+        by = proj_bytes(m, m->Q + 2 * m->KV, m->H) + (double)rows * (m->H * 4 + m->Q * 4 + 2 * m->KV * 2);
         return run_gemm(c, kGQkv, l, kEpiQkv, g, s);
       case SF_KERNEL_ATTENTION: {
         AttnArgs aa{};
@@ -1008,17 +1076,17 @@ extern "C" sf_status sf_time_kernel(sf_cache* c, int32_t kernel, int32_t iters, 
       case SF_KERNEL_OPROJ:
         g.w = Ly.wo; g.a = c->a_o; g.k = m->Q; g.kb = m->Q / kTileK; g.nb = m->nb_h; g.nw = c->nw_o;
         g.x = c->x; g.a_next = c->a_h; g.gain_next = Ly.g2; g.ssq_out = c->ssq; g.n_out = m->H; g.sp = c->sp_o;
-        by = (double)m->H * m->Q * 2 + (double)rows * (m->Q * 4 + m->H * (4 + 4 + 4));
+        by = proj_bytes(m, m->H, m->Q) + (double)rows * (m->Q * 4 + m->H * (4 + 4 + 4));
         return run_gemm(c, kGO, l, kEpiResid, g, s);
       case SF_KERNEL_GATEUP:
         g.w = Ly.wgu; g.a = c->a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_gu; g.nw = c->nw_gu;
         g.h = c->a_f; g.ffn = m->F; g.sp = 1;
-        by = (double)2 * m->F * m->H * 2 + (double)rows * (m->H * 4 + m->F * 4);
+        by = proj_bytes(m, 2.0 * m->F, m->H) + (double)rows * (m->H * 4 + m->F * 4);
         return run_gemm(c, kGGateUp, l, kEpiSwiglu, g, s);
       case SF_KERNEL_DOWN:
         g.w = Ly.wd; g.a = c->a_f; g.k = m->F; g.kb = m->F / kTileK; g.nb = m->nb_h; g.nw = c->nw_d;
         g.x = c->x; g.a_next = c->a_h; g.gain_next = Ly.g1; g.ssq_out = c->ssq; g.n_out = m->H; g.sp = c->sp_d;
-        by = (double)m->H * m->F * 2 + (double)rows * (m->F * 4 + m->H * (4 + 4 + 4));
+        by = proj_bytes(m, m->H, m->F) + (double)rows * (m->F * 4 + m->H * (4 + 4 + 4));
         return run_gemm(c, kGDown, l, kEpiResid, g, s);
       default:
         g.w = m->head; g.a = c->a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_head; g.nw = c->nw_head;

@@ -44,6 +44,15 @@ struct Stage {
 
 enum Epi { kEpiQkv = 0, kEpiResid = 1, kEpiSwiglu = 2, kEpiArgmax = 3 };
 
+// NF4 projections: the 16 levels as bf16 bits (quantiles of the standard normal distribution
+// with an exact zero, normalised to [-1, 1]: the 4-bit NormalFloat table, each level rounded
+// to bf16), 64-input blocks, and the packed block of 1 KB of codes + 32 bf16 row scales.
+constexpr uint16_t kNf4Bits[16] = {0xBF80, 0xBF32, 0xBF06, 0xBECA, 0xBE92, 0xBE3D, 0xBDBA, 0x0000,
+                                   0x3DA3, 0x3E25, 0x3E7C, 0x3EAD, 0x3EE2, 0x3F10, 0x3F39, 0x3F80};
+constexpr int kNf4Block = 64;
+constexpr int kNf4BlockBytes = 1024 + 64;
+constexpr int kNf4MaxRows = 64;               // rows per pass of the NF4 GEMM (up to four m tiles)
+
 struct GemmArgs {
   const uint4* w;          // packed weight tiles [nb][kb][64 lanes] x 16 B (32 rows x 16 k per tile)
   const uint16_t* a;       // bf16 activations [2*rows][k]: hi parts, then lo parts
@@ -138,6 +147,8 @@ hipError_t launch_embed(const EmbedArgs& e, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int dh, int B, hipStream_t s);
 int attention_spans(int cap);
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t s);
+hipError_t launch_gemm_nf4(int epi, const GemmArgs& g, hipStream_t s);
+hipError_t launch_pack_nf4(uint8_t* dst, const uint8_t* const* rowptr, int N, int nblk, hipStream_t s);
 hipError_t launch_pack(uint4* dst, const uint16_t* const* rowptr, int nb, int kb, hipStream_t s);
 hipError_t launch_gather_f32(float* dst, const uint16_t* const* eltptr, int n, hipStream_t s);
 hipError_t launch_rope_table(float2* rope, int cap, int half, double base, hipStream_t s);

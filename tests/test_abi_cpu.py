@@ -109,3 +109,17 @@ def test_null_handles_are_rejected():
 def test_weight_order_matches_generator_names():
     for shape in (synth.TINY, synth.QWEN05B, synth.QWEN7B, synth.QWEN7B_HALF):
         assert sfb.weight_order(sfb.desc_from_shape(shape)) == synth.tensor_names(shape)
+
+
+def test_nf4_table_matches_oracle():
+    """The library's NF4 level table (what the GEMM decodes codes to) equals the oracle's
+    table built from the format's definition."""
+    from oracle import nf4
+    assert np.array_equal(sfb.sf_nf4_levels().astype(np.float64), nf4.table().numpy())
+
+
+def test_nf4_weight_order_pairs_projections():
+    d = sfb.desc_from_shape(synth.TINY)
+    names = sfb.weight_order(d, nf4=True)
+    assert len(names) == len(sfb.weight_order(d)) + 7 * d.n_layers
+    assert names[2:4] == ["l0.wq", "l0.wq"]
