@@ -59,6 +59,7 @@ def main():
     ap.add_argument("--no-batched", action="store_true", help="skip the 32-sequence batched verify line")
     ap.add_argument("--no-round", action="store_true", help="skip the device-resident draft+verify round line")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill (time to first token) line")
+    ap.add_argument("--no-nf4", action="store_true", help="skip the NF4 14B-shape verify line")
     ap.add_argument("--kernel-iters", type=int, default=56)
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="also run plain device copies of 1 GiB, so HBM byte counters can be scaled")
@@ -329,6 +330,63 @@ def main():
         sfb.sf_model_free(dmodel)
         log(f"round: {spec_round}")
 
+    # NF4 verify at the Qwen2.5-14B shape (48 layers, hidden 5120, 40/8 heads, FFN 13824,
+    # vocab 152064): projections in 4-bit NormalFloat (codes uniform over the levels, per-64
+    # bf16 scales), embedding and head bf16; one sequence, K=8, synthetic KV at context 512.
+    nf4_line = None
+    if not args.no_nf4:
+        S14 = synth.QWEN14B
+        s14 = synth.seeds(8)
+        t0 = time.time()
+        w14 = synth.nf4_model_weights(S14, s14["weights"])
+        log(f"nf4 14b weights generated in {time.time() - t0:.1f}s")
+        d14 = sfb.desc_from_shape(S14)
+        t14, p14 = sfb.upload_weights(w14, d14)
+        del w14
+        torch.cuda.synchronize()
+        m14 = sfb.sf_model_create_nf4(d14, p14, stream.cuda_stream)
+        del t14, p14
+        torch.cuda.synchronize()
+        ctx14 = 512
+        c14 = sfb.sf_cache_alloc(m14, 1, ctx14 + 64, K)
+        kb14, vb14 = synth.synthetic_kv(S14, ctx14, s14["kv"])
+        kd14 = torch.from_numpy(kb14.view(np.int16)).cuda()
+        vd14 = torch.from_numpy(vb14.view(np.int16)).cuda()
+        sfb.sf_kv_write(c14, 0, kd14, vd14, ctx14, ctx14)
+        del kd14, vd14, kb14, vb14
+        sfb.sf_set_next(c14, 0, int(hist[ctx14]))
+        d14v = torch.from_numpy(np.zeros(K, dtype=np.int32)).cuda()
+        k14 = torch.tensor([K], dtype=torch.int32, device="cuda")
+        for _ in range(3):
+            sfb.sf_verify_device(c14, d14v, k14, sfb.SF_NO_COMMIT)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        n14 = max(5, args.steps)
+        e0.record(stream)
+        for _ in range(n14):
+            sfb.sf_verify_device(c14, d14v, k14, sfb.SF_NO_COMMIT)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms14 = e0.elapsed_time(e1) / n14
+        us_v, by_v = sfb.sf_time_kernel(c14, sfb.SF_KERNEL_VERIFY, 5)
+        k14n = {}
+        for kid, nm in names.items():
+            us, by = sfb.sf_time_kernel(c14, kid, args.kernel_iters)
+            k14n[nm] = {"us": round(us, 3), "bytes": int(by), "GBps": round(by / us / 1e3, 1)}
+        bf16_bytes = (S14.param_count() - S14.vocab * S14.hidden) * 2.0
+        nf4_line = {"model": "qwen2.5-14b-shape, NF4 projections (4-bit codes + bf16 scale per 64), bf16 head",
+                    "context": ctx14, "K": K, "ms": round(ms14, 4),
+                    "verify_tokens_per_s": round((K + 1) / ms14 * 1e3, 1),
+                    "alg_bytes": int(by_v), "alg_GBps": round(by_v / (ms14 * 1e-3) / 1e9, 1),
+                    "frac_peak": round(by_v / (ms14 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "bytes_vs_bf16": round(bf16_bytes / by_v, 3),
+                    "kernels": k14n}
+        sfb.sf_cache_free(c14)
+        sfb.sf_model_free(m14)
+        torch.cuda.synchronize()
+        log(f"nf4 14b: {nf4_line}")
+
     cpu = None
     if not args.no_cpu:
         import oracle
@@ -377,6 +435,7 @@ def main():
         "device_round_0.5b_drafter": spec_round,
         "prefill_ttft": prefill,
         "snapshot_rollback_ctx512": snapshot_rb,
+        "nf4_14b_verify_ctx512": nf4_line,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

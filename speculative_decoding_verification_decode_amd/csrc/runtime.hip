@@ -436,7 +436,8 @@ static hipError_t enqueue_forward(sf_cache* c, const Run& r) {
     if ((e = run_gemm(c, kGQkv, l, kEpiQkv, g, s)) != hipSuccess) return e;
 
     aa.kc = kc; aa.vc = vc;
-    if (c->prefetch_o && c->nchunk * m->nkv >= kPrefetchGroups) { aa.pf_w = Ly.wo; aa.pf_nb = m->nb_h; aa.pf_kb = m->Q / kTileK; aa.pf_sp = c->sp_o; }
+    // The warm-up walks the bf16 tile layout of the O weights, so NF4 blocks never take it.
+    if (c->prefetch_o && !m->nf4 && c->nchunk * m->nkv >= kPrefetchGroups) { aa.pf_w = Ly.wo; aa.pf_nb = m->nb_h; aa.pf_kb = m->Q / kTileK; aa.pf_sp = c->sp_o; }
     if ((e = launch_attention(aa, m->dh, r.B, s)) != hipSuccess) return e;
 
     g = base;
@@ -533,6 +534,7 @@ extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacit
   c->sp_head = 1;
   if (const char* v = getenv("SF_KH")) c->kh = (atoi(v) == 8) ? 8 : 4;
   if (const char* v = getenv("SF_PREFETCH")) c->prefetch_o = atoi(v) != 0;
+  if (m->nf4) c->prefetch_o = false;   // its address walk assumes bf16 tiles (2 bytes per weight)
 
   hipStream_t s = m->stream;
   auto bail = [&](sf_status st) { cache_release(c); return st; };

@@ -74,8 +74,11 @@ def test_nf4_tiny_prefill_and_lockstep_verify():
 
 
 def test_nf4_14b_shape_two_layers_verify_matches_oracle():
+    """Capacity 576 gives 9 attention spans x 8 KV heads, the size at which bf16 caches warm
+    the O weights into L2 during attention; NF4 caches must not take that path (it walks the
+    bf16 tile layout, which is 3.8 times larger than the NF4 blocks)."""
     sfb = need_gpu()
-    S, K, CAP = synth.QWEN14B_2L, 8, 256
+    S, K, CAP = synth.QWEN14B_2L, 8, 576
     say("[nf4-14b-2l] weights")
     w = synth.nf4_model_weights(S, synth.seeds(8)["weights"])
     eng = sfb.Engine(S, w, n_seqs=1, capacity=CAP, k_max=K)
