@@ -96,7 +96,7 @@ struct sf_cache {
   int kh = 4;                      // GEMM: weight tiles per pipelined batch (one-tile row counts)
   int* cnt = nullptr;              // k-split arrival counters [layer][QKV, O, down][block]
   int cnt_stride = 0;
-  bool prefetch_o = true;   // warm the O projection's weights into L2 during attention
+  bool prefetch_o = true;   // warm the O projection's weights into L2 during attention (large O only)
   hipGraphExec_t gx_verify = nullptr, gx_draft = nullptr;
   uint16_t *snap_k = nullptr, *snap_v = nullptr;   // state snapshot: K/V rows [len, len+T)
   int32_t *snap_len = nullptr, *snap_next = nullptr;
@@ -110,7 +110,9 @@ struct sf_cache {
 // ------------------------------------------------------------------------------------------
 // Waves per GEMM workgroup: four, so that up to five workgroups share a compute unit (the
 // kernel keeps about 100 registers per lane with 4-tile batches) and one streams while
-// another finishes.  8 is kept for experiments (SF_NW_*).
+// another finishes.  Four is also the batched kernel's k split, which a row's result must
+// share at every row count (bitwise batch invariance), so eight (SF_NW_*) is for
+// experiments only.
 static int choose_nw(int nb, int kb, const char* env) {
   (void)nb;
   (void)kb;
@@ -123,13 +125,15 @@ static int choose_nw(int nb, int kb, const char* env) {
 }
 
 // Workgroups per n block.  Narrow projections (O, down: 112 blocks at 7B) have too few
-// 32-row blocks to occupy the GPU, so their k range is split over about 256/nb workgroups
-// (each wave keeping at least four 16-k tiles); the last to finish adds the partial sums.
-// Measured at the 7B verify shape: down 35.9 us with 2 splits vs 44.9 with 4, O 11.6 vs 12.6,
-// QKV (144 blocks) best unsplit.
+// 32-row blocks to occupy the GPU, so their k range is split over about 256/nb workgroups,
+// at most 4, each wave keeping at least eight 16-k tiles; the last to finish adds the
+// partial sums.  Measured at the 7B verify shape: down 35.9 us with 2 splits vs 44.9 with 4,
+// O 11.6 vs 12.6, QKV (144 blocks) best unsplit; at the 0.5B draft shape (k ranges of 56
+// tiles) an unsplit QKV and O and a down split 4 ways (not 8) were each 24-30 us faster per
+// step.  SF_SP_* override.
 static int choose_sp(int nb, int kb, int nw, const char* env) {
   int sp = std::max(1, 256 / nb);
-  sp = std::max(1, std::min(sp, kb / (nw * 4)));
+  sp = std::max(1, std::min({sp, kb / (nw * 8), 4}));
   if (const char* v = getenv(env)) {
     int o = atoi(v);
     if (o >= 1) sp = o;
@@ -533,6 +537,9 @@ extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacit
   c->sp_d = choose_sp(m->nb_h, m->F / kTileK, c->nw_d, "SF_SP_D");
   c->sp_head = 1;
   if (const char* v = getenv("SF_KH")) c->kh = (atoi(v) == 8) ? 8 : 4;
+  // The warm-up pays for O weights that do not already stay in L2 between uses (25.7 MB at
+  // 7B); at the 0.5B shape (1.6 MB) it measured 35 us slower per draft step.
+  c->prefetch_o = (double)m->H * m->Q * 2 >= 8.0 * (1 << 20);
   if (const char* v = getenv("SF_PREFETCH")) c->prefetch_o = atoi(v) != 0;
   if (m->nf4) c->prefetch_o = false;   // its address walk assumes bf16 tiles (2 bytes per weight)
 
