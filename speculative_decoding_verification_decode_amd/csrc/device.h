@@ -98,21 +98,31 @@ __device__ __forceinline__ int tile_idx(int nl, int m) {
 // ----------------------------------------------------------------------------------------------
 // Attention, phase 1 (MFMA).  Workgroup (x0, kv head, sequence x row group) takes up to 64
 // query rows of one KV head (slot-major: row = slot*G + head-in-group, G = nq/nkv) against
-// spans x0, x0 + xstep, ... (positions [x*kSpan, (x+1)*kSpan)), each in chunks of 64
+// spans x0, x0 + xstep, ... (span_first(x) .. + span_chunks(x) chunks), each in chunks of 64
 // position-aligned keys, writing one partial per span; each chunk's K/V loads are issued
-// while the previous chunk is computed.  One chunk per span:
-// four-chunk spans (smaller partials, fewer workgroups) measured 0.27 ms slower per 7B verify
-// at contexts 512 and 2048 (each chunk is about 3 us of latency-bound work) and only 2% faster
-// at 8192.
+// while the previous chunk is computed.  Spans are one chunk below position 2048 and four
+// chunks from there on: every span's partial costs about as many bytes as its K/V, so long
+// contexts (and batches of them) write four times fewer partials and merge fewer spans,
+// while short contexts, where each chunk is about 3 us of latency-bound work, keep the
+// short critical path (four-chunk spans everywhere measured 0.27 ms slower per 7B verify at
+// contexts 512 and 2048).
 // Wave w owns query rows 16w..16w+15: S = Q K^T and O += P V are 16x16x32 bf16 MFMAs, the
 // softmax is the usual running (max, sum) per row in base 2.  K is staged in LDS row-major,
 // V transposed, P goes through LDS to change from the MFMA output layout to the input one.
 // Q and P enter the MFMAs as bf16 hi + lo pairs (two MFMAs each); K and V are the bf16 cache.
 // Spans are fixed by absolute position, so a row's result does not depend on the length.
-constexpr int kSpanChunks = 1;
-constexpr int kSpan = kSpanChunks * kChunk;
+constexpr int kSpanSplit = 2048;                      // first position of the four-chunk spans
+constexpr int kShortSpans = kSpanSplit / kChunk;      // one-chunk spans below it
+constexpr int kLongChunks = 4;
+__host__ __device__ constexpr int span_first(int x) {
+  return x < kShortSpans ? x * kChunk : kSpanSplit + (x - kShortSpans) * kLongChunks * kChunk;
+}
+__host__ __device__ constexpr int span_chunks(int x) { return x < kShortSpans ? 1 : kLongChunks; }
+__host__ __device__ constexpr int span_of(int p) {
+  return p < kSpanSplit ? p / kChunk : kShortSpans + (p - kSpanSplit) / (kLongChunks * kChunk);
+}
 // Spans a row can need at the largest cache capacity, held 64 per register slot in the merge.
-constexpr int kSpanSlots = (kMaxCapacity / kSpan + 63) / 64;
+constexpr int kSpanSlots = (span_of(kMaxCapacity - 1) + 1 + 63) / 64;
 
 template <int DH, bool kCoh>
 __device__ void attn_spans(const AttnArgs& a, int x0, int xstep, int kvh, int b, int rg) {
@@ -126,7 +136,7 @@ __device__ void attn_spans(const AttnArgs& a, int x0, int xstep, int kvh, int b,
   const int G = a.nq / a.nkv, nrows = a.T * G;
   const int L = a.len[b];
   const int plast = L + a.T - 1;
-  int x = x0, span0 = x * kSpan;
+  int x = x0, span0 = span_first(x);
   if (span0 > plast) return;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -210,7 +220,8 @@ __device__ void attn_spans(const AttnArgs& a, int x0, int xstep, int kvh, int b,
 #pragma unroll
     for (int r = 0; r < 4; ++r) { mrun[r] = -INFINITY; lrun[r] = 0.f; }
 
-    for (int ci = 0; ci < kSpanChunks; ++ci) {
+    const int nch = span_chunks(x);
+    for (int ci = 0; ci < nch; ++ci) {
       const int c0 = span0 + ci * kChunk;
       if (c0 > plast) break;
       __syncthreads();   // every wave is done with the previous chunk's K and V
@@ -229,7 +240,7 @@ __device__ void attn_spans(const AttnArgs& a, int x0, int xstep, int kvh, int b,
       // The next chunk's K/V loads (this span's next chunk, else the first chunk of this
       // workgroup's next span) go out now and land while this chunk is computed.
       {
-        const int nc = (ci + 1 < kSpanChunks && c0 + kChunk <= plast) ? c0 + kChunk : (x + xstep) * kSpan;
+        const int nc = (ci + 1 < nch && c0 + kChunk <= plast) ? c0 + kChunk : span_first(x + xstep);
         if (nc <= plast) load_kv(nc);
       }
       __syncthreads();
@@ -315,12 +326,12 @@ __device__ void attn_spans(const AttnArgs& a, int x0, int xstep, int kvh, int b,
       }
     }
     x += xstep;
-    span0 = x * kSpan;
+    span0 = span_first(x);
     if (span0 > plast) break;
   }
 }
 
-// Attention, phase 2: one wave per (row, q head); merge spans 0..p/kSpan in order.  Span
+// Attention, phase 2: one wave per (row, q head); merge spans 0..span_of(p) in order.  Span
 // maxima and sums are spread over lanes; the weighted sum of partial outputs runs over
 // spans in increasing order.
 template <int DH, bool kCoh>
@@ -330,7 +341,7 @@ __device__ void combine_pair(const AttnArgs& a, int r, int h) {
   const int b = r / a.T, slot = r - b * a.T;
   const int kvh = h / G, qr = slot * G + (h - kvh * G);
   const int p = a.len[b] + slot;
-  const int np = p / kSpan + 1;
+  const int np = span_of(p) + 1;
   const size_t rstride = DH + 2;
   const size_t sstride = (size_t)nrows * rstride;
   const float* base = a.part + ((size_t)b * a.nkv + kvh) * a.nchunk * sstride + (size_t)qr * rstride;

@@ -937,7 +937,7 @@ hipError_t launch_attention(const AttnArgs& a, int dh, int B, hipStream_t s) {
   return hipGetLastError();
 }
 
-int attention_spans(int cap) { return (cap + kSpan - 1) / kSpan; }
+int attention_spans(int cap) { return span_of(cap - 1) + 1; }
 
 // ----------------------------------------------------------------------------------------------
 // Accept: per sequence, merge the LM head's per-block (max, index) pairs into the greedy
