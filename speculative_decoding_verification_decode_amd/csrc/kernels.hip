@@ -318,42 +318,15 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
 // NF4 skinny GEMM: Y[m][n] = sum_b scale[n][b] * sum_{k in block b} level[code[n][k]] * A[m][k]
 // for m < rows <= 64, blocks of 64 inputs.  Packed weights, per 32-row block and 64-input
 // block, 1088 bytes: 1 KB of codes (lane l: row l%32, inputs 8*(l/32) .. +8 of each of the
-// four 16-input k tiles, one dword per tile whose byte j holds the codes of inputs j and j+4)
-// then the 32 rows' scales as bf16.  A wave turns a tile's dword into the 8 bf16 levels of a
-// v_mfma_f32_32x32x16_bf16 operand with byte permutes (no memory lookups), runs the block's
-// four k tiles into a block accumulator with the activations as the A operand (so a lane's
-// 16 outputs share its weight row and its block scale), and adds scale * block accumulator.
+// four 16-input k tiles, one dword per tile holding the 8 codes two per byte, even input in
+// the low nibble) then the 32 rows' scales as bf16.  A code byte indexes a 256-entry LDS
+// table of bf16 level pairs, which is one dword of a v_mfma_f32_32x32x16_bf16 operand; the
+// table is stored 32 times, copy c in bank c, and lane l reads copy l%32, so a wave's lookups
+// never conflict.  The block's four k tiles run into a block accumulator with the activations
+// as the A operand (so a lane's 16 outputs share its weight row and its block scale), and the
+// total gains scale * block accumulator.
 // Everything after the k loop (cross-wave sum in wave order, k split by last arrival,
 // epilogues) is k_gemm's, with the accumulator image transposed.
-
-// Byte tables for v_perm_b32: dword q holds byte `hi` of levels 4q .. 4q+3.
-constexpr uint32_t nf4_bytes(int q, int hi) {
-  uint32_t v = 0;
-  for (int e = 0; e < 4; ++e) v |= (uint32_t)((kNf4Bits[4 * q + e] >> (8 * hi)) & 0xFF) << (8 * e);
-  return v;
-}
-
-// Codes dword c (byte j = code of input j | code of input j+4 << 4) -> bf16x8 levels of
-// inputs 0..7.  Per group of four codes: the low three bits select a byte from the 8-entry
-// half tables, bit 3 picks the half (0x00 / 0xFF byte masks from the permute's constant
-// selectors 12 and 13), and two more permutes interleave low and high bytes.
-__device__ __forceinline__ u32x4 nf4_levels8(uint32_t c, const uint32_t (&tl)[4], const uint32_t (&th)[4]) {
-  const uint32_t sa = c & 0x07070707u;
-  const uint32_t sb = (c >> 4) & 0x07070707u;
-  const uint32_t ma = __builtin_amdgcn_perm(0u, 0u, ((c >> 3) & 0x01010101u) | 0x0C0C0C0Cu);
-  const uint32_t mb = __builtin_amdgcn_perm(0u, 0u, ((c >> 7) & 0x01010101u) | 0x0C0C0C0Cu);
-  auto pick = [](uint32_t m, uint32_t x, uint32_t y) { return (x & m) | (y & ~m); };
-  const uint32_t la = pick(ma, __builtin_amdgcn_perm(tl[3], tl[2], sa), __builtin_amdgcn_perm(tl[1], tl[0], sa));
-  const uint32_t ha = pick(ma, __builtin_amdgcn_perm(th[3], th[2], sa), __builtin_amdgcn_perm(th[1], th[0], sa));
-  const uint32_t lb = pick(mb, __builtin_amdgcn_perm(tl[3], tl[2], sb), __builtin_amdgcn_perm(tl[1], tl[0], sb));
-  const uint32_t hb = pick(mb, __builtin_amdgcn_perm(th[3], th[2], sb), __builtin_amdgcn_perm(th[1], th[0], sb));
-  u32x4 o;
-  o.x = __builtin_amdgcn_perm(ha, la, 0x05010400u);
-  o.y = __builtin_amdgcn_perm(ha, la, 0x07030602u);
-  o.z = __builtin_amdgcn_perm(hb, lb, 0x05010400u);
-  o.w = __builtin_amdgcn_perm(hb, lb, 0x07030602u);
-  return o;
-}
 
 // Position of output (n_local nl, operand row m) in the transposed accumulator image: lane
 // nl + 32*((m%8)/4), register 4*((m%32)/8) + m%4 of m tile m/32.
@@ -362,11 +335,17 @@ __device__ __forceinline__ int tile_idx_t(int nl, int m) {
   return (m >> 5) * 1024 + ((nl & 31) + (((ml >> 2) & 1) << 5)) * 16 + ((ml >> 3) << 2) + (ml & 3);
 }
 
+__constant__ uint16_t c_nf4_bits[16] = {kNf4Bits[0],  kNf4Bits[1],  kNf4Bits[2],  kNf4Bits[3],
+                                        kNf4Bits[4],  kNf4Bits[5],  kNf4Bits[6],  kNf4Bits[7],
+                                        kNf4Bits[8],  kNf4Bits[9],  kNf4Bits[10], kNf4Bits[11],
+                                        kNf4Bits[12], kNf4Bits[13], kNf4Bits[14], kNf4Bits[15]};
+
 template <int EPI, int MT, int NW, int KB>
 __global__ __launch_bounds__(NW * 64) void k_gemm_nf4(const GemmArgs g) {
   constexpr int kThreads = NW * 64;
   constexpr int kRealRows = MT * 16;
   __shared__ float tile[NW][MT * 1024];
+  __shared__ uint32_t tab[256 * 32];   // level pairs of a code byte, 32 bank-rotated copies
   __shared__ float rscale[kRealRows + NW];
 
   const int tid = threadIdx.x;
@@ -408,8 +387,6 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_nf4(const GemmArgs g) {
     }
   };
 
-  const uint32_t tl[4] = {nf4_bytes(0, 0), nf4_bytes(1, 0), nf4_bytes(2, 0), nf4_bytes(3, 0)};
-  const uint32_t th[4] = {nf4_bytes(0, 1), nf4_bytes(1, 1), nf4_bytes(2, 1), nf4_bytes(3, 1)};
 
   f32x16 acc[MT];
 #pragma unroll
@@ -450,6 +427,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_nf4(const GemmArgs g) {
         }
     }
   };
+  const uint32_t tab_lane = (lane & 31) * 4;
   auto mma = [&](const Stage& st) {
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
@@ -457,9 +435,18 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_nf4(const GemmArgs g) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) part[mt] = (f32x16){};
       const uint32_t cw[4] = {st.c[i].x, st.c[i].y, st.c[i].z, st.c[i].w};
+      u32x4 wv[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const bf16x8 w = as_bf16x8(nf4_levels8(cw[t], tl, th));
+        uint32_t d[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          d[j] = *(const uint32_t*)((const char*)tab + ((((cw[t] >> (8 * j)) & 0xFFu) << 7) | tab_lane));
+        wv[t] = (u32x4){d[0], d[1], d[2], d[3]};
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16x8 w = as_bf16x8(wv[t]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
           part[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(st.a[i][mt][t]), w, part[mt], 0, 0, 0);
@@ -475,7 +462,14 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_nf4(const GemmArgs g) {
     Stage s0, s1;
     load(b0, s0);
     __builtin_amdgcn_sched_barrier(0);
+    // Entry e (codes of an even and an odd input, low nibble first) -> their bf16 level pair;
+    // thread t fills entry t's 32 copies starting at copy `lane`, so no store conflicts.
+    for (int e = tid; e < 256; e += kThreads) {
+      const uint32_t v = (uint32_t)c_nf4_bits[e & 15] | ((uint32_t)c_nf4_bits[e >> 4] << 16);
+      for (int c = 0; c < 32; ++c) tab[e * 32 + ((c + lane) & 31)] = v;
+    }
     row_scales();
+    __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     for (int b = b0; b < b1; b += 2 * KB) {
       load(b + KB, s1);
@@ -556,7 +550,8 @@ hipError_t launch_gemm_nf4(int epi, const GemmArgs& g, hipStream_t s) {
 
 // Pack NF4 projections: block (32-row block nb, 64-input block b) of 1088 bytes from row
 // pointer tables (rows [0, N): codes, two per byte, even input in the low nibble; rows
-// [N, 2N): bf16 scales per 64 inputs).  One thread per lane of a block.
+// [N, 2N): bf16 scales per 64 inputs).  One thread per lane of a block; a lane's dword for k
+// tile t is the 4 source bytes of its 8 inputs.
 __global__ void k_pack_nf4(uint8_t* dst, const uint8_t* const* rowptr, int N, int nb, int nblk) {
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (size_t)nb * nblk * 64) return;
@@ -570,10 +565,7 @@ __global__ void k_pack_nf4(uint8_t* dst, const uint8_t* const* rowptr, int N, in
     const int k0 = b * kNf4Block + t * 16 + (lane >> 5) * 8;
     uint32_t v = 0;
     for (int j = 0; j < 4; ++j) {
-      const int ka = k0 + j, kb = k0 + j + 4;
-      const uint32_t ca = (codes[ka >> 1] >> (4 * (ka & 1))) & 0xF;
-      const uint32_t cb = (codes[kb >> 1] >> (4 * (kb & 1))) & 0xF;
-      v |= (ca | (cb << 4)) << (8 * j);
+      v |= (uint32_t)codes[(k0 >> 1) + j] << (8 * j);   // codes of inputs k0+2j, k0+2j+1
     }
     out[t] = v;
   }
