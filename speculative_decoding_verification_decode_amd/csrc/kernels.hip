@@ -340,17 +340,22 @@ __constant__ uint16_t c_nf4_bits[16] = {kNf4Bits[0],  kNf4Bits[1],  kNf4Bits[2],
                                         kNf4Bits[8],  kNf4Bits[9],  kNf4Bits[10], kNf4Bits[11],
                                         kNf4Bits[12], kNf4Bits[13], kNf4Bits[14], kNf4Bits[15]};
 
-template <int EPI, int MT, int NW, int KB>
+// NR (1 or 2) consecutive 32-row blocks per workgroup share every activation load.
+template <int EPI, int MT, int NW, int KB, int NR>
 __global__ __launch_bounds__(NW * 64) void k_gemm_nf4(const GemmArgs g) {
   constexpr int kThreads = NW * 64;
   constexpr int kRealRows = MT * 16;
-  __shared__ float tile[NW][MT * 1024];
-  __shared__ uint32_t tab[256 * 32];   // level pairs of a code byte, 32 bank-rotated copies
+  constexpr int kTab = 256 * 32, kImg = NR * MT * 1024;
+  // The level-pair table (code byte -> bf16 pair, 32 bank-rotated copies) during the k loop,
+  // then the waves' accumulator images.
+  __shared__ uint32_t lds[kTab > NW * kImg ? kTab : NW * kImg];
+  uint32_t* const tab = lds;
+  float* const tile = (float*)lds;
   __shared__ float rscale[kRealRows + NW];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int nb = blockIdx.x / g.sp, spi = blockIdx.x - nb * g.sp;
+  const int nb0 = (blockIdx.x / g.sp) * NR, spi = blockIdx.x % g.sp;
   const int nblk = g.kb / 4;                                   // 64-input blocks
   const int U = g.sp * NW, u = spi * NW + wave;
   const int b0 = (int)(((long)nblk * u) / U), b1 = (int)(((long)nblk * (u + 1)) / U);
@@ -387,16 +392,20 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_nf4(const GemmArgs g) {
     }
   };
 
-
-  f32x16 acc[MT];
+  f32x16 acc[NR][MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x16){};
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[r][mt] = (f32x16){};
 
   // Buffer range checks return zeros for blocks at or past b1 and for operand rows past
   // 2*rows, so every batch issues all of its loads.
-  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const uint8_t*)g.w + (size_t)nb * nblk * kNf4BlockBytes), (short)0, b1 * kNf4BlockBytes,
-      kBufferWord3);
+  __amdgpu_buffer_rsrc_t wres[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+    wres[r] = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint8_t*)g.w + (size_t)(nb0 + r) * nblk * kNf4BlockBytes), (short)0, b1 * kNf4BlockBytes,
+        kBufferWord3);
   const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
       (void*)g.a, (short)0, (int)act_bytes(2 * g.rows, g.k), kBufferWord3);
   const int ext_rows = 2 * g.rows;
@@ -407,16 +416,19 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_nf4(const GemmArgs g) {
   for (int mt = 0; mt < MT; ++mt) mt_ok[mt] = mt * 32 + (lane & 31) < ext_rows;
 
   struct Stage {
-    u32x4 c[KB];
-    uint16_t s[KB];
+    u32x4 c[KB][NR];
+    uint16_t s[KB][NR];
     u32x4 a[KB][MT][4];
   };
   auto load = [&](int b, Stage& st) {
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
       const int bo = (b + i) * kNf4BlockBytes;
-      st.c[i] = __builtin_amdgcn_raw_buffer_load_b128(wres, bo + lane * 16, 0, kCacheStream);
-      st.s[i] = __builtin_amdgcn_raw_buffer_load_b16(wres, bo + 1024 + (lane & 31) * 2, 0, kCacheStream);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        st.c[i][r] = __builtin_amdgcn_raw_buffer_load_b128(wres[r], bo + lane * 16, 0, kCacheStream);
+        st.s[i][r] = __builtin_amdgcn_raw_buffer_load_b16(wres[r], bo + 1024 + (lane & 31) * 2, 0, kCacheStream);
+      }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -431,31 +443,34 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_nf4(const GemmArgs g) {
   auto mma = [&](const Stage& st) {
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
-      f32x16 part[MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) part[mt] = (f32x16){};
-      const uint32_t cw[4] = {st.c[i].x, st.c[i].y, st.c[i].z, st.c[i].w};
-      u32x4 wv[4];
+      for (int r = 0; r < NR; ++r) {
+        f32x16 part[MT];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        uint32_t d[4];
+        for (int mt = 0; mt < MT; ++mt) part[mt] = (f32x16){};
+        const uint32_t cw[4] = {st.c[i][r].x, st.c[i][r].y, st.c[i][r].z, st.c[i][r].w};
+        u32x4 wv[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          d[j] = *(const uint32_t*)((const char*)tab + ((((cw[t] >> (8 * j)) & 0xFFu) << 7) | tab_lane));
-        wv[t] = (u32x4){d[0], d[1], d[2], d[3]};
-      }
+        for (int t = 0; t < 4; ++t) {
+          uint32_t d[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bf16x8 w = as_bf16x8(wv[t]);
+          for (int j = 0; j < 4; ++j)
+            d[j] = *(const uint32_t*)((const char*)tab + ((((cw[t] >> (8 * j)) & 0xFFu) << 7) | tab_lane));
+          wv[t] = (u32x4){d[0], d[1], d[2], d[3]};
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bf16x8 w = as_bf16x8(wv[t]);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            part[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(st.a[i][mt][t]), w, part[mt], 0, 0, 0);
+        }
+        const float sc = __uint_as_float((uint32_t)st.s[i][r] << 16);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          part[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(st.a[i][mt][t]), w, part[mt], 0, 0, 0);
+#pragma unroll
+          for (int q = 0; q < 16; ++q) acc[r][mt][q] = fmaf(sc, part[mt][q], acc[r][mt][q]);
       }
-      const float sc = __uint_as_float((uint32_t)st.s[i] << 16);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[mt][r] = fmaf(sc, part[mt][r], acc[mt][r]);
     }
   };
   {
@@ -483,58 +498,71 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_nf4(const GemmArgs g) {
     }
   }
 
+  __syncthreads();   // every wave is done with the table
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int r = 0; r < NR; ++r)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) tile[wave][mt * 1024 + lane * 16 + r] = acc[mt][r];
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) tile[wave * kImg + (r * MT + mt) * 1024 + lane * 16 + q] = acc[r][mt][q];
   __syncthreads();
-  for (int e = tid; e < MT * 1024; e += kThreads) {
-    float v = tile[0][e];
+  for (int e = tid; e < kImg; e += kThreads) {
+    float v = tile[e];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) v += tile[w][e];
-    tile[0][e] = v;
+    for (int w = 1; w < NW; ++w) v += tile[w * kImg + e];
+    tile[e] = v;
   }
   __syncthreads();
-  const float* img = tile[0];
 
   __shared__ int last_arrival;
   const bool split = g.sp > 1;
-  float* const pblk = g.part + (size_t)nb * g.sp * g.rows * 32;   // [split][row][32]
-  auto tval = [&](int nl, int m) { return img[tile_idx_t(nl, m)] + img[tile_idx_t(nl, g.rows + m)]; };
-  if (split) {
-    for (int e = tid; e < 32 * kRealRows; e += kThreads) {
-      const int nl = e & 31, m = e >> 5;
-      if (m < g.rows) st<true>(pblk + ((size_t)spi * g.rows + m) * 32 + nl, tval(nl, m));
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int nb = nb0 + r;
+    const float* img = tile + r * MT * 1024;
+    float* const pblk = g.part + (size_t)nb * g.sp * g.rows * 32;   // [split][row][32]
+    auto tval = [&](int nl, int m) { return img[tile_idx_t(nl, m)] + img[tile_idx_t(nl, g.rows + m)]; };
+    if (split) {
+      for (int e = tid; e < 32 * kRealRows; e += kThreads) {
+        const int nl = e & 31, m = e >> 5;
+        if (m < g.rows) st<true>(pblk + ((size_t)spi * g.rows + m) * 32 + nl, tval(nl, m));
+      }
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0) {
+        const int old = __hip_atomic_fetch_add(g.counters + nb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_arrival = ((old + 1) % g.sp) == 0;
+      }
+      __syncthreads();
+      if (!last_arrival) continue;   // workgroup-uniform
+      asm volatile("" ::: "memory");
     }
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) {
-      const int old = __hip_atomic_fetch_add(g.counters + nb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last_arrival = ((old + 1) % g.sp) == 0;
-    }
-    __syncthreads();
-    if (!last_arrival) return;
-    asm volatile("" ::: "memory");
+    auto val = [&](int nl, int m) {
+      if (!split) return tval(nl, m);
+      float s = 0.f;
+      for (int q = 0; q < g.sp; ++q) s += pblk[((size_t)q * g.rows + m) * 32 + nl];
+      return s;
+    };
+    gemm_epilogue<EPI, kRealRows, kThreads>(g, nb, 0, rscale, val);
+    __syncthreads();   // the next block's partial stores reuse nothing, but keep the epilogues apart
   }
-  auto val = [&](int nl, int m) {
-    if (!split) return tval(nl, m);
-    float s = 0.f;
-    for (int q = 0; q < g.sp; ++q) s += pblk[((size_t)q * g.rows + m) * 32 + nl];
-    return s;
-  };
-  gemm_epilogue<EPI, kRealRows, kThreads>(g, nb, 0, rscale, val);
 }
 
 template <int EPI>
 static hipError_t gemm_nf4(const GemmArgs& g, hipStream_t s) {
   if (g.rows < 1 || g.rows > 64 || g.kb % 4) return hipErrorInvalidValue;
   const int mt = (2 * g.rows + 31) / 32;
-  const dim3 grid(g.nb * g.sp), block(256);
+  const dim3 block(256);
   switch (mt) {
-    case 1: k_gemm_nf4<EPI, 1, 4, 2><<<grid, block, 0, s>>>(g); break;
-    case 2: k_gemm_nf4<EPI, 2, 4, 1><<<grid, block, 0, s>>>(g); break;
-    default: k_gemm_nf4<EPI, 4, 4, 1><<<grid, block, 0, s>>>(g); break;
+    case 1:
+      // Two row blocks per workgroup halve the activation traffic, where that still leaves a
+      // workgroup per CU (gate/up at the 14B shape: 864 blocks; 32.5 -> 25.4 us).
+      if (g.nb % 2 == 0 && g.nb / 2 * g.sp >= 256) k_gemm_nf4<EPI, 1, 4, 1, 2><<<dim3(g.nb / 2 * g.sp), block, 0, s>>>(g);
+      else k_gemm_nf4<EPI, 1, 4, 2, 1><<<dim3(g.nb * g.sp), block, 0, s>>>(g);
+      break;
+    case 2: k_gemm_nf4<EPI, 2, 4, 1, 1><<<dim3(g.nb * g.sp), block, 0, s>>>(g); break;
+    default: k_gemm_nf4<EPI, 4, 4, 1, 1><<<dim3(g.nb * g.sp), block, 0, s>>>(g); break;
   }
   return hipGetLastError();
 }
