@@ -76,6 +76,18 @@ def test_model_create_rejects_bad_shapes_on_host(field, value):
     assert e.value.code == sfb.SF_E_ARG
 
 
+@pytest.mark.parametrize("field,value", [("hidden", 288), ("ffn", 1056)])
+def test_nf4_model_create_rejects_shapes_off_the_64_input_blocks(field, value):
+    """NF4 scales cover 64 consecutive inputs, so hidden and ffn must be multiples of 64
+    (multiples of 32 suffice for bf16 stacks); refused before any device work."""
+    d = sfb.desc_from_shape(synth.TINY)
+    setattr(d, field, value)
+    ptrs = [1] * len(sfb.weight_order(d, nf4=True))
+    with pytest.raises(sfb.SFError) as e:
+        sfb.sf_model_create_nf4(d, ptrs, None)
+    assert e.value.code == sfb.SF_E_ARG
+
+
 def test_model_create_rejects_null_weight_on_host():
     d = sfb.desc_from_shape(synth.TINY)
     ptrs = [1] * len(sfb.weight_order(d))
