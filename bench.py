@@ -396,17 +396,24 @@ def main():
         oc.load(kbits, vbits, ctx, next_token=int(hist[ctx]))
         d = drafts[ctx].cpu().numpy()
         kk = int(ks[ctx].item())
+        # Verifies of the same pass (the cache is not committed) until about 10 s of CPU work.
         t0 = time.perf_counter()
-        r = oracle.verify(m, oc, d, kk, commit=False)
-        sec = time.perf_counter() - t0
+        nv = 0
+        while True:
+            r = oracle.verify(m, oc, d, kk, commit=False)
+            nv += 1
+            if time.perf_counter() - t0 >= 10.0 or nv >= 30:
+                break
+        sec = (time.perf_counter() - t0) / nv
         # Sanity: the GPU pass at this context agrees with the oracle where the gap rule applies.
         gap = r["gap"].numpy()
         agree = sum(1 for j in range(K + 1) if gap[j] > 0.1 and int(tgt[0][j]) == int(r["target"][j]))
         under = int((gap > 0.1).sum())
         cpu = {"value": round((K + 1) / sec, 4), "unit": "verify tokens/s", "cores": torch.get_num_threads(),
-               "kind": "oracle", "seconds": round(sec, 2),
-               "sample": f"one verify (9 positions) of the full 28-layer stack + head at context {ctx}, "
-                         f"float64 torch on host; GPU targets agree on {agree}/{under} gap>0.1 slots"}
+               "kind": "oracle", "seconds_per_verify": round(sec, 3), "verifies": nv,
+               "sample": f"{nv} verifies (9 positions each) of the full 28-layer stack + head at context "
+                         f"{ctx}, float64 torch on host, about 10 s in total; GPU targets agree on "
+                         f"{agree}/{under} gap>0.1 slots"}
 
     out = {
         "metric": "verify tokens/s (Qwen2.5-7B-shape, K=8, 1 GPU)",
