@@ -128,6 +128,17 @@ template <int DH, bool kCoh>
 __device__ void attn_spans(const AttnArgs& a, int x0, int xstep, int kvh, int b, int rg) {
   constexpr int KP = DH + 8;        // K row pitch (bf16): 16-byte aligned, conflict-free b128 reads
   constexpr int VP = kChunk + 8;    // V^T row pitch
+  static_assert(DH % 64 == 0 && kChunk == 64, "K/V piece mapping and V^T swizzle assume 64-position chunks");
+  // Piece idx of a chunk's K/V (16 bytes: 8 dims of one position) -> position j and first dim:
+  // a wave's 64 pieces are 8 positions x 8 dim groups, so that the transposed V stores of a
+  // wave (rows d, column j, column groups swizzled by (d/8)%8) fall in 32 different banks.
+  auto piece = [](int idx, int& j, int& d8) {
+    j = (idx >> 3) & 63;
+    d8 = (((idx >> 9) << 3) | (idx & 7)) * 8;
+  };
+  // V^T element (d, j) sits in row d at column group (j/8) ^ ((d/8) % 8): 16-byte groups of 8
+  // positions stay contiguous for the PV operand reads.
+  auto vt_col = [](int d, int j) { return ((((j >> 3) ^ ((d >> 3) & 7)) << 3) | (j & 7)); };
   constexpr int PP = kChunk + 8;    // P row pitch
   __shared__ __attribute__((aligned(16))) uint16_t Kl[kChunk * KP];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[DH * VP];
@@ -154,7 +165,8 @@ __device__ void attn_spans(const AttnArgs& a, int x0, int xstep, int kvh, int b,
 #pragma unroll
     for (int u = 0; u < kKvPerThread; ++u) {
       const int idx = tid + u * 256;
-      const int j = idx / (DH / 8), d8 = (idx - j * (DH / 8)) * 8;
+      int j, d8;
+      piece(idx, j, d8);
       const int pos = min(c0 + j, plast);
       kreg[u] = *(const u32x4*)(kbase + (size_t)pos * DH + d8);
       vreg[u] = *(const u32x4*)(vbase + (size_t)pos * DH + d8);
@@ -228,13 +240,14 @@ __device__ void attn_spans(const AttnArgs& a, int x0, int xstep, int kvh, int b,
 #pragma unroll
       for (int u = 0; u < kKvPerThread; ++u) {
         const int idx = tid + u * 256;
-        const int j = idx / (DH / 8), d8 = (idx - j * (DH / 8)) * 8;
+        int j, d8;
+        piece(idx, j, d8);
         *(u32x4*)(&Kl[j * KP + d8]) = kreg[u];
         const uint32_t vw[4] = {vreg[u].x, vreg[u].y, vreg[u].z, vreg[u].w};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          Vt[(d8 + 2 * t) * VP + j] = (uint16_t)(vw[t] & 0xFFFFu);
-          Vt[(d8 + 2 * t + 1) * VP + j] = (uint16_t)(vw[t] >> 16);
+          Vt[(d8 + 2 * t) * VP + vt_col(d8, j)] = (uint16_t)(vw[t] & 0xFFFFu);
+          Vt[(d8 + 2 * t + 1) * VP + vt_col(d8, j)] = (uint16_t)(vw[t] >> 16);
         }
       }
       // The next chunk's K/V loads (this span's next chunk, else the first chunk of this
@@ -305,7 +318,8 @@ __device__ void attn_spans(const AttnArgs& a, int x0, int xstep, int kvh, int b,
           for (int ks = 0; ks < 2; ++ks) {
             const u32x4 pa = *(const u32x4*)(&Pl[wave][0][l16 * PP + ks * 32 + g4 * 8]);
             const u32x4 pl = *(const u32x4*)(&Pl[wave][1][l16 * PP + ks * 32 + g4 * 8]);
-            const bf16x8 vb = as_bf16x8(*(const u32x4*)(&Vt[(nt * 16 + l16) * VP + ks * 32 + g4 * 8]));
+            const int vd = nt * 16 + l16;
+            const bf16x8 vb = as_bf16x8(*(const u32x4*)(&Vt[vd * VP + vt_col(vd, ks * 32 + g4 * 8)]));
             o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pa), vb, o[nt], 0, 0, 0);
             o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pl), vb, o[nt], 0, 0, 0);
           }
