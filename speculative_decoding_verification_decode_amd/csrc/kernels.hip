@@ -335,10 +335,15 @@ __device__ __forceinline__ int tile_idx_t(int nl, int m) {
   return (m >> 5) * 1024 + ((nl & 31) + (((ml >> 2) & 1) << 5)) * 16 + ((ml >> 3) << 2) + (ml & 3);
 }
 
-__constant__ uint16_t c_nf4_bits[16] = {kNf4Bits[0],  kNf4Bits[1],  kNf4Bits[2],  kNf4Bits[3],
-                                        kNf4Bits[4],  kNf4Bits[5],  kNf4Bits[6],  kNf4Bits[7],
-                                        kNf4Bits[8],  kNf4Bits[9],  kNf4Bits[10], kNf4Bits[11],
-                                        kNf4Bits[12], kNf4Bits[13], kNf4Bits[14], kNf4Bits[15]};
+// bf16 bits of level i, selected from immediates: no memory load, so filling the table does
+// not wait behind the weight loads already in flight (loads complete in issue order).
+__device__ __forceinline__ uint32_t nf4_bits(int i) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    w = (i >> 1) == q ? ((uint32_t)kNf4Bits[2 * q] | ((uint32_t)kNf4Bits[2 * q + 1] << 16)) : w;
+  return (w >> ((i & 1) * 16)) & 0xFFFFu;
+}
 
 // NR (1 or 2) consecutive 32-row blocks per workgroup share every activation load.
 template <int EPI, int MT, int NW, int KB, int NR>
@@ -480,7 +485,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_nf4(const GemmArgs g) {
     // Entry e (codes of an even and an odd input, low nibble first) -> their bf16 level pair;
     // thread t fills entry t's 32 copies starting at copy `lane`, so no store conflicts.
     for (int e = tid; e < 256; e += kThreads) {
-      const uint32_t v = (uint32_t)c_nf4_bits[e & 15] | ((uint32_t)c_nf4_bits[e >> 4] << 16);
+      const uint32_t v = nf4_bits(e & 15) | (nf4_bits(e >> 4) << 16);
       for (int c = 0; c < 32; ++c) tab[e * 32 + ((c + lane) & 31)] = v;
     }
     row_scales();
