@@ -879,56 +879,10 @@ hipError_t launch_embed(const EmbedArgs& e, hipStream_t s) {
   return hipGetLastError();
 }
 
-// L2 warm-up of the next GEMM's weights while the attention runs (it leaves HBM mostly idle).
-// The kPrefetchGroups workgroups with linear index g0 .. g0+63 take part; workgroups are
-// dispatched to the 8 XCDs round-robin by linear index, so workgroup `lin` sits on XCD
-// lin % 8 and touches one 4-byte word per 128-byte line of the chunks that the GEMM's
-// workgroups on that XCD will stream.  Skipped when the step's K/V (which the attention
-// streams through the same L2) would leave too little room.
-constexpr double kPrefetchMaxKvBytes = 8.0 * (1 << 20);
-__device__ void prefetch_chunks(const AttnArgs& a, int B, int lin, int g0) {
-  double kv = 0.0;
-  for (int b = 0; b < B; ++b) kv += (double)(a.len[b] + a.T) * a.nkv * a.dh * 4;
-  if (kv > kPrefetchMaxKvBytes) return;
-  const int x = lin & 7;
-  const int first = g0 + ((x - g0) % 8 + 8) % 8;          // first prefetch group on XCD x
-  const int nx = (g0 + kPrefetchGroups - 1 - first) / 8 + 1;
-  const int rank = (lin - first) / 8;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int chunks = a.pf_nb * a.pf_sp;
-  const int per_chunk = ((a.pf_kb + a.pf_sp - 1) / a.pf_sp + 7) / 8;   // 8 KB pieces per chunk
-  const int nc = (chunks - x + 7) / 8;                                // chunks on XCD x
-  const int total = nc * per_chunk, stride = nx * 4;
-  const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)a.pf_w, (short)0, a.pf_nb * a.pf_kb * 1024, kBufferWord3);
-  auto offset = [&](int it) {
-    const int c = it / per_chunk, piece = it - c * per_chunk;
-    const int i = x + 8 * c, nb = i / a.pf_sp, spi = i - nb * a.pf_sp;
-    const int t0 = a.pf_kb * spi / a.pf_sp, t1 = a.pf_kb * (spi + 1) / a.pf_sp;
-    const int off = piece * 8192 + lane * 128;
-    return (it < total && off < (t1 - t0) * 1024) ? (nb * a.pf_kb + t0) * 1024 + off : 0x7FFFFFF0;
-  };
-  unsigned acc = 0;
-  for (int it0 = rank * 4 + wave; it0 < total; it0 += 16 * stride) {
-    unsigned v[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = __builtin_amdgcn_raw_buffer_load_b32(res, offset(it0 + j * stride), 0, 0);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) acc ^= v[j];
-  }
-  asm volatile("" ::"v"(acc));
-}
-
-// Grid (spans, kv heads, sequences x row groups [+ 1 warm-up slice when a.pf_w is set]).
+// Grid (spans, kv heads, sequences x row groups).
 template <int DH>
-__global__ __launch_bounds__(256) void k_attn(const AttnArgs a, int B) {
+__global__ __launch_bounds__(256) void k_attn(const AttnArgs a) {
   const int G = a.nq / a.nkv, ngroups = (a.T * G + 63) / 64;
-  if ((int)blockIdx.z == B * ngroups) {
-    const int g0 = B * ngroups * gridDim.x * gridDim.y;
-    const int lin = g0 + blockIdx.x + gridDim.x * blockIdx.y;
-    if (lin < g0 + kPrefetchGroups) prefetch_chunks(a, B, lin, g0);
-    return;
-  }
   attn_spans<DH, false>(a, blockIdx.x, gridDim.x, blockIdx.y, blockIdx.z / ngroups, blockIdx.z % ngroups);
 }
 
@@ -946,16 +900,14 @@ hipError_t launch_attention(const AttnArgs& a, int dh, int B, hipStream_t s) {
   // workgroups per CU, else fewer, each taking every nx-th span (its next span's K/V loads
   // overlap the current span's compute).  A span's partial does not depend on the choice.
   const int nx = std::min(a.nchunk, std::max(1, kAttnWorkgroups / (a.nkv * B * ngroups)));
-  AttnArgs aw = a;
-  if (aw.pf_w && nx * a.nkv < kPrefetchGroups) aw.pf_w = nullptr;   // warm-up slice too small
-  const dim3 grid(nx, a.nkv, B * ngroups + (aw.pf_w ? 1 : 0));
+  const dim3 grid(nx, a.nkv, B * ngroups);
   const int ncomb = (a.rows * a.nq + 3) / 4;
   if (dh == 128) {
-    k_attn<128><<<grid, 256, 0, s>>>(aw, B);
-    k_combine<128><<<ncomb, 256, 0, s>>>(aw);
+    k_attn<128><<<grid, 256, 0, s>>>(a);
+    k_combine<128><<<ncomb, 256, 0, s>>>(a);
   } else if (dh == 64) {
-    k_attn<64><<<grid, 256, 0, s>>>(aw, B);
-    k_combine<64><<<ncomb, 256, 0, s>>>(aw);
+    k_attn<64><<<grid, 256, 0, s>>>(a);
+    k_combine<64><<<ncomb, 256, 0, s>>>(a);
   } else {
     return hipErrorInvalidValue;
   }

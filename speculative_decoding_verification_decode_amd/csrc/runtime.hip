@@ -96,7 +96,6 @@ struct sf_cache {
   int kh = 4;                      // GEMM: weight tiles per pipelined batch (one-tile row counts)
   int* cnt = nullptr;              // k-split arrival counters [layer][QKV, O, down][block]
   int cnt_stride = 0;
-  bool prefetch_o = true;   // warm the O projection's weights into L2 during attention (large O only)
   hipGraphExec_t gx_verify = nullptr, gx_draft = nullptr;
   uint16_t *snap_k = nullptr, *snap_v = nullptr;   // state snapshot: K/V rows [len, len+T)
   int32_t *snap_len = nullptr, *snap_next = nullptr;
@@ -443,8 +442,6 @@ static hipError_t enqueue_forward(sf_cache* c, const Run& r) {
     if ((e = run_gemm(c, kGQkv, l, kEpiQkv, g, s)) != hipSuccess) return e;
 
     aa.kc = kc; aa.vc = vc;
-    // The warm-up walks the bf16 tile layout of the O weights, so NF4 blocks never take it.
-    if (c->prefetch_o && !m->nf4 && c->nchunk * m->nkv >= kPrefetchGroups) { aa.pf_w = Ly.wo; aa.pf_nb = m->nb_h; aa.pf_kb = m->Q / kTileK; aa.pf_sp = c->sp_o; }
     if ((e = launch_attention(aa, m->dh, r.B, s)) != hipSuccess) return e;
 
     g = base;
@@ -540,11 +537,6 @@ extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacit
   c->sp_d = choose_sp(m->nb_h, m->F / kTileK, c->nw_d, "SF_SP_D", m->nf4);
   c->sp_head = 1;
   if (const char* v = getenv("SF_KH")) c->kh = (atoi(v) == 8) ? 8 : 4;
-  // The warm-up pays for O weights that do not already stay in L2 between uses (25.7 MB at
-  // 7B); at the 0.5B shape (1.6 MB) it measured 35 us slower per draft step.
-  c->prefetch_o = (double)m->H * m->Q * 2 >= 8.0 * (1 << 20);
-  if (const char* v = getenv("SF_PREFETCH")) c->prefetch_o = atoi(v) != 0;
-  if (m->nf4) c->prefetch_o = false;   // its address walk assumes bf16 tiles (2 bytes per weight)
 
   hipStream_t s = m->stream;
   auto bail = [&](sf_status st) { cache_release(c); return st; };

@@ -118,15 +118,8 @@ struct AttnArgs {
   float* part;             // [seq][nkv][span][T*G][dh+2]
   uint16_t* out;           // combine output as hi/lo bf16 rows [2*rows][nq*dh]
   int rows;
-  // Weights of the GEMM that follows (packed tiles, nullptr: none), warmed into the L2 of
-  // the XCD that will stream them: that GEMM's workgroup i runs on XCD i % 8 and streams
-  // k tiles [kb*spi/sp, kb*(spi+1)/sp) of block i / sp, spi = i % sp.
-  const uint4* pf_w;
-  int pf_nb, pf_kb, pf_sp;
   int dh;
 };
-// Workgroups of the attention grid's warm-up slice (needs span workgroups * kv heads >= this).
-constexpr int kPrefetchGroups = 64;
 // Target number of attention workgroups (a few per CU): beyond it, a workgroup takes several spans.
 constexpr int kAttnWorkgroups = 2048;
 
