@@ -410,7 +410,6 @@ __device__ void combine_pair(const AttnArgs& a, int r, int h) {
     }
   }
   const float inv = 1.0f / Ls;
-  const size_t qd = (size_t)a.nq * DH;
   store_split<kCoh>(a.out, a.rows, r, h * DH + lane, o0 * inv);
   if (DH > 64) store_split<kCoh>(a.out, a.rows, r, h * DH + lane + 64, o1 * inv);
 }
