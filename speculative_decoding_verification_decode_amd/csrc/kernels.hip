@@ -896,10 +896,11 @@ __global__ __launch_bounds__(256) void k_combine(const AttnArgs a) {
 hipError_t launch_attention(const AttnArgs& a, int dh, int B, hipStream_t s) {
   const int G = a.nq / a.nkv;
   const int ngroups = (a.T * G + 63) / 64;
-  // Workgroups along the spans: all of them when the grid stays within about eight
-  // workgroups per CU, else fewer, each taking every nx-th span (its next span's K/V loads
-  // overlap the current span's compute).  A span's partial does not depend on the choice.
-  const int nx = std::min(a.nchunk, std::max(1, kAttnWorkgroups / (a.nkv * B * ngroups)));
+  // One workgroup per span (workgroups past a sequence's length exit at once).  Capping the
+  // grid so that workgroups take several spans each measured slower for the 32-sequence
+  // batch (2048 workgroups: 21.2 ms per pass, 4096: 22.2, one per span: 20.8).  A span's
+  // partial does not depend on the choice.
+  const int nx = a.nchunk;
   const dim3 grid(nx, a.nkv, B * ngroups);
   const int ncomb = (a.rows * a.nq + 3) / 4;
   if (dh == 128) {

@@ -120,8 +120,6 @@ struct AttnArgs {
   int rows;
   int dh;
 };
-// Target number of attention workgroups (a few per CU): beyond it, a workgroup takes several spans.
-constexpr int kAttnWorkgroups = 2048;
 
 struct AcceptArgs {
   const float2* amax;      // [rows][nparts]
