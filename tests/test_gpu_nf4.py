@@ -74,9 +74,10 @@ def test_nf4_tiny_prefill_and_lockstep_verify():
 
 
 def test_nf4_14b_shape_two_layers_verify_matches_oracle():
-    """Capacity 576 gives 9 attention spans x 8 KV heads, the size at which bf16 caches warm
-    the O weights into L2 during attention; NF4 caches must not take that path (it walks the
-    bf16 tile layout, which is 3.8 times larger than the NF4 blocks)."""
+    """Two layers of the 14B shape with NF4 projections, capacity 576 (9 attention spans x 8 KV
+    heads): prefill and two verifies against the oracle's NF4 model.  This capacity once
+    faulted when an L2 warm-up walked the bf16 tile layout over NF4 blocks; the case stays as a
+    regression test."""
     sfb = need_gpu()
     S, K, CAP = synth.QWEN14B_2L, 8, 576
     say("[nf4-14b-2l] weights")
