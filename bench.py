@@ -254,8 +254,9 @@ def main():
 
     # Prefill (time to first token): prompts of 512 and 2048 seeded ids from an empty cache,
     # in passes of up to 512 positions, host-inclusive (sf_prefill returns the next token).
-    # Work per prompt: 2 flops per weight per position (layers and head) plus the causal
-    # attention's QK^T and PV, 4*dh flops per (query head, position pair).
+    # Work per prompt: 2 flops per layer weight per position, the LM head once (only the last
+    # position's logits give the next token), plus the causal attention's QK^T and PV, 4*dh
+    # flops per (query head, position pair).
     prefill = None
     if not args.no_prefill:
         pc = sfb.sf_cache_alloc(model, 1, 2048 + 16, K)
@@ -270,7 +271,7 @@ def main():
                 t0 = time.perf_counter()
                 sfb.sf_prefill(pc, 0, prompt)
                 best = min(best, time.perf_counter() - t0)
-            flops = 2.0 * n * (params_layers + S.vocab * S.hidden) + \
+            flops = 2.0 * (n * params_layers + S.vocab * S.hidden) + \
                 S.n_layers * S.n_q_heads * 4.0 * S.head_dim * n * (n + 1) / 2
             prefill[str(n)] = {"ms": round(best * 1e3, 3), "prompt_tokens_per_s": round(n / best, 1),
                                "tflops": round(flops / best / 1e12, 1),

@@ -128,7 +128,8 @@ sf_status sf_cache_free(sf_cache* cache);
  * there is no pipeline to fill, so up to eight such pieces (512 positions) go through
  * one pass together, which lets each weight byte serve 512 rows.  Not graph-captured.  The pass size (1..512) can be lowered for a cache by setting
  * SF_PREFILL_CHUNK in the environment before sf_cache_alloc; results are bit-identical
- * for any pass size.
+ * for any pass size.  Only the last position's logits are computed: earlier passes skip
+ * the LM head, and the last one runs it for the rows it needs.
  * Errors: SF_E_ARG (token id outside [0,V), n < 1), SF_E_CAPACITY (n > capacity). */
 sf_status sf_prefill(sf_cache* cache, int32_t seq, const int32_t* tokens, int32_t n,
                      int32_t* next_token);

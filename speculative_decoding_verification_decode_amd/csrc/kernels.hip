@@ -631,8 +631,9 @@ hipError_t launch_pack_nf4(uint8_t* dst, const uint8_t* const* rowptr, int N, in
 // against (kBlocks + 4) KB of operands, where the row-group mode of k_gemm does 4 MFMAs per
 // 5 KB.  The accumulators and a ring of kStages k tiles of operands stay in registers, loaded
 // kStages-1 tiles ahead of the MFMAs that use them.
+// The launch covers G 64-row groups from row row0.
 template <int EPI, int kStages, int kBlocks>
-__device__ __forceinline__ void gemm_b_body(const GemmArgs& g) {
+__device__ __forceinline__ void gemm_b_body(const GemmArgs& g, int row0, int G) {
   constexpr int NW = 4, kThreads = 256, kRealRows = 64, MT = 4;
   // Cross-wave images of one weight block: wave w's accumulator register r of m tile mt, lane l
   // at red[w][(mt*16 + r)*kRedPitch + l].  Consecutive lanes hit consecutive banks when the
@@ -647,13 +648,13 @@ __device__ __forceinline__ void gemm_b_body(const GemmArgs& g) {
   // Workgroup (group split gs, row group rg) has linear index ((gs/8)*G + rg)*8 + gs%8: the G
   // row groups of one group of weight blocks run on the same XCD (workgroups go to the XCDs
   // round-robin by index) and close together in time, so the weights come from HBM once.
-  const int G = (g.rows + 63) / 64, ngroups = g.nb / kBlocks;
+  const int ngroups = g.nb / kBlocks;
   const int q = blockIdx.x >> 3;
   const int rg = q % G;
   const int gs = (q / G) * 8 + (blockIdx.x & 7);
   if (gs >= ngroups * g.sp) return;   // padding of the last group of 8
   const int bgrp = gs / g.sp, spi = gs - bgrp * g.sp;
-  const int nb0 = bgrp * kBlocks, r0 = rg * 64;
+  const int nb0 = bgrp * kBlocks, r0 = row0 + rg * 64;
   const int U = g.sp * NW, u = spi * NW + wave;
   const int kt0 = (int)(((long)g.kb * u) / U), kt1 = (int)(((long)g.kb * (u + 1)) / U);
 
@@ -784,7 +785,8 @@ __device__ __forceinline__ void gemm_b_body(const GemmArgs& g) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(g.counters + nb0 * G + rg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int old = __hip_atomic_fetch_add(g.counters + nb0 * ((g.rows + 63) / 64) + r0 / 64, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
     last_arrival = ((old + 1) % g.sp) == 0;
   }
   __syncthreads();
@@ -806,8 +808,8 @@ __device__ __forceinline__ void gemm_b_body(const GemmArgs& g) {
 // and one's epilogue overlaps the other's k loop: 32-sequence verify 20.0 -> 18.1 ms and a
 // 512-token prefill 27.0 -> 23.6 ms against four blocks per wave at one workgroup per CU.
 template <int EPI>
-__global__ __launch_bounds__(256, 2) void k_gemm_b(const GemmArgs g) {
-  gemm_b_body<EPI, 3, 2>(g);
+__global__ __launch_bounds__(256, 2) void k_gemm_b(const GemmArgs g, int row0, int G) {
+  gemm_b_body<EPI, 3, 2>(g, row0, G);
 }
 
 template <int EPI, int NW>
@@ -817,8 +819,10 @@ static hipError_t gemm_mt(const GemmArgs& g, hipStream_t s) {
   if (g.rows > 64) {
     const int G = (g.rows + 63) / 64;
     if (g.nb % 2 == 0) {
+      // Row groups before the one holding row_lo are skipped (their outputs are not needed).
+      const int rg_lo = std::min(std::max(g.row_lo, 0), g.rows - 1) / 64;
       const int ngs = (g.nb / 2) * g.sp;
-      k_gemm_b<EPI><<<dim3(((ngs + 7) / 8) * 8 * G), dim3(256), 0, s>>>(g);
+      k_gemm_b<EPI><<<dim3(((ngs + 7) / 8) * 8 * (G - rg_lo)), dim3(256), 0, s>>>(g, rg_lo * 64, G - rg_lo);
     } else {
       const int nbs = g.nb * g.sp;
       k_gemm<EPI, 4, 4, 4, true><<<dim3(((nbs + 7) / 8) * 8 * G), dim3(256), 0, s>>>(g);
@@ -944,6 +948,10 @@ __global__ __launch_bounds__(1024) void k_accept(const AcceptArgs a) {
   const int wave = tid >> 6, lane = tid & 63;
   if (a.has_head) {
     for (int slot = wave; slot < a.T; slot += 16) {
+      if (slot < a.slot_lo) {
+        if (lane == 0) tgt[slot] = 0;
+        continue;
+      }
       const float2* row = a.amax + (size_t)(b * a.T + slot) * a.nparts;
       float bv = -INFINITY;
       int bi = 0x7FFFFFFF;

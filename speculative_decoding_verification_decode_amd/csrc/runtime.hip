@@ -73,6 +73,8 @@ struct Run {
   float* logits;
   bool draft_mode;
   bool prefill;
+  // First row whose LM-head output is needed; -1: none (the pass only writes K/V and commits).
+  int head_from = 0;
 };
 
 struct sf_cache {
@@ -467,18 +469,21 @@ static hipError_t enqueue_forward(sf_cache* c, const Run& r) {
     if ((e = run_gemm(c, kGDown, l, kEpiResid, g, s)) != hipSuccess) return e;
   }
 
-  if (d.has_head) {
+  const bool head = d.has_head && r.head_from >= 0;
+  if (head) {
     GemmArgs g = base;
     g.w = m->head; g.a = c->a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_head; g.nw = c->nw_head;
     g.sp = 1;
     g.amax = c->amax; g.logits = r.logits; g.vocab = m->V;
+    g.row_lo = r.head_from;
     if ((e = run_gemm(c, kGHead, 0, kEpiArgmax, g, s)) != hipSuccess) return e;
   }
 
   AcceptArgs ac{};
   ac.amax = c->amax; ac.nparts = m->nb_head; ac.stage = c->stage_d; ac.len = len; ac.next = next;
   ac.result = c->res_d; ac.draft_out = r.draft_mode ? c->dout_d : nullptr; ac.B = r.B; ac.T = r.T;
-  ac.has_head = d.has_head;
+  ac.has_head = head;
+  ac.slot_lo = head ? r.head_from : 0;
   return launch_accept(ac, s);
 }
 
@@ -743,7 +748,11 @@ extern "C" sf_status sf_prefill(sf_cache* c, int32_t seq, const int32_t* tokens,
     st->step[0] = 0;
     for (int j = 1; j < cnt; ++j) st->draft[j - 1] = tokens[j0 + j];
     HIPCHK(hipMemcpyAsync(c->stage_d, st, stage_bytes(1, cnt - 1), hipMemcpyHostToDevice, s));
-    hipError_t e = enqueue_forward(c, Run{1, cnt, seq, cnt - 1, nullptr, false, true});
+    // Every position is forced accepted and the next pass stages its own first token, so only
+    // the last pass's last row needs the LM head (a pass without it commits len += cnt).
+    Run run{1, cnt, seq, cnt - 1, nullptr, false, true};
+    run.head_from = (j0 + cnt == n) ? cnt - 1 : -1;
+    hipError_t e = enqueue_forward(c, run);
     if (e != hipSuccess) return fail(SF_E_HIP, std::string("prefill forward: ") + hipGetErrorString(e));
     HIPCHK(hipStreamSynchronize(s));  // the pinned stage block is reused by the next chunk
     last_cnt = cnt;

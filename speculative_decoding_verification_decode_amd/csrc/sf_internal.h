@@ -61,6 +61,7 @@ struct GemmArgs {
   float* part;             // split partials [nb][sp][rows][32] (sp > 1)
   int* counters;           // [nb] arrivals of the splits of each block (sp > 1); only grow
   int nw;                  // waves per workgroup: 4 or 8
+  int row_lo;              // batched kernel: outputs of rows below row_lo are not needed (0: all)
   int kh;                  // weight tiles per pipelined batch (4 or 8) for single-tile row counts
   // RMSNorm folded into the consumer: row scale = 1/sqrt(sum(ssq_in[r][*])/k + eps)
   const float* ssq_in;
@@ -130,6 +131,7 @@ struct AcceptArgs {
   int32_t* result;         // accepted[B] then target[B][T]
   int32_t* draft_out;      // [B][kMaxDraftSteps]
   int B, T, has_head;
+  int slot_lo;             // targets of slots below slot_lo are not computed (reported as 0)
 };
 
 // Launchers (kernels.hip).
