@@ -9,6 +9,10 @@
 
 namespace sf {
 
+// A pass whose kernels carry a gate runs only while the device flag is set; the kernels of a
+// gated-off pass return at once (whole launches, so split arrival counters stay consistent).
+__device__ __forceinline__ bool gated_off(const int* gate) { return gate && *gate == 0; }
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));

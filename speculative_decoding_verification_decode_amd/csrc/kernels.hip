@@ -136,6 +136,7 @@ __device__ void gemm_epilogue(const GemmArgs& g, int nb, int r0, const float* rs
 // same as in the compact layout: the per-row result does not depend on the batch.
 template <int EPI, int MT, int NW, int KH = kHalf, bool WIDE = false>
 __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
+  if (gated_off(g.gate)) return;
   static_assert(!WIDE || MT == 4, "wide row groups hold two hi and two lo m tiles");
   constexpr int kThreads = NW * 64;
   constexpr int kRealRows = MT * 16;
@@ -356,6 +357,7 @@ __device__ __forceinline__ uint32_t nf4_bits(int i) {
 // NR (1 or 2) consecutive 32-row blocks per workgroup share every activation load.
 template <int EPI, int MT, int NW, int KB, int NR>
 __global__ __launch_bounds__(NW * 64) void k_gemm_nf4(const GemmArgs g) {
+  if (gated_off(g.gate)) return;
   constexpr int kThreads = NW * 64;
   constexpr int kRealRows = MT * 16;
   constexpr int kTab = 256 * 32, kImg = NR * MT * 1024;
@@ -634,6 +636,7 @@ hipError_t launch_pack_nf4(uint8_t* dst, const uint8_t* const* rowptr, int N, in
 // The launch covers G 64-row groups from row row0.
 template <int EPI, int kStages, int kBlocks>
 __device__ __forceinline__ void gemm_b_body(const GemmArgs& g, int row0, int G) {
+  if (gated_off(g.gate)) return;
   constexpr int NW = 4, kThreads = 256, kRealRows = 64, MT = 4;
   // Cross-wave images of one weight block: wave w's accumulator register r of m tile mt, lane l
   // at red[w][(mt*16 + r)*kRedPitch + l].  Consecutive lanes hit consecutive banks when the
@@ -864,6 +867,7 @@ hipError_t launch_gemm(int epi, const GemmArgs& g, hipStream_t s) {
 // writes the fp32 residual, x * ln1 gain as hi/lo bf16 rows, and per-32-column sums of
 // squares.  Thread t handles columns 8t..8t+7; four consecutive lanes form a 32-column block.
 __global__ __launch_bounds__(256) void k_embed(const EmbedArgs e) {
+  if (gated_off(e.gate)) return;
   const int r = blockIdx.x;
   const int b = r / e.T, slot = r - b * e.T;
   int tok;
@@ -902,12 +906,14 @@ hipError_t launch_embed(const EmbedArgs& e, hipStream_t s) {
 // Grid (spans, kv heads, sequences x row groups).
 template <int DH>
 __global__ __launch_bounds__(256) void k_attn(const AttnArgs a) {
+  if (gated_off(a.gate)) return;
   const int G = a.nq / a.nkv, ngroups = (a.T * G + 63) / 64;
   attn_spans<DH, false>(a, blockIdx.x, gridDim.x, blockIdx.y, blockIdx.z / ngroups, blockIdx.z % ngroups);
 }
 
 template <int DH>
 __global__ __launch_bounds__(256) void k_combine(const AttnArgs a) {
+  if (gated_off(a.gate)) return;
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= a.rows * a.nq) return;
   combine_pair<DH, false>(a, item / a.nq, item % a.nq);
@@ -943,6 +949,7 @@ int attention_spans(int cap) { return span_of(cap - 1) + 1; }
 // order independent), count the leading drafts that match, and commit.  Wave w merges the
 // rows w, w+16, ... of the sequence.
 __global__ __launch_bounds__(1024) void k_accept(const AcceptArgs a) {
+  if (gated_off(a.gate)) return;
   __shared__ int tgt[kMaxRows];   // one per slot: up to k_max+1 in a verify, a whole prefill chunk
   const int b = blockIdx.x, tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -1168,6 +1175,12 @@ __global__ void k_round(const RoundArgs a, int phase) {
       } else {
         a.scratch[a.B + b] = 1;
       }
+    }
+    __syncthreads();
+    if (b == 0) {   // the catch-up pass runs only if some sequence needs it
+      int any = 0;
+      for (int i = 0; i < a.B; ++i) any |= a.scratch[a.B + i];
+      a.scratch[2 * a.B] = any;
     }
   } else {
     if (b == 0) a.dstage->flags = 0;

@@ -75,6 +75,8 @@ struct Run {
   bool prefill;
   // First row whose LM-head output is needed; -1: none (the pass only writes K/V and commits).
   int head_from = 0;
+  // Device flag: the pass's kernels run only while it is nonzero (nullptr: always run).
+  const int* gate = nullptr;
 };
 
 struct sf_cache {
@@ -419,18 +421,19 @@ static hipError_t enqueue_forward(sf_cache* c, const Run& r) {
   EmbedArgs ea{};
   ea.embed = m->embed; ea.stage = c->stage_d; ea.len = len; ea.next = next; ea.gain = m->layers[0].g1;
   ea.x = c->x; ea.a = c->a_h; ea.ssq = c->ssq; ea.rows = rows; ea.T = r.T; ea.H = m->H; ea.V = m->V;
-  ea.kmax = r.kmax;
+  ea.kmax = r.kmax; ea.gate = r.gate;
   if ((e = launch_embed(ea, s)) != hipSuccess) return e;
 
   GemmArgs base{};
   base.rows = rows; base.ssq_in = c->ssq; base.part = c->part; base.sp = 1;
   base.nparts_in = m->H / kTileN; base.eps = d.rms_eps; base.T = r.T; base.len = len; base.cap = c->cap;
   base.seq_stride = (long)c->seq_stride; base.rope = c->rope; base.nq = m->nq; base.nkv = m->nkv; base.dh = m->dh;
+  base.gate = r.gate;
 
   AttnArgs aa{};
   aa.q = c->q; aa.seq_stride = (long)c->seq_stride; aa.cap = c->cap; aa.len = len; aa.T = r.T; aa.nq = m->nq;
   aa.nkv = m->nkv; aa.nchunk = c->nchunk; aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)m->dh));
-  aa.part = c->apart; aa.out = c->a_o; aa.rows = rows; aa.dh = m->dh;
+  aa.part = c->apart; aa.out = c->a_o; aa.rows = rows; aa.dh = m->dh; aa.gate = r.gate;
 
   for (int l = 0; l < m->L; ++l) {
     const Layer& Ly = m->layers[l];
@@ -482,7 +485,7 @@ static hipError_t enqueue_forward(sf_cache* c, const Run& r) {
   AcceptArgs ac{};
   ac.amax = c->amax; ac.nparts = m->nb_head; ac.stage = c->stage_d; ac.len = len; ac.next = next;
   ac.result = c->res_d; ac.draft_out = r.draft_mode ? c->dout_d : nullptr; ac.B = r.B; ac.T = r.T;
-  ac.has_head = head;
+  ac.has_head = head; ac.gate = r.gate;
   ac.slot_lo = head ? r.head_from : 0;
   return launch_accept(ac, s);
 }
@@ -892,7 +895,8 @@ extern "C" sf_status sf_round_create(sf_cache* d, sf_cache* v, int32_t k, sf_rou
   r->d = d;
   r->v = v;
   r->k = k;
-  hipError_t e = hipMalloc((void**)&r->scratch, (size_t)2 * d->B * 4);
+  // [0, B): verifier lengths; [B, 2B): catch-up needed per sequence; [2B]: any of them.
+  hipError_t e = hipMalloc((void**)&r->scratch, (size_t)(2 * d->B + 1) * 4);
   if (e != hipSuccess) {
     round_release(r);
     return fail(SF_E_NOMEM, std::string("hipMalloc: ") + hipGetErrorString(e));
@@ -912,7 +916,10 @@ extern "C" sf_status sf_round_create(sf_cache* d, sf_cache* v, int32_t k, sf_rou
     if (c == hipSuccess) c = launch_round(a, kRoundStage, s);
     if (c == hipSuccess) c = enqueue_forward(v, verify);
     if (c == hipSuccess) c = launch_round(a, kRoundReconcile, s);
-    if (c == hipSuccess) c = enqueue_forward(d, draft);   // catch-up step, commit off
+    // Catch-up step, commit off; its kernels return at once unless a sequence needs it.
+    Run catchup = draft;
+    catchup.gate = r->scratch + 2 * d->B;
+    if (c == hipSuccess) c = enqueue_forward(d, catchup);
     if (c == hipSuccess) c = launch_round(a, kRoundFinish, s);
     const hipError_t ce = hipStreamEndCapture(s, &graph);
     e = (c != hipSuccess) ? c : ce;

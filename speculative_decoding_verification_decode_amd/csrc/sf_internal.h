@@ -93,6 +93,7 @@ struct GemmArgs {
   float2* amax;            // [rows][nb] (value, index bits)
   float* logits;           // optional fp32 [rows][vocab]
   int vocab;
+  const int* gate;        // nullptr, or the pass runs only while *gate != 0 (device flag)
 };
 
 struct EmbedArgs {
@@ -105,6 +106,7 @@ struct EmbedArgs {
   uint16_t* a;             // x * gain as hi/lo bf16 rows [2*rows][H]
   float* ssq;              // [rows][H/32]
   int rows, T, H, V, kmax;
+  const int* gate;        // nullptr, or the pass runs only while *gate != 0 (device flag)
 };
 
 struct AttnArgs {
@@ -120,6 +122,7 @@ struct AttnArgs {
   uint16_t* out;           // combine output as hi/lo bf16 rows [2*rows][nq*dh]
   int rows;
   int dh;
+  const int* gate;        // nullptr, or the pass runs only while *gate != 0 (device flag)
 };
 
 struct AcceptArgs {
@@ -132,6 +135,7 @@ struct AcceptArgs {
   int32_t* draft_out;      // [B][kMaxDraftSteps]
   int B, T, has_head;
   int slot_lo;             // targets of slots below slot_lo are not computed (reported as 0)
+  const int* gate;        // nullptr, or the pass runs only while *gate != 0 (device flag)
 };
 
 // Launchers (kernels.hip).
