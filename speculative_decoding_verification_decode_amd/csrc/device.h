@@ -11,6 +11,8 @@ namespace sf {
 
 // A pass whose kernels carry a gate runs only while the device flag is set; the kernels of a
 // gated-off pass return at once (whole launches, so split arrival counters stay consistent).
+// Only the instances used by one-row bf16 passes (compact GEMM, attention, merge, embed,
+// accept) check it; any other kernel given a gate simply runs.
 __device__ __forceinline__ bool gated_off(const int* gate) { return gate && *gate == 0; }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

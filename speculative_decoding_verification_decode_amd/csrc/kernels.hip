@@ -134,9 +134,12 @@ __device__ void gemm_epilogue(const GemmArgs& g, int nb, int r0, const float* rs
 // (rows + 64rg ..), so each weight tile feeds four MFMAs, and the groups of one block share
 // the block's weights through L2 (see the index mapping below).  A row's arithmetic is the
 // same as in the compact layout: the per-row result does not depend on the batch.
-template <int EPI, int MT, int NW, int KH = kHalf, bool WIDE = false>
+// GATED: the kernel of a gated pass (see gated_off); the check sits in separate instances
+// because reading the flag at entry delays every kernel's first loads (7B verify +1.4%).
+template <int EPI, int MT, int NW, int KH = kHalf, bool WIDE = false, bool GATED = false>
 __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
-  if (gated_off(g.gate)) return;
+  if constexpr (GATED)
+    if (gated_off(g.gate)) return;
   static_assert(!WIDE || MT == 4, "wide row groups hold two hi and two lo m tiles");
   constexpr int kThreads = NW * 64;
   constexpr int kRealRows = MT * 16;
@@ -357,7 +360,6 @@ __device__ __forceinline__ uint32_t nf4_bits(int i) {
 // NR (1 or 2) consecutive 32-row blocks per workgroup share every activation load.
 template <int EPI, int MT, int NW, int KB, int NR>
 __global__ __launch_bounds__(NW * 64) void k_gemm_nf4(const GemmArgs g) {
-  if (gated_off(g.gate)) return;
   constexpr int kThreads = NW * 64;
   constexpr int kRealRows = MT * 16;
   constexpr int kTab = 256 * 32, kImg = NR * MT * 1024;
@@ -636,7 +638,6 @@ hipError_t launch_pack_nf4(uint8_t* dst, const uint8_t* const* rowptr, int N, in
 // The launch covers G 64-row groups from row row0.
 template <int EPI, int kStages, int kBlocks>
 __device__ __forceinline__ void gemm_b_body(const GemmArgs& g, int row0, int G) {
-  if (gated_off(g.gate)) return;
   constexpr int NW = 4, kThreads = 256, kRealRows = 64, MT = 4;
   // Cross-wave images of one weight block: wave w's accumulator register r of m tile mt, lane l
   // at red[w][(mt*16 + r)*kRedPitch + l].  Consecutive lanes hit consecutive banks when the
@@ -834,7 +835,8 @@ static hipError_t gemm_mt(const GemmArgs& g, hipStream_t s) {
   }
   switch (mt) {
     case 1:
-      if (g.kh == 4) k_gemm<EPI, 1, NW, 4><<<grid, block, 0, s>>>(g);
+      if (g.gate) k_gemm<EPI, 1, NW, 4, false, true><<<grid, block, 0, s>>>(g);
+      else if (g.kh == 4) k_gemm<EPI, 1, NW, 4><<<grid, block, 0, s>>>(g);
       else k_gemm<EPI, 1, NW><<<grid, block, 0, s>>>(g);
       break;
     case 2: k_gemm<EPI, 2, NW><<<grid, block, 0, s>>>(g); break;
@@ -866,8 +868,10 @@ hipError_t launch_gemm(int epi, const GemmArgs& g, hipStream_t s) {
 // Embedding: row r = (sequence b, slot i) takes [pending or stage.first, d_1..d_k, 0...][i],
 // writes the fp32 residual, x * ln1 gain as hi/lo bf16 rows, and per-32-column sums of
 // squares.  Thread t handles columns 8t..8t+7; four consecutive lanes form a 32-column block.
+template <bool GATED>
 __global__ __launch_bounds__(256) void k_embed(const EmbedArgs e) {
-  if (gated_off(e.gate)) return;
+  if constexpr (GATED)
+    if (gated_off(e.gate)) return;
   const int r = blockIdx.x;
   const int b = r / e.T, slot = r - b * e.T;
   int tok;
@@ -899,21 +903,24 @@ __global__ __launch_bounds__(256) void k_embed(const EmbedArgs e) {
 }
 
 hipError_t launch_embed(const EmbedArgs& e, hipStream_t s) {
-  k_embed<<<e.rows, 256, 0, s>>>(e);
+  if (e.gate) k_embed<true><<<e.rows, 256, 0, s>>>(e);
+  else k_embed<false><<<e.rows, 256, 0, s>>>(e);
   return hipGetLastError();
 }
 
 // Grid (spans, kv heads, sequences x row groups).
-template <int DH>
+template <int DH, bool GATED = false>
 __global__ __launch_bounds__(256) void k_attn(const AttnArgs a) {
-  if (gated_off(a.gate)) return;
+  if constexpr (GATED)
+    if (gated_off(a.gate)) return;
   const int G = a.nq / a.nkv, ngroups = (a.T * G + 63) / 64;
   attn_spans<DH, false>(a, blockIdx.x, gridDim.x, blockIdx.y, blockIdx.z / ngroups, blockIdx.z % ngroups);
 }
 
-template <int DH>
+template <int DH, bool GATED = false>
 __global__ __launch_bounds__(256) void k_combine(const AttnArgs a) {
-  if (gated_off(a.gate)) return;
+  if constexpr (GATED)
+    if (gated_off(a.gate)) return;
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= a.rows * a.nq) return;
   combine_pair<DH, false>(a, item / a.nq, item % a.nq);
@@ -930,11 +937,21 @@ hipError_t launch_attention(const AttnArgs& a, int dh, int B, hipStream_t s) {
   const dim3 grid(nx, a.nkv, B * ngroups);
   const int ncomb = (a.rows * a.nq + 3) / 4;
   if (dh == 128) {
-    k_attn<128><<<grid, 256, 0, s>>>(a);
-    k_combine<128><<<ncomb, 256, 0, s>>>(a);
+    if (a.gate) {
+      k_attn<128, true><<<grid, 256, 0, s>>>(a);
+      k_combine<128, true><<<ncomb, 256, 0, s>>>(a);
+    } else {
+      k_attn<128><<<grid, 256, 0, s>>>(a);
+      k_combine<128><<<ncomb, 256, 0, s>>>(a);
+    }
   } else if (dh == 64) {
-    k_attn<64><<<grid, 256, 0, s>>>(a);
-    k_combine<64><<<ncomb, 256, 0, s>>>(a);
+    if (a.gate) {
+      k_attn<64, true><<<grid, 256, 0, s>>>(a);
+      k_combine<64, true><<<ncomb, 256, 0, s>>>(a);
+    } else {
+      k_attn<64><<<grid, 256, 0, s>>>(a);
+      k_combine<64><<<ncomb, 256, 0, s>>>(a);
+    }
   } else {
     return hipErrorInvalidValue;
   }
@@ -948,8 +965,10 @@ int attention_spans(int cap) { return span_of(cap - 1) + 1; }
 // choice at each of the T positions (largest value, lowest index on ties; the merge is
 // order independent), count the leading drafts that match, and commit.  Wave w merges the
 // rows w, w+16, ... of the sequence.
+template <bool GATED>
 __global__ __launch_bounds__(1024) void k_accept(const AcceptArgs a) {
-  if (gated_off(a.gate)) return;
+  if constexpr (GATED)
+    if (gated_off(a.gate)) return;
   __shared__ int tgt[kMaxRows];   // one per slot: up to k_max+1 in a verify, a whole prefill chunk
   const int b = blockIdx.x, tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -1009,7 +1028,8 @@ __global__ __launch_bounds__(1024) void k_accept(const AcceptArgs a) {
 
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t s) {
   if (a.T < 1 || a.T > kMaxRows) return hipErrorInvalidValue;
-  k_accept<<<a.B, 1024, 0, s>>>(a);
+  if (a.gate) k_accept<true><<<a.B, 1024, 0, s>>>(a);
+  else k_accept<false><<<a.B, 1024, 0, s>>>(a);
   return hipGetLastError();
 }
 
