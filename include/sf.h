@@ -294,6 +294,18 @@ sf_status sf_sync(sf_cache* cache);
 sf_status sf_time_kernel(sf_cache* cache, int32_t kernel, int32_t iters, float* avg_us,
                          double* bytes);
 
+/* sf_debug_counters: waits for the stream, then reports the sum and the largest value of
+ * the cache's k-split arrival counters (host *sum, *max).  The last of the workgroups
+ * splitting an output block resets its counter, so both are 0 between passes; a test reads
+ * them to check that no counter grows from pass to pass.  Errors: SF_E_ARG, SF_E_HIP. */
+sf_status sf_debug_counters(sf_cache* cache, int64_t* sum, int32_t* max);
+
+/* Error injection for tests of the failure path: with SF_FAULT=alloc in the environment every
+ * device allocation of sf_model_create(_nf4), sf_cache_alloc and sf_round_create fails as an
+ * out-of-memory hipMalloc would (SF_E_NOMEM, nothing left allocated); with SF_FAULT=launch
+ * every graph replay and eager pass fails as a failed launch would (SF_E_HIP), before the
+ * call changes any sequence's length or pending token.  Read at every use. */
+
 /* sf_last_error: message of the calling thread's last failed call ("" if none). */
 const char* sf_last_error(void);
 

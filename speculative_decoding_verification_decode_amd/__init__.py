@@ -92,6 +92,7 @@ def lib():
             "sf_kv_read": [_P, _I, _P, _P, _I, _I],
             "sf_sync": [_P],
             "sf_time_kernel": [_P, _I, _I, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double)],
+            "sf_debug_counters": [_P, ctypes.POINTER(ctypes.c_int64), _PI],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -294,6 +295,13 @@ def sf_time_kernel(cache, kernel, iters):
     us, by = ctypes.c_float(0), ctypes.c_double(0)
     _check(lib().sf_time_kernel(cache, kernel, iters, ctypes.byref(us), ctypes.byref(by)))
     return us.value, by.value
+
+
+def sf_debug_counters(cache):
+    """(sum, max) of the cache's k-split arrival counters; both 0 between passes."""
+    sm, mx = ctypes.c_int64(0), ctypes.c_int32(0)
+    _check(lib().sf_debug_counters(cache, ctypes.byref(sm), ctypes.byref(mx)))
+    return sm.value, mx.value
 
 
 # ------------------------------------------------------------------ torch conveniences

@@ -11,8 +11,8 @@ namespace sf {
 
 // A pass whose kernels carry a gate runs only while the device flag is set; the kernels of a
 // gated-off pass return at once (whole launches, so split arrival counters stay consistent).
-// Only the instances used by one-row bf16 passes (compact GEMM, attention, merge, embed,
-// accept) check it; any other kernel given a gate simply runs.
+// Every kernel a one-row-per-sequence pass can launch (compact and NF4 GEMMs of any m-tile
+// count, attention, merge, embed, accept) has a gated instance that checks it.
 __device__ __forceinline__ bool gated_off(const int* gate) { return gate && *gate == 0; }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -418,6 +418,19 @@ __device__ void combine_pair(const AttnArgs& a, int r, int h) {
   const float inv = 1.0f / Ls;
   store_split<kCoh>(a.out, a.rows, r, h * DH + lane, o0 * inv);
   if (DH > 64) store_split<kCoh>(a.out, a.rows, r, h * DH + lane + 64, o1 * inv);
+}
+
+// k split by last arrival: each of the sp workgroups of one output block calls this once,
+// after its partial tile is stored agent-coherently and those stores have completed; exactly
+// one of them (the one whose arrival completes the count) gets true and then reads the
+// others' partials with agent-coherent loads.  That one puts the counter back to zero: all sp
+// arrivals of this launch have happened, and the next launch that uses the counter starts
+// after this kernel has ended, so a counter is zero between launches and never exceeds sp.
+__device__ __forceinline__ bool split_arrive(int* counter, int sp) {
+  const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (old + 1 != sp) return false;
+  __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
 }
 
 __device__ __forceinline__ void amax_merge(float& bv, int& bi, float v, int i) {

@@ -287,7 +287,8 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
   // k split over g.sp workgroups per block: each stores its partial tile (agent-coherent,
   // so the others see it without a cache flush) and counts its arrival on the block's
   // counter; the one that brings the count to a multiple of sp adds the partials in split
-  // order and runs the epilogue.  The counters only grow, by sp per launch.
+  // order and runs the epilogue.  The last arriver also puts the counter back to zero, so
+  // every counter stays in [0, sp) and is zero between launches (no growth, no wrap).
   __shared__ int last_arrival;
   const bool split = g.sp > 1;
   float* const pblk = g.part + (size_t)nb * g.sp * g.rows * 32;   // [split][row][32]
@@ -304,11 +305,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) {
-      const int old = __hip_atomic_fetch_add(g.counters + nb * G + rg, 1, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-      last_arrival = ((old + 1) % g.sp) == 0;
-    }
+    if (tid == 0) last_arrival = split_arrive(g.counters + nb * G + rg, g.sp);
     __syncthreads();
     if (!last_arrival) return;
     asm volatile("" ::: "memory");
@@ -320,7 +317,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
   auto val = [&](int nl, int m) {
     if (!split) return tval(nl, m);
     float s = 0.f;
-    for (int q = 0; q < g.sp; ++q) s += pblk[((size_t)q * g.rows + r0 + m) * 32 + nl];
+    for (int q = 0; q < g.sp; ++q) s += ld<true>(pblk + ((size_t)q * g.rows + r0 + m) * 32 + nl);
     return s;
   };
   gemm_epilogue<EPI, kRealRows, kThreads>(g, nb, r0, rscale, val);
@@ -358,8 +355,10 @@ __device__ __forceinline__ uint32_t nf4_bits(int i) {
 }
 
 // NR (1 or 2) consecutive 32-row blocks per workgroup share every activation load.
-template <int EPI, int MT, int NW, int KB, int NR>
+template <int EPI, int MT, int NW, int KB, int NR, bool GATED = false>
 __global__ __launch_bounds__(NW * 64) void k_gemm_nf4(const GemmArgs g) {
+  if constexpr (GATED)
+    if (gated_off(g.gate)) return;
   constexpr int kThreads = NW * 64;
   constexpr int kRealRows = MT * 16;
   constexpr int kTab = 256 * 32, kImg = NR * MT * 1024;
@@ -547,10 +546,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_nf4(const GemmArgs g) {
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (tid == 0) {
-        const int old = __hip_atomic_fetch_add(g.counters + nb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last_arrival = ((old + 1) % g.sp) == 0;
-      }
+      if (tid == 0) last_arrival = split_arrive(g.counters + nb, g.sp);
       __syncthreads();
       if (!last_arrival) continue;   // workgroup-uniform
       asm volatile("" ::: "memory");
@@ -558,7 +554,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_nf4(const GemmArgs g) {
     auto val = [&](int nl, int m) {
       if (!split) return tval(nl, m);
       float s = 0.f;
-      for (int q = 0; q < g.sp; ++q) s += pblk[((size_t)q * g.rows + m) * 32 + nl];
+      for (int q = 0; q < g.sp; ++q) s += ld<true>(pblk + ((size_t)q * g.rows + m) * 32 + nl);
       return s;
     };
     gemm_epilogue<EPI, kRealRows, kThreads>(g, nb, 0, rscale, val);
@@ -566,22 +562,30 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_nf4(const GemmArgs g) {
   }
 }
 
-template <int EPI>
-static hipError_t gemm_nf4(const GemmArgs& g, hipStream_t s) {
-  if (g.rows < 1 || g.rows > 64 || g.kb % 4) return hipErrorInvalidValue;
-  const int mt = (2 * g.rows + 31) / 32;
+template <int EPI, bool GATED>
+static hipError_t gemm_nf4_mt(const GemmArgs& g, int mt, hipStream_t s) {
   const dim3 block(256);
   switch (mt) {
     case 1:
       // Two row blocks per workgroup halve the activation traffic, where that still leaves a
       // workgroup per CU (gate/up at the 14B shape: 864 blocks; 32.5 -> 25.4 us).
-      if (g.nb % 2 == 0 && g.nb / 2 * g.sp >= 256) k_gemm_nf4<EPI, 1, 4, 1, 2><<<dim3(g.nb / 2 * g.sp), block, 0, s>>>(g);
-      else k_gemm_nf4<EPI, 1, 4, 2, 1><<<dim3(g.nb * g.sp), block, 0, s>>>(g);
+      if (g.nb % 2 == 0 && g.nb / 2 * g.sp >= 256)
+        k_gemm_nf4<EPI, 1, 4, 1, 2, GATED><<<dim3(g.nb / 2 * g.sp), block, 0, s>>>(g);
+      else
+        k_gemm_nf4<EPI, 1, 4, 2, 1, GATED><<<dim3(g.nb * g.sp), block, 0, s>>>(g);
       break;
-    case 2: k_gemm_nf4<EPI, 2, 4, 1, 1><<<dim3(g.nb * g.sp), block, 0, s>>>(g); break;
-    default: k_gemm_nf4<EPI, 4, 4, 1, 1><<<dim3(g.nb * g.sp), block, 0, s>>>(g); break;
+    case 2: k_gemm_nf4<EPI, 2, 4, 1, 1, GATED><<<dim3(g.nb * g.sp), block, 0, s>>>(g); break;
+    default: k_gemm_nf4<EPI, 4, 4, 1, 1, GATED><<<dim3(g.nb * g.sp), block, 0, s>>>(g); break;
   }
   return hipGetLastError();
+}
+
+template <int EPI>
+static hipError_t gemm_nf4(const GemmArgs& g, hipStream_t s) {
+  if (g.rows < 1 || g.rows > 64 || g.kb % 4) return hipErrorInvalidValue;
+  const int mt = (2 * g.rows + 31) / 32;
+  if (g.gate) return gemm_nf4_mt<EPI, true>(g, mt, s);
+  return gemm_nf4_mt<EPI, false>(g, mt, s);
 }
 
 hipError_t launch_gemm_nf4(int epi, const GemmArgs& g, hipStream_t s) {
@@ -788,11 +792,7 @@ __device__ __forceinline__ void gemm_b_body(const GemmArgs& g, int row0, int G) 
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(g.counters + nb0 * ((g.rows + 63) / 64) + r0 / 64, 1, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-    last_arrival = ((old + 1) % g.sp) == 0;
-  }
+  if (tid == 0) last_arrival = split_arrive(g.counters + nb0 * ((g.rows + 63) / 64) + r0 / 64, g.sp);
   __syncthreads();
   if (!last_arrival) return;
   asm volatile("" ::: "memory");
@@ -800,7 +800,7 @@ __device__ __forceinline__ void gemm_b_body(const GemmArgs& g, int row0, int G) 
     const float* const pblk = g.part + (size_t)(nb0 + j) * g.sp * g.rows * 32;
     auto val = [&](int nl, int m) {
       float s = 0.f;
-      for (int q2 = 0; q2 < g.sp; ++q2) s += pblk[((size_t)q2 * g.rows + r0 + m) * 32 + nl];
+      for (int q2 = 0; q2 < g.sp; ++q2) s += ld<true>(pblk + ((size_t)q2 * g.rows + r0 + m) * 32 + nl);
       return s;
     };
     gemm_epilogue<EPI, kRealRows, kThreads>(g, nb0 + j, r0, rscale, val);
@@ -821,6 +821,8 @@ static hipError_t gemm_mt(const GemmArgs& g, hipStream_t s) {
   const int mt = (2 * g.rows + 31) / 32;
   const dim3 grid(g.nb * g.sp), block(NW * 64);
   if (g.rows > 64) {
+    // A gated pass is a drafter step of one row per sequence (at most 64 rows), never here.
+    if (g.gate) return hipErrorInvalidValue;
     const int G = (g.rows + 63) / 64;
     if (g.nb % 2 == 0) {
       // Row groups before the one holding row_lo are skipped (their outputs are not needed).
@@ -839,9 +841,15 @@ static hipError_t gemm_mt(const GemmArgs& g, hipStream_t s) {
       else if (g.kh == 4) k_gemm<EPI, 1, NW, 4><<<grid, block, 0, s>>>(g);
       else k_gemm<EPI, 1, NW><<<grid, block, 0, s>>>(g);
       break;
-    case 2: k_gemm<EPI, 2, NW><<<grid, block, 0, s>>>(g); break;
+    case 2:
+      if (g.gate) k_gemm<EPI, 2, NW, kHalf, false, true><<<grid, block, 0, s>>>(g);
+      else k_gemm<EPI, 2, NW><<<grid, block, 0, s>>>(g);
+      break;
     case 3:
-    case 4: k_gemm<EPI, 4, NW, 4><<<grid, block, 0, s>>>(g); break;
+    case 4:
+      if (g.gate) k_gemm<EPI, 4, NW, 4, false, true><<<grid, block, 0, s>>>(g);
+      else k_gemm<EPI, 4, NW, 4><<<grid, block, 0, s>>>(g);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

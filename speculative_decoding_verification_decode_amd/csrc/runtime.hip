@@ -31,6 +31,25 @@ static sf_status fail(sf_status code, const std::string& msg) {
     if (e_ != hipSuccess) return fail(SF_E_HIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
   } while (0)
 
+// Fault injection for tests of the error path.  SF_FAULT=alloc makes every device allocation
+// fail as an out-of-memory hipMalloc would (the call returns SF_E_NOMEM); SF_FAULT=launch makes
+// every graph replay and eager pass fail as a failed launch would (SF_E_HIP), before the call
+// changes any sequence state.  Read at every use, so a process can switch it on and off.
+static bool injected(const char* what) {
+  const char* v = getenv("SF_FAULT");
+  return v && strcmp(v, what) == 0;
+}
+
+static hipError_t dev_malloc(void** p, size_t bytes) {
+  if (injected("alloc")) return hipErrorOutOfMemory;
+  return hipMalloc(p, bytes);
+}
+
+static hipError_t graph_launch(hipGraphExec_t x, hipStream_t s) {
+  if (injected("launch")) return hipErrorLaunchFailure;
+  return hipGraphLaunch(x, s);
+}
+
 namespace {
 
 struct Layer {
@@ -41,7 +60,7 @@ struct Layer {
 struct DevAllocs {
   std::vector<void*> ptrs;
   hipError_t alloc(void** p, size_t bytes) {
-    hipError_t e = hipMalloc(p, std::max<size_t>(bytes, 256));
+    hipError_t e = dev_malloc(p, std::max<size_t>(bytes, 256));
     if (e == hipSuccess) ptrs.push_back(*p);
     return e;
   }
@@ -68,6 +87,23 @@ struct sf_model {
   DevAllocs mem;
 };
 
+// Per-pass working memory: everything a pass writes besides the KV pool and the sequence state
+// (length, pending token).  A cache owns one set (allocated in sf_cache_alloc, captured by its
+// graphs); the no-allocation entry point carves another from a static device array.
+struct Scratch {
+  Stage* stage_d = nullptr;        // staging block: flags, k, drafts
+  float* x = nullptr;              // residual [rows][H] fp32
+  uint16_t *a_h = nullptr, *a_o = nullptr, *a_f = nullptr;   // GEMM operands (hi/lo, MFMA order)
+  uint16_t* hidden = nullptr;      // bf16 hidden-state output [rows][H] (hidden-only stacks)
+  float *ssq = nullptr, *q = nullptr, *apart = nullptr;
+  float2* amax = nullptr;          // LM head per-block (max, index) [rows][V/32]
+  float* part = nullptr;           // k-split partials
+  int* cnt = nullptr;              // k-split arrival counters [layer][QKV, O, down][block][row group]
+  int cnt_stride = 0;
+  int32_t* res_d = nullptr;        // {accepted[B], target[B][T]}
+  int32_t* dout_d = nullptr;       // draft-step outputs [B][kMaxDraftSteps]
+};
+
 struct Run {
   int B, T, seq0, kmax;
   float* logits;
@@ -77,6 +113,8 @@ struct Run {
   int head_from = 0;
   // Device flag: the pass's kernels run only while it is nonzero (nullptr: always run).
   const int* gate = nullptr;
+  // Working memory of the pass (nullptr: the cache's own).
+  const Scratch* sc = nullptr;
 };
 
 struct sf_cache {
@@ -86,20 +124,13 @@ struct sf_cache {
   size_t layer_stride, seq_stride;  // elements
   uint16_t *kpool = nullptr, *vpool = nullptr;
   int32_t *len = nullptr, *next = nullptr;
-  Stage* stage_d = nullptr;
+  Scratch sc;
   Stage* stage_h = nullptr;
-  float* x = nullptr;
-  uint16_t *a_h = nullptr, *a_o = nullptr, *a_f = nullptr, *hidden = nullptr;
-  float *ssq = nullptr, *q = nullptr, *apart = nullptr;
-  float2* amax = nullptr;
   float2* rope = nullptr;
-  int32_t *res_d = nullptr, *res_h = nullptr, *dout_d = nullptr, *dout_h = nullptr;
+  int32_t *res_h = nullptr, *dout_h = nullptr;
   int nw_qkv, nw_o, nw_gu, nw_d, nw_head;
   int sp_qkv, sp_o, sp_gu, sp_d, sp_head;
-  float* part = nullptr;
   int kh = 4;                      // GEMM: weight tiles per pipelined batch (one-tile row counts)
-  int* cnt = nullptr;              // k-split arrival counters [layer][QKV, O, down][block]
-  int cnt_stride = 0;
   hipGraphExec_t gx_verify = nullptr, gx_draft = nullptr;
   uint16_t *snap_k = nullptr, *snap_v = nullptr;   // state snapshot: K/V rows [len, len+T)
   int32_t *snap_len = nullptr, *snap_next = nullptr;
@@ -165,7 +196,7 @@ static sf_status check_desc(const sf_model_desc* d) {
 template <typename Fn>
 static sf_status with_table(const std::vector<const uint16_t*>& tab, hipStream_t s, Fn fn) {
   const uint16_t** dt = nullptr;
-  HIPCHK(hipMalloc((void**)&dt, tab.size() * sizeof(void*)));
+  HIPCHK(dev_malloc((void**)&dt, tab.size() * sizeof(void*)));
   hipError_t e = hipMemcpyAsync(dt, tab.data(), tab.size() * sizeof(void*), hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = fn(dt);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
@@ -184,6 +215,7 @@ static sf_status create_model(const sf_model_desc* desc, const void* const* weig
                               sf_model** out, bool nf4) {
   if (sf_status st = check_desc(desc)) return st;
   if (!weights || !out) return fail(SF_E_ARG, "weights or out is NULL");
+  *out = nullptr;
   if (nf4 && (desc->hidden % kNf4Block || desc->ffn % kNf4Block || (desc->n_q_heads * desc->head_dim) % kNf4Block))
     return fail(SF_E_ARG, "NF4 needs hidden, ffn and n_q_heads*head_dim to be multiples of 64");
   sf_model* m = new sf_model();
@@ -393,12 +425,13 @@ enum GemmKind { kGQkv = 0, kGO = 1, kGGateUp = 2, kGDown = 3, kGHead = 4 };
 
 // One GEMM of kind `kind` in layer `layer`; a k split (g.sp > 1) uses the arrival counters
 // of that layer and kind.
-static hipError_t run_gemm(const sf_cache* c, int kind, int layer, int epi, GemmArgs g, hipStream_t s) {
+static hipError_t run_gemm(const sf_cache* c, const Scratch& S, int kind, int layer, int epi, GemmArgs g,
+                           hipStream_t s) {
   g.kh = c->kh;
   if (g.sp > 1) {
     if (kind == kGGateUp || kind == kGHead) return hipErrorInvalidValue;
     const int slot = layer * 3 + (kind == kGQkv ? 0 : kind == kGO ? 1 : 2);
-    g.counters = c->cnt + (size_t)slot * c->cnt_stride;
+    g.counters = S.cnt + (size_t)slot * S.cnt_stride;
   }
   if (c->m->nf4 && kind != kGHead) return launch_gemm_nf4(epi, g, s);
   return launch_gemm(epi, g, s);
@@ -409,8 +442,10 @@ static hipError_t run_gemm(const sf_cache* c, int kind, int layer, int epi, Gemm
 // One forward pass (embed .. accept) enqueued on the model stream.  Used both eagerly and
 // under stream capture, so it must not allocate or synchronise.
 static hipError_t enqueue_forward(sf_cache* c, const Run& r) {
+  if (injected("launch")) return hipErrorLaunchFailure;
   sf_model* m = c->m;
   const sf_model_desc& d = m->d;
+  const Scratch& S = r.sc ? *r.sc : c->sc;
   hipStream_t s = m->stream;
   const int rows = r.B * r.T;
   int32_t* len = c->len + r.seq0;
@@ -419,21 +454,21 @@ static hipError_t enqueue_forward(sf_cache* c, const Run& r) {
   hipError_t e;
 
   EmbedArgs ea{};
-  ea.embed = m->embed; ea.stage = c->stage_d; ea.len = len; ea.next = next; ea.gain = m->layers[0].g1;
-  ea.x = c->x; ea.a = c->a_h; ea.ssq = c->ssq; ea.rows = rows; ea.T = r.T; ea.H = m->H; ea.V = m->V;
+  ea.embed = m->embed; ea.stage = S.stage_d; ea.len = len; ea.next = next; ea.gain = m->layers[0].g1;
+  ea.x = S.x; ea.a = S.a_h; ea.ssq = S.ssq; ea.rows = rows; ea.T = r.T; ea.H = m->H; ea.V = m->V;
   ea.kmax = r.kmax; ea.gate = r.gate;
   if ((e = launch_embed(ea, s)) != hipSuccess) return e;
 
   GemmArgs base{};
-  base.rows = rows; base.ssq_in = c->ssq; base.part = c->part; base.sp = 1;
+  base.rows = rows; base.ssq_in = S.ssq; base.part = S.part; base.sp = 1;
   base.nparts_in = m->H / kTileN; base.eps = d.rms_eps; base.T = r.T; base.len = len; base.cap = c->cap;
   base.seq_stride = (long)c->seq_stride; base.rope = c->rope; base.nq = m->nq; base.nkv = m->nkv; base.dh = m->dh;
   base.gate = r.gate;
 
   AttnArgs aa{};
-  aa.q = c->q; aa.seq_stride = (long)c->seq_stride; aa.cap = c->cap; aa.len = len; aa.T = r.T; aa.nq = m->nq;
+  aa.q = S.q; aa.seq_stride = (long)c->seq_stride; aa.cap = c->cap; aa.len = len; aa.T = r.T; aa.nq = m->nq;
   aa.nkv = m->nkv; aa.nchunk = c->nchunk; aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)m->dh));
-  aa.part = c->apart; aa.out = c->a_o; aa.rows = rows; aa.dh = m->dh; aa.gate = r.gate;
+  aa.part = S.apart; aa.out = S.a_o; aa.rows = rows; aa.dh = m->dh; aa.gate = r.gate;
 
   for (int l = 0; l < m->L; ++l) {
     const Layer& Ly = m->layers[l];
@@ -441,50 +476,50 @@ static hipError_t enqueue_forward(sf_cache* c, const Run& r) {
     uint16_t* vc = c->vpool + (size_t)l * c->layer_stride + kvoff;
 
     GemmArgs g = base;
-    g.w = Ly.wqkv; g.a = c->a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_qkv; g.nw = c->nw_qkv;
+    g.w = Ly.wqkv; g.a = S.a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_qkv; g.nw = c->nw_qkv;
     g.sp = c->sp_qkv; g.n_out = m->Q + 2 * m->KV;
-    g.bias = Ly.bqkv; g.q = c->q; g.kc = kc; g.vc = vc;
-    if ((e = run_gemm(c, kGQkv, l, kEpiQkv, g, s)) != hipSuccess) return e;
+    g.bias = Ly.bqkv; g.q = S.q; g.kc = kc; g.vc = vc;
+    if ((e = run_gemm(c, S, kGQkv, l, kEpiQkv, g, s)) != hipSuccess) return e;
 
     aa.kc = kc; aa.vc = vc;
     if ((e = launch_attention(aa, m->dh, r.B, s)) != hipSuccess) return e;
 
     g = base;
-    g.w = Ly.wo; g.a = c->a_o; g.k = m->Q; g.kb = m->Q / kTileK; g.nb = m->nb_h; g.nw = c->nw_o;
+    g.w = Ly.wo; g.a = S.a_o; g.k = m->Q; g.kb = m->Q / kTileK; g.nb = m->nb_h; g.nw = c->nw_o;
     g.sp = c->sp_o;
-    g.x = c->x; g.a_next = c->a_h; g.gain_next = Ly.g2; g.ssq_out = c->ssq; g.n_out = m->H;
-    if ((e = run_gemm(c, kGO, l, kEpiResid, g, s)) != hipSuccess) return e;
+    g.x = S.x; g.a_next = S.a_h; g.gain_next = Ly.g2; g.ssq_out = S.ssq; g.n_out = m->H;
+    if ((e = run_gemm(c, S, kGO, l, kEpiResid, g, s)) != hipSuccess) return e;
 
     g = base;
-    g.w = Ly.wgu; g.a = c->a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_gu; g.nw = c->nw_gu;
+    g.w = Ly.wgu; g.a = S.a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_gu; g.nw = c->nw_gu;
     g.sp = 1;
-    g.h = c->a_f; g.ffn = m->F;
-    if ((e = run_gemm(c, kGGateUp, l, kEpiSwiglu, g, s)) != hipSuccess) return e;
+    g.h = S.a_f; g.ffn = m->F;
+    if ((e = run_gemm(c, S, kGGateUp, l, kEpiSwiglu, g, s)) != hipSuccess) return e;
 
     const bool last = (l + 1 == m->L);
     g = base;
-    g.w = Ly.wd; g.a = c->a_f; g.k = m->F; g.kb = m->F / kTileK; g.nb = m->nb_h; g.nw = c->nw_d;
-    g.x = c->x; g.a_next = c->a_h;
+    g.w = Ly.wd; g.a = S.a_f; g.k = m->F; g.kb = m->F / kTileK; g.nb = m->nb_h; g.nw = c->nw_d;
+    g.x = S.x; g.a_next = S.a_h;
     g.gain_next = !last ? m->layers[l + 1].g1 : (d.has_head ? m->gfinal : m->ones);
-    g.ssq_out = c->ssq; g.n_out = m->H;
-    g.hidden = (last && !d.has_head) ? c->hidden : nullptr;
+    g.ssq_out = S.ssq; g.n_out = m->H;
+    g.hidden = (last && !d.has_head) ? S.hidden : nullptr;
     g.sp = c->sp_d;
-    if ((e = run_gemm(c, kGDown, l, kEpiResid, g, s)) != hipSuccess) return e;
+    if ((e = run_gemm(c, S, kGDown, l, kEpiResid, g, s)) != hipSuccess) return e;
   }
 
   const bool head = d.has_head && r.head_from >= 0;
   if (head) {
     GemmArgs g = base;
-    g.w = m->head; g.a = c->a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_head; g.nw = c->nw_head;
+    g.w = m->head; g.a = S.a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_head; g.nw = c->nw_head;
     g.sp = 1;
-    g.amax = c->amax; g.logits = r.logits; g.vocab = m->V;
+    g.amax = S.amax; g.logits = r.logits; g.vocab = m->V;
     g.row_lo = r.head_from;
-    if ((e = run_gemm(c, kGHead, 0, kEpiArgmax, g, s)) != hipSuccess) return e;
+    if ((e = run_gemm(c, S, kGHead, 0, kEpiArgmax, g, s)) != hipSuccess) return e;
   }
 
   AcceptArgs ac{};
-  ac.amax = c->amax; ac.nparts = m->nb_head; ac.stage = c->stage_d; ac.len = len; ac.next = next;
-  ac.result = c->res_d; ac.draft_out = r.draft_mode ? c->dout_d : nullptr; ac.B = r.B; ac.T = r.T;
+  ac.amax = S.amax; ac.nparts = m->nb_head; ac.stage = S.stage_d; ac.len = len; ac.next = next;
+  ac.result = S.res_d; ac.draft_out = r.draft_mode ? S.dout_d : nullptr; ac.B = r.B; ac.T = r.T;
   ac.has_head = head; ac.gate = r.gate;
   ac.slot_lo = head ? r.head_from : 0;
   return launch_accept(ac, s);
@@ -507,6 +542,36 @@ static sf_status capture(sf_cache* c, const Run& r, hipGraphExec_t* out) {
   return SF_OK;
 }
 
+// Lay out the working memory of passes of up to R rows on cache c: take(&ptr, bytes) hands out
+// each buffer (an allocation for the cache's own set, a piece of the static array for the
+// no-allocation entry point).  With `own`, also the result and draft-output buffers, which the
+// no-allocation entry point takes from its caller or does not need.
+template <typename Take>
+static sf_status plan_scratch(const sf_cache* c, size_t R, Scratch& S, bool own, Take take) {
+  const sf_model* m = c->m;
+  sf_status st;
+  if ((st = take((void**)&S.stage_d, sizeof(Stage)))) return st;
+  if ((st = take((void**)&S.x, R * m->H * 4))) return st;
+  if ((st = take((void**)&S.a_h, act_bytes(2 * (int)R, m->H)))) return st;
+  if ((st = take((void**)&S.a_o, act_bytes(2 * (int)R, m->Q)))) return st;
+  if ((st = take((void**)&S.a_f, act_bytes(2 * (int)R, m->F)))) return st;
+  if ((st = take((void**)&S.hidden, R * m->H * 2))) return st;
+  if ((st = take((void**)&S.ssq, R * (m->H / kTileN) * 4))) return st;
+  const size_t n_qkv = (size_t)m->Q + 2 * m->KV;
+  const size_t pe = std::max({(size_t)c->sp_qkv * n_qkv, (size_t)c->sp_o * m->H, (size_t)c->sp_d * m->H});
+  if ((st = take((void**)&S.part, pe * R * 4))) return st;
+  S.cnt_stride = std::max(m->nb_qkv, m->nb_h) * (int)((R + 63) / 64);   // [block][64-row group]
+  if ((st = take((void**)&S.cnt, (size_t)m->L * 3 * S.cnt_stride * 4))) return st;
+  if ((st = take((void**)&S.q, R * m->Q * 4))) return st;
+  if ((st = take((void**)&S.apart, R * m->nq * (size_t)c->nchunk * (m->dh + 2) * 4))) return st;
+  if ((st = take((void**)&S.amax, R * m->nb_head * 8))) return st;
+  if (own) {
+    if ((st = take((void**)&S.res_d, 4 * kMaxRows * 4))) return st;
+    if ((st = take((void**)&S.dout_d, (size_t)c->B * kMaxDraftSteps * 4))) return st;
+  }
+  return SF_OK;
+}
+
 static void cache_release(sf_cache* c) {
   if (c->gx_verify) (void)hipGraphExecDestroy(c->gx_verify);
   if (c->gx_draft) (void)hipGraphExecDestroy(c->gx_draft);
@@ -522,6 +587,7 @@ static void cache_release(sf_cache* c) {
 extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacity, int32_t k_max,
                                     sf_cache** out) {
   if (!m || !out) return fail(SF_E_ARG, "model or out is NULL");
+  *out = nullptr;
   if (k_max < 0 || k_max >= kMaxK) return fail(SF_E_ARG, "k_max must be in 0..15");
   if (n_seqs < 1 || n_seqs > kMaxSeqs || n_seqs * (k_max + 1) > kMaxRows)
     return fail(SF_E_ARG, "n_seqs must be in 1..64 and n_seqs*(k_max+1) in 1..512");
@@ -570,26 +636,8 @@ extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacit
   TRY(dalloc((void**)&c->vpool, pool));
   TRY(dalloc((void**)&c->len, n_seqs * 4));
   TRY(dalloc((void**)&c->next, n_seqs * 4));
-  TRY(dalloc((void**)&c->stage_d, sizeof(Stage)));
-  TRY(dalloc((void**)&c->x, R * m->H * 4));
-  TRY(dalloc((void**)&c->a_h, act_bytes(2 * (int)R, m->H)));
-  TRY(dalloc((void**)&c->a_o, act_bytes(2 * (int)R, m->Q)));
-  TRY(dalloc((void**)&c->a_f, act_bytes(2 * (int)R, m->F)));
-  TRY(dalloc((void**)&c->hidden, R * m->H * 2));
-  TRY(dalloc((void**)&c->ssq, R * (m->H / kTileN) * 4));
-  {
-    const size_t n_qkv = (size_t)m->Q + 2 * m->KV;
-    size_t pe = std::max({(size_t)c->sp_qkv * n_qkv, (size_t)c->sp_o * m->H, (size_t)c->sp_d * m->H});
-    TRY(dalloc((void**)&c->part, pe * R * 4));
-    c->cnt_stride = std::max(m->nb_qkv, m->nb_h) * (int)((R + 63) / 64);   // [block][64-row group]
-    TRY(dalloc((void**)&c->cnt, (size_t)m->L * 3 * c->cnt_stride * 4));
-  }
-  TRY(dalloc((void**)&c->q, R * m->Q * 4));
-  TRY(dalloc((void**)&c->apart, R * m->nq * (size_t)c->nchunk * (m->dh + 2) * 4));
-  TRY(dalloc((void**)&c->amax, R * m->nb_head * 8));
+  TRY(plan_scratch(c, R, c->sc, true, dalloc));
   TRY(dalloc((void**)&c->rope, (size_t)capacity * (m->dh / 2) * 8));
-  TRY(dalloc((void**)&c->res_d, 4 * kMaxRows * 4));
-  TRY(dalloc((void**)&c->dout_d, (size_t)n_seqs * kMaxDraftSteps * 4));
   {
     const size_t snap = (size_t)m->L * n_seqs * m->nkv * c->T * m->dh * 2;
     TRY(dalloc((void**)&c->snap_k, snap));
@@ -629,7 +677,7 @@ extern "C" sf_status sf_cache_free(sf_cache* c) {
 static sf_status refresh(sf_cache* c) {
   hipStream_t s = c->m->stream;
   HIPCHK(hipStreamSynchronize(s));
-  HIPCHK(hipMemcpy(c->res_h, c->res_d, 4 * kMaxRows * 4, hipMemcpyDeviceToHost));
+  HIPCHK(hipMemcpy(c->res_h, c->sc.res_d, 4 * kMaxRows * 4, hipMemcpyDeviceToHost));
   HIPCHK(hipMemcpy(c->res_h, c->len, c->B * 4, hipMemcpyDeviceToHost));
   for (int b = 0; b < c->B; ++b) c->len_h[b] = c->res_h[b];
   HIPCHK(hipMemcpy(c->res_h, c->next, c->B * 4, hipMemcpyDeviceToHost));
@@ -672,16 +720,16 @@ extern "C" sf_status sf_verify(sf_cache* c, const int32_t* draft, const int32_t*
     st->step[b] = 0;
     for (int j = 0; j < c->kmax; ++j) st->draft[b * c->kmax + j] = (j < kb) ? draft[b * c->kmax + j] : 0;
   }
-  HIPCHK(hipMemcpyAsync(c->stage_d, st, stage_bytes(c->B, c->kmax), hipMemcpyHostToDevice, s));
+  HIPCHK(hipMemcpyAsync(c->sc.stage_d, st, stage_bytes(c->B, c->kmax), hipMemcpyHostToDevice, s));
   if (dbg) {
     hipError_t e = enqueue_forward(c, Run{c->B, c->T, 0, c->kmax, (float*)dev_out, false, false});
     if (e != hipSuccess) return fail(SF_E_HIP, std::string("forward: ") + hipGetErrorString(e));
   } else {
-    HIPCHK(hipGraphLaunch(c->gx_verify, s));
+    HIPCHK(graph_launch(c->gx_verify, s));
   }
-  HIPCHK(hipMemcpyAsync(c->res_h, c->res_d, 4 * kMaxRows * 4, hipMemcpyDeviceToHost, s));
+  HIPCHK(hipMemcpyAsync(c->res_h, c->sc.res_d, 4 * kMaxRows * 4, hipMemcpyDeviceToHost, s));
   if (!m->d.has_head && dev_out)
-    HIPCHK(hipMemcpyAsync(dev_out, c->hidden, (size_t)c->B * c->T * m->H * 2, hipMemcpyDeviceToDevice, s));
+    HIPCHK(hipMemcpyAsync(dev_out, c->sc.hidden, (size_t)c->B * c->T * m->H * 2, hipMemcpyDeviceToDevice, s));
   HIPCHK(hipStreamSynchronize(s));
   for (int b = 0; b < c->B; ++b) {
     const int M = c->res_h[b];
@@ -709,10 +757,10 @@ extern "C" sf_status sf_verify_device(sf_cache* c, const int32_t* dev_draft, con
     if (c->len_hi[b] + c->T > c->cap)
       return fail(SF_E_CAPACITY, "sequence " + std::to_string(b) + ": length may exceed capacity (sf_sync first)");
   hipStream_t s = c->m->stream;
-  const int32_t* dd = dev_draft ? dev_draft : c->res_d;
-  hipError_t e = launch_stage_device(c->stage_d, dd, dev_k, c->B, c->kmax, (int)flags, s);
+  const int32_t* dd = dev_draft ? dev_draft : c->sc.res_d;
+  hipError_t e = launch_stage_device(c->sc.stage_d, dd, dev_k, c->B, c->kmax, (int)flags, s);
   if (e != hipSuccess) return fail(SF_E_HIP, std::string("stage: ") + hipGetErrorString(e));
-  HIPCHK(hipGraphLaunch(c->gx_verify, s));
+  HIPCHK(graph_launch(c->gx_verify, s));
   if (!(flags & SF_NO_COMMIT)) {
     for (int b = 0; b < c->B; ++b) c->len_hi[b] += c->T;
     c->dirty = true;
@@ -722,8 +770,8 @@ extern "C" sf_status sf_verify_device(sf_cache* c, const int32_t* dev_draft, con
 
 extern "C" sf_status sf_results_device(sf_cache* c, int32_t** dev_accepted, int32_t** dev_target) {
   if (!c) return fail(SF_E_ARG, "cache is NULL");
-  if (dev_accepted) *dev_accepted = c->res_d;
-  if (dev_target) *dev_target = c->res_d + c->B;
+  if (dev_accepted) *dev_accepted = c->sc.res_d;
+  if (dev_target) *dev_target = c->sc.res_d + c->B;
   return SF_OK;
 }
 
@@ -739,6 +787,7 @@ extern "C" sf_status sf_prefill(sf_cache* c, int32_t seq, const int32_t* tokens,
     if (sf_status st = refresh(c)) return st;
   }
   hipStream_t s = m->stream;
+  if (injected("launch")) return fail(SF_E_HIP, "prefill forward: injected launch failure (SF_FAULT=launch)");
   HIPCHK(launch_set_state(c->len, c->next, seq, 0, 0, 1, s));
   int last_cnt = 1;
   for (int j0 = 0; j0 < n; j0 += c->pchunk) {
@@ -750,7 +799,7 @@ extern "C" sf_status sf_prefill(sf_cache* c, int32_t seq, const int32_t* tokens,
     st->first[0] = tokens[j0];
     st->step[0] = 0;
     for (int j = 1; j < cnt; ++j) st->draft[j - 1] = tokens[j0 + j];
-    HIPCHK(hipMemcpyAsync(c->stage_d, st, stage_bytes(1, cnt - 1), hipMemcpyHostToDevice, s));
+    HIPCHK(hipMemcpyAsync(c->sc.stage_d, st, stage_bytes(1, cnt - 1), hipMemcpyHostToDevice, s));
     // Every position is forced accepted and the next pass stages its own first token, so only
     // the last pass's last row needs the LM head (a pass without it commits len += cnt).
     Run run{1, cnt, seq, cnt - 1, nullptr, false, true};
@@ -760,7 +809,7 @@ extern "C" sf_status sf_prefill(sf_cache* c, int32_t seq, const int32_t* tokens,
     HIPCHK(hipStreamSynchronize(s));  // the pinned stage block is reused by the next chunk
     last_cnt = cnt;
   }
-  HIPCHK(hipMemcpy(c->res_h, c->res_d, (1 + last_cnt) * 4, hipMemcpyDeviceToHost));
+  HIPCHK(hipMemcpy(c->res_h, c->sc.res_d, (1 + last_cnt) * 4, hipMemcpyDeviceToHost));
   c->len_h[seq] = n;
   c->len_hi[seq] = n;
   int nxt = 0;
@@ -849,10 +898,10 @@ extern "C" sf_status sf_draft_step(sf_cache* c, int32_t n_steps, int32_t* tokens
   st->flags = 0;
   st->kmax = 0;
   for (int b = 0; b < c->B; ++b) { st->k[b] = 0; st->step[b] = 0; }
-  HIPCHK(hipMemcpyAsync(c->stage_d, st, stage_bytes(c->B, 0), hipMemcpyHostToDevice, s));
-  for (int i = 0; i < n_steps; ++i) HIPCHK(hipGraphLaunch(c->gx_draft, s));
-  HIPCHK(hipMemcpyAsync(c->dout_h, c->dout_d, (size_t)c->B * kMaxDraftSteps * 4, hipMemcpyDeviceToHost, s));
-  HIPCHK(hipMemcpyAsync(c->res_h, c->res_d, 4 * kMaxRows * 4, hipMemcpyDeviceToHost, s));
+  HIPCHK(hipMemcpyAsync(c->sc.stage_d, st, stage_bytes(c->B, 0), hipMemcpyHostToDevice, s));
+  for (int i = 0; i < n_steps; ++i) HIPCHK(graph_launch(c->gx_draft, s));
+  HIPCHK(hipMemcpyAsync(c->dout_h, c->sc.dout_d, (size_t)c->B * kMaxDraftSteps * 4, hipMemcpyDeviceToHost, s));
+  HIPCHK(hipMemcpyAsync(c->res_h, c->sc.res_d, 4 * kMaxRows * 4, hipMemcpyDeviceToHost, s));
   HIPCHK(hipStreamSynchronize(s));
   for (int b = 0; b < c->B; ++b) {
     for (int i = 0; i < n_steps; ++i)
@@ -896,14 +945,14 @@ extern "C" sf_status sf_round_create(sf_cache* d, sf_cache* v, int32_t k, sf_rou
   r->v = v;
   r->k = k;
   // [0, B): verifier lengths; [B, 2B): catch-up needed per sequence; [2B]: any of them.
-  hipError_t e = hipMalloc((void**)&r->scratch, (size_t)(2 * d->B + 1) * 4);
+  hipError_t e = dev_malloc((void**)&r->scratch, (size_t)(2 * d->B + 1) * 4);
   if (e != hipSuccess) {
     round_release(r);
     return fail(SF_E_NOMEM, std::string("hipMalloc: ") + hipGetErrorString(e));
   }
   RoundArgs a{};
-  a.dstage = d->stage_d; a.vstage = v->stage_d; a.dlen = d->len; a.dnext = d->next; a.vlen = v->len;
-  a.vnext = v->next; a.dout = d->dout_d; a.vres = v->res_d; a.scratch = r->scratch;
+  a.dstage = d->sc.stage_d; a.vstage = v->sc.stage_d; a.dlen = d->len; a.dnext = d->next; a.vlen = v->len;
+  a.vnext = v->next; a.dout = d->sc.dout_d; a.vres = v->sc.res_d; a.scratch = r->scratch;
   a.B = d->B; a.k = k; a.vkmax = v->kmax; a.vT = v->T;
   const Run draft{d->B, 1, 0, 0, nullptr, true, false};
   const Run verify{v->B, v->T, 0, v->kmax, nullptr, false, false};
@@ -951,7 +1000,7 @@ extern "C" sf_status sf_round_run(sf_round* r, int32_t n_rounds) {
       return fail(SF_E_CAPACITY, "sequence " + std::to_string(b) + ": the rounds may exceed a capacity");
   }
   hipStream_t s = d->m->stream;
-  for (int i = 0; i < n_rounds; ++i) HIPCHK(hipGraphLaunch(r->gx, s));
+  for (int i = 0; i < n_rounds; ++i) HIPCHK(graph_launch(r->gx, s));
   for (int b = 0; b < d->B; ++b) {
     d->len_hi[b] += (int)grow;
     v->len_hi[b] += (int)grow;
@@ -1045,15 +1094,15 @@ extern "C" sf_status sf_time_kernel(sf_cache* c, int32_t kernel, int32_t iters, 
     st->kmax = c->kmax;
     for (int b = 0; b < c->B; ++b) { st->k[b] = 0; st->step[b] = 0; }
     for (int j = 0; j < c->B * c->kmax; ++j) st->draft[j] = 0;
-    HIPCHK(hipMemcpyAsync(c->stage_d, st, stage_bytes(c->B, c->kmax), hipMemcpyHostToDevice, s));
-    HIPCHK(hipGraphLaunch(c->gx_verify, s));  // warm-up
+    HIPCHK(hipMemcpyAsync(c->sc.stage_d, st, stage_bytes(c->B, c->kmax), hipMemcpyHostToDevice, s));
+    HIPCHK(graph_launch(c->gx_verify, s));  // warm-up
     HIPCHK(hipEventRecord(c->ev0, s));
-    for (int i = 0; i < iters; ++i) HIPCHK(hipGraphLaunch(c->gx_verify, s));
+    for (int i = 0; i < iters; ++i) HIPCHK(graph_launch(c->gx_verify, s));
     HIPCHK(hipEventRecord(c->ev1, s));
     HIPCHK(hipEventSynchronize(c->ev1));
     float ms = 0.f;
     HIPCHK(hipEventElapsedTime(&ms, c->ev0, c->ev1));
-    HIPCHK(hipMemcpy(c->res_h, c->res_d, 4 * kMaxRows * 4, hipMemcpyDeviceToHost));
+    HIPCHK(hipMemcpy(c->res_h, c->sc.res_d, 4 * kMaxRows * 4, hipMemcpyDeviceToHost));
     *avg_us = ms * 1000.f / iters;
     if (bytes) {
       const double kvdim = (double)m->KV;
@@ -1068,7 +1117,7 @@ extern "C" sf_status sf_time_kernel(sf_cache* c, int32_t kernel, int32_t iters, 
     return SF_OK;
   }
   GemmArgs base{};
-  base.rows = rows; base.ssq_in = c->ssq; base.part = c->part; base.sp = 1;
+  base.rows = rows; base.ssq_in = c->sc.ssq; base.part = c->sc.part; base.sp = 1;
   base.nparts_in = m->H / kTileN; base.eps = m->d.rms_eps; base.T = c->T; base.len = c->len; base.cap = c->cap;
   base.seq_stride = (long)c->seq_stride; base.rope = c->rope; base.nq = m->nq; base.nkv = m->nkv; base.dh = m->dh;
   double by = 0;
@@ -1080,39 +1129,39 @@ extern "C" sf_status sf_time_kernel(sf_cache* c, int32_t kernel, int32_t iters, 
     GemmArgs g = base;
     switch (kernel) {
       case SF_KERNEL_QKV:
-        g.w = Ly.wqkv; g.a = c->a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_qkv; g.nw = c->nw_qkv;
-        g.bias = Ly.bqkv; g.q = c->q; g.kc = kc; g.vc = vc; g.sp = c->sp_qkv; g.n_out = m->Q + 2 * m->KV;
+        g.w = Ly.wqkv; g.a = c->sc.a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_qkv; g.nw = c->nw_qkv;
+        g.bias = Ly.bqkv; g.q = c->sc.q; g.kc = kc; g.vc = vc; g.sp = c->sp_qkv; g.n_out = m->Q + 2 * m->KV;
         by = proj_bytes(m, m->Q + 2 * m->KV, m->H) + (double)rows * (m->H * 4 + m->Q * 4 + 2 * m->KV * 2);
-        return run_gemm(c, kGQkv, l, kEpiQkv, g, s);
+        return run_gemm(c, c->sc, kGQkv, l, kEpiQkv, g, s);
       case SF_KERNEL_ATTENTION: {
         AttnArgs aa{};
-        aa.q = c->q; aa.kc = kc; aa.vc = vc; aa.seq_stride = (long)c->seq_stride; aa.cap = c->cap; aa.len = c->len;
+        aa.q = c->sc.q; aa.kc = kc; aa.vc = vc; aa.seq_stride = (long)c->seq_stride; aa.cap = c->cap; aa.len = c->len;
         aa.T = c->T; aa.nq = m->nq; aa.nkv = m->nkv; aa.nchunk = c->nchunk;
         aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)m->dh));
-        aa.part = c->apart; aa.out = c->a_o; aa.rows = rows; aa.dh = m->dh;
+        aa.part = c->sc.apart; aa.out = c->sc.a_o; aa.rows = rows; aa.dh = m->dh;
         by = L_total * 2.0 * m->KV * 2 + (double)rows * (m->Q * 4 + m->Q * 2);
         return launch_attention(aa, m->dh, c->B, s);
       }
       case SF_KERNEL_OPROJ:
-        g.w = Ly.wo; g.a = c->a_o; g.k = m->Q; g.kb = m->Q / kTileK; g.nb = m->nb_h; g.nw = c->nw_o;
-        g.x = c->x; g.a_next = c->a_h; g.gain_next = Ly.g2; g.ssq_out = c->ssq; g.n_out = m->H; g.sp = c->sp_o;
+        g.w = Ly.wo; g.a = c->sc.a_o; g.k = m->Q; g.kb = m->Q / kTileK; g.nb = m->nb_h; g.nw = c->nw_o;
+        g.x = c->sc.x; g.a_next = c->sc.a_h; g.gain_next = Ly.g2; g.ssq_out = c->sc.ssq; g.n_out = m->H; g.sp = c->sp_o;
         by = proj_bytes(m, m->H, m->Q) + (double)rows * (m->Q * 4 + m->H * (4 + 4 + 4));
-        return run_gemm(c, kGO, l, kEpiResid, g, s);
+        return run_gemm(c, c->sc, kGO, l, kEpiResid, g, s);
       case SF_KERNEL_GATEUP:
-        g.w = Ly.wgu; g.a = c->a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_gu; g.nw = c->nw_gu;
-        g.h = c->a_f; g.ffn = m->F; g.sp = 1;
+        g.w = Ly.wgu; g.a = c->sc.a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_gu; g.nw = c->nw_gu;
+        g.h = c->sc.a_f; g.ffn = m->F; g.sp = 1;
         by = proj_bytes(m, 2.0 * m->F, m->H) + (double)rows * (m->H * 4 + m->F * 4);
-        return run_gemm(c, kGGateUp, l, kEpiSwiglu, g, s);
+        return run_gemm(c, c->sc, kGGateUp, l, kEpiSwiglu, g, s);
       case SF_KERNEL_DOWN:
-        g.w = Ly.wd; g.a = c->a_f; g.k = m->F; g.kb = m->F / kTileK; g.nb = m->nb_h; g.nw = c->nw_d;
-        g.x = c->x; g.a_next = c->a_h; g.gain_next = Ly.g1; g.ssq_out = c->ssq; g.n_out = m->H; g.sp = c->sp_d;
+        g.w = Ly.wd; g.a = c->sc.a_f; g.k = m->F; g.kb = m->F / kTileK; g.nb = m->nb_h; g.nw = c->nw_d;
+        g.x = c->sc.x; g.a_next = c->sc.a_h; g.gain_next = Ly.g1; g.ssq_out = c->sc.ssq; g.n_out = m->H; g.sp = c->sp_d;
         by = proj_bytes(m, m->H, m->F) + (double)rows * (m->F * 4 + m->H * (4 + 4 + 4));
-        return run_gemm(c, kGDown, l, kEpiResid, g, s);
+        return run_gemm(c, c->sc, kGDown, l, kEpiResid, g, s);
       default:
-        g.w = m->head; g.a = c->a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_head; g.nw = c->nw_head;
-        g.amax = c->amax; g.vocab = m->V; g.sp = 1;
+        g.w = m->head; g.a = c->sc.a_h; g.k = m->H; g.kb = m->H / kTileK; g.nb = m->nb_head; g.nw = c->nw_head;
+        g.amax = c->sc.amax; g.vocab = m->V; g.sp = 1;
         by = (double)m->V * m->H * 2 + (double)rows * (m->H * 4 + m->nb_head * 8);
-        return run_gemm(c, kGHead, 0, kEpiArgmax, g, s);
+        return run_gemm(c, c->sc, kGHead, 0, kEpiArgmax, g, s);
     }
   };
   hipError_t e = launch(0);  // warm-up
@@ -1128,6 +1177,23 @@ extern "C" sf_status sf_time_kernel(sf_cache* c, int32_t kernel, int32_t iters, 
   HIPCHK(hipEventElapsedTime(&ms, c->ev0, c->ev1));
   *avg_us = ms * 1000.f / iters;
   if (bytes) *bytes = by;
+  return SF_OK;
+}
+
+extern "C" sf_status sf_debug_counters(sf_cache* c, int64_t* sum, int32_t* max) {
+  if (!c || !sum || !max) return fail(SF_E_ARG, "NULL argument");
+  const size_t n = (size_t)c->m->L * 3 * c->sc.cnt_stride;
+  std::vector<int32_t> h(n);
+  HIPCHK(hipStreamSynchronize(c->m->stream));
+  HIPCHK(hipMemcpy(h.data(), c->sc.cnt, n * 4, hipMemcpyDeviceToHost));
+  int64_t s = 0;
+  int32_t mx = 0;
+  for (int32_t v : h) {
+    s += v;
+    mx = std::max(mx, v);
+  }
+  *sum = s;
+  *max = mx;
   return SF_OK;
 }
 

@@ -59,7 +59,7 @@ struct GemmArgs {
   int k, kb, nb, rows;     // in-features, k tiles (k/16), 32-row n blocks, valid rows
   int sp;                  // workgroups splitting each block's k range
   float* part;             // split partials [nb][sp][rows][32] (sp > 1)
-  int* counters;           // [nb] arrivals of the splits of each block (sp > 1); only grow
+  int* counters;           // [nb] arrivals of the splits of each block (sp > 1); zero between launches
   int nw;                  // waves per workgroup: 4 or 8
   int row_lo;              // batched kernel: outputs of rows below row_lo are not needed (0: all)
   int kh;                  // weight tiles per pipelined batch (4 or 8) for single-tile row counts

@@ -135,3 +135,29 @@ def test_nf4_weight_order_pairs_projections():
     names = sfb.weight_order(d, nf4=True)
     assert len(names) == len(sfb.weight_order(d)) + 7 * d.n_layers
     assert names[2:4] == ["l0.wq", "l0.wq"]
+
+
+@pytest.mark.parametrize("nf4", [False, True])
+def test_injected_allocation_failure_is_reported_and_leaves_nothing(monkeypatch, nf4):
+    """SF_FAULT=alloc: the first device allocation of sf_model_create fails as an out-of-memory
+    hipMalloc would; the call returns SF_E_NOMEM with a message, hands out no model, and the
+    next call (fault off) is checked afresh.  The weights and stream are stand-ins that the
+    library never touches before its first allocation."""
+    d = sfb.desc_from_shape(synth.TINY)
+    ptrs = [1] * len(sfb.weight_order(d, nf4=nf4))
+    create = sfb.sf_model_create_nf4 if nf4 else sfb.sf_model_create
+    monkeypatch.setenv("SF_FAULT", "alloc")
+    with pytest.raises(sfb.SFError) as e:
+        create(d, ptrs, 0x1000)
+    assert e.value.code == sfb.SF_E_NOMEM and "hipMalloc" in str(e.value)
+    L = _lib()
+    out = ctypes.c_void_p()
+    arr = (ctypes.c_void_p * len(ptrs))(*ptrs)
+    fn = L.sf_model_create_nf4 if nf4 else L.sf_model_create
+    assert fn(ctypes.byref(d), arr, ctypes.c_void_p(0x1000), ctypes.byref(out)) == sfb.SF_E_NOMEM
+    assert not out.value
+    monkeypatch.delenv("SF_FAULT")
+    ptrs[3] = 0
+    with pytest.raises(sfb.SFError) as e:
+        create(d, ptrs, 0x1000)
+    assert e.value.code == sfb.SF_E_ARG

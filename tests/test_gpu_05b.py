@@ -102,3 +102,55 @@ def test_64_rounds_graph_loop_with_rollback(setup):
     ln, _ = sfb.sf_cache_state(eng.cache, 0)
     say(f"[0.5b] after 64 rounds: length {ln}")
     assert 512 < ln <= 512 + 64 * 8
+
+
+def test_draft_pass_logits_and_prefill_match_oracle(setup):
+    """The drafter at logit level (tied head, V=151936, head_dim 64).  A second cache of the
+    same model with k_max=0 runs exactly the draft step's one-row pass; after a 512-token
+    prefill its debug logits, at the prefill's pending token and after each of four lockstep
+    steps, are within 0.05 of the oracle's, and the graph-replayed draft step returns their
+    argmax (same kernels, same bits).  The prefill's K/V are within 0.02 relative of the
+    oracle's cache."""
+    sfb, model, eng = setup
+    c0 = sfb.sf_cache_alloc(eng.model, 1, 2048, 0)
+    try:
+        prompt = synth.prompt_ids(S.vocab, 512, synth.seeds(2)["prompt"] + 9)
+        say("[0.5b] prefill (logit check)")
+        nxt = sfb.sf_prefill(c0, 0, prompt)
+        c = oracle.KVCache(S, 2048)
+        z = oracle.prefill(model, c, prompt)
+        if oracle.top_gap(z[-1:])[0].item() > GAP:
+            assert nxt == c.next_token
+        shape = (S.n_layers, S.n_kv_heads, 512, S.head_dim)
+        kg = torch.zeros(shape, dtype=torch.int16, device="cuda")
+        vg = torch.zeros_like(kg)
+        sfb.sf_kv_read(c0, 0, kg, vg, 512, 512)
+        torch.cuda.synchronize()
+        kg = kg.cpu().view(torch.bfloat16).double()
+        vg = vg.cpu().view(torch.bfloat16).double()
+        ko, vo = c.k[:, :, :512].double(), c.v[:, :, :512].double()
+        rel_k = ((kg - ko).norm() / ko.norm()).item()
+        rel_v = ((vg - vo).norm() / vo.norm()).item()
+        say(f"[0.5b] prefill KV rel err k {rel_k:.2e} v {rel_v:.2e}")
+        assert rel_k < 0.02 and rel_v < 0.02
+        sfb.sf_set_next(c0, 0, c.next_token)
+        logits = torch.empty((1, S.vocab), dtype=torch.float32, device="cuda")
+        worst = 0.0
+        for i in range(5):
+            sfb.sf_verify(c0, np.zeros((1, 0), np.int32), None, sfb.SF_DEBUG_LOGITS | sfb.SF_NO_COMMIT,
+                          dev_out=logits)
+            torch.cuda.synchronize()
+            zg = logits.cpu()
+            r = oracle.verify(model, c, [], 0)
+            err = (zg.double() - r["logits"]).abs().max().item()
+            worst = max(worst, err)
+            assert err <= 0.05, (i, err)
+            tok = int(sfb.sf_draft_step(c0, 1)[0][0])
+            assert tok == int(oracle.argmax_lowest(zg)[0]), i
+            if r["gap"][0] > GAP:
+                assert tok == c.next_token
+            sfb.sf_set_next(c0, 0, c.next_token)
+            assert sfb.sf_cache_state(c0, 0) == (c.length, c.next_token)
+        say(f"[0.5b] draft-pass max |dlogit| {worst:.4g}")
+    finally:
+        sfb.sf_cache_free(c0)

@@ -68,7 +68,7 @@ def _oracle_cache(kv, ctx, nxt, shape=S):
     return c
 
 
-@pytest.mark.parametrize("ctx", [512, 8192])
+@pytest.mark.parametrize("ctx", [512, 2048, 8192])
 def test_full_stack_verify_matches_oracle(eng, weights, kv, hist, ctx):
     sfb = need_gpu()
     nxt = int(hist[ctx])
@@ -178,8 +178,9 @@ def test_half_stack_hidden_states_match_oracle(weights, kv, hist):
 
 def test_batched_32_sequences_matches_oracle_and_single_runs(weights, kv):
     """32 sequences x 9 positions (288 rows, the row-grouped GEMM path) at contexts drawn
-    from U{256..8192}: two sequences against the oracle, and both bitwise equal to the same
-    sequence verified alone."""
+    from U{256..8192}: eight sequences (the shortest and longest context and six between)
+    against the oracle, and the shortest and longest bitwise equal to the same sequence
+    verified alone."""
     sfb = need_gpu()
     Bn = 32
     rng = np.random.default_rng(synth.seeds(5)["contexts"])
@@ -202,14 +203,18 @@ def test_batched_32_sequences_matches_oracle_and_single_runs(weights, kv):
         assert (acc_g == acc).all() and (tgt_g == tgt).all()
         model = oracle.Model(S, weights)
         one_logits = torch.empty((K + 1, S.vocab), dtype=torch.float32, device="cuda")
-        for b in (int(np.argmin(ctx)), int(np.argmax(ctx))):
-            sfb.sf_kv_write(one.cache, 0, kd, vd, int(ctx[b]), kv[0].shape[2])
-            sfb.sf_set_next(one.cache, 0, int(nxt[b]))
-            a1, t1 = sfb.sf_verify(one.cache, drafts[b:b + 1], None, sfb.SF_DEBUG_LOGITS | sfb.SF_NO_COMMIT,
-                                   dev_out=one_logits)
-            torch.cuda.synchronize()
-            assert torch.equal(one_logits.cpu(), logits.view(Bn, K + 1, S.vocab)[b].cpu()), f"sequence {b}"
-            assert a1[0] == acc[b] and (t1[0] == tgt[b]).all()
+        ends = (int(np.argmin(ctx)), int(np.argmax(ctx)))
+        order = np.argsort(ctx)
+        between = [int(order[i]) for i in np.linspace(1, Bn - 2, 6).round().astype(int)]
+        for b in list(ends) + between:
+            if b in ends:
+                sfb.sf_kv_write(one.cache, 0, kd, vd, int(ctx[b]), kv[0].shape[2])
+                sfb.sf_set_next(one.cache, 0, int(nxt[b]))
+                a1, t1 = sfb.sf_verify(one.cache, drafts[b:b + 1], None, sfb.SF_DEBUG_LOGITS | sfb.SF_NO_COMMIT,
+                                       dev_out=one_logits)
+                torch.cuda.synchronize()
+                assert torch.equal(one_logits.cpu(), logits.view(Bn, K + 1, S.vocab)[b].cpu()), f"sequence {b}"
+                assert a1[0] == acc[b] and (t1[0] == tgt[b]).all()
             say(f"[7b-batched] seq {b} ctx {ctx[b]}: oracle")
             r = oracle.verify(model, _oracle_cache(kv, int(ctx[b]), int(nxt[b])), drafts[b], K, commit=False)
             err = (logits.view(Bn, K + 1, S.vocab)[b].double().cpu() - r["logits"]).abs().max().item()

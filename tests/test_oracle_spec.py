@@ -364,3 +364,51 @@ def test_snapshot_verify_equals_in_place_verify_and_greedy(tiny):
     g = oracle.KVCache(synth.TINY, 96)
     oracle.prefill(tiny, g, prompt)
     assert stream == oracle.greedy_decode(tiny, g, len(stream))
+
+
+# ---------------------------------------------------------------- prefill's pending token, cache loading
+
+def test_prefill_pending_token_is_the_greedy_choice_after_the_last_prompt_token(tiny):
+    """After a prompt of n tokens the pending token is the argmax (lowest index on ties) of the
+    logits at position n-1: the same choice a single-token pass makes when the last prompt
+    token is fed on top of a prefill of the first n-1 (so taking any other row of the prefill's
+    logits, e.g. position 0, fails here: the chosen prompt makes those choices differ)."""
+    S = synth.TINY
+    prompt = synth.prompt_ids(S.vocab, 21, 404)
+    c1 = oracle.KVCache(S, 64)
+    z = oracle.prefill(tiny, c1, prompt)
+    assert c1.length == 21
+    assert c1.next_token == int(oracle.argmax_lowest(z)[-1])
+    assert int(oracle.argmax_lowest(z)[0]) != c1.next_token
+    c2 = oracle.KVCache(S, 64)
+    oracle.prefill(tiny, c2, prompt[:-1])
+    oracle.set_next(c2, int(prompt[-1]))
+    r = oracle.verify(tiny, c2, [], 0)
+    assert int(r["target"][0]) == c1.next_token
+    assert (r["logits"][0] - z[-1]).abs().max().item() < 1e-10
+    assert (c2.length, c2.next_token) == (c1.length, c1.next_token)
+
+
+def test_kvcache_load_places_exactly_the_given_positions(tiny):
+    """KVCache.load copies positions [0, n_pos) of bf16 bit arrays [layer][kv head][pos][dim]
+    into the cache and nothing else: a cache loaded from another cache's exported bits holds
+    the same bytes, zeros past n_pos (the source's junk there is not taken), the given length
+    and pending token, and verifies to exactly the same logits."""
+    S = synth.TINY
+    src = _prefilled(tiny, n=30, seed=405, cap=64)
+    kb = src.k.view(torch.int16).numpy().view(np.uint16).copy()
+    vb = src.v.view(torch.int16).numpy().view(np.uint16).copy()
+    kb[:, :, 30:] = 0x3F80        # junk (bf16 1.0) past the loaded positions
+    vb[:, :, 30:] = 0xBF80
+    c = oracle.KVCache(S, 48)
+    c.load(kb, vb, 30, next_token=src.next_token)
+    assert (c.length, c.next_token) == (30, src.next_token)
+    assert torch.equal(c.k[:, :, :30].view(torch.int16), src.k[:, :, :30].view(torch.int16))
+    assert torch.equal(c.v[:, :, :30].view(torch.int16), src.v[:, :, :30].view(torch.int16))
+    assert not c.k[:, :, 30:].view(torch.int16).any() and not c.v[:, :, 30:].view(torch.int16).any()
+    # Element order: layer, kv head, position, dim (a swapped axis would move this value).
+    assert c.k[1, 0, 7, 5].item() == src.k[1, 0, 7, 5].item() != c.k[0, 1, 7, 5].item()
+    d = [9, 8, 7, 6]
+    ra = oracle.verify(tiny, src.copy(), d, 4, commit=False)
+    rb = oracle.verify(tiny, c, d, 4, commit=False)
+    assert torch.equal(ra["logits"], rb["logits"])
