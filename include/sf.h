@@ -177,6 +177,29 @@ sf_status sf_verify(sf_cache* cache, const int32_t* draft, const int32_t* k, uin
 sf_status sf_verify_device(sf_cache* cache, const int32_t* dev_draft, const int32_t* dev_k,
                            uint32_t flags);
 
+/* sf_verify_device_static: sf_verify_device's pass for callers that cannot allocate device
+ * memory or call anything that does (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The same kernels, enqueued eagerly on the model stream
+ * without waiting, with the pass's working memory (activations, split-K partials and
+ * counters, attention partials, LM-head maxima, staging block) taken from one static device
+ * array of 16 MiB per GPU instead of the cache's own scratch; no hipMalloc, hipFree or other
+ * allocating call is made (the array's device address is looked up once per device, on the
+ * first call there).
+ *   dev_draft, dev_k, flags  as sf_verify_device (SF_NO_COMMIT, SF_FORCE_ACCEPT).
+ *   dev_result  device int32 [n_seqs + n_seqs*(k_max+1)], caller-owned: accepted[n_seqs]
+ *               then target[n_seqs][k_max+1], written by the pass (results are not placed at
+ *               sf_results_device's address).
+ * The cache's KV pool, lengths and pending tokens are read and committed exactly as by
+ * sf_verify_device, and the results are bit-identical to it.  Limit: the pass's working
+ * memory must fit the array (a single-sequence 7B-shape K=8 verify at capacity 8208 needs
+ * about 9.4 MB; 32-sequence batches do not fit) -- larger passes fail with SF_E_CAPACITY
+ * before any work is enqueued.  Every call on one GPU shares that GPU's array, which keeps
+ * the last call's contents: calls whose passes overlap in time on one GPU (other streams,
+ * other threads) race and must be serialised by the caller.
+ * Errors: SF_E_ARG, SF_E_CAPACITY, SF_E_HIP. */
+sf_status sf_verify_device_static(sf_cache* cache, const int32_t* dev_draft, const int32_t* dev_k,
+                                  uint32_t flags, int32_t* dev_result);
+
 /* sf_results_device: device addresses (fixed for the cache's lifetime) of the
  * last pass's results: accepted int32 [n_seqs] and target int32 [n_seqs][k_max+1]. */
 sf_status sf_results_device(sf_cache* cache, int32_t** dev_accepted, int32_t** dev_target);

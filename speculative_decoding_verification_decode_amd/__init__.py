@@ -76,6 +76,7 @@ def lib():
             "sf_verify": [_P, _PI, _PI, ctypes.c_uint32, _PI, _PI, _P],
             "sf_verify_device": [_P, _P, _P, ctypes.c_uint32],
             "sf_results_device": [_P, ctypes.POINTER(_P), ctypes.POINTER(_P)],
+            "sf_verify_device_static": [_P, _P, _P, ctypes.c_uint32, _P],
             "sf_rollback": [_P, _I, _I],
             "sf_set_next": [_P, _I, _I],
             "sf_snapshot_save": [_P],
@@ -219,6 +220,11 @@ def sf_verify(cache, draft, k=None, flags=0, n_seqs=None, k_max=None, dev_out=No
 
 def sf_verify_device(cache, dev_draft, dev_k=None, flags=0):
     _check(lib().sf_verify_device(cache, _ptr(dev_draft), _ptr(dev_k), flags))
+
+
+def sf_verify_device_static(cache, dev_draft, dev_k, flags, dev_result):
+    """The no-allocation verify: results (accepted then targets, int32) go to dev_result."""
+    _check(lib().sf_verify_device_static(cache, _ptr(dev_draft), _ptr(dev_k), flags, _ptr(dev_result)))
 
 
 def sf_results_device(cache):

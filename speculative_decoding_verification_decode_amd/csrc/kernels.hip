@@ -1149,6 +1149,18 @@ hipError_t launch_snapshot(const SnapArgs& a, int save, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Zero n ints (a fill kernel, so that callers may capture it in a graph).
+__global__ void k_zero(int* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
+}
+
+hipError_t launch_zero(int* p, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int grid = (int)std::min<size_t>((n + 255) / 256, 1024);
+  k_zero<<<grid, 256, 0, s>>>(p, n);
+  return hipGetLastError();
+}
+
 // Device-resident drafts -> fixed staging block (draft [B][kmax], k [B] or all kmax).
 __global__ void k_stage_device(Stage* st, const int32_t* draft, const int32_t* k, int B, int kmax, int flags) {
   const int t = threadIdx.x;

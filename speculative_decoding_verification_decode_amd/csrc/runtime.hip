@@ -13,6 +13,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -74,6 +75,7 @@ struct DevAllocs {
 
 struct sf_model {
   sf_model_desc d;
+  int dev = 0;                     // the device current at creation (weights and stream live there)
   hipStream_t stream = nullptr;
   bool own_stream = false;
   int H, Q, KV, F, V, dh, nq, nkv, L;
@@ -220,6 +222,7 @@ static sf_status create_model(const sf_model_desc* desc, const void* const* weig
     return fail(SF_E_ARG, "NF4 needs hidden, ffn and n_q_heads*head_dim to be multiples of 64");
   sf_model* m = new sf_model();
   m->nf4 = nf4;
+  if (hipGetDevice(&m->dev) != hipSuccess) m->dev = 0;
   m->d = *desc;
   const sf_model_desc& d = *desc;
   m->H = d.hidden; m->nq = d.n_q_heads; m->nkv = d.n_kv_heads; m->dh = d.head_dim;
@@ -421,10 +424,11 @@ extern "C" sf_status sf_model_free(sf_model* m) {
   return SF_OK;
 }
 
-enum GemmKind { kGQkv = 0, kGO = 1, kGGateUp = 2, kGDown = 3, kGHead = 4 };
 
 // One GEMM of kind `kind` in layer `layer`; a k split (g.sp > 1) uses the arrival counters
 // of that layer and kind.
+enum GemmKind { kGQkv = 0, kGO = 1, kGGateUp = 2, kGDown = 3, kGHead = 4 };
+
 static hipError_t run_gemm(const sf_cache* c, const Scratch& S, int kind, int layer, int epi, GemmArgs g,
                            hipStream_t s) {
   g.kh = c->kh;
@@ -761,6 +765,89 @@ extern "C" sf_status sf_verify_device(sf_cache* c, const int32_t* dev_draft, con
   hipError_t e = launch_stage_device(c->sc.stage_d, dd, dev_k, c->B, c->kmax, (int)flags, s);
   if (e != hipSuccess) return fail(SF_E_HIP, std::string("stage: ") + hipGetErrorString(e));
   HIPCHK(graph_launch(c->gx_verify, s));
+  if (!(flags & SF_NO_COMMIT)) {
+    for (int b = 0; b < c->B; ++b) c->len_hi[b] += c->T;
+    c->dirty = true;
+  }
+  return SF_OK;
+}
+
+// ------------------------------------------------------------------------------------------
+// The no-allocation verify: sf_verify_device's pass, run eagerly with its working memory
+// taken from one static device array instead of the cache's own scratch, for callers that
+// cannot allocate (graph capture, tight serving loops).
+//
+// `scratch` is the array as this file's device code object holds it, one copy per GPU, kept
+// until the process ends.  In host code its name is a host-side stand-in, not a device
+// address; the device address of each GPU's copy comes from hipGetSymbolAddress, taken once
+// per device with that device current, and only that address is used afterwards.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+static void* g_scratch_ptr[kMaxDevices] = {};
+static std::mutex g_scratch_mu;
+
+static sf_status static_scratch(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(SF_E_ARG, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    HIPCHK(hipGetDevice(&cur));
+    if (cur != dev) HIPCHK(hipSetDevice(dev));
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) HIPCHK(hipSetDevice(cur));
+    if (e != hipSuccess || !ptr)
+      return fail(SF_E_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SF_OK;
+}
+
+extern "C" sf_status sf_verify_device_static(sf_cache* c, const int32_t* dev_draft, const int32_t* dev_k,
+                                             uint32_t flags, int32_t* dev_result) {
+  if (!c || !dev_result) return fail(SF_E_ARG, "cache or dev_result is NULL");
+  if (flags & ~(SF_NO_COMMIT | SF_FORCE_ACCEPT)) return fail(SF_E_ARG, "unsupported flags");
+  if (!dev_draft && c->kmax > 0) return fail(SF_E_ARG, "dev_draft is NULL");
+  for (int b = 0; b < c->B; ++b)
+    if (c->len_hi[b] + c->T > c->cap)
+      return fail(SF_E_CAPACITY, "sequence " + std::to_string(b) + ": length may exceed capacity (sf_sync first)");
+  // Lay the pass's working memory out in the static array (256-byte aligned pieces).
+  Scratch S;
+  size_t need = 0;
+  auto count = [&](void** p, size_t bytes) -> sf_status {
+    *p = nullptr;
+    need += (std::max<size_t>(bytes, 256) + 255) & ~(size_t)255;
+    return SF_OK;
+  };
+  plan_scratch(c, (size_t)c->B * c->T, S, false, count);
+  if (need > kStaticScratchBytes)
+    return fail(SF_E_CAPACITY, "this pass needs " + std::to_string(need) + " bytes of working memory; the static "
+                "scratch holds " + std::to_string(kStaticScratchBytes) + " (fewer sequences or a smaller capacity fit)");
+  void* base = nullptr;
+  if (sf_status st = static_scratch(c->m->dev, &base)) return st;
+  size_t off = 0;
+  auto carve = [&](void** p, size_t bytes) -> sf_status {
+    *p = (uint8_t*)base + off;
+    off += (std::max<size_t>(bytes, 256) + 255) & ~(size_t)255;
+    return SF_OK;
+  };
+  plan_scratch(c, (size_t)c->B * c->T, S, false, carve);
+  S.res_d = dev_result;
+  hipStream_t s = c->m->stream;
+  // The array keeps the previous call's contents: the split-K arrival counters must start at
+  // zero (cleared by a fill kernel, which a capturing caller may record); everything else is
+  // written before it is read.
+  hipError_t e = launch_zero(S.cnt, (size_t)c->m->L * 3 * S.cnt_stride, s);
+  if (e == hipSuccess) e = launch_stage_device(S.stage_d, dev_draft ? dev_draft : dev_result, dev_k, c->B, c->kmax,
+                                               (int)flags, s);
+  if (e == hipSuccess) {
+    Run r{c->B, c->T, 0, c->kmax, nullptr, false, false};
+    r.sc = &S;
+    e = enqueue_forward(c, r);
+  }
+  if (e != hipSuccess) return fail(SF_E_HIP, std::string("static verify: ") + hipGetErrorString(e));
   if (!(flags & SF_NO_COMMIT)) {
     for (int b = 0; b < c->B; ++b) c->len_hi[b] += c->T;
     c->dirty = true;

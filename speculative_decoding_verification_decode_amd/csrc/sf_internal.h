@@ -166,6 +166,7 @@ struct RoundArgs {
   int B, k, vkmax, vT;
 };
 hipError_t launch_round(const RoundArgs& r, int phase, hipStream_t s);
+hipError_t launch_zero(int* p, size_t n, hipStream_t s);
 hipError_t launch_stage_device(Stage* stage, const int32_t* draft, const int32_t* k, int B, int kmax,
                                int flags, hipStream_t s);
 hipError_t launch_copy_kv(uint16_t* pool, uint16_t* src, long pool_layer_stride, int nkv, int cap,
