@@ -433,6 +433,33 @@ __device__ __forceinline__ bool split_arrive(int* counter, int sp) {
   return true;
 }
 
+// One warm-up workgroup (index q among wa.nwarm): read the head tiles of the GEMM workgroups
+// q, q + nwarm, ... with cached 16-byte loads, eight in flight per thread.
+__device__ __forceinline__ void warm_gemm(const WarmArgs& wa, int q) {
+  uint32_t acc = 0;
+  for (int i = q; i < wa.n; i += wa.nwarm) {
+    const int nb = i / wa.sp, spi = i - nb * wa.sp;
+    const int t1 = (int)((long)wa.kb * (spi + 1) / wa.sp);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(wa.w + (size_t)nb * wa.kb * 64), (short)0, t1 * 1024, kBufferWord3);
+    for (int w = 0; w < 4; ++w) {
+      const int u = spi * 4 + w, U = wa.sp * 4;
+      const int a = (int)(((long)wa.kb * u) / U), b = min((int)(((long)wa.kb * (u + 1)) / U), a + wa.head);
+      for (int j = a * 64 + (int)threadIdx.x; j < b * 64; j += 256 * 8) {
+        u32x4 v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int jj = j + e * 256;
+          v[e] = __builtin_amdgcn_raw_buffer_load_b128(r, jj < b * 64 ? jj * 16 : 0x7FFFFFF0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc ^= v[e].x ^ v[e].y ^ v[e].z ^ v[e].w;
+      }
+    }
+  }
+  if (acc == 0x9E3779B9u) wa.sink[0] = acc;
+}
+
 __device__ __forceinline__ void amax_merge(float& bv, int& bi, float v, int i) {
   if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
 }

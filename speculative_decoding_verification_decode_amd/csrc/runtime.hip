@@ -104,6 +104,7 @@ struct Scratch {
   int cnt_stride = 0;
   int32_t* res_d = nullptr;        // {accepted[B], target[B][T]}
   int32_t* dout_d = nullptr;       // draft-step outputs [B][kMaxDraftSteps]
+  uint32_t* sink = nullptr;        // target of the L2 warm-ups' checksums (never read)
 };
 
 struct Run {
@@ -133,6 +134,7 @@ struct sf_cache {
   int nw_qkv, nw_o, nw_gu, nw_d, nw_head;
   int sp_qkv, sp_o, sp_gu, sp_d, sp_head;
   int kh = 4;                      // GEMM: weight tiles per pipelined batch (one-tile row counts)
+  bool warm_o = true;              // read the O projection's weights into L2 during attention
   hipGraphExec_t gx_verify = nullptr, gx_draft = nullptr;
   uint16_t *snap_k = nullptr, *snap_v = nullptr;   // state snapshot: K/V rows [len, len+T)
   int32_t *snap_len = nullptr, *snap_next = nullptr;
@@ -486,6 +488,14 @@ static hipError_t enqueue_forward(sf_cache* c, const Run& r) {
     if ((e = run_gemm(c, S, kGQkv, l, kEpiQkv, g, s)) != hipSuccess) return e;
 
     aa.kc = kc; aa.vc = vc;
+    // While attention runs (latency-bound, HBM mostly idle) extra workgroups read the O
+    // projection's weights into the L2 of the XCD each O workgroup will run on.  Compact
+    // (<= 64-row) bf16 passes only: other GEMM layouts map workgroups to blocks differently.
+    aa.warm = WarmArgs{};
+    if (c->warm_o && rows <= 64 && !m->nf4) {
+      aa.warm.w = Ly.wo; aa.warm.kb = m->Q / kTileK; aa.warm.sp = c->sp_o; aa.warm.n = m->nb_h * c->sp_o;
+      aa.warm.head = 1 << 30; aa.warm.nwarm = (aa.warm.n + 7) & ~7; aa.warm.sink = S.sink;
+    }
     if ((e = launch_attention(aa, m->dh, r.B, s)) != hipSuccess) return e;
 
     g = base;
@@ -569,6 +579,7 @@ static sf_status plan_scratch(const sf_cache* c, size_t R, Scratch& S, bool own,
   if ((st = take((void**)&S.q, R * m->Q * 4))) return st;
   if ((st = take((void**)&S.apart, R * m->nq * (size_t)c->nchunk * (m->dh + 2) * 4))) return st;
   if ((st = take((void**)&S.amax, R * m->nb_head * 8))) return st;
+  if ((st = take((void**)&S.sink, 256))) return st;
   if (own) {
     if ((st = take((void**)&S.res_d, 4 * kMaxRows * 4))) return st;
     if ((st = take((void**)&S.dout_d, (size_t)c->B * kMaxDraftSteps * 4))) return st;
@@ -615,6 +626,7 @@ extern "C" sf_status sf_cache_alloc(sf_model* m, int32_t n_seqs, int32_t capacit
   c->sp_d = choose_sp(m->nb_h, m->F / kTileK, c->nw_d, "SF_SP_D", m->nf4);
   c->sp_head = 1;
   if (const char* v = getenv("SF_KH")) c->kh = (atoi(v) == 8) ? 8 : 4;
+  if (const char* v = getenv("SF_WARM_O")) c->warm_o = atoi(v) != 0;
 
   hipStream_t s = m->stream;
   auto bail = [&](sf_status st) { cache_release(c); return st; };
@@ -681,7 +693,6 @@ extern "C" sf_status sf_cache_free(sf_cache* c) {
 static sf_status refresh(sf_cache* c) {
   hipStream_t s = c->m->stream;
   HIPCHK(hipStreamSynchronize(s));
-  HIPCHK(hipMemcpy(c->res_h, c->sc.res_d, 4 * kMaxRows * 4, hipMemcpyDeviceToHost));
   HIPCHK(hipMemcpy(c->res_h, c->len, c->B * 4, hipMemcpyDeviceToHost));
   for (int b = 0; b < c->B; ++b) c->len_h[b] = c->res_h[b];
   HIPCHK(hipMemcpy(c->res_h, c->next, c->B * 4, hipMemcpyDeviceToHost));
@@ -731,7 +742,8 @@ extern "C" sf_status sf_verify(sf_cache* c, const int32_t* draft, const int32_t*
   } else {
     HIPCHK(graph_launch(c->gx_verify, s));
   }
-  HIPCHK(hipMemcpyAsync(c->res_h, c->sc.res_d, 4 * kMaxRows * 4, hipMemcpyDeviceToHost, s));
+  // Results {accepted[B], target[B][T]}, behind the pass.
+  HIPCHK(hipMemcpyAsync(c->res_h, c->sc.res_d, (size_t)(c->B + c->B * c->T) * 4, hipMemcpyDeviceToHost, s));
   if (!m->d.has_head && dev_out)
     HIPCHK(hipMemcpyAsync(dev_out, c->sc.hidden, (size_t)c->B * c->T * m->H * 2, hipMemcpyDeviceToDevice, s));
   HIPCHK(hipStreamSynchronize(s));
@@ -988,7 +1000,6 @@ extern "C" sf_status sf_draft_step(sf_cache* c, int32_t n_steps, int32_t* tokens
   HIPCHK(hipMemcpyAsync(c->sc.stage_d, st, stage_bytes(c->B, 0), hipMemcpyHostToDevice, s));
   for (int i = 0; i < n_steps; ++i) HIPCHK(graph_launch(c->gx_draft, s));
   HIPCHK(hipMemcpyAsync(c->dout_h, c->sc.dout_d, (size_t)c->B * kMaxDraftSteps * 4, hipMemcpyDeviceToHost, s));
-  HIPCHK(hipMemcpyAsync(c->res_h, c->sc.res_d, 4 * kMaxRows * 4, hipMemcpyDeviceToHost, s));
   HIPCHK(hipStreamSynchronize(s));
   for (int b = 0; b < c->B; ++b) {
     for (int i = 0; i < n_steps; ++i)

@@ -109,6 +109,19 @@ struct EmbedArgs {
   const int* gate;        // nullptr, or the pass runs only while *gate != 0 (device flag)
 };
 
+// L2 warm-up of a compact GEMM that runs later in the same pass: its workgroup i (grid index i,
+// n workgroups, sp per 32-row block, 4 waves each splitting the block split's k tiles) will
+// stream, per wave, k tiles from kt0; the warm-up reads the first `head` tiles of every wave's
+// range with cached loads (head >= the range: all of them).  Workgroup i of every launch runs on
+// XCD i % 8, so a warm-up workgroup whose index matches i modulo 8 leaves the lines in the L2
+// that GEMM workgroup reads through.
+struct WarmArgs {
+  const uint4* w;          // packed weight tiles of the GEMM (nullptr: no warm-up)
+  int kb, sp, n, head;
+  int nwarm;               // warm-up workgroups (a multiple of 8); workgroup q takes i = q, q+nwarm, ...
+  uint32_t* sink;          // one word the loads' checksum may reach (keeps them alive)
+};
+
 struct AttnArgs {
   const float* q;
   const uint16_t* kc;
@@ -123,6 +136,7 @@ struct AttnArgs {
   int rows;
   int dh;
   const int* gate;        // nullptr, or the pass runs only while *gate != 0 (device flag)
+  WarmArgs warm;          // the O projection's weights, read into L2 while attention runs
 };
 
 struct AcceptArgs {
