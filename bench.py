@@ -8,12 +8,26 @@ cache holds seeded synthetic K/V for the context; drafts come from the
 prompt-lookup proposer over a seeded repeating history.  Every timed pass runs
 with SF_NO_COMMIT so each step verifies at exactly the nominal context.
 
+Beside the headline it measures, each on its own seeded synthetic workload:
+  - the hidden-state half shard (layers 0..13 of the same stack, no head): 256 verifies from
+    1024 prior positions, each followed by a seeded rollback of 0..8 of its 9 positions;
+  - the 0.5B-shape drafter alone: 64 rounds of one 8-step graph-replay call after a 512-token
+    GPU prefill, each followed by a seeded rollback of 0..8 rejected drafts;
+  - the prompt-lookup loop: a 4096-token repeating history prefilled on the GPU, then 64
+    committed verify steps whose drafts the n-gram proposer finds in the committed stream
+    (acceptance histogram and committed tokens/s);
+  - 32 sequences in one pass, prefill time to first token, the device-resident round, the
+    snapshot rollback and the NF4 14B-shape verify;
+  - the oracle on the host for each workload (a bounded sample of each).
+Times reported with "repeats" are the median and range over five timed repeats.
+
 Prints one JSON line (see the field list at the end of main()).
 """
 import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -30,8 +44,38 @@ KERNEL_SRCS = [os.path.join(ROOT, "speculative_decoding_verification_decode_amd"
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gate_up_7b_k8_hbm_traffic.md")
 
 
+REPEATS = 5
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def spread(xs, nd=4):
+    """Median, min and max of repeated timings."""
+    return {"median": round(statistics.median(xs), nd), "min": round(min(xs), nd), "max": round(max(xs), nd),
+            "repeats": len(xs)}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def weight_bytes_per_layer(S):
+    """bf16 bytes of one layer's projections, biases and norm gains."""
+    proj = S.hidden * (S.q_dim + 2 * S.kv_dim) + S.q_dim * S.hidden + 3 * S.hidden * S.ffn
+    return 2 * (proj + (S.q_dim + 2 * S.kv_dim) + 2 * S.hidden)
+
+
+def kv_cache_bytes(S, positions, n_layers=None):
+    """bf16 K and V bytes of `positions` cache positions over the layers."""
+    return (S.n_layers if n_layers is None else n_layers) * positions * 2 * S.kv_dim * 2
 
 
 def measured_traffic():
@@ -60,6 +104,9 @@ def main():
     ap.add_argument("--no-round", action="store_true", help="skip the device-resident draft+verify round line")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill (time to first token) line")
     ap.add_argument("--no-nf4", action="store_true", help="skip the NF4 14B-shape verify line")
+    ap.add_argument("--no-half", action="store_true", help="skip the hidden-state half-shard line")
+    ap.add_argument("--no-draft", action="store_true", help="skip the 0.5B drafter round line")
+    ap.add_argument("--no-ngram", action="store_true", help="skip the prompt-lookup loop line")
     ap.add_argument("--kernel-iters", type=int, default=56)
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="also run plain device copies of 1 GiB, so HBM byte counters can be scaled")
@@ -138,19 +185,24 @@ def main():
     tokens_per_step = len(CONTEXTS) * (K + 1)
     value = tokens_per_step * args.steps / wall
 
-    # Per-context device time (HIP events on the library stream).
+    # Per-context device time (HIP events on the library stream), median over REPEATS timed
+    # repeats of n back-to-back verifies each.
     per_ctx = {}
     for ctx in CONTEXTS:
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
+        reps = []
         n = max(5, args.steps)
-        e0.record(stream)
-        for _ in range(n):
-            sfb.sf_verify_device(caches[ctx], drafts[ctx], ks[ctx], sfb.SF_NO_COMMIT)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / n
-        per_ctx[ctx] = {"ms": round(ms, 4), "verify_tokens_per_s": round((K + 1) / ms * 1e3, 1)}
+        for _ in range(REPEATS):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(n):
+                sfb.sf_verify_device(caches[ctx], drafts[ctx], ks[ctx], sfb.SF_NO_COMMIT)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            reps.append(e0.elapsed_time(e1) / n)
+        ms = statistics.median(reps)
+        per_ctx[ctx] = {"ms": round(ms, 4), "ms_spread": spread(reps),
+                        "verify_tokens_per_s": round((K + 1) / ms * 1e3, 1)}
 
     # Snapshot form of rollback at context 512: saving and restoring the state one pass
     # overwrites (length, pending token, 9 K/V rows of every layer), timed with HIP events;
@@ -182,7 +234,7 @@ def main():
     t0 = time.perf_counter()
     nh = 10
     for _ in range(nh):
-        acc, tgt = sfb.sf_verify(c512, hd, hk, sfb.SF_NO_COMMIT)
+        _, tgt512 = sfb.sf_verify(c512, hd, hk, sfb.SF_NO_COMMIT)
     host_ms = (time.perf_counter() - t0) * 1e3 / nh
 
     # Per-kernel timing at the verify shape, cycling layers so weights stream from HBM.
@@ -219,6 +271,7 @@ def main():
     # Batched verify: 32 sequences x 9 positions in one pass, contexts drawn from U{256..8192}
     # (one pool), each sequence's K/V a prefix of the same synthetic array.
     batched = None
+    batch_work = None
     if not args.no_batched:
         Bn = 32
         rng = np.random.default_rng(synth.seeds(5)["contexts"])
@@ -234,23 +287,190 @@ def main():
         for _ in range(2):
             sfb.sf_verify_device(cb, bd, None, sfb.SF_NO_COMMIT)
         torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        nb_ = max(3, args.steps // 2)
-        e0.record(stream)
-        for _ in range(nb_):
-            sfb.sf_verify_device(cb, bd, None, sfb.SF_NO_COMMIT)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        bms = e0.elapsed_time(e1) / nb_
+        nb_ = max(3, args.steps // 4)
+        breps = []
+        for _ in range(REPEATS):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(nb_):
+                sfb.sf_verify_device(cb, bd, None, sfb.SF_NO_COMMIT)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            breps.append(e0.elapsed_time(e1) / nb_)
+        bms = statistics.median(breps)
         w_bytes = S.n_layers * layer_bytes + kern["lm_head"]["bytes"]
         kvb = float(sum(int(c) + K + 1 for c in bctx)) * 2 * S.kv_dim * 2 * S.n_layers
         batched = {"sequences": Bn, "rows": Bn * (K + 1), "contexts": "U{256..8192}, mean %.0f" % bctx.mean(),
-                   "ms": round(bms, 4), "verify_tokens_per_s": round(Bn * (K + 1) / bms * 1e3, 1),
+                   "ms": round(bms, 4), "ms_spread": spread(breps),
+                   "verify_tokens_per_s": round(Bn * (K + 1) / bms * 1e3, 1),
                    "alg_GBps": round((w_bytes + kvb) / (bms * 1e-3) / 1e9, 1),
                    "frac_peak": round((w_bytes + kvb) / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         sfb.sf_cache_free(cb)
+        batch_work = (bctx, bd.cpu().numpy())
         log(f"batched: {batched}")
+
+    # Hidden-state half shard: layers 0..13 of the same stack (no final norm, no head), the
+    # pass writing bf16 x of its 9 positions.  From 1024 prior positions of synthetic K/V, 256
+    # verifies of seeded drafts, each committing its 9 positions and then rolled back to keep
+    # 9 - r of them (r ~ U{0..8}) with a seeded pending token.  Host-inclusive steps (one H2D,
+    # the graph, the results and hidden-state copies, the rollback); device time per pass
+    # from HIP events around each verify.
+    half = None
+    if not args.no_half:
+        H = synth.QWEN7B_HALF
+        hdesc = sfb.desc_from_shape(H)
+        htensors, hptrs = sfb.upload_weights(w, hdesc)
+        torch.cuda.synchronize()
+        hmodel = sfb.sf_model_create(hdesc, hptrs, stream.cuda_stream)
+        del htensors, hptrs
+        hc = sfb.sf_cache_alloc(hmodel, 1, 4096, K)
+        kdev = torch.from_numpy(kbits[:H.n_layers].view(np.int16)).cuda()
+        vdev = torch.from_numpy(vbits[:H.n_layers].view(np.int16)).cuda()
+        sfb.sf_kv_write(hc, 0, kdev, vdev, 1024, kbits.shape[2])
+        del kdev, vdev
+        hrng = np.random.default_rng(synth.seeds(3)["draft"])
+        sfb.sf_set_next(hc, 0, int(hrng.integers(0, S.vocab)))
+        hid = torch.empty((K + 1, H.hidden), dtype=torch.int16, device="cuda")
+        n_half = 256
+        hd = hrng.integers(0, S.vocab, size=(n_half, K)).astype(np.int32)
+        for i in range(2):   # warm-up passes, then back to 1024 positions
+            sfb.sf_verify(hc, hd[i:i + 1], None, 0, dev_out=hid)
+        sfb.sf_rollback(hc, 0, 1024)
+        L = 1024
+        evs = []
+        kv_pos = 0
+        t0 = time.perf_counter()
+        for i in range(n_half):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            sfb.sf_verify(hc, hd[i:i + 1], None, 0, dev_out=hid)
+            e1.record(stream)
+            evs.append((e0, e1))
+            kv_pos += L + K + 1
+            r = synth.rejected_suffix(hrng, K)
+            L = L + K + 1 - r
+            sfb.sf_rollback(hc, 0, L)
+            sfb.sf_set_next(hc, 0, int(hrng.integers(0, S.vocab)))
+        torch.cuda.synchronize()
+        hwall = time.perf_counter() - t0
+        dms = [a.elapsed_time(b) for a, b in evs]
+        hms = statistics.median(dms)
+        hbytes = (H.n_layers * layer_bytes + kv_cache_bytes(S, kv_pos / n_half, H.n_layers)
+                  + (K + 1) * H.hidden * 2 * 2)
+        half = {"model": "qwen2.5-7b-shape layers 0..13, hidden-state output (bf16 x), no head",
+                "K": K, "steps": n_half, "contexts": f"1024..{L}", "rollback": "r ~ U{0..8} of 9 positions",
+                "device_ms_per_pass": round(hms, 4), "device_ms_spread": spread(dms),
+                "wall_ms_per_step": round(hwall * 1e3 / n_half, 4),
+                "verify_tokens_per_s": round((K + 1) / hms * 1e3, 1),
+                "alg_bytes_per_pass": int(hbytes), "alg_GBps": round(hbytes / (hms * 1e-3) / 1e9, 1),
+                "frac_peak": round(hbytes / (hms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        sfb.sf_cache_free(hc)
+        sfb.sf_model_free(hmodel)
+        log(f"half shard: {half}")
+
+    # The drafter alone: Qwen2.5-0.5B shape (24 layers, tied head), a 512-token prompt
+    # prefilled on the GPU, then 64 rounds of one call of 8 graph-replayed single-token steps,
+    # each round followed by the seeded outcome of a verify: r ~ U{0..8} drafts rejected,
+    # the cache rewound to keep the pending token and 8 - r drafts, and a seeded correction
+    # as the new pending token (nothing to do when r = 0).
+    draft_line = None
+    if not args.no_draft:
+        SD = synth.QWEN05B
+        s2 = synth.seeds(2)
+        wd2 = synth.model_weights(SD, s2["weights"])
+        ddesc = sfb.desc_from_shape(SD)
+        dtensors, dptrs = sfb.upload_weights(wd2, ddesc)
+        torch.cuda.synchronize()
+        dm2 = sfb.sf_model_create(ddesc, dptrs, stream.cuda_stream)
+        del dtensors, dptrs, wd2
+        n_rounds2 = 64
+        dc2 = sfb.sf_cache_alloc(dm2, 1, 512 + (n_rounds2 + 2) * 8 + 16, 0)
+        sfb.sf_prefill(dc2, 0, synth.prompt_ids(SD.vocab, 512, s2["prompt"]))
+        drng = np.random.default_rng(s2["draft"] + 1)
+        sfb.sf_draft_step(dc2, 8)    # warm-up round, then back to the prompt
+        sfb.sf_rollback(dc2, 0, 512)
+        L, _ = sfb.sf_cache_state(dc2, 0)
+        evs = []
+        kv_pos = 0
+        t0 = time.perf_counter()
+        for _ in range(n_rounds2):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            sfb.sf_draft_step(dc2, 8)
+            e1.record(stream)
+            evs.append((e0, e1))
+            kv_pos += sum(L + i + 1 for i in range(8))
+            r = synth.rejected_suffix(drng, 8)
+            if r:
+                L = L + 1 + (8 - r)
+                sfb.sf_rollback(dc2, 0, L)
+                sfb.sf_set_next(dc2, 0, int(drng.integers(0, SD.vocab)))
+            else:
+                L = L + 8
+        torch.cuda.synchronize()
+        dwall = time.perf_counter() - t0
+        rms_ = [a.elapsed_time(b) for a, b in evs]
+        drms = statistics.median(rms_)
+        step_w = SD.n_layers * weight_bytes_per_layer(SD) + SD.vocab * SD.hidden * 2 + SD.hidden * 2
+        dbytes = 8 * step_w + kv_cache_bytes(SD, kv_pos / n_rounds2)
+        draft_line = {"model": "qwen2.5-0.5b-shape drafter, tied head, random-init bf16", "prompt": 512,
+                      "rounds": n_rounds2, "steps_per_round": 8, "contexts": f"512..{L}",
+                      "device_ms_per_round": round(drms, 4), "device_ms_spread": spread(rms_),
+                      "wall_ms_per_round": round(dwall * 1e3 / n_rounds2, 4),
+                      "us_per_step": round(drms * 1e3 / 8, 1),
+                      "draft_tokens_per_s": round(8 / drms * 1e3, 1),
+                      "alg_bytes_per_round": int(dbytes), "alg_GBps": round(dbytes / (drms * 1e-3) / 1e9, 1),
+                      "frac_peak": round(dbytes / (drms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        sfb.sf_cache_free(dc2)
+        sfb.sf_model_free(dm2)
+        log(f"draft rounds: {draft_line}")
+
+    # The prompt-lookup loop at the 7B shape: the first 4096 tokens of the repeating history
+    # prefilled on the GPU, then 64 steps of: n-gram proposal (the last 2..4 tokens of the
+    # committed stream plus the pending token, looked up earlier in the stream, up to 8
+    # following tokens), a committing verify with k = the proposal's length, and the stream
+    # extended by the pending token and the M accepted drafts.  Host-inclusive.
+    ngram_loop = None
+    if not args.no_ngram:
+        n_prompt, n_steps4 = 4096, 64
+        c4 = sfb.sf_cache_alloc(model, 1, n_prompt + n_steps4 * (K + 1) + 16, K)
+        prompt4 = hist[:n_prompt]
+        t0 = time.perf_counter()
+        nxt = sfb.sf_prefill(c4, 0, prompt4)
+        pf_ms = (time.perf_counter() - t0) * 1e3
+        toks = [int(t) for t in prompt4]
+        histo = [0] * (K + 1)
+        n_prop = []
+        t0 = time.perf_counter()
+        for _ in range(n_steps4):
+            prop = sfb.sf_ngram_propose(np.array(toks + [nxt], dtype=np.int32), 2, 4, K)
+            d = np.zeros((1, K), dtype=np.int32)
+            d[0, :len(prop)] = prop
+            acc, tgt = sfb.sf_verify(c4, d, np.array([len(prop)], dtype=np.int32), 0)
+            M = int(acc[0])
+            toks.append(nxt)
+            toks.extend(int(t) for t in prop[:M])
+            nxt = int(tgt[0][M])
+            histo[M] += 1
+            n_prop.append(len(prop))
+        lwall = time.perf_counter() - t0
+        L4, _ = sfb.sf_cache_state(c4, 0)
+        committed4 = L4 - n_prompt
+        assert committed4 == sum((m + 1) * c for m, c in enumerate(histo))
+        ngram_loop = {"model": "this model", "history": "repeating spans (16 x 32 ids, 10% substituted)",
+                      "prompt": n_prompt, "prefill_ms": round(pf_ms, 2), "steps": n_steps4,
+                      "accepted_histogram": {str(m): c for m, c in enumerate(histo)},
+                      "mean_accepted": round(sum(m * c for m, c in enumerate(histo)) / n_steps4, 3),
+                      "mean_proposed": round(sum(n_prop) / n_steps4, 3),
+                      "steps_without_proposal": sum(1 for k_ in n_prop if k_ == 0),
+                      "committed_tokens": committed4,
+                      "committed_tokens_per_s": round(committed4 / lwall, 1),
+                      "wall_ms_per_step": round(lwall * 1e3 / n_steps4, 4)}
+        sfb.sf_cache_free(c4)
+        log(f"n-gram loop: {ngram_loop}")
 
     # Prefill (time to first token): prompts of 512 and 2048 seeded ids from an empty cache,
     # in passes of up to 512 positions, host-inclusive (sf_prefill returns the next token).
@@ -388,33 +608,112 @@ def main():
         torch.cuda.synchronize()
         log(f"nf4 14b: {nf4_line}")
 
+    # The oracle on the host, one bounded sample per workload (float64 torch; K/V loaded from
+    # the same synthetic bytes as the GPU's, except the tiny workload, which prefills its own).
     cpu = None
+    cpu_all = None
     if not args.no_cpu:
         import oracle
-        ctx = CONTEXTS[0]
-        m = oracle.Model(S, w)
-        oc = oracle.KVCache(S, ctx + K + 1)
-        oc.load(kbits, vbits, ctx, next_token=int(hist[ctx]))
-        d = drafts[ctx].cpu().numpy()
-        kk = int(ks[ctx].item())
-        # Verifies of the same pass (the cache is not committed) until about 10 s of CPU work.
-        t0 = time.perf_counter()
-        nv = 0
-        while True:
-            r = oracle.verify(m, oc, d, kk, commit=False)
-            nv += 1
-            if time.perf_counter() - t0 >= 10.0 or nv >= 30:
-                break
-        sec = (time.perf_counter() - t0) / nv
-        # Sanity: the GPU pass at this context agrees with the oracle where the gap rule applies.
-        gap = r["gap"].numpy()
-        agree = sum(1 for j in range(K + 1) if gap[j] > 0.1 and int(tgt[0][j]) == int(r["target"][j]))
+        threads = torch.get_num_threads()
+        cpu_all = {"threads": threads, "os_cpu_count": os.cpu_count(), "cpu_model": cpu_model()}
+        m7 = oracle.Model(S, w)
+
+        def oracle_verify_at(model_, shape, ctx, draft, k, nxt, kb=kbits, vb=vbits):
+            oc = oracle.KVCache(shape, ctx + K + 1)
+            oc.load(kb[:shape.n_layers], vb[:shape.n_layers], ctx, next_token=int(nxt))
+            t0 = time.perf_counter()
+            r = oracle.verify(model_, oc, draft, k, commit=False)
+            return time.perf_counter() - t0, r
+
+        # Full stack, one verify at each headline context (the headline's step).
+        per = {}
+        r512 = None
+        for ctx in CONTEXTS:
+            sec, r = oracle_verify_at(m7, S, ctx, drafts[ctx].cpu().numpy(), int(ks[ctx].item()), hist[ctx])
+            per[str(ctx)] = round(sec, 3)
+            if ctx == CONTEXTS[0]:
+                r512 = r
+        step_sec = sum(per.values())
+        # Sanity: the GPU pass at ctx 512 agrees with the oracle where the gap rule applies.
+        gap = r512["gap"].numpy()
+        agree = sum(1 for j in range(K + 1) if gap[j] > 0.1 and int(tgt512[0][j]) == int(r512["target"][j]))
         under = int((gap > 0.1).sum())
-        cpu = {"value": round((K + 1) / sec, 4), "unit": "verify tokens/s", "cores": torch.get_num_threads(),
-               "kind": "oracle", "seconds_per_verify": round(sec, 3), "verifies": nv,
-               "sample": f"{nv} verifies (9 positions each) of the full 28-layer stack + head at context "
-                         f"{ctx}, float64 torch on host, about 10 s in total; GPU targets agree on "
-                         f"{agree}/{under} gap>0.1 slots"}
+        cpu = {"value": round(len(CONTEXTS) * (K + 1) / step_sec, 4), "unit": "verify tokens/s", "cores": threads,
+               "kind": "oracle", "seconds_per_verify": per,
+               "sample": f"one verify (9 positions) of the full 28-layer stack + head at each context "
+                         f"{'/'.join(map(str, CONTEXTS))}, the headline's step, float64 torch on host "
+                         f"({threads} threads, {cpu_all['cpu_model']}); GPU targets agree on {agree}/{under} "
+                         f"gap>0.1 slots at ctx {CONTEXTS[0]}"}
+        cpu_all["full_stack_k8"] = cpu
+        log(f"cpu full stack: {per}")
+
+        # Tiny decoder: the whole 16-step lockstep run (prefill of a 64-token prompt; per step
+        # the oracle's own 4-token greedy continuation, corrupted at a seeded slot, then a
+        # committing K=4 verify).
+        T1 = synth.TINY
+        s1 = synth.seeds(1)
+        m1 = oracle.Model(T1, synth.model_weights(T1, s1["weights"]), cache=True)
+        oc = oracle.KVCache(T1, 128)
+        t0 = time.perf_counter()
+        oracle.prefill(m1, oc, synth.prompt_ids(T1.vocab, 64, s1["prompt"]))
+        rng1 = np.random.default_rng(s1["draft"])
+        tv = 0.0
+        n1 = 0
+        for _ in range(16):
+            if oc.length + 5 > oc.capacity:
+                break
+            cont = oracle.greedy_continuation(m1, oc, 4)
+            d1, _ = synth.corrupt_draft(cont, T1.vocab, rng1)
+            t1 = time.perf_counter()
+            oracle.verify(m1, oc, d1, 4)
+            tv += time.perf_counter() - t1
+            n1 += 1
+        run_sec = time.perf_counter() - t0
+        cpu_all["tiny_16_steps"] = {"seconds_per_run": round(run_sec, 3), "verify_seconds": round(tv, 4),
+                                    "steps": n1, "verify_tokens_per_s": round(n1 * 5 / tv, 1),
+                                    "sample": "the whole lockstep run (up to 16 steps, capacity 128), K=4"}
+
+        # 0.5B drafter: one round of 8 committing single-token steps at context 512.
+        SD = synth.QWEN05B
+        s2 = synth.seeds(2)
+        md = oracle.Model(SD, synth.model_weights(SD, s2["weights"]))
+        kb2, vb2 = synth.synthetic_kv(SD, 512, s2["kv"])
+        oc = oracle.KVCache(SD, 512 + 8)
+        oc.load(kb2, vb2, 512, next_token=int(hist[512]))
+        t0 = time.perf_counter()
+        for _ in range(8):
+            oracle.verify(md, oc, [], 0)
+        rsec = time.perf_counter() - t0
+        cpu_all["drafter_round"] = {"seconds_per_round": round(rsec, 3),
+                                    "draft_tokens_per_s": round(8 / rsec, 3),
+                                    "sample": "one round of 8 steps at context 512 (synthetic K/V)"}
+
+        # Half shard: one 9-position verify at context 1024.
+        H = synth.QWEN7B_HALF
+        mh = oracle.Model(H, w)
+        hd0 = np.random.default_rng(synth.seeds(3)["draft"]).integers(0, S.vocab, size=K).astype(np.int32)
+        hsec, _ = oracle_verify_at(mh, H, 1024, hd0, K, hist[1024])
+        cpu_all["half_shard_ctx1024"] = {"seconds_per_verify": round(hsec, 3),
+                                         "verify_tokens_per_s": round((K + 1) / hsec, 3),
+                                         "sample": "one verify at context 1024"}
+
+        # 32-sequence pass: the oracle verifies sequences one by one (the batch's rows are
+        # independent); two of the 32 are timed, those whose contexts are nearest the batch
+        # mean, and the pass time is 32 times their mean.
+        if batch_work is not None:
+            bctx, bdr = batch_work
+            order = np.argsort(np.abs(bctx - bctx.mean()))[:2]
+            secs = []
+            for b in order:
+                sec, _ = oracle_verify_at(m7, S, int(bctx[b]), bdr[b], K, hist[int(bctx[b])])
+                secs.append(sec)
+            pass_sec = len(bctx) * sum(secs) / len(secs)
+            cpu_all["batched_32"] = {"seconds_per_pass": round(pass_sec, 3),
+                                     "verify_tokens_per_s": round(len(bctx) * (K + 1) / pass_sec, 3),
+                                     "sample": f"2 of {len(bctx)} sequences (contexts "
+                                               f"{', '.join(str(int(bctx[b])) for b in order)}), scaled by "
+                                               f"{len(bctx)}/2"}
+        log(f"cpu baselines: {cpu_all}")
 
     out = {
         "metric": "verify tokens/s (Qwen2.5-7B-shape, K=8, 1 GPU)",
@@ -444,8 +743,12 @@ def main():
         "prefill_ttft": prefill,
         "snapshot_rollback_ctx512": snapshot_rb,
         "nf4_14b_verify_ctx512": nf4_line,
+        "half_shard_ctx1024": half,
+        "drafter_rounds_0.5b": draft_line,
+        "ngram_loop_ctx4096": ngram_loop,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "cpu_baselines": cpu_all,
     }
     print(json.dumps(out))
     for c in caches.values():
