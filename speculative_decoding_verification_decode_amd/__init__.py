@@ -15,7 +15,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsf.so")
+# SF_LIB names another build of the same library (the host-AddressSanitizer build that the CPU
+# tests make); by default the in-tree libsf.so.
+LIB_PATH = os.environ.get("SF_LIB") or os.path.join(_HERE, "libsf.so")
 
 SF_OK = 0
 SF_E_ARG = -1

@@ -1,6 +1,7 @@
 """Build libsf.so in-tree with hipcc for gfx950.
 
     python -m speculative_decoding_verification_decode_amd.build
+    python -m speculative_decoding_verification_decode_amd.build --asan OUT_DIR   (host ASan build)
 """
 import os
 import subprocess
@@ -44,5 +45,26 @@ def build(verbose=False):
     return LIB
 
 
+# Host code under AddressSanitizer: the same sources with the device code built as usual and
+# only the host pass instrumented.  Loaded through SF_LIB with the ASan runtime preloaded.
+ASAN_HOST_FLAGS = ["-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_asan(out_dir):
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    out = os.path.join(out_dir, "libsf_asan.so")
+    flags = [f for f in FLAGS if f != "-O3"] + ASAN_HOST_FLAGS
+    cmd = [HIPCC, *flags, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", out, *srcs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in ln]
+        sys.stderr.write("\n".join(msgs) + "\n")
+        raise RuntimeError("hipcc failed building the AddressSanitizer library")
+    return out
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if sys.argv[1:2] == ["--asan"]:
+        print(build_asan(sys.argv[2] if len(sys.argv) > 2 else os.getcwd()))
+    else:
+        print(build(verbose=True))
