@@ -266,7 +266,11 @@ def main():
     roofline = {"bound": "hbm", "kernel": "k_gemm<SWIGLU> (gate/up projection, 9 rows)",
                 "achieved": g["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(g["GBps"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                "launch_us": g["us"], "alg_bytes_per_launch": g["bytes"]}
+                "launch_us": g["us"], "alg_bytes_per_launch": g["bytes"],
+                # The whole verify beside the dominant kernel: algorithmic bytes of the timed
+                # steps over their wall time, and per context over its device time.
+                "whole_step_frac": round(total_bytes * args.steps / wall / 1e9 / HBM_PEAK_GBS, 4),
+                "per_context_frac": {str(c): per_ctx[c]["frac_peak"] for c in CONTEXTS}}
 
     # Batched verify: 32 sequences x 9 positions in one pass, contexts drawn from U{256..8192}
     # (one pool), each sequence's K/V a prefix of the same synthetic array.
