@@ -12,6 +12,7 @@ path, through the C ABI, on the two-layer decoder.
   no sequence's length or pending token moves; the next call works as before.
 - A device-resident round over three sequences, one of whose rounds is mixed (some sequences
   accept every draft, others do not), against the oracle sequence by sequence.
+- Device drafts outside the vocabulary: clamped into the pass, never accepted.
 """
 import numpy as np
 import pytest
@@ -210,3 +211,49 @@ def test_round_over_three_sequences_with_a_mixed_round():
             sfb.sf_round_free(rnd)
         d.close()
         v.close()
+
+
+def test_device_drafts_outside_the_vocabulary_are_clamped_and_never_accepted():
+    """sf_verify_device does not range-check device drafts (they never reach the host): ids
+    outside [0, V) feed the clamped id (0 or V-1) into the pass and never count as accepted.
+    Targets equal those of a host verify with the clamped drafts; M stops at the first
+    out-of-range draft."""
+    sfb = need_gpu()
+    w = synth.model_weights(S, synth.seeds(1)["weights"])
+    eng = sfb.Engine(S, w, n_seqs=2, capacity=128, k_max=K)
+    try:
+        for b, seed in enumerate((31, 37)):
+            sfb.sf_prefill(eng.cache, b, synth.prompt_ids(S.vocab, 24, seed))
+        sfb.sf_sync(eng.cache)
+        # sequence 0: its own greedy continuation with an out-of-range id at slot 2;
+        # sequence 1: a negative id first.
+        acc0, tgt0 = sfb.sf_verify(eng.cache, np.zeros((2, K), np.int32), np.zeros(2, np.int32), sfb.SF_NO_COMMIT)
+        raw = np.array([[int(tgt0[0][0]), 0, S.vocab + 7, 3], [-5, 1, 2, 3]], dtype=np.int32)
+        d = torch.from_numpy(raw).cuda()
+        sfb.sf_verify_device(eng.cache, d, None, sfb.SF_NO_COMMIT)
+        sfb.sf_sync(eng.cache)
+        pa, _ = sfb.sf_results_device(eng.cache)
+        res = _read_device(pa, 2 + 2 * (K + 1))
+        acc_d, tgt_d = res[:2], res[2:].reshape(2, K + 1)
+        clamped = np.clip(raw, 0, S.vocab - 1).astype(np.int32)
+        acc_h, tgt_h = sfb.sf_verify(eng.cache, clamped, None, sfb.SF_NO_COMMIT)
+        assert (tgt_d == tgt_h).all()
+        for b in range(2):
+            M = 0
+            while M < K and raw[b][M] == tgt_h[b][M]:
+                M += 1
+            assert int(acc_d[b]) == M, (b, acc_d, M)
+        assert int(acc_d[1]) == 0 and int(acc_d[0]) <= 2
+    finally:
+        eng.close()
+
+
+def _read_device(addr, n):
+    """n int32 values at a device address, copied to the host (hipMemcpy, device to host)."""
+    import ctypes
+    out = np.zeros(n, dtype=np.int32)
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    hip.hipMemcpy.restype = ctypes.c_int
+    assert hip.hipMemcpy(out.ctypes.data_as(ctypes.c_void_p), ctypes.c_void_p(addr), n * 4, 2) == 0
+    return out
