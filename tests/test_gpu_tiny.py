@@ -341,3 +341,53 @@ def test_largest_capacity_and_longest_draft():
             check_targets(tgt[0], r, K)
     finally:
         p.close()
+
+
+def test_prompt_lookup_loop_commits_the_greedy_stream():
+    """The prompt-lookup loop the benchmark runs, at the tiny shape (head gain 32): prefill a
+    repeating history, then committing verifies whose drafts the n-gram proposer finds in
+    the committed stream (pending token included).  Proposals equal the oracle proposer's on
+    the same stream, and the committed stream is plain greedy decoding of the oracle, token
+    for token while its choices clear the gap ([ShardFlow] "Speculative Decoding: The Idea":
+    the output is the target model's own; [Sangama] "Speculative decoding: correct, but
+    slower (for now)": the client's n-gram guesses)."""
+    sfb = need_gpu()
+    K = 8
+    w = synth.with_head_gain(synth.model_weights(S, synth.seeds(1)["weights"]), 32.0)
+    model = oracle.Model(S, w, cache=True)
+    prompt = synth.lookup_history(S.vocab, 160, 5151)
+    eng = sfb.Engine(S, w, n_seqs=1, capacity=512, k_max=K)
+    try:
+        nxt = sfb.sf_prefill(eng.cache, 0, prompt)
+        toks = [int(t) for t in prompt]
+        stream, accepted = [], []
+        for _ in range(40):
+            h = np.array(toks + [nxt], dtype=np.int32)
+            prop = sfb.sf_ngram_propose(h, 2, 4, K)
+            assert prop.tolist() == oracle.propose(h.tolist(), 2, 4, K)
+            d = np.zeros((1, K), dtype=np.int32)
+            d[0, :len(prop)] = prop
+            acc, tgt = sfb.sf_verify(eng.cache, d, np.array([len(prop)], dtype=np.int32), 0)
+            M = int(acc[0])
+            stream += [nxt] + [int(t) for t in prop[:M]]
+            toks += [nxt] + [int(t) for t in prop[:M]]
+            accepted.append(M)
+            nxt = int(tgt[0][M])
+        assert sfb.sf_cache_state(eng.cache, 0) == (len(prompt) + len(stream), nxt)
+        # Every committed token is the oracle's greedy choice after the committed prefix
+        # (the oracle is fed the GPU's stream, so a near-tie does not desynchronise the rest).
+        c = oracle.KVCache(S, 512)
+        z = oracle.prefill(model, c, prompt)
+        gap = oracle.top_gap(z[-1:])[0].item()
+        n_cmp = 0
+        for i, t in enumerate(stream):
+            if gap > GAP:
+                assert t == c.next_token, (i, t, c.next_token)
+                n_cmp += 1
+            oracle.set_next(c, t)
+            gap = oracle.verify(model, c, [], 0)["gap"][0].item()
+        say(f"[tiny] lookup loop: {len(stream)} tokens in 40 steps, accepted {sum(accepted)}, "
+            f"{n_cmp} checked against the oracle's greedy choice")
+        assert n_cmp >= (3 * len(stream)) // 4 and sum(accepted) > 0
+    finally:
+        eng.close()
