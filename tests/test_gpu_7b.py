@@ -62,8 +62,8 @@ def _load_ctx(sfb, cache, kv, ctx, nxt, n_layers=None):
     torch.cuda.synchronize()
 
 
-def _oracle_cache(kv, ctx, nxt, shape=S):
-    c = oracle.KVCache(shape, ctx + K + 1)
+def _oracle_cache(kv, ctx, nxt, shape=S, capacity=None):
+    c = oracle.KVCache(shape, capacity or ctx + K + 1)
     c.load(kv[0][:shape.n_layers], kv[1][:shape.n_layers], ctx, next_token=nxt)
     return c
 
@@ -147,11 +147,25 @@ def test_prefill_one_and_two_passes_match_oracle(eng, weights, monkeypatch):
 
 
 def test_half_stack_hidden_states_match_oracle(weights, kv, hist):
+    """The first-half shard's step as the benchmark runs it: a committing verify from 1024
+    positions, a rollback that keeps the pending token and two drafts with a new pending
+    token, and a second verify on top; both passes' hidden states against the oracle doing
+    the same (max |d(x/rms x)| within the logit tolerance)."""
     sfb = need_gpu()
     H = synth.QWEN7B_HALF
     ctx = 1024
     say("[7b-half] engine")
     e = sfb.Engine(H, weights, n_seqs=1, capacity=4096, k_max=K)
+    model = oracle.Model(H, weights)
+    oc = _oracle_cache(kv, ctx, int(hist[ctx]), H, capacity=ctx + 2 * (K + 1) + 8)
+
+    def check(xg, xo, what):
+        ng = xg / xg.pow(2).mean(-1, keepdim=True).sqrt()
+        no = xo / xo.pow(2).mean(-1, keepdim=True).sqrt()
+        err = (ng - no).abs().max().item()
+        say(f"[7b-half] {what}: max |d(x/rms x)| {err:.4g}")
+        assert err <= LOGIT_TOL
+
     try:
         nxt = int(hist[ctx])
         _load_ctx(sfb, e.cache, kv, ctx, nxt, n_layers=H.n_layers)
@@ -164,14 +178,19 @@ def test_half_stack_hidden_states_match_oracle(weights, kv, hist):
         sfb.sf_rollback(e.cache, 0, ctx + 3)
         assert sfb.sf_cache_state(e.cache, 0)[0] == ctx + 3
         say("[7b-half] oracle")
-        r = oracle.verify(oracle.Model(H, weights), _oracle_cache(kv, ctx, nxt, H), d, K, commit=False)
-        xg = hid.cpu().view(torch.bfloat16).double()
-        xo = r["hidden"]
-        ng = xg / xg.pow(2).mean(-1, keepdim=True).sqrt()
-        no = xo / xo.pow(2).mean(-1, keepdim=True).sqrt()
-        err = (ng - no).abs().max().item()
-        say(f"[7b-half] max |d(x/rms x)| {err:.4g}")
-        assert err <= LOGIT_TOL
+        r = oracle.verify(model, oc, d, K, commit=True)
+        check(hid.cpu().view(torch.bfloat16).double(), r["hidden"], "first pass")
+        # the second step on top of the rewound cache, with a new pending token
+        oracle.rollback(oc, ctx + 3)
+        t2 = int(hist[ctx + 40])
+        oracle.set_next(oc, t2)
+        sfb.sf_set_next(e.cache, 0, t2)
+        d2 = hist[ctx + 41:ctx + 41 + K].astype(np.int32)
+        sfb.sf_verify(e.cache, d2[None], None, 0, dev_out=hid)
+        torch.cuda.synchronize()
+        assert sfb.sf_cache_state(e.cache, 0)[0] == ctx + 3 + K + 1
+        r2 = oracle.verify(model, oc, d2, K, commit=True)
+        check(hid.cpu().view(torch.bfloat16).double(), r2["hidden"], "after the rollback")
     finally:
         e.close()
 
