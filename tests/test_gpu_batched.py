@@ -75,3 +75,56 @@ def test_batched_tiny_matches_oracle_and_single_sequence_runs():
     finally:
         eng.close()
         one.close()
+
+
+def test_largest_batch_64_sequences_512_rows():
+    """The largest pass the library takes: 64 sequences x 8 positions (k_max 7, 512 rows, eight
+    64-row groups), contexts drawn from U{10..200} and per-sequence k in 0..7.  Eight sampled
+    sequences against the oracle, two of them also bitwise against the same sequence verified
+    alone, and every sequence's committed state."""
+    sfb = need_gpu()
+    Bm, Km, cap = 64, 7, 256
+    rng = np.random.default_rng(6464)
+    ctx = rng.integers(10, 201, size=Bm)
+    nxt = rng.integers(0, S.vocab, size=Bm)
+    drafts = rng.integers(0, S.vocab, size=(Bm, Km)).astype(np.int32)
+    ks = rng.integers(0, Km + 1, size=Bm).astype(np.int32)
+    kv = synth.synthetic_kv(S, cap, 6465)
+    w = synth.model_weights(S, synth.seeds(5)["weights"])
+    eng = sfb.Engine(S, w, n_seqs=Bm, capacity=cap, k_max=Km)
+    one = sfb.Engine(S, w, n_seqs=1, capacity=cap, k_max=Km)
+    try:
+        _fill(sfb, eng, kv, ctx, nxt)
+        logits = torch.empty((Bm * (Km + 1), S.vocab), dtype=torch.float32, device="cuda")
+        acc, tgt = sfb.sf_verify(eng.cache, drafts, ks, sfb.SF_DEBUG_LOGITS | sfb.SF_NO_COMMIT, dev_out=logits)
+        acc_g, tgt_g = sfb.sf_verify(eng.cache, drafts, ks, 0)   # graph replay, commits
+        torch.cuda.synchronize()
+        assert (acc_g == acc).all() and (tgt_g == tgt).all()
+        lg = logits.double().cpu().view(Bm, Km + 1, S.vocab)
+        model = oracle.Model(S, w)
+        one_logits = torch.empty((Km + 1, S.vocab), dtype=torch.float32, device="cuda")
+        sample = sorted(set([0, Bm - 1] + rng.choice(Bm, size=6, replace=False).tolist()))
+        worst = 0.0
+        for b in sample:
+            c = oracle.KVCache(S, int(ctx[b]) + Km + 1)
+            c.load(kv[0], kv[1], int(ctx[b]), next_token=int(nxt[b]))
+            r = oracle.verify(model, c, drafts[b], int(ks[b]), commit=True)
+            worst = max(worst, (lg[b] - r["logits"]).abs().max().item())
+            check_targets(tgt[b], r, Km)
+            if accepted_decided(r, int(acc[b]), int(ks[b])):
+                assert acc[b] == r["accepted"]
+                assert sfb.sf_cache_state(eng.cache, b) == (c.length, c.next_token)
+            if b in (sample[0], sample[-1]):
+                _fill(sfb, one, kv, [ctx[b]], [nxt[b]])
+                sfb.sf_verify(one.cache, drafts[b:b + 1], ks[b:b + 1], sfb.SF_DEBUG_LOGITS | sfb.SF_NO_COMMIT,
+                              dev_out=one_logits)
+                torch.cuda.synchronize()
+                assert torch.equal(one_logits.cpu(), logits.view(Bm, Km + 1, S.vocab)[b].cpu()), f"sequence {b}"
+        for b in range(Bm):
+            L, t = sfb.sf_cache_state(eng.cache, b)
+            assert L == int(ctx[b]) + int(acc[b]) + 1 and t == int(tgt[b][int(acc[b])])
+        say(f"[batched] 64 x 8 rows: max |dlogit| vs oracle over {len(sample)} sequences: {worst:.3g}")
+        assert worst <= LOGIT_TOL
+    finally:
+        eng.close()
+        one.close()
