@@ -253,6 +253,25 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    # Measured HBM rates beside the nominal peak: the fastest stream of this run (the LM head's
+    # 1.09 GB weight stream), and torch's own copy (1 GiB read + 1 GiB written) and sum (2 GiB
+    # read) on the default stream, median of five after a warm-up.
+    probe = {"lm_head_stream_GBps": kern["lm_head"]["GBps"]}
+    src = torch.ones(1 << 30, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for name, fn, nbytes in (("torch_copy_GBps", lambda: dst.copy_(src[: 1 << 29]), 2 << 30),
+                             ("torch_sum_read_GBps", lambda: src.sum(dtype=torch.float32), 2 << 30)):
+        fn()
+        ts = []
+        for _ in range(5):
+            ev0.record()
+            fn()
+            ev1.record()
+            ev1.synchronize()
+            ts.append(ev0.elapsed_time(ev1) * 1e-3)
+        probe[name] = round(nbytes / statistics.median(ts) / 1e9, 1)
+    del src, dst
     layer_bytes = sum(kern[n]["bytes"] for n in ("qkv", "o_proj", "gate_up", "down"))
     # Algorithmic bytes of one verify: every layer's weights and activations once, the
     # LM head once, and K/V of positions 0..ctx+K read once per layer.
@@ -741,6 +760,7 @@ def main():
         "hbm_frac_peak": round(total_bytes * args.steps / wall / 1e9 / HBM_PEAK_GBS, 4),
         "per_context": {str(k): v for k, v in per_ctx.items()},
         "host_inclusive_verify_ms_ctx512": round(host_ms, 4),
+        "hbm_probe": probe,
         "kernels_at_verify_shape": kern,
         "batched_32": batched,
         "device_round_0.5b_drafter": spec_round,
