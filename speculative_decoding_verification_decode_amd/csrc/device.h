@@ -162,7 +162,10 @@ __device__ void attn_spans(const AttnArgs& a, int x0, int xstep, int kvh, int b,
   const bool active = wrow0 < nrows;
 
   // K/V of a chunk: each thread loads kKvPerThread 16-byte pieces of K and of V, all
-  // issued before any is used (positions past the last row's are zero).
+  // issued before any is used.  Positions past the last row's are read at the last position
+  // and zeroed when staged in LDS, not here: a select on a loaded value right after the load
+  // would make the wave wait for the load at once, so the next chunk's loads would not
+  // overlap the current chunk's work.
   const uint16_t* kbase = a.kc + (size_t)b * a.seq_stride + (size_t)kvh * a.cap * DH;
   const uint16_t* vbase = a.vc + (size_t)b * a.seq_stride + (size_t)kvh * a.cap * DH;
   constexpr int kKvPerThread = kChunk * DH / 8 / 256;
@@ -176,7 +179,6 @@ __device__ void attn_spans(const AttnArgs& a, int x0, int xstep, int kvh, int b,
       const int pos = min(c0 + j, plast);
       kreg[u] = *(const u32x4*)(kbase + (size_t)pos * DH + d8);
       vreg[u] = *(const u32x4*)(vbase + (size_t)pos * DH + d8);
-      if (c0 + j > plast) { kreg[u] = (u32x4){0u, 0u, 0u, 0u}; vreg[u] = kreg[u]; }
     }
   };
   // Q as the MFMA A operand: lane holds row wrow0 + l16, dims ks*32 + 8*g4 .. +8, as a
@@ -248,8 +250,11 @@ __device__ void attn_spans(const AttnArgs& a, int x0, int xstep, int kvh, int b,
         const int idx = tid + u * 256;
         int j, d8;
         piece(idx, j, d8);
-        *(u32x4*)(&Kl[j * KP + d8]) = kreg[u];
-        const uint32_t vw[4] = {vreg[u].x, vreg[u].y, vreg[u].z, vreg[u].w};
+        const bool past = c0 + j > plast;
+        const u32x4 kz = past ? (u32x4){0u, 0u, 0u, 0u} : kreg[u];
+        const u32x4 vz = past ? (u32x4){0u, 0u, 0u, 0u} : vreg[u];
+        *(u32x4*)(&Kl[j * KP + d8]) = kz;
+        const uint32_t vw[4] = {vz.x, vz.y, vz.z, vz.w};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           Vt[(d8 + 2 * t) * VP + vt_col(d8, j)] = (uint16_t)(vw[t] & 0xFFFFu);
