@@ -995,27 +995,47 @@ __global__ __launch_bounds__(1024) void k_accept(const AcceptArgs a) {
   __shared__ int tgt[kMaxRows];   // one per slot: up to k_max+1 in a verify, a whole prefill chunk
   const int b = blockIdx.x, tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
+  // The merge is order independent, so the parts of a row may be split over waves: with S
+  // slots to reduce, each gets max(1, 16/S) waves (all sixteen for a one-row drafter step),
+  // each lane keeping sixteen loads in flight.
+  __shared__ float red_v[16];
+  __shared__ int red_i[16];
+  const int nslots = a.T - a.slot_lo;
+  const int wps = (a.has_head && nslots > 0 && nslots <= 16) ? 16 / nslots : 1;
   if (a.has_head) {
-    for (int slot = wave; slot < a.T; slot += 16) {
-      if (slot < a.slot_lo) {
-        if (lane == 0) tgt[slot] = 0;
-        continue;
-      }
+    for (int slot = tid; slot < a.slot_lo; slot += 1024) tgt[slot] = 0;
+    for (int item = wave; item < nslots * wps; item += 16) {
+      const int slot = a.slot_lo + item / wps, part = item % wps;
       const float2* row = a.amax + (size_t)(b * a.T + slot) * a.nparts;
+      const int stride = 64 * wps;
       float bv = -INFINITY;
       int bi = 0x7FFFFFFF;
-      int p = lane;
-      for (; p + 7 * 64 < a.nparts; p += 8 * 64) {
-        float2 e[8];
+      int p = lane + 64 * part;
+      for (; p + 15 * stride < a.nparts; p += 16 * stride) {
+        float2 e[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) e[u] = row[p + u * 64];
+        for (int u = 0; u < 16; ++u) e[u] = row[p + u * stride];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) amax_merge(bv, bi, e[u].x, __float_as_int(e[u].y));
+        for (int u = 0; u < 16; ++u) amax_merge(bv, bi, e[u].x, __float_as_int(e[u].y));
       }
-      for (; p < a.nparts; p += 64) amax_merge(bv, bi, row[p].x, __float_as_int(row[p].y));
+      for (; p < a.nparts; p += stride) amax_merge(bv, bi, row[p].x, __float_as_int(row[p].y));
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) amax_merge(bv, bi, __shfl_xor(bv, o), __shfl_xor(bi, o));
-      if (lane == 0) tgt[slot] = (bi == 0x7FFFFFFF) ? 0 : bi;
+      if (wps == 1) {
+        if (lane == 0) tgt[slot] = (bi == 0x7FFFFFFF) ? 0 : bi;
+      } else if (lane == 0) {
+        red_v[item] = bv;
+        red_i[item] = bi;
+      }
+    }
+    if (wps > 1) {
+      __syncthreads();
+      if (tid < nslots) {
+        float bv = -INFINITY;
+        int bi = 0x7FFFFFFF;
+        for (int q = 0; q < wps; ++q) amax_merge(bv, bi, red_v[tid * wps + q], red_i[tid * wps + q]);
+        tgt[a.slot_lo + tid] = (bi == 0x7FFFFFFF) ? 0 : bi;
+      }
     }
   }
   __syncthreads();
