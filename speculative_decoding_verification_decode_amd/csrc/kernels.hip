@@ -1010,15 +1010,15 @@ __global__ __launch_bounds__(1024) void k_accept(const AcceptArgs a) {
       const int stride = 64 * wps;
       float bv = -INFINITY;
       int bi = 0x7FFFFFFF;
-      int p = lane + 64 * part;
-      for (; p + 15 * stride < a.nparts; p += 16 * stride) {
+      // Batches of sixteen loads, the last one masked, so every batch is one round trip.
+      for (int p = lane + 64 * part; p < a.nparts; p += 16 * stride) {
         float2 e[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) e[u] = row[p + u * stride];
+        for (int u = 0; u < 16; ++u)
+          e[u] = (p + u * stride < a.nparts) ? row[p + u * stride] : make_float2(-INFINITY, __int_as_float(0x7FFFFFFF));
 #pragma unroll
         for (int u = 0; u < 16; ++u) amax_merge(bv, bi, e[u].x, __float_as_int(e[u].y));
       }
-      for (; p < a.nparts; p += stride) amax_merge(bv, bi, row[p].x, __float_as_int(row[p].y));
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) amax_merge(bv, bi, __shfl_xor(bv, o), __shfl_xor(bi, o));
       if (wps == 1) {
