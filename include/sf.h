@@ -323,6 +323,22 @@ sf_status sf_time_kernel(sf_cache* cache, int32_t kernel, int32_t iters, float* 
  * them to check that no counter grows from pass to pass.  Errors: SF_E_ARG, SF_E_HIP. */
 sf_status sf_debug_counters(sf_cache* cache, int64_t* sum, int32_t* max);
 
+/* Bits of sf_debug_checks: invariants the kernels of a checking build record when violated
+ * (they still clamp or skip as the regular build does; nothing traps). */
+#define SF_CHECK_TOKEN   1u   /* a token id outside [0, vocab) reached the embedding (clamped) */
+#define SF_CHECK_K       2u   /* a staged draft count outside [0, k_max] (clamped by the accept) */
+#define SF_CHECK_POS     4u   /* a K/V append or attention row at or past the capacity (skipped) */
+#define SF_CHECK_COMMIT  8u   /* a commit that would move a length past the capacity */
+#define SF_CHECK_NAN    16u   /* a NaN logit in the LM head's output */
+
+/* sf_debug_checks: the checking build (libsf_checks.so, built by `build.py --checks` and by
+ * the package build) records the SF_CHECK_* invariants above in one word per device instead
+ * of only clamping; this waits for the device, returns the word of the current device (host
+ * *bits) and with clear != 0 sets it to zero.  For callers that feed device-resident inputs
+ * (sf_verify_device, sf_round_run) which the host cannot check.  The regular build returns
+ * SF_E_STATE ("built without device checks") and *bits = 0.  Errors: SF_E_ARG, SF_E_HIP. */
+sf_status sf_debug_checks(uint32_t* bits, int32_t clear);
+
 /* Error injection for tests of the failure path: with SF_FAULT=alloc in the environment every
  * device allocation of sf_model_create(_nf4), sf_cache_alloc and sf_round_create fails as an
  * out-of-memory hipMalloc would (SF_E_NOMEM, nothing left allocated); with SF_FAULT=launch

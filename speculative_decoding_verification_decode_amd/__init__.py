@@ -96,6 +96,7 @@ def lib():
             "sf_sync": [_P],
             "sf_time_kernel": [_P, _I, _I, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double)],
             "sf_debug_counters": [_P, ctypes.POINTER(ctypes.c_int64), _PI],
+            "sf_debug_checks": [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -188,14 +189,32 @@ def sf_model_free(model):
     _check(lib().sf_model_free(model))
 
 
+# (n_seqs, k_max) of every cache this module allocated, by handle: the library writes
+# [n_seqs] and [n_seqs][...] host outputs, so their buffers are sized from the cache itself.
+_CACHE_SHAPES = {}
+
+
+def _handle(cache):
+    return cache.value if isinstance(cache, ctypes.c_void_p) else cache
+
+
+def _cache_shape(cache):
+    try:
+        return _CACHE_SHAPES[_handle(cache)]
+    except KeyError:
+        raise ValueError("not a cache allocated through sf_cache_alloc") from None
+
+
 def sf_cache_alloc(model, n_seqs, capacity, k_max):
     out = _P()
     _check(lib().sf_cache_alloc(model, n_seqs, capacity, k_max, ctypes.byref(out)))
+    _CACHE_SHAPES[out.value] = (int(n_seqs), int(k_max))
     return out
 
 
 def sf_cache_free(cache):
     _check(lib().sf_cache_free(cache))
+    _CACHE_SHAPES.pop(_handle(cache), None)
 
 
 def sf_prefill(cache, seq, tokens):
@@ -205,13 +224,20 @@ def sf_prefill(cache, seq, tokens):
     return nxt.value
 
 
-def sf_verify(cache, draft, k=None, flags=0, n_seqs=None, k_max=None, dev_out=None):
-    """draft: int array [n_seqs][k_max].  Returns (accepted [n_seqs], target [n_seqs][k_max+1])."""
+def sf_verify(cache, draft, k=None, flags=0, dev_out=None):
+    """draft: int array [n_seqs][k_max] of the cache's shape (one sequence: a 1-D array of at
+    most k_max drafts, zero-padded here); k: [n_seqs] or None.  Returns (accepted [n_seqs],
+    target [n_seqs][k_max+1])."""
+    n_seqs, k_max = _cache_shape(cache)
+    if draft is not None:
+        draft = np.asarray(draft, dtype=np.int32)
+        if n_seqs == 1 and draft.ndim <= 1 and draft.size <= k_max:
+            draft = np.concatenate([draft.reshape(-1), np.zeros(k_max - draft.size, np.int32)])
+        if draft.size != n_seqs * k_max:
+            raise ValueError(f"draft has {draft.size} ids; the cache takes [{n_seqs}][{k_max}]")
     d, dp = _i32(draft)
-    if n_seqs is None:
-        n_seqs = d.shape[0] if (d is not None and d.ndim == 2) else 1
-    if k_max is None:
-        k_max = d.shape[-1] if (d is not None and d.ndim) else 0
+    if k is not None and np.asarray(k).size != n_seqs:
+        raise ValueError(f"k has {np.asarray(k).size} entries; the cache has {n_seqs} sequences")
     kk, kp = _i32(k)
     acc = np.zeros(n_seqs, dtype=np.int32)
     tgt = np.zeros((n_seqs, k_max + 1), dtype=np.int32)
@@ -257,7 +283,9 @@ def sf_cache_state(cache, seq):
     return ln.value, nx.value
 
 
-def sf_draft_step(cache, n_steps, n_seqs=1):
+def sf_draft_step(cache, n_steps):
+    """Tokens [n_seqs][n_steps] of n_steps greedy steps of every sequence of the cache."""
+    n_seqs, _ = _cache_shape(cache)
     out = np.zeros((n_seqs, n_steps), dtype=np.int32)
     _check(lib().sf_draft_step(cache, n_steps, out.ctypes.data_as(_PI)))
     return out
@@ -310,6 +338,17 @@ def sf_debug_counters(cache):
     sm, mx = ctypes.c_int64(0), ctypes.c_int32(0)
     _check(lib().sf_debug_counters(cache, ctypes.byref(sm), ctypes.byref(mx)))
     return sm.value, mx.value
+
+
+SF_CHECK_TOKEN, SF_CHECK_K, SF_CHECK_POS, SF_CHECK_COMMIT, SF_CHECK_NAN = 1, 2, 4, 8, 16
+
+
+def sf_debug_checks(clear=False):
+    """Invariant bits (SF_CHECK_*) the checking build's kernels recorded on the current device,
+    optionally cleared; raises SFError (SF_E_STATE) on the regular build."""
+    bits = ctypes.c_uint32(0)
+    _check(lib().sf_debug_checks(ctypes.byref(bits), 1 if clear else 0))
+    return bits.value
 
 
 # ------------------------------------------------------------------ torch conveniences

@@ -2,6 +2,7 @@
 
     python -m speculative_decoding_verification_decode_amd.build
     python -m speculative_decoding_verification_decode_amd.build --asan OUT_DIR   (host ASan build)
+    python -m speculative_decoding_verification_decode_amd.build --checks         (device-checking build)
 """
 import os
 import subprocess
@@ -63,8 +64,29 @@ def build_asan(out_dir):
     return out
 
 
+# Checking build: the same sources with SF_CHECKS=1, so kernels record violated invariants
+# (token ids, draft counts, positions and commits against the capacity, NaN logits) in a
+# device word that sf_debug_checks reads.  A library of its own, loaded through SF_LIB.
+CHECKS_LIB = os.path.join(PKG, "libsf_checks.so")
+
+
+def build_checks(out=CHECKS_LIB):
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-DSF_CHECKS=1", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp, *srcs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in ln]
+        sys.stderr.write("\n".join(msgs) + "\n")
+        raise RuntimeError("hipcc failed building the checking library")
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     if sys.argv[1:2] == ["--asan"]:
         print(build_asan(sys.argv[2] if len(sys.argv) > 2 else os.getcwd()))
+    elif sys.argv[1:2] == ["--checks"]:
+        print(build_checks())
     else:
         print(build(verbose=True))

@@ -15,6 +15,23 @@ namespace sf {
 // count, attention, merge, embed, accept) has a gated instance that checks it.
 __device__ __forceinline__ bool gated_off(const int* gate) { return gate && *gate == 0; }
 
+// Checking build (SF_CHECKS=1, a library of its own): a violated invariant sets its bit in a
+// per-device word with a vector atomic; the regular build compiles the checks away.
+#ifndef SF_CHECKS
+#define SF_CHECKS 0
+#endif
+#if SF_CHECKS
+extern __device__ unsigned int g_checks;
+#endif
+__device__ __forceinline__ void check(bool ok, unsigned bit) {
+#if SF_CHECKS
+  if (!ok) atomicOr(&g_checks, bit);
+#else
+  (void)ok;
+  (void)bit;
+#endif
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -153,6 +170,7 @@ __device__ void attn_spans(const AttnArgs& a, int x0, int xstep, int kvh, int b,
   const int G = a.nq / a.nkv, nrows = a.T * G;
   const int L = a.len[b];
   const int plast = L + a.T - 1;
+  if (threadIdx.x == 0 && x0 == 0) check(plast < a.cap, kChkPos);
   int x = x0, span0 = span_first(x);
   if (span0 > plast) return;
 

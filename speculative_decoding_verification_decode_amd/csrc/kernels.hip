@@ -18,6 +18,24 @@
 
 namespace sf {
 
+#if SF_CHECKS
+__device__ unsigned int g_checks = 0;
+hipError_t read_checks(uint32_t* bits, bool clear) {
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpyFromSymbol(bits, HIP_SYMBOL(g_checks), sizeof(uint32_t));
+  if (e == hipSuccess && clear) {
+    const uint32_t zero = 0;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(g_checks), &zero, sizeof(uint32_t));
+  }
+  return e;
+}
+#else
+hipError_t read_checks(uint32_t* bits, bool) {
+  *bits = 0;
+  return hipErrorNotSupported;
+}
+#endif
+
 // Squares of the residual block for the next norm's sums; one array per row count, shared by
 // every epilogue instance of a kernel (they run one after another).
 template <int kRealRows>
@@ -49,6 +67,7 @@ __device__ void gemm_epilogue(const GemmArgs& g, int nb, int r0, const float* rs
       const float y2 = val(p + 16, m) * s + g.bias[nb * 32 + p + 16];
       const int b = mr / g.T, slot = mr - b * g.T;
       const int pos = g.len[b] + slot;
+      check(pos < g.cap, kChkPos);
       if (pos < g.cap) {
         if (sec == 2) {
           uint16_t* dst = g.vc + (size_t)b * g.seq_stride + ((size_t)head * g.cap + pos) * g.dh;
@@ -111,6 +130,7 @@ __device__ void gemm_epilogue(const GemmArgs& g, int nb, int r0, const float* rs
       int bi = nb * 32;
       for (int nl = 0; nl < 32; ++nl) {
         const float v = val(nl, m) * s;
+        check(v == v, kChkNaN);
         if (g.logits) g.logits[(size_t)mr * g.vocab + nb * 32 + nl] = v;
         if (v > best) { best = v; bi = nb * 32 + nl; }
       }
@@ -889,6 +909,7 @@ __global__ __launch_bounds__(256) void k_embed(const EmbedArgs e) {
     const int j = slot - 1;
     tok = (j < e.stage->k[b]) ? e.stage->draft[b * e.kmax + j] : 0;
   }
+  if (threadIdx.x == 0) check(tok >= 0 && tok < e.V, kChkToken);
   tok = min(max(tok, 0), e.V - 1);
   const uint16_t* src = e.embed + (size_t)tok * e.H;
   const int nparts = e.H >> 5;
@@ -1043,6 +1064,7 @@ __global__ __launch_bounds__(1024) void k_accept(const AcceptArgs a) {
     Stage* st = a.stage;
     const int flags = st->flags;
     int k = st->k[b];
+    check(k >= 0 && k <= a.T - 1, kChkK);
     k = min(max(k, 0), a.T - 1);
     int M = 0;
     if (a.has_head) {
@@ -1054,6 +1076,7 @@ __global__ __launch_bounds__(1024) void k_accept(const AcceptArgs a) {
       a.result[b] = M;
       for (int j = 0; j < a.T; ++j) a.result[a.B + b * a.T + j] = tgt[j];
       if (!(flags & kFlagNoCommit)) {
+        check(a.cap == 0 || a.len[b] + M + 1 <= a.cap, kChkCommit);
         a.len[b] += M + 1;
         a.next[b] = tgt[M];
       }
@@ -1064,7 +1087,10 @@ __global__ __launch_bounds__(1024) void k_accept(const AcceptArgs a) {
       }
     } else {
       a.result[b] = 0;
-      if (!(flags & kFlagNoCommit)) a.len[b] += k + 1;
+      if (!(flags & kFlagNoCommit)) {
+        check(a.cap == 0 || a.len[b] + k + 1 <= a.cap, kChkCommit);
+        a.len[b] += k + 1;
+      }
     }
   }
 }

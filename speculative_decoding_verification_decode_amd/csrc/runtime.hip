@@ -536,6 +536,7 @@ static hipError_t enqueue_forward(sf_cache* c, const Run& r) {
   ac.result = S.res_d; ac.draft_out = r.draft_mode ? S.dout_d : nullptr; ac.B = r.B; ac.T = r.T;
   ac.has_head = head; ac.gate = r.gate;
   ac.slot_lo = head ? r.head_from : 0;
+  ac.cap = c->cap;
   return launch_accept(ac, s);
 }
 
@@ -1292,6 +1293,15 @@ extern "C" sf_status sf_debug_counters(sf_cache* c, int64_t* sum, int32_t* max) 
   }
   *sum = s;
   *max = mx;
+  return SF_OK;
+}
+
+extern "C" sf_status sf_debug_checks(uint32_t* bits, int32_t clear) {
+  if (!bits) return fail(SF_E_ARG, "bits is NULL");
+  *bits = 0;
+  const hipError_t e = read_checks(bits, clear != 0);
+  if (e == hipErrorNotSupported) return fail(SF_E_STATE, "built without device checks");
+  if (e != hipSuccess) return fail(SF_E_HIP, std::string("checks: ") + hipGetErrorString(e));
   return SF_OK;
 }
 

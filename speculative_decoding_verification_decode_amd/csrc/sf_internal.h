@@ -29,7 +29,9 @@ __host__ __device__ constexpr size_t act_bytes(int ext, int k) { return (size_t)
 // Stage flags (device side).
 constexpr int kFlagNoCommit = 1;
 constexpr int kFlagForce = 2;
-constexpr int kFlagFirst = 8;                 // row 0 of each sequence takes stage.first, not the pending token
+constexpr int kFlagFirst = 8;
+// Invariant bits of the checking build (the SF_CHECK_* values of sf.h).
+constexpr unsigned kChkToken = 1u, kChkK = 2u, kChkPos = 4u, kChkCommit = 8u, kChkNaN = 16u;                 // row 0 of each sequence takes stage.first, not the pending token
 
 // Staging block: one host->device copy per pass.
 struct Stage {
@@ -149,11 +151,15 @@ struct AcceptArgs {
   int32_t* draft_out;      // [B][kMaxDraftSteps]
   int B, T, has_head;
   int slot_lo;             // targets of slots below slot_lo are not computed (reported as 0)
+  int cap;                 // cache capacity (checking build: a commit past it is recorded; 0: unchecked)
   const int* gate;        // nullptr, or the pass runs only while *gate != 0 (device flag)
 };
 
 // Launchers (kernels.hip).
 hipError_t launch_gemm(int epi, const GemmArgs& g, hipStream_t s);
+// Checking build: read (and optionally clear) the current device's invariant word; the
+// regular build returns hipErrorNotSupported.
+hipError_t read_checks(uint32_t* bits, bool clear);
 hipError_t launch_embed(const EmbedArgs& e, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int dh, int B, hipStream_t s);
 int attention_spans(int cap);

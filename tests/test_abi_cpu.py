@@ -161,3 +161,35 @@ def test_injected_allocation_failure_is_reported_and_leaves_nothing(monkeypatch,
     with pytest.raises(sfb.SFError) as e:
         create(d, ptrs, 0x1000)
     assert e.value.code == sfb.SF_E_ARG
+
+
+def test_debug_checks_on_the_regular_build_report_state():
+    """The regular library compiles the device checks away: sf_debug_checks says so
+    (SF_E_STATE, bits 0) without touching a device, and rejects a NULL pointer."""
+    L = _lib()
+    bits = ctypes.c_uint32(7)
+    assert L.sf_debug_checks(ctypes.byref(bits), 0) == sfb.SF_E_STATE
+    assert bits.value == 0 and "without device checks" in sfb.sf_last_error()
+    assert L.sf_debug_checks(None, 0) == sfb.SF_E_ARG
+
+
+def test_checking_library_builds_and_exports_every_symbol():
+    """The checking build (SF_CHECKS=1) compiles for gfx950 and exports the same C ABI."""
+    from speculative_decoding_verification_decode_amd import build as b
+    path = b.CHECKS_LIB if os.path.exists(b.CHECKS_LIB) else b.build_checks()
+    hdr = open(os.path.join(ROOT, "include", "sf.h")).read()
+    declared = set(re.findall(r"^(?:sf_status|int32_t|const char\*)\s+(sf_\w+)\s*\(", hdr, re.M))
+    L = ctypes.CDLL(path)
+    missing = [n for n in sorted(declared) if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_binding_sizes_outputs_from_the_cache_and_rejects_unknown_handles():
+    """The library writes [n_seqs] and [n_seqs][...] host outputs, so the binding takes their
+    sizes from the cache it allocated, never from the caller; a handle it did not allocate is
+    refused before any call into the library."""
+    bogus = ctypes.c_void_p(0x1000)
+    with pytest.raises(ValueError):
+        sfb.sf_draft_step(bogus, 2)
+    with pytest.raises(ValueError):
+        sfb.sf_verify(bogus, np.zeros((1, 4), np.int32))
