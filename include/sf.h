@@ -238,7 +238,7 @@ sf_status sf_cache_state(sf_cache* cache, int32_t seq, int32_t* length, int32_t*
  * [ShardFlow] "CUDA Graphs: What They Are and Why They Helped").  tokens: host
  * int32 [n_seqs][n_steps] receives the generated tokens (may be NULL).  Each step
  * commits: length += 1, pending = the new token.
- * Errors: SF_E_STATE (hidden-state stack), SF_E_ARG (n_steps < 1 or > 4096),
+ * Errors: SF_E_STATE (hidden-state stack), SF_E_ARG (n_steps < 1 or > 256),
  * SF_E_CAPACITY (length + n_steps > capacity). */
 sf_status sf_draft_step(sf_cache* cache, int32_t n_steps, int32_t* tokens);
 
