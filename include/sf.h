@@ -57,7 +57,7 @@ typedef struct sf_model_desc {
     int32_t n_kv_heads;   /* divides n_q_heads */
     int32_t head_dim;     /* 64 or 128 */
     int32_t ffn;          /* F; multiple of 32 */
-    int32_t vocab;        /* V; multiple of 16 */
+    int32_t vocab;        /* V; multiple of 32 */
     float rope_base;
     float rms_eps;
     int32_t has_head;     /* 1: final RMSNorm + LM head + argmax; 0: stack emits hidden states */
@@ -126,8 +126,9 @@ sf_status sf_cache_free(sf_cache* cache);
  * stacks return 0).  [Sangama] "What made it faster", item 4, splits long prompts into
  * 64-token pieces so that pipeline stages work on different pieces at once; on one GPU
  * there is no pipeline to fill, so up to eight such pieces (512 positions) go through
- * one pass together, which lets each weight byte serve 512 rows.  Not graph-captured.  The pass size (1..512) can be lowered for a cache by setting
- * SF_PREFILL_CHUNK in the environment before sf_cache_alloc; results are bit-identical
+ * one pass together, which lets each weight byte serve 512 rows.  Not graph-captured.  The
+ * pass size (1..512) can be lowered for a cache by setting SF_PREFILL_CHUNK in the
+ * environment before sf_cache_alloc; results are bit-identical
  * for any pass size.  Only the last position's logits are computed: earlier passes skip
  * the LM head, and the last one runs it for the rows it needs.
  * Errors: SF_E_ARG (token id outside [0,V), n < 1), SF_E_CAPACITY (n > capacity). */
@@ -170,7 +171,8 @@ sf_status sf_verify(sf_cache* cache, const int32_t* draft, const int32_t* k, uin
  *   dev_draft  device int32 [n_seqs][k_max]; dev_k device int32 [n_seqs] or NULL (k_max).
  *   Drafts are copied into the library's fixed staging buffer on the stream, then
  *   the captured graph is replayed.  Token ids are not range-checked here (they
- *   are never read on the host); ids outside [0,V) are clamped by the kernels.
+ *   are never read on the host); ids outside [0,V) are clamped by the kernels, and a k
+ *   outside 0..k_max by the accept step (the checking build records both: sf_debug_checks).
  *   Results: see sf_results_device.  Host-side length bookkeeping assumes the
  *   worst case (length + k_max + 1 per committing call) until sf_sync.
  * Errors: SF_E_ARG, SF_E_CAPACITY. */
