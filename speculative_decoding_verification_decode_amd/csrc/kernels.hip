@@ -306,9 +306,9 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(const GemmArgs g) {
 
   // k split over g.sp workgroups per block: each stores its partial tile (agent-coherent,
   // so the others see it without a cache flush) and counts its arrival on the block's
-  // counter; the one that brings the count to a multiple of sp adds the partials in split
-  // order and runs the epilogue.  The last arriver also puts the counter back to zero, so
-  // every counter stays in [0, sp) and is zero between launches (no growth, no wrap).
+  // counter; the one whose arrival brings the count to sp adds the partials in split order
+  // and runs the epilogue.  That last arriver also puts the counter back to zero, so every
+  // counter stays in [0, sp) and is zero between launches (no growth, no wrap).
   __shared__ int last_arrival;
   const bool split = g.sp > 1;
   float* const pblk = g.part + (size_t)nb * g.sp * g.rows * 32;   // [split][row][32]
