@@ -15,7 +15,8 @@ Beside the headline it measures, each on its own seeded synthetic workload:
     GPU prefill, each followed by a seeded rollback of 0..8 rejected drafts;
   - the prompt-lookup loop: a 4096-token repeating history prefilled on the GPU, then 64
     committed verify steps whose drafts the n-gram proposer finds in the committed stream
-    (acceptance histogram and committed tokens/s);
+    (acceptance histogram and committed tokens/s), on the random-init stack and on a stack of
+    the same shape whose greedy next token is the history's most frequent successor;
   - 32 sequences in one pass, prefill time to first token, the device-resident round, the
     snapshot rollback and the NF4 14B-shape verify;
   - the oracle on the host for each workload (a bounded sample of each).
@@ -455,44 +456,67 @@ def main():
     # prefilled on the GPU, then 64 steps of: n-gram proposal (the last 2..4 tokens of the
     # committed stream plus the pending token, looked up earlier in the stream, up to 8
     # following tokens), a committing verify with k = the proposal's length, and the stream
-    # extended by the pending token and the M accepted drafts.  Host-inclusive.
+    # extended by the pending token and the M accepted drafts.  Host-inclusive.  Run on two
+    # stacks of the same shape and cost: the random-init weights (which follow no text, so the
+    # lookup never finds what they will say) and the successor-planted stack (greedy next
+    # token = the prompt's most frequent successor of the current token: a stand-in for a
+    # model that has learned the history's statistics).
     ngram_loop = None
     if not args.no_ngram:
         n_prompt, n_steps4 = 4096, 64
-        c4 = sfb.sf_cache_alloc(model, 1, n_prompt + n_steps4 * (K + 1) + 16, K)
         prompt4 = hist[:n_prompt]
-        t0 = time.perf_counter()
-        nxt = sfb.sf_prefill(c4, 0, prompt4)
-        pf_ms = (time.perf_counter() - t0) * 1e3
-        toks = [int(t) for t in prompt4]
-        histo = [0] * (K + 1)
-        n_prop = []
-        t0 = time.perf_counter()
-        for _ in range(n_steps4):
-            prop = sfb.sf_ngram_propose(np.array(toks + [nxt], dtype=np.int32), 2, 4, K)
-            d = np.zeros((1, K), dtype=np.int32)
-            d[0, :len(prop)] = prop
-            acc, tgt = sfb.sf_verify(c4, d, np.array([len(prop)], dtype=np.int32), 0)
-            M = int(acc[0])
-            toks.append(nxt)
-            toks.extend(int(t) for t in prop[:M])
-            nxt = int(tgt[0][M])
-            histo[M] += 1
-            n_prop.append(len(prop))
-        lwall = time.perf_counter() - t0
-        L4, _ = sfb.sf_cache_state(c4, 0)
-        committed4 = L4 - n_prompt
-        assert committed4 == sum((m + 1) * c for m, c in enumerate(histo))
-        ngram_loop = {"model": "this model", "history": "repeating spans (16 x 32 ids, 10% substituted)",
-                      "prompt": n_prompt, "prefill_ms": round(pf_ms, 2), "steps": n_steps4,
-                      "accepted_histogram": {str(m): c for m, c in enumerate(histo)},
-                      "mean_accepted": round(sum(m * c for m, c in enumerate(histo)) / n_steps4, 3),
-                      "mean_proposed": round(sum(n_prop) / n_steps4, 3),
-                      "steps_without_proposal": sum(1 for k_ in n_prop if k_ == 0),
-                      "committed_tokens": committed4,
-                      "committed_tokens_per_s": round(committed4 / lwall, 1),
-                      "wall_ms_per_step": round(lwall * 1e3 / n_steps4, 4)}
-        sfb.sf_cache_free(c4)
+
+        def lookup_loop(mdl):
+            c4 = sfb.sf_cache_alloc(mdl, 1, n_prompt + n_steps4 * (K + 1) + 16, K)
+            t0 = time.perf_counter()
+            nxt = sfb.sf_prefill(c4, 0, prompt4)
+            pf_ms = (time.perf_counter() - t0) * 1e3
+            toks = [int(t) for t in prompt4]
+            histo = [0] * (K + 1)
+            n_prop = []
+            t0 = time.perf_counter()
+            for _ in range(n_steps4):
+                prop = sfb.sf_ngram_propose(np.array(toks + [nxt], dtype=np.int32), 2, 4, K)
+                d = np.zeros((1, K), dtype=np.int32)
+                d[0, :len(prop)] = prop
+                acc, tgt = sfb.sf_verify(c4, d, np.array([len(prop)], dtype=np.int32), 0)
+                M = int(acc[0])
+                toks.append(nxt)
+                toks.extend(int(t) for t in prop[:M])
+                nxt = int(tgt[0][M])
+                histo[M] += 1
+                n_prop.append(len(prop))
+            lwall = time.perf_counter() - t0
+            L4, _ = sfb.sf_cache_state(c4, 0)
+            committed4 = L4 - n_prompt
+            assert committed4 == sum((m + 1) * c for m, c in enumerate(histo))
+            sfb.sf_cache_free(c4)
+            return {"prefill_ms": round(pf_ms, 2),
+                    "accepted_histogram": {str(m): c for m, c in enumerate(histo)},
+                    "mean_accepted": round(sum(m * c for m, c in enumerate(histo)) / n_steps4, 3),
+                    "mean_proposed": round(sum(n_prop) / n_steps4, 3),
+                    "steps_without_proposal": sum(1 for k_ in n_prop if k_ == 0),
+                    "committed_tokens": committed4,
+                    "committed_tokens_per_s": round(committed4 / lwall, 1),
+                    "wall_ms_per_step": round(lwall * 1e3 / n_steps4, 4)}
+
+        t0 = time.time()
+        wp = synth.successor_stack(w, synth.history_successors(prompt4, S.vocab, sd["prompt"] + 1))
+        ptensors, pptrs = sfb.upload_weights(wp, desc)
+        torch.cuda.synchronize()
+        pmodel = sfb.sf_model_create(desc, pptrs, stream.cuda_stream)
+        del ptensors, pptrs, wp
+        torch.cuda.synchronize()
+        log(f"successor-planted stack ready in {time.time() - t0:.1f}s")
+        planted = lookup_loop(pmodel)
+        sfb.sf_model_free(pmodel)
+        ngram_loop = {"history": "repeating spans (16 x 32 ids, 10% substituted)", "prompt": n_prompt,
+                      "steps": n_steps4, "K": K,
+                      "successor_planted": dict(model="7B-shape stack whose greedy next token is the "
+                                                "prompt's most frequent successor of the current one "
+                                                "(layers scaled by 2^-8, head built from the embedding)",
+                                                **planted),
+                      "random_init": dict(model="this model (random-init weights)", **lookup_loop(model))}
         log(f"n-gram loop: {ngram_loop}")
 
     # Prefill (time to first token): prompts of 512 and 2048 seeded ids from an empty cache,

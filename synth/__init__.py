@@ -25,6 +25,8 @@ from .gen import (
     seeds,
     with_head_gain,
     near_copy,
+    history_successors,
+    successor_stack,
     nf4_tensor,
     nf4_model_weights,
 )
@@ -32,5 +34,5 @@ from .gen import (
 __all__ = [
     "Shape", "TINY", "QWEN05B", "QWEN7B", "QWEN7B_HALF", "QWEN14B", "QWEN14B_2L", "SHAPES", "tensor_names", "tensor_shape",
     "bf16_normal", "model_weights", "prompt_ids", "corrupt_draft", "synthetic_kv", "lookup_history",
-    "batch_contexts", "rejected_suffix", "seeds", "with_head_gain", "near_copy", "nf4_tensor", "nf4_model_weights",
+    "batch_contexts", "rejected_suffix", "seeds", "with_head_gain", "near_copy", "history_successors", "successor_stack", "nf4_tensor", "nf4_model_weights",
 ]

@@ -95,6 +95,56 @@ def with_head_gain(weights, gain):
     return out
 
 
+def history_successors(hist, vocab, seed):
+    """succ[t] = the id that most often follows t in `hist` (ties: the smallest such id); an
+    id never followed by anything there gets a seeded uniform id."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    succ = rng.integers(0, vocab, size=vocab, dtype=np.int64)
+    h = np.asarray(hist, dtype=np.int64)
+    keys, counts = np.unique(h[:-1] * vocab + h[1:], return_counts=True)
+    a, b = keys // vocab, keys % vocab
+    order = np.lexsort((b, -counts, a))        # by a, then most frequent, then smallest b
+    a, b = a[order], b[order]
+    first = np.ones(len(a), dtype=bool)
+    first[1:] = a[1:] != a[:-1]
+    succ[a[first]] = b[first]
+    return succ.astype(np.int32)
+
+
+def successor_stack(weights, succ, shift=8, threads=None):
+    """A stack (untied head) whose greedy next token is succ[current token], a stand-in for a
+    trained model that has learned a history's successor statistics (random-init weights follow
+    no text, so a prompt-lookup drafter never finds what they will say).  Every layer's
+    projections and biases are scaled by 2**-shift, an exponent shift (exact for every result in
+    the normal range; results below it, which N(0, 0.02) weights never produce, become signed
+    zeros), which keeps the residual stream within about 1% of the current token's embedding
+    after 28 layers; the LM head's row v is the sum of the embeddings of the ids u with
+    succ[u] = v (the embedding row itself when there is one such u, zero when there is none),
+    so that embedding scores its successor highest by a wide margin (|e|^2 against the e.e' of
+    unrelated rows).  The embedding, norms and all shapes are those of `weights`, so a pass
+    costs the same."""
+    def scaled(u):
+        e = (u >> np.uint16(7)) & np.uint16(0xFF)
+        return np.where(e > shift, u - np.uint16(shift << 7), u & np.uint16(0x8000)).astype(np.uint16)
+    out = dict(weights)
+    names = [n for n in weights if n.split(".")[-1] in ("wq", "wk", "wv", "wo", "wg", "wu", "wd", "bq", "bk", "bv")]
+    with ThreadPoolExecutor(_threads(threads)) as pool:
+        for name, arr in zip(names, pool.map(lambda n: scaled(weights[n]), names)):
+            out[name] = arr
+    emb = weights["embed"]
+    succ = np.asarray(succ, dtype=np.int64)
+    order = np.argsort(succ, kind="stable")
+    rows, starts, sizes = np.unique(succ[order], return_index=True, return_counts=True)
+    head = np.zeros_like(emb)
+    one = sizes == 1
+    head[rows[one]] = emb[order[starts[one]]]
+    for v, s0, n in zip(rows[~one], starts[~one], sizes[~one]):
+        acc = (emb[order[s0:s0 + n]].astype(np.uint32) << np.uint32(16)).view(np.float32).sum(axis=0, dtype=np.float32)
+        head[v] = _f32_to_bf16_bits(acc)
+    out["lm_head"] = head
+    return out
+
+
 def near_copy(weights, other, eps):
     """A stack close to `weights`: every projection becomes bf16(w + eps * o), o the same
     tensor of `other`; embeddings, norms and the head are shared.  Used as a drafter that

@@ -343,19 +343,26 @@ def test_largest_capacity_and_longest_draft():
         p.close()
 
 
-def test_prompt_lookup_loop_commits_the_greedy_stream():
-    """The prompt-lookup loop the benchmark runs, at the tiny shape (head gain 32): prefill a
-    repeating history, then committing verifies whose drafts the n-gram proposer finds in
-    the committed stream (pending token included).  Proposals equal the oracle proposer's on
-    the same stream, and the committed stream is plain greedy decoding of the oracle, token
-    for token while its choices clear the gap ([ShardFlow] "Speculative Decoding: The Idea":
-    the output is the target model's own; [Sangama] "Speculative decoding: correct, but
-    slower (for now)": the client's n-gram guesses)."""
+@pytest.mark.parametrize("planted", [False, True], ids=["random", "successor"])
+def test_prompt_lookup_loop_commits_the_greedy_stream(planted):
+    """The prompt-lookup loop the benchmark runs, at the tiny shape: prefill a repeating
+    history, then committing verifies whose drafts the n-gram proposer finds in the committed
+    stream (pending token included).  Proposals equal the oracle proposer's on the same
+    stream, and the committed stream is plain greedy decoding of the oracle, token for token
+    while its choices clear the gap ([ShardFlow] "Speculative Decoding: The Idea": the output
+    is the target model's own; [Sangama] "Speculative decoding: correct, but slower (for
+    now)": the client's n-gram guesses).  Two stacks: random-init weights with head gain 32,
+    and the successor-planted stack the benchmark's loop uses (greedy next = the history's
+    most frequent successor), under which the drafts are mostly accepted."""
     sfb = need_gpu()
     K = 8
-    w = synth.with_head_gain(synth.model_weights(S, synth.seeds(1)["weights"]), 32.0)
-    model = oracle.Model(S, w, cache=True)
     prompt = synth.lookup_history(S.vocab, 160, 5151)
+    w = synth.model_weights(S, synth.seeds(1)["weights"])
+    if planted:
+        w = synth.successor_stack(w, synth.history_successors(prompt, S.vocab, 5152))
+    else:
+        w = synth.with_head_gain(w, 32.0)
+    model = oracle.Model(S, w, cache=True)
     eng = sfb.Engine(S, w, n_seqs=1, capacity=512, k_max=K)
     try:
         nxt = sfb.sf_prefill(eng.cache, 0, prompt)
@@ -386,8 +393,10 @@ def test_prompt_lookup_loop_commits_the_greedy_stream():
                 n_cmp += 1
             oracle.set_next(c, t)
             gap = oracle.verify(model, c, [], 0)["gap"][0].item()
-        say(f"[tiny] lookup loop: {len(stream)} tokens in 40 steps, accepted {sum(accepted)}, "
-            f"{n_cmp} checked against the oracle's greedy choice")
+        say(f"[tiny] lookup loop ({'successor' if planted else 'random'}): {len(stream)} tokens in 40 steps, "
+            f"accepted {sum(accepted)}, {n_cmp} checked against the oracle's greedy choice")
         assert n_cmp >= (3 * len(stream)) // 4 and sum(accepted) > 0
+        if planted:
+            assert n_cmp == len(stream) and sum(accepted) >= 2 * len(accepted)
     finally:
         eng.close()
