@@ -461,10 +461,29 @@ def main():
     # lookup never finds what they will say) and the successor-planted stack (greedy next
     # token = the prompt's most frequent successor of the current token: a stand-in for a
     # model that has learned the history's statistics).
+    # The successor-planted stack of the same shape (built once, for this loop and the round):
+    # its greedy next token is the most frequent successor of the current token in the first
+    # 4096 tokens of the history.
+    n_prompt = 4096
+    prompt4 = hist[:n_prompt]
+    succ_v = synth.history_successors(prompt4, S.vocab, sd["prompt"] + 1)
+    planted_model = []
+
+    def planted_verifier():
+        if not planted_model:
+            t0 = time.time()
+            wp = synth.successor_stack(w, succ_v)
+            ptensors, pptrs = sfb.upload_weights(wp, desc)
+            torch.cuda.synchronize()
+            planted_model.append(sfb.sf_model_create(desc, pptrs, stream.cuda_stream))
+            del ptensors, pptrs, wp
+            torch.cuda.synchronize()
+            log(f"successor-planted stack ready in {time.time() - t0:.1f}s")
+        return planted_model[0]
+
     ngram_loop = None
     if not args.no_ngram:
-        n_prompt, n_steps4 = 4096, 64
-        prompt4 = hist[:n_prompt]
+        n_steps4 = 64
 
         def lookup_loop(mdl):
             c4 = sfb.sf_cache_alloc(mdl, 1, n_prompt + n_steps4 * (K + 1) + 16, K)
@@ -500,16 +519,7 @@ def main():
                     "committed_tokens_per_s": round(committed4 / lwall, 1),
                     "wall_ms_per_step": round(lwall * 1e3 / n_steps4, 4)}
 
-        t0 = time.time()
-        wp = synth.successor_stack(w, synth.history_successors(prompt4, S.vocab, sd["prompt"] + 1))
-        ptensors, pptrs = sfb.upload_weights(wp, desc)
-        torch.cuda.synchronize()
-        pmodel = sfb.sf_model_create(desc, pptrs, stream.cuda_stream)
-        del ptensors, pptrs, wp
-        torch.cuda.synchronize()
-        log(f"successor-planted stack ready in {time.time() - t0:.1f}s")
-        planted = lookup_loop(pmodel)
-        sfb.sf_model_free(pmodel)
+        planted = lookup_loop(planted_verifier())
         ngram_loop = {"history": "repeating spans (16 x 32 ids, 10% substituted)", "prompt": n_prompt,
                       "steps": n_steps4, "K": K,
                       "successor_planted": dict(model="7B-shape stack whose greedy next token is the "
@@ -555,48 +565,75 @@ def main():
     # weights yield.
     spec_round = None
     if not args.no_round:
-        SD = synth.QWEN05B
-        sr = synth.seeds(6)
-        wd = synth.model_weights(SD, sr["weights"])
-        dtensors, dptrs = sfb.upload_weights(wd, sfb.desc_from_shape(SD))
-        torch.cuda.synchronize()
-        dmodel = sfb.sf_model_create(sfb.desc_from_shape(SD), dptrs, stream.cuda_stream)
-        del dtensors, dptrs, wd
-        torch.cuda.synchronize()
-        n_rounds = max(4, args.steps)
+        n_rounds = max(64, args.steps)             # enough rounds for a stable acceptance mean
         rcap = 512 + (n_rounds + 2) * (K + 1) + K + 1
-        vcache = sfb.sf_cache_alloc(model, 1, rcap, K)
-        dcache = sfb.sf_cache_alloc(dmodel, 1, rcap, 0)
-        prompt = synth.prompt_ids(SD.vocab, 512, sr["prompt"])
-        nxt = sfb.sf_prefill(vcache, 0, prompt)
-        sfb.sf_prefill(dcache, 0, prompt)
-        sfb.sf_set_next(dcache, 0, nxt)
-        rnd = sfb.sf_round_create(dcache, vcache, K)
-        sfb.sf_round_run(rnd, 1)                      # warm-up round
-        L0, _ = sfb.sf_cache_state(vcache, 0)
-        sfb.sf_sync(dcache)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e0.record(stream)
-        sfb.sf_round_run(rnd, n_rounds)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        rwall = time.perf_counter() - t0
-        rms = e0.elapsed_time(e1) / n_rounds
-        L1, _ = sfb.sf_cache_state(vcache, 0)
-        committed = L1 - L0
-        spec_round = {"drafter": "qwen2.5-0.5b-shape, random-init bf16", "verifier": "this model", "K": K,
-                      "prompt": 512, "rounds": n_rounds, "contexts": f"{L0}..{L1}",
-                      "ms_per_round": round(rms, 4), "committed_tokens": committed,
-                      "mean_accepted": round(committed / n_rounds - 1, 3),
-                      "committed_tokens_per_s": round(committed / (rms * n_rounds) * 1e3, 1),
-                      "wall_ms_per_round": round(rwall * 1e3 / n_rounds, 4)}
-        sfb.sf_round_free(rnd)
-        sfb.sf_cache_free(dcache)
-        sfb.sf_cache_free(vcache)
-        sfb.sf_model_free(dmodel)
+
+        def make_model(shape, wts):
+            tens, pts = sfb.upload_weights(wts, sfb.desc_from_shape(shape))
+            torch.cuda.synchronize()
+            m_ = sfb.sf_model_create(sfb.desc_from_shape(shape), pts, stream.cuda_stream)
+            del tens, pts
+            torch.cuda.synchronize()
+            return m_
+
+        def run_round(dmodel, vmodel, prompt):
+            vcache = sfb.sf_cache_alloc(vmodel, 1, rcap, K)
+            dcache = sfb.sf_cache_alloc(dmodel, 1, rcap, 0)
+            nxt = sfb.sf_prefill(vcache, 0, prompt)
+            sfb.sf_prefill(dcache, 0, prompt)
+            sfb.sf_set_next(dcache, 0, nxt)
+            rnd = sfb.sf_round_create(dcache, vcache, K)
+            sfb.sf_round_run(rnd, 1)                      # warm-up round
+            L0, _ = sfb.sf_cache_state(vcache, 0)
+            sfb.sf_sync(dcache)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            e0.record(stream)
+            sfb.sf_round_run(rnd, n_rounds)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            rwall = time.perf_counter() - t0
+            rms = e0.elapsed_time(e1) / n_rounds
+            L1, _ = sfb.sf_cache_state(vcache, 0)
+            committed = L1 - L0
+            sfb.sf_round_free(rnd)
+            sfb.sf_cache_free(dcache)
+            sfb.sf_cache_free(vcache)
+            return {"rounds": n_rounds, "contexts": f"{L0}..{L1}", "ms_per_round": round(rms, 4),
+                    "committed_tokens": committed,
+                    "committed_tokens_per_round": round(committed / n_rounds, 3),
+                    "mean_accepted": round(committed / n_rounds - 1, 3),
+                    "committed_tokens_per_s": round(committed / (rms * n_rounds) * 1e3, 1),
+                    "wall_ms_per_round": round(rwall * 1e3 / n_rounds, 4)}
+
+        sr = synth.seeds(6)
+        # Random-init pair: the drafter's guesses never match.
+        SD = synth.QWEN05B
+        dm = make_model(SD, synth.model_weights(SD, sr["weights"]))
+        rand = run_round(dm, model, synth.prompt_ids(SD.vocab, 512, sr["prompt"]))
+        sfb.sf_model_free(dm)
+        # Successor-planted pair: the verifier is the planted 7B-shape stack; the drafter (0.5B
+        # shape, untied head) follows the same successor map on all but a seeded 22% of ids, so a
+        # draft agrees with the verifier's choice with probability about 0.78 per position and
+        # a round commits about 4.07 tokens in expectation (the pages' tokens per round trip).
+        SDu = synth.QWEN05B_UNTIED
+        base_d = succ_v[:SDu.vocab]
+        succ_d = synth.perturb_successors(np.where(base_d < SDu.vocab, base_d, base_d % SDu.vocab),
+                                          0.22, sr["prompt"] + 1)
+        dmp = make_model(SDu, synth.successor_stack(synth.model_weights(SDu, sr["weights"]), succ_d))
+        plant = run_round(dmp, planted_verifier(), (prompt4[:512] % SDu.vocab).astype(np.int32))
+        sfb.sf_model_free(dmp)
+        spec_round = {"verifier_K": K, "prompt": 512,
+                      "successor_planted": dict(drafter="qwen2.5-0.5b-shape, untied head, following the verifier's "
+                                                "successor map on all but 22% of ids",
+                                                verifier="the successor-planted 7B-shape stack", **plant),
+                      "random_init": dict(drafter="qwen2.5-0.5b-shape, random-init bf16", verifier="this model",
+                                          **rand)}
         log(f"round: {spec_round}")
+
+    if planted_model:
+        sfb.sf_model_free(planted_model[0])
 
     # NF4 verify at the Qwen2.5-14B shape (48 layers, hidden 5120, 40/8 heads, FFN 13824,
     # vocab 152064): projections in 4-bit NormalFloat (codes uniform over the levels, per-64

@@ -11,7 +11,7 @@ generated in fixed 2**22-element chunks, each from its own PCG64 stream keyed
 by (seed, tensor name, chunk index), so the bytes do not depend on the number
 of threads used.
 """
-from .shapes import (Shape, TINY, QWEN05B, QWEN7B, QWEN7B_HALF, QWEN14B, QWEN14B_2L, SHAPES, tensor_names,
+from .shapes import (Shape, TINY, QWEN05B, QWEN05B_UNTIED, QWEN7B, QWEN7B_HALF, QWEN14B, QWEN14B_2L, SHAPES, tensor_names,
                      tensor_shape)
 from .gen import (
     bf16_normal,
@@ -27,12 +27,13 @@ from .gen import (
     near_copy,
     history_successors,
     successor_stack,
+    perturb_successors,
     nf4_tensor,
     nf4_model_weights,
 )
 
 __all__ = [
-    "Shape", "TINY", "QWEN05B", "QWEN7B", "QWEN7B_HALF", "QWEN14B", "QWEN14B_2L", "SHAPES", "tensor_names", "tensor_shape",
+    "Shape", "TINY", "QWEN05B", "QWEN05B_UNTIED", "QWEN7B", "QWEN7B_HALF", "QWEN14B", "QWEN14B_2L", "SHAPES", "tensor_names", "tensor_shape",
     "bf16_normal", "model_weights", "prompt_ids", "corrupt_draft", "synthetic_kv", "lookup_history",
-    "batch_contexts", "rejected_suffix", "seeds", "with_head_gain", "near_copy", "history_successors", "successor_stack", "nf4_tensor", "nf4_model_weights",
+    "batch_contexts", "rejected_suffix", "seeds", "with_head_gain", "near_copy", "history_successors", "successor_stack", "perturb_successors", "nf4_tensor", "nf4_model_weights",
 ]

@@ -111,6 +111,16 @@ def history_successors(hist, vocab, seed):
     return succ.astype(np.int32)
 
 
+def perturb_successors(succ, frac, seed):
+    """A copy of succ with a seeded fraction `frac` of the ids given a uniform new successor:
+    the map of a drafter that agrees with the verifier's on about 1 - frac of the ids."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = np.array(succ, dtype=np.int32)
+    hit = rng.random(len(out)) < frac
+    out[hit] = rng.integers(0, len(out), size=int(hit.sum()), dtype=np.int64).astype(np.int32)
+    return out
+
+
 def successor_stack(weights, succ, shift=8, threads=None):
     """A stack (untied head) whose greedy next token is succ[current token], a stand-in for a
     trained model that has learned a history's successor statistics (random-init weights follow

@@ -69,7 +69,10 @@ QWEN14B = Shape("qwen2.5-14b", n_layers=48, hidden=5120, n_q_heads=40, n_kv_head
 # Two layers of the 14B stack with its full embedding and head: every kernel at its real shape.
 QWEN14B_2L = replace(QWEN14B, name="qwen2.5-14b-2l", n_layers=2)
 
-SHAPES = {s.name: s for s in (TINY, QWEN05B, QWEN7B, QWEN7B_HALF, QWEN14B, QWEN14B_2L)}
+# The 0.5B shape with an untied LM head: the drafter of a successor-planted pair (a planted
+# head must differ from the embedding); a step reads the same bytes as the tied shape.
+QWEN05B_UNTIED = replace(QWEN05B, name="qwen2.5-0.5b-untied", tied_head=False)
+SHAPES = {s.name: s for s in (TINY, QWEN05B, QWEN05B_UNTIED, QWEN7B, QWEN7B_HALF, QWEN14B, QWEN14B_2L)}
 
 
 def tensor_names(shape):

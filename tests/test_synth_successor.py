@@ -65,3 +65,17 @@ def test_successor_stack_greedy_choice_is_the_successor():
             z = oracle.prefill(model, c, prompt)
             assert c.next_token == succ[prompt[-1]], (n, prompt[-1])
             assert oracle.top_gap(z[-1:])[0].item() > 1.0
+
+
+def test_perturb_successors_changes_the_stated_fraction():
+    """The drafter's successor map of the device round: every id keeps its successor except a
+    seeded fraction, which get uniform ids; the same seed gives the same map."""
+    succ = synth.history_successors(synth.lookup_history(5000, 20000, 4), 5000, 9)
+    out = synth.perturb_successors(succ, 0.22, 31)
+    assert out.dtype == np.int32 and out.shape == succ.shape
+    assert out.min() >= 0 and out.max() < len(succ)
+    changed = np.mean(out != succ)
+    assert 0.19 < changed < 0.23, changed          # 0.22 less the 1/5000 that redraw the same id
+    assert np.array_equal(out, synth.perturb_successors(succ, 0.22, 31))
+    assert not np.array_equal(out, synth.perturb_successors(succ, 0.22, 32))
+    assert np.array_equal(synth.perturb_successors(succ, 0.0, 31), succ)
