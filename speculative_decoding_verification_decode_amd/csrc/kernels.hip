@@ -15,6 +15,7 @@
 #include "device.h"
 
 #include <algorithm>
+#include <cstdlib>
 
 namespace sf {
 
@@ -836,6 +837,310 @@ __global__ __launch_bounds__(256, 2) void k_gemm_b(const GemmArgs g, int row0, i
   gemm_b_body<EPI, 3, 2>(g, row0, G);
 }
 
+// ----------------------------------------------------------------------------------------------
+// LDS-staged batched GEMM for passes of more than 64 rows: the residual projections whose k
+// range is split (O and down; 4 blocks x 4 row tiles per workgroup) and the unsplit gate/up and
+// LM head (8 blocks x 2 row tiles).  A workgroup of eight waves owns NBT 32-row weight blocks x RT
+// 32-row row tiles of one k split, and wave w computes the two blocks of pair w % (NBT/2)
+// against row tile w / (NBT/2) (its hi and lo m tiles: four MFMAs per k tile).  The NBT weight
+// fragments and 2*RT activation fragments of every k tile go from memory straight into an LDS
+// ring (buffer loads with an LDS destination: four stages of two k tiles, three loads per wave
+// per stage), so a weight fragment feeds 2*RT MFMAs and an activation fragment NBT, against one
+// or two in the row-group kernel; the next k tile's fragments are read from LDS while the
+// current tile's MFMAs run, and one barrier per stage both publishes a stage and frees the
+// slot that is refilled next.
+// Per output, the arithmetic is k_gemm's: split spi's k range is walked in the compact
+// kernel's four wave chunks in turn, each chunk an MFMA chain from zero over its k tiles in
+// order, and the chunk results are added in chunk order into a running sum (the first one
+// copied), which is the compact kernel's chain-then-wave-order sum; hi and lo sums are then
+// added, and the splits' partials are added in split order by the last arriver.  So a row's
+// result is bitwise the one of a single-sequence pass.
+constexpr int kTiledRing = 6144;   // u32x4 of the LDS ring: 96 KB
+template <int EPI, int NBT, int RT>
+__global__ __launch_bounds__(512, 1) void k_gemm_t(const GemmArgs g, int row0, int G) {
+  static_assert(EPI == kEpiResid || EPI == kEpiSwiglu || EPI == kEpiArgmax, "no QKV epilogue here");
+  constexpr bool kScaled = (EPI == kEpiSwiglu || EPI == kEpiArgmax);
+  constexpr int NW = 8, kThreads = NW * 64, KT = 2, S = 4;
+  constexpr int kPairs = NBT / 2, kRealRows = 32 * RT;
+  static_assert(kPairs * RT == NW, "one wave per (block pair, row tile)");
+  constexpr int kFr = NBT + 2 * RT;        // 1 KB fragments per k tile: weight blocks, then (row tile, hi/lo)
+  constexpr int kLoads = KT * kFr / NW;    // LDS-destination loads per wave per stage
+  static_assert(KT * kFr == kLoads * NW, "a stage's loads divide evenly over the waves");
+  constexpr int kStage = KT * kFr * 64;    // u32x4 per stage
+  constexpr int kImgPitch = 33;            // output image row pitch (floats)
+  // After the k loop the ring holds the output image, the residual epilogue's squares and the
+  // split arrival flag: the kernel has no other LDS array (a second one makes the compiler
+  // wait for every LDS-destination load before each LDS read, serialising the ring).
+  constexpr int kImgFloats = NBT * kRealRows * kImgPitch, kSqFloats = 32 * kRealRows;
+  static_assert(kImgFloats + kSqFloats + kRealRows + 1 <= kTiledRing * 4, "image, squares, scales and flag fit");
+  // Loads of stages s+2 .. s+3 may still be in flight when stage s+1 must have landed.
+  constexpr int kAhead = kLoads * (S - 2);
+  static_assert(kAhead < 16, "vmcnt immediate");
+  static_assert(S * kStage <= kTiledRing, "ring size");
+  // (sized by a constant, not by the template arguments: the LDS-destination load builtin
+  // must not see a dependent type)
+  __shared__ u32x4 ring[kTiledRing];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  // Workgroup (group split gs, row group rg) has linear index ((gs/8)*G + rg)*8 + gs%8, as in
+  // k_gemm_b: the row groups of one group of blocks share its weights through one XCD's L2.
+  const int q = blockIdx.x >> 3;
+  const int rg = q % G;
+  const int gs = (q / G) * 8 + (blockIdx.x & 7);
+  if (gs >= (g.nb / NBT) * g.sp) return;   // padding of the last group of 8
+  const int nt = gs / g.sp, spi = gs - nt * g.sp;
+  const int nb0 = nt * NBT, r0 = row0 + rg * kRealRows;
+  const int pr = wave % kPairs, rt = wave / kPairs;
+  const bool wave_rows = r0 + rt * 32 < g.rows;
+  const int U = 4 * g.sp;
+  auto bound = [&](int u) { return __builtin_amdgcn_readfirstlane((int)(((long)g.kb * u) / U)); };
+  const int kt0 = bound(4 * spi), kt1 = bound(4 * spi + 4);
+  const int ext = 2 * g.rows, tsp = act_tile_pieces(ext);
+
+  // This wave's loads: entry e = wave*kLoads + p of a stage is k tile e / kFr, fragment
+  // f = e % kFr (weight block nb0 + f, or activation row tile (f-NBT)/2, part (f-NBT)%2).  The
+  // buffer range check returns zeros for weight tiles at or past kt1 and for rows past the
+  // batch (their base offset lies past the activation buffer).
+  __amdgpu_buffer_rsrc_t src[kLoads];
+  int voff[kLoads], step[kLoads], ldst[kLoads], tof[kLoads];
+#pragma unroll
+  for (int p = 0; p < kLoads; ++p) {
+    const int e = wave * kLoads + p, t = e / kFr, f = e - t * kFr;
+    tof[p] = t;
+    ldst[p] = (t * kFr + f) * 64;
+    if (f < NBT) {
+      src[p] = __builtin_amdgcn_make_buffer_rsrc((void*)(g.w + (size_t)(nb0 + f) * g.kb * 64), (short)0, kt1 * 1024,
+                                                 kBufferWord3);
+      voff[p] = lane * 16;
+      step[p] = 1024;
+    } else {
+      const int rr = (f - NBT) >> 1, h = (f - NBT) & 1, row = r0 + rr * 32 + (lane & 31);
+      src[p] = __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, (int)act_bytes(ext, g.k), kBufferWord3);
+      voff[p] = row < g.rows ? ((lane >> 5) * ext + h * g.rows + row) * 16 : 0x40000000;
+      step[p] = tsp * 16;
+    }
+  }
+  auto issue = [&](int st_, int slot) {
+#pragma unroll
+    for (int p = 0; p < kLoads; ++p) {
+      const int kt = kt0 + st_ * KT + tof[p];
+      // (plain locals: the builtin rejects operands whose type depends on the template arguments)
+      const __amdgpu_buffer_rsrc_t r = src[p];
+      const int off = voff[p] + kt * step[p], dst = slot * kStage + ldst[p];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)&ring[dst], 16, off, 0, 0, 0);
+    }
+  };
+  // Own loads of the next stage landed, every wave's too, and every wave is done with the
+  // slot refilled next (its LDS reads completed).
+  auto wait_bar = [&]() {
+    __builtin_amdgcn_s_waitcnt((kAhead & 15) | (7 << 4) | (0 << 8));
+    __builtin_amdgcn_s_barrier();
+  };
+  auto rd = [&](int slot, int t, u32x4 (&f)[4]) {
+    const u32x4* base = ring + slot * kStage + t * kFr * 64 + lane;
+    f[0] = base[(2 * pr) * 64];
+    f[1] = base[(2 * pr + 1) * 64];
+    f[2] = base[(NBT + 2 * rt) * 64];
+    f[3] = base[(NBT + 2 * rt + 1) * 64];
+  };
+
+  f32x16 acc[2][2], sum[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) acc[j][h] = sum[j][h] = (f32x16){};
+  int chunk = 0;
+  int bnd = bound(4 * spi + 1);
+  const int nst = (kt1 - kt0 + KT - 1) / KT;
+
+#pragma unroll
+  for (int st_ = 0; st_ < S - 1; ++st_) issue(st_, st_);
+  // Row scale of the folded RMSNorm (gate/up, LM head), as k_gemm computes it: wave w owns rows
+  // w, w+NW, ...; lane l sums parts l, l+64, l+128 in that order, then the wave reduces across
+  // lanes.  Lane j keeps the scale of row w + NW*j until the ring is free after the k loop.  The
+  // loads go out after the ring's first stages, so both latencies overlap.
+  float my_scale = 0.f;
+  if constexpr (kScaled) {
+    constexpr int kRowsPerWave = kRealRows / NW;
+    static_assert(kRowsPerWave <= 64, "one row per lane");
+    const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)g.ssq_in, (short)0, g.rows * g.nparts_in * 4, kBufferWord3);
+    float ssq_v[kRowsPerWave][kSsqPerLane];
+#pragma unroll
+    for (int j = 0; j < kRowsPerWave; ++j) {
+      const int mr = r0 + wave + NW * j;
+#pragma unroll
+      for (int i = 0; i < kSsqPerLane; ++i) {
+        const int pp = lane + 64 * i;
+        const int off = (mr < g.rows && pp < g.nparts_in) ? (mr * g.nparts_in + pp) * 4 : 0x7FFFFFF0;
+        ssq_v[j][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sres, off, 0, 0));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kRowsPerWave; ++j) {
+      const int mr = r0 + wave + NW * j;
+      float t2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < kSsqPerLane; ++i) t2 += ssq_v[j][i];
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) t2 += __shfl_xor(t2, o);
+      const float sc = (mr < g.rows) ? 1.0f / sqrtf(t2 / (float)g.k + g.eps) : 0.f;
+      if (lane == j) my_scale = sc;
+    }
+  }
+  wait_bar();
+  u32x4 wf[2][4];
+  rd(0, 0, wf[0]);
+  for (int s0 = 0; s0 < nst; s0 += S) {
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      const int st_ = s0 + i;
+      if (st_ < nst) {
+        // Slot (i-1) % S was read by every wave before the last barrier: refill it.
+        issue(st_ + S - 1, (i + S - 1) % S);
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+          const int kt = kt0 + st_ * KT + t;
+          if (t + 1 < KT) {
+            rd(i, t + 1, wf[(t + 1) & 1]);
+          } else {
+            wait_bar();
+            rd((i + 1) % S, 0, wf[(t + 1) & 1]);
+          }
+          if (__builtin_expect(kt < kt1 && wave_rows, 1)) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              acc[j][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(wf[t & 1][j]), as_bf16x8(wf[t & 1][2]),
+                                                                  acc[j][0], 0, 0, 0);
+              acc[j][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(wf[t & 1][j]), as_bf16x8(wf[t & 1][3]),
+                                                                  acc[j][1], 0, 0, 0);
+            }
+          }
+          // End of a chunk (rare; kept out of the loop's straight-line path).
+          if (__builtin_expect(kt + 1 == bnd, 0)) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                sum[j][h] = chunk == 0 ? acc[j][h] : sum[j][h] + acc[j][h];
+                acc[j][h] = (f32x16){};
+              }
+            ++chunk;
+            bnd = bound(4 * spi + chunk + 1);
+          }
+        }
+      }
+    }
+  }
+  // Every load has landed (the stages past the end included) and every wave is done reading
+  // the ring before it becomes the output image.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  float* const img = reinterpret_cast<float*>(ring);
+  float* const sq = img + kImgFloats;
+  float* const rscale = sq + kSqFloats;
+  int* const last_arrival = reinterpret_cast<int*>(rscale + kRealRows);
+  if constexpr (kScaled)
+    if (lane < kRealRows / NW) rscale[wave + NW * lane] = my_scale;
+  if (wave_rows) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int nl = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), m = rt * 32 + (lane & 31);
+        img[((2 * pr + j) * kRealRows + m) * kImgPitch + nl] = sum[j][0][r] + sum[j][1][r];
+      }
+  }
+  __syncthreads();
+  if constexpr (EPI != kEpiResid) {
+    // Unsplit (gate/up, LM head): the epilogues read the image.
+    for (int nbl = 0; nbl < NBT; ++nbl) {
+      auto val = [&](int nl, int m) { return img[(nbl * kRealRows + m) * kImgPitch + nl]; };
+      gemm_epilogue<EPI, kRealRows, kThreads>(g, nb0 + nbl, r0, rscale, val);
+      __syncthreads();
+    }
+    return;
+  }
+  // k split: every workgroup stores its partial tile; the last of the sp workgroups of this
+  // group of blocks and row group adds the partials in split order and runs the residual
+  // epilogue.
+  for (int e = tid; e < NBT * 32 * kRealRows; e += kThreads) {
+    const int nl = e & 31, m = (e >> 5) % kRealRows, nbl = e / (32 * kRealRows);
+    if (r0 + m < g.rows)
+      st<true>(g.part + (((size_t)(nb0 + nbl) * g.sp + spi) * g.rows + r0 + m) * 32 + nl,
+               img[(nbl * kRealRows + m) * kImgPitch + nl]);
+  }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) *last_arrival = split_arrive(g.counters + nt * G + rg, g.sp);
+  __syncthreads();
+  if (!*last_arrival) return;
+  asm volatile("" ::: "memory");
+  // The residual epilogue of gemm_epilogue for all NBT blocks, with every load of a thread's
+  // outputs (the splits' partials, the residual, the next norm's gain) issued before any of
+  // its stores: the per-output form waits for one load round trip per output in turn.
+  // Thread t owns outputs e = t + kThreads*i: column nl = e%32, row m = (e/32)%kRealRows of
+  // block e/(32*kRealRows).
+  constexpr int kPer = NBT * 32 * kRealRows / kThreads;
+  static_assert(kPer * kThreads == NBT * 32 * kRealRows && (32 * kRealRows) % kThreads == 0, "output split");
+  float tot[kPer], xv[kPer], gn[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) tot[i] = 0.f;
+  for (int q2 = 0; q2 < g.sp; ++q2) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = tid + kThreads * i, nl = e & 31, m = (e >> 5) % kRealRows, nbl = e / (32 * kRealRows);
+      const int mr = min(r0 + m, g.rows - 1);
+      tot[i] += ld<true>(g.part + (((size_t)(nb0 + nbl) * g.sp + q2) * g.rows + mr) * 32 + nl);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = tid + kThreads * i, nl = e & 31, m = (e >> 5) % kRealRows, nbl = e / (32 * kRealRows);
+    const int mr = min(r0 + m, g.rows - 1), n = (nb0 + nbl) * 32 + nl;
+    xv[i] = g.x[(size_t)mr * g.n_out + n];
+    gn[i] = g.gain_next[n];
+  }
+  constexpr int kPerBlock = 32 * kRealRows / kThreads;
+#pragma unroll
+  for (int nbl = 0; nbl < NBT; ++nbl) {
+#pragma unroll
+    for (int i = nbl * kPerBlock; i < (nbl + 1) * kPerBlock; ++i) {
+      const int e = tid + kThreads * i, nl = e & 31, m = (e >> 5) % kRealRows, mr = r0 + m;
+      float v = 0.f;
+      if (mr < g.rows) {
+        const int n = (nb0 + nbl) * 32 + nl;
+        const size_t o = (size_t)mr * g.n_out + n;
+        v = xv[i] + tot[i];
+        g.x[o] = v;
+        store_split(g.a_next, g.rows, mr, n, v * gn[i]);
+        if (g.hidden) g.hidden[o] = f2bf(v);
+      }
+      sq[e - nbl * 32 * kRealRows] = v * v;
+    }
+    __syncthreads();
+    if (tid < kRealRows && r0 + tid < g.rows) {
+      float t2 = 0.f;
+#pragma unroll
+      for (int nl = 0; nl < 32; ++nl) t2 += sq[tid * 32 + nl];
+      g.ssq_out[(size_t)(r0 + tid) * g.nb + nb0 + nbl] = t2;
+    }
+    __syncthreads();
+  }
+}
+
+// The LDS-staged kernel is the default for the split residual projections of passes of more
+// than 64 rows; SF_TILED=0 selects the row-group kernel instead (the same results).
+static bool tiled_enabled() {
+  static const bool on = [] {
+    const char* v = getenv("SF_TILED");
+    return !(v && atoi(v) == 0);
+  }();
+  return on;
+}
+
 template <int EPI, int NW>
 static hipError_t gemm_mt(const GemmArgs& g, hipStream_t s) {
   const int mt = (2 * g.rows + 31) / 32;
@@ -846,7 +1151,20 @@ static hipError_t gemm_mt(const GemmArgs& g, hipStream_t s) {
     const int G = (g.rows + 63) / 64;
     // Row groups before the one holding row_lo are skipped (their outputs are not needed).
     const int rg_lo = std::min(std::max(g.row_lo, 0), g.rows - 1) / 64;
-    if (g.nb % 2 == 0) {
+    if (EPI == kEpiResid && g.sp > 1 && g.nb % 4 == 0 && g.kb >= 8 * g.sp && tiled_enabled()) {
+      if constexpr (EPI == kEpiResid) {
+        const int r0t = (rg_lo * 64 / 128) * 128, Gt = (g.rows - r0t + 127) / 128;
+        const int ngs = (g.nb / 4) * g.sp;
+        k_gemm_t<EPI, 4, 4><<<dim3(((ngs + 7) / 8) * 8 * Gt), dim3(512), 0, s>>>(g, r0t, Gt);
+      }
+    } else if ((EPI == kEpiSwiglu || EPI == kEpiArgmax) && g.sp == 1 && g.nb % 8 == 0 && g.kb >= 8 &&
+               tiled_enabled()) {
+      if constexpr (EPI == kEpiSwiglu || EPI == kEpiArgmax) {
+        const int r0t = rg_lo * 64, Gt = G - rg_lo;
+        const int ngs = g.nb / 8;
+        k_gemm_t<EPI, 8, 2><<<dim3(((ngs + 7) / 8) * 8 * Gt), dim3(512), 0, s>>>(g, r0t, Gt);
+      }
+    } else if (g.nb % 2 == 0) {
       const int ngs = (g.nb / 2) * g.sp;
       k_gemm_b<EPI><<<dim3(((ngs + 7) / 8) * 8 * (G - rg_lo)), dim3(256), 0, s>>>(g, rg_lo * 64, G - rg_lo);
     } else {
