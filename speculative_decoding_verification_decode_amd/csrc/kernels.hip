@@ -50,57 +50,96 @@ __device__ __forceinline__ float* resid_sq() {
 // Called by every thread of the workgroup.
 template <int EPI, int kRealRows, int kThreads, typename Val>
 __device__ void gemm_epilogue(const GemmArgs& g, int nb, int r0, const float* rscale, Val val) {
+  // Every product is rounded before it is added (no fused multiply-add): the epilogues are
+  // instantiated in several kernels, and a sequence's result must not depend on which one ran
+  // it, whatever the compiler would fuse in each.
+#pragma clang fp contract(off)
   const int tid = threadIdx.x;
   if constexpr (EPI == kEpiQkv) {
     // Packed rows of n block nb: 0..15 = head dims i0..i0+15, 16..31 = their RoPE partners.
-    for (int it = tid; it < 16 * kRealRows; it += kThreads) {
-      const int p = it & 15, m = it >> 4, mr = r0 + m;
-      if (mr >= g.rows) continue;
-      const int half = g.dh >> 1, bph = g.dh >> 5;
-      const int qb = g.nq * bph, kvb = g.nkv * bph;
-      int sec, head, blk;
-      if (nb < qb) { sec = 0; head = nb / bph; blk = nb - head * bph; }
-      else if (nb < qb + kvb) { sec = 1; head = (nb - qb) / bph; blk = nb - qb - head * bph; }
-      else { sec = 2; head = (nb - qb - kvb) / bph; blk = nb - qb - kvb - head * bph; }
+    const int half = g.dh >> 1, bph = g.dh >> 5;
+    const int qb = g.nq * bph, kvb = g.nkv * bph;
+    int sec, head, blk;
+    if (nb < qb) { sec = 0; head = nb / bph; blk = nb - head * bph; }
+    else if (nb < qb + kvb) { sec = 1; head = (nb - qb) / bph; blk = nb - qb - head * bph; }
+    else { sec = 2; head = (nb - qb - kvb) / bph; blk = nb - qb - kvb - head * bph; }
+    // Loads first (bias, length, RoPE table), stores after, as in the residual epilogue.
+    constexpr int kIt = (16 * kRealRows + kThreads - 1) / kThreads;
+    float y1v[kIt], y2v[kIt];
+    float2 csv[kIt];
+    int posv[kIt];
+#pragma unroll
+    for (int j = 0; j < kIt; ++j) {
+      const int it = tid + j * kThreads, p = it & 15, m = it >> 4, mr = r0 + m;
+      posv[j] = -1;
+      y1v[j] = y2v[j] = 0.f;
+      csv[j] = make_float2(0.f, 0.f);
+      if (it < 16 * kRealRows && mr < g.rows) {
+        const int i = blk * 16 + p;
+        const float s = rscale[m];
+        y1v[j] = val(p, m) * s + g.bias[nb * 32 + p];
+        y2v[j] = val(p + 16, m) * s + g.bias[nb * 32 + p + 16];
+        const int b = mr / g.T, slot = mr - b * g.T;
+        const int pos = g.len[b] + slot;
+        check(pos < g.cap, kChkPos);
+        posv[j] = pos;
+        if (sec != 2 && pos < g.cap) csv[j] = g.rope[(size_t)pos * half + i];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kIt; ++j) {
+      const int it = tid + j * kThreads, p = it & 15, m = it >> 4, mr = r0 + m;
+      const int pos = posv[j];
+      if (pos < 0 || pos >= g.cap) continue;
       const int i = blk * 16 + p;
-      const float s = rscale[m];
-      const float y1 = val(p, m) * s + g.bias[nb * 32 + p];
-      const float y2 = val(p + 16, m) * s + g.bias[nb * 32 + p + 16];
-      const int b = mr / g.T, slot = mr - b * g.T;
-      const int pos = g.len[b] + slot;
-      check(pos < g.cap, kChkPos);
-      if (pos < g.cap) {
-        if (sec == 2) {
-          uint16_t* dst = g.vc + (size_t)b * g.seq_stride + ((size_t)head * g.cap + pos) * g.dh;
-          dst[i] = f2bf(y1);
-          dst[i + half] = f2bf(y2);
+      const int b = mr / g.T;
+      const float y1 = y1v[j], y2 = y2v[j];
+      if (sec == 2) {
+        uint16_t* dst = g.vc + (size_t)b * g.seq_stride + ((size_t)head * g.cap + pos) * g.dh;
+        dst[i] = f2bf(y1);
+        dst[i + half] = f2bf(y2);
+      } else {
+        const float2 cs = csv[j];
+        const float o1 = y1 * cs.x - y2 * cs.y;
+        const float o2 = y2 * cs.x + y1 * cs.y;
+        if (sec == 0) {
+          float* dst = g.q + ((size_t)mr * g.nq + head) * g.dh;
+          dst[i] = o1;
+          dst[i + half] = o2;
         } else {
-          const float2 cs = g.rope[(size_t)pos * half + i];
-          const float o1 = y1 * cs.x - y2 * cs.y;
-          const float o2 = y2 * cs.x + y1 * cs.y;
-          if (sec == 0) {
-            float* dst = g.q + ((size_t)mr * g.nq + head) * g.dh;
-            dst[i] = o1;
-            dst[i + half] = o2;
-          } else {
-            uint16_t* dst = g.kc + (size_t)b * g.seq_stride + ((size_t)head * g.cap + pos) * g.dh;
-            dst[i] = f2bf(o1);
-            dst[i + half] = f2bf(o2);
-          }
+          uint16_t* dst = g.kc + (size_t)b * g.seq_stride + ((size_t)head * g.cap + pos) * g.dh;
+          dst[i] = f2bf(o1);
+          dst[i + half] = f2bf(o2);
         }
       }
     }
   } else if constexpr (EPI == kEpiResid) {
     float* const sq = resid_sq<kRealRows>();
-    for (int e = tid; e < 32 * kRealRows; e += kThreads) {
-      const int nl = e & 31, m = e >> 5, mr = r0 + m;
+    // Every load of a thread's outputs (residual, result or split partials, gain) is issued
+    // before its first store; stored one after another, each output waited one round trip.
+    constexpr int kIt = (32 * kRealRows + kThreads - 1) / kThreads;
+    float vin[kIt], gin[kIt];
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) {
+      const int e = tid + i * kThreads, nl = e & 31, m = e >> 5, mr = r0 + m;
+      vin[i] = gin[i] = 0.f;
+      if (e < 32 * kRealRows && mr < g.rows) {
+        const int n = nb * 32 + nl;
+        vin[i] = g.x[(size_t)mr * g.n_out + n] + val(nl, m);
+        gin[i] = g.gain_next[n];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) {
+      const int e = tid + i * kThreads, nl = e & 31, m = e >> 5, mr = r0 + m;
+      if (e >= 32 * kRealRows) break;
       float v = 0.f;
       if (mr < g.rows) {
         const int n = nb * 32 + nl;
         const size_t o = (size_t)mr * g.n_out + n;
-        v = g.x[o] + val(nl, m);
+        v = vin[i];
         g.x[o] = v;
-        store_split(g.a_next, g.rows, mr, n, v * g.gain_next[n]);
+        store_split(g.a_next, g.rows, mr, n, v * gin[i]);
         if (g.hidden) g.hidden[o] = f2bf(v);
       }
       sq[e] = v * v;
@@ -1083,6 +1122,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_t(const GemmArgs g, int row0, i
   // its stores: the per-output form waits for one load round trip per output in turn.
   // Thread t owns outputs e = t + kThreads*i: column nl = e%32, row m = (e/32)%kRealRows of
   // block e/(32*kRealRows).
+  {
+#pragma clang fp contract(off)
   constexpr int kPer = NBT * 32 * kRealRows / kThreads;
   static_assert(kPer * kThreads == NBT * 32 * kRealRows && (32 * kRealRows) % kThreads == 0, "output split");
   float tot[kPer], xv[kPer], gn[kPer];
@@ -1128,6 +1169,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_t(const GemmArgs g, int row0, i
       g.ssq_out[(size_t)(r0 + tid) * g.nb + nb0 + nbl] = t2;
     }
     __syncthreads();
+  }
   }
 }
 
