@@ -128,3 +128,51 @@ def test_largest_batch_64_sequences_512_rows():
     finally:
         eng.close()
         one.close()
+
+
+@pytest.mark.parametrize("splits", [(2, 4), (4, 8)], ids=["O2-down4", "O4-down8"])
+def test_batched_k_splits_bitwise_single_runs(monkeypatch, splits):
+    """More k splits than the tiny shape's defaults (SF_SP_O / SF_SP_D, read when a cache is
+    allocated), so the batched residual projections run the LDS-staged kernel with 8 to 32
+    k chunks and a last arriver over 2 to 8 splits: 13 sequences x 5 positions (65 rows: one
+    64-row group and a one-row tail) bitwise against each sequence verified alone, and one
+    sequence against the oracle."""
+    sfb = need_gpu()
+    sp_o, sp_d = splits
+    monkeypatch.setenv("SF_SP_O", str(sp_o))
+    monkeypatch.setenv("SF_SP_D", str(sp_d))
+    Bs, Ks = 13, 4
+    rng = np.random.default_rng(7300 + sp_d)
+    ctx = rng.integers(20, CAP - Ks - 1, size=Bs)
+    nxt = rng.integers(0, S.vocab, size=Bs)
+    drafts = rng.integers(0, S.vocab, size=(Bs, Ks)).astype(np.int32)
+    ks = rng.integers(0, Ks + 1, size=Bs).astype(np.int32)
+    kv = synth.synthetic_kv(S, CAP, 7301)
+    w = synth.model_weights(S, synth.seeds(5)["weights"])
+    say(f"[batched splits] O {sp_o}, down {sp_d}: {Bs} x {Ks + 1} rows")
+    eng = sfb.Engine(S, w, n_seqs=Bs, capacity=CAP, k_max=Ks)
+    one = sfb.Engine(S, w, n_seqs=1, capacity=CAP, k_max=Ks)
+    try:
+        _fill(sfb, eng, kv, ctx, nxt)
+        logits = torch.empty((Bs * (Ks + 1), S.vocab), dtype=torch.float32, device="cuda")
+        acc, tgt = sfb.sf_verify(eng.cache, drafts, ks, sfb.SF_DEBUG_LOGITS | sfb.SF_NO_COMMIT, dev_out=logits)
+        torch.cuda.synchronize()
+        one_logits = torch.empty((Ks + 1, S.vocab), dtype=torch.float32, device="cuda")
+        for b in range(Bs):
+            _fill(sfb, one, kv, [ctx[b]], [nxt[b]])
+            a1, t1 = sfb.sf_verify(one.cache, drafts[b:b + 1], ks[b:b + 1], sfb.SF_DEBUG_LOGITS | sfb.SF_NO_COMMIT,
+                                   dev_out=one_logits)
+            torch.cuda.synchronize()
+            assert a1[0] == acc[b] and (t1[0] == tgt[b]).all()
+            assert torch.equal(one_logits.cpu(), logits.view(Bs, Ks + 1, S.vocab)[b].cpu()), f"sequence {b}"
+        b = Bs - 1
+        c = oracle.KVCache(S, int(ctx[b]) + Ks + 1)
+        c.load(kv[0], kv[1], int(ctx[b]), next_token=int(nxt[b]))
+        r = oracle.verify(oracle.Model(S, w), c, drafts[b], int(ks[b]), commit=True)
+        worst = (logits.double().cpu().view(Bs, Ks + 1, S.vocab)[b] - r["logits"]).abs().max().item()
+        check_targets(tgt[b], r, Ks)
+        say(f"[batched splits] last sequence max |dlogit| vs oracle: {worst:.3g}")
+        assert worst <= LOGIT_TOL
+    finally:
+        eng.close()
+        one.close()
