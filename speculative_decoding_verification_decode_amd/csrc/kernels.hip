@@ -1303,7 +1303,7 @@ constexpr int kWarmMinLen = 4096;
 // that order of the index); then a.warm.nwarm warm-up workgroups for the O projection, starting
 // at an index that is a multiple of 8 (the ones before it, fewer than 8, exit).
 template <int DH, bool GATED = false>
-__global__ __launch_bounds__(256) void k_attn(const AttnArgs a, int nx, int natt) {
+__global__ __launch_bounds__(256, 2) void k_attn(const AttnArgs a, int nx, int natt) {
   if constexpr (GATED)
     if (gated_off(a.gate)) return;
   const int bid = blockIdx.x;
