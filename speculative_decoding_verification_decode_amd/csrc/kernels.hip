@@ -884,10 +884,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_b(const GemmArgs g, int row0, i
 // against row tile w / (NBT/2) (its hi and lo m tiles: four MFMAs per k tile).  The NBT weight
 // fragments and 2*RT activation fragments of every k tile go from memory straight into an LDS
 // ring (buffer loads with an LDS destination: four stages of two k tiles, three loads per wave
-// per stage), so a weight fragment feeds 2*RT MFMAs and an activation fragment NBT, against one
-// or two in the row-group kernel; the next k tile's fragments are read from LDS while the
-// current tile's MFMAs run, and one barrier per stage both publishes a stage and frees the
-// slot that is refilled next.
+// per stage), so one fetch of a weight fragment feeds 2*RT MFMAs and one of an activation
+// fragment NBT, against four and two in the row-group kernel; the next k tile's fragments are
+// read from LDS while the current tile's MFMAs run, and one barrier per stage both publishes a
+// stage and frees the slot that is refilled next.
 // Per output, the arithmetic is k_gemm's: split spi's k range is walked in the compact
 // kernel's four wave chunks in turn, each chunk an MFMA chain from zero over its k tiles in
 // order, and the chunk results are added in chunk order into a running sum (the first one
@@ -1173,8 +1173,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_t(const GemmArgs g, int row0, i
   }
 }
 
-// The LDS-staged kernel is the default for the split residual projections of passes of more
-// than 64 rows; SF_TILED=0 selects the row-group kernel instead (the same results).
+// The LDS-staged kernel is the default for passes of more than 64 rows wherever it applies (the
+// split O and down, the gate/up, the LM head); SF_TILED=0 selects the row-group kernel instead
+// (the same results).
 static bool tiled_enabled() {
   static const bool on = [] {
     const char* v = getenv("SF_TILED");
