@@ -24,7 +24,11 @@
  *     sf_cache_alloc; every later call reuses fixed addresses, so captured graph
  *     replays stay valid ([ShardFlow] "Why It Kept Breaking (and How I Fixed
  *     It)": captured addresses must not change; fixes 1 and 2).
- *   - All device work runs on the stream given to sf_model_create.
+ *   - All device work runs on the stream given to sf_model_create.  Caller device
+ *     buffers are read and written in that stream's order only: work the caller issued
+ *     on other streams that writes them (a fill, a copy) must be complete, or ordered
+ *     before that stream, when the call is made (sf_kv_write and sf_kv_read excepted:
+ *     they wait for the whole device first).
  *   - bf16 = 16-bit brain float stored as uint16 bit patterns.
  */
 #ifndef SF_H
@@ -287,7 +291,9 @@ int32_t sf_ngram_propose(const int32_t* hist, int32_t n_hist, int32_t min_n, int
 /* sf_kv_write / sf_kv_read: copy positions [0, n_pos) of sequence `seq` between
  * the KV pool and caller device buffers k, v laid out bf16
  * [n_layers][n_kv_heads][src_positions][head_dim] (src_positions >= n_pos).
- * sf_kv_write also sets length = n_pos (pending token unchanged).
+ * sf_kv_write also sets length = n_pos (pending token unchanged).  Both first wait for
+ * all work on the device (the buffers may have been written or filled on any stream),
+ * copy on the model stream, and return when the copy is done.
  * Errors: SF_E_ARG, SF_E_CAPACITY (n_pos > capacity). */
 sf_status sf_kv_write(sf_cache* cache, int32_t seq, const void* dev_k, const void* dev_v,
                       int32_t n_pos, int32_t src_positions);

@@ -1139,6 +1139,9 @@ extern "C" sf_status sf_kv_write(sf_cache* c, int32_t seq, const void* dev_k, co
   if (seq < 0 || seq >= c->B) return fail(SF_E_ARG, "seq out of range");
   if (n_pos < 0 || src_positions < n_pos) return fail(SF_E_ARG, "bad n_pos / src_positions");
   if (n_pos > c->cap) return fail(SF_E_CAPACITY, "n_pos exceeds capacity");
+  // The caller's buffers may have been written on any stream (a torch fill or copy on its own
+  // stream does not order before the model stream): wait for the whole device first.
+  HIPCHK(hipDeviceSynchronize());
   if (c->dirty) {
     if (sf_status st = refresh(c)) return st;
   }
@@ -1161,6 +1164,9 @@ extern "C" sf_status sf_kv_read(sf_cache* c, int32_t seq, void* dev_k, void* dev
   if (!c || !dev_k || !dev_v) return fail(SF_E_ARG, "NULL argument");
   if (seq < 0 || seq >= c->B) return fail(SF_E_ARG, "seq out of range");
   if (n_pos < 0 || dst_positions < n_pos || n_pos > c->cap) return fail(SF_E_ARG, "bad n_pos / dst_positions");
+  // As in sf_kv_write: a fill of the destination still pending on another stream must not
+  // land after the copy.
+  HIPCHK(hipDeviceSynchronize());
   sf_model* m = c->m;
   hipStream_t s = m->stream;
   const size_t off = (size_t)seq * c->seq_stride;

@@ -40,6 +40,7 @@ def _pair_run(sfb, model, n_seqs, k_max, cap, prompts, drafts, ks, flags):
         d = torch.from_numpy(np.ascontiguousarray(drafts, dtype=np.int32)).cuda()
         kk = torch.from_numpy(np.asarray(ks, dtype=np.int32)).cuda()
         res = torch.full((n_seqs + n_seqs * (k_max + 1),), -7, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()   # the fill runs on torch's stream, the passes on the model stream
         sfb.sf_verify_device(a, d, kk, flags)
         sfb.sf_verify_device_static(b, d, kk, flags, res)
         sfb.sf_sync(a)
