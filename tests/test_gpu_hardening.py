@@ -13,6 +13,8 @@ path, through the C ABI, on the two-layer decoder.
 - A device-resident round over three sequences, one of whose rounds is mixed (some sequences
   accept every draft, others do not), against the oracle sequence by sequence.
 - Device drafts outside the vocabulary: clamped into the pass, never accepted.
+- K/V copies against work still queued on torch's own stream: sf_kv_read's destination fill
+  and sf_kv_write's source copy, each behind a long torch product, are ordered before the copy.
 """
 import numpy as np
 import pytest
@@ -244,6 +246,49 @@ def test_device_drafts_outside_the_vocabulary_are_clamped_and_never_accepted():
                 M += 1
             assert int(acc_d[b]) == M, (b, acc_d, M)
         assert int(acc_d[1]) == 0 and int(acc_d[0]) <= 2
+    finally:
+        eng.close()
+
+
+def test_kv_copies_wait_for_work_queued_on_other_streams():
+    sfb = need_gpu()
+    w = synth.model_weights(S, synth.seeds(2)["weights"])
+    eng = sfb.Engine(S, w, n_seqs=1, capacity=128, k_max=K)
+    n = 60
+    shape = (S.n_layers, S.n_kv_heads, 128, S.head_dim)
+    try:
+        sfb.sf_prefill(eng.cache, 0, synth.prompt_ids(S.vocab, n, 77))
+        rk = torch.zeros(shape, dtype=torch.int16, device="cuda")
+        rv = torch.zeros_like(rk)
+        torch.cuda.synchronize()
+        sfb.sf_kv_read(eng.cache, 0, rk, rv, n, 128)
+        assert (rk[:, :, :n] != 0).any() and (rv[:, :, :n] != 0).any()
+        busy = torch.randn(4096, 4096, device="cuda")
+        torch.cuda.synchronize()
+        say("[kv order] read into buffers filled behind a long product on torch's stream")
+        for _ in range(3):
+            kg = torch.empty(shape, dtype=torch.int16, device="cuda")
+            vg = torch.empty_like(kg)
+            torch.mm(busy, busy)
+            kg.fill_(-1)
+            vg.fill_(-1)
+            sfb.sf_kv_read(eng.cache, 0, kg, vg, n, 128)
+            torch.cuda.synchronize()
+            assert torch.equal(kg[:, :, :n], rk[:, :, :n]) and torch.equal(vg[:, :, :n], rv[:, :, :n])
+        say("[kv order] write from buffers copied behind a long product on torch's stream")
+        for _ in range(3):
+            sk = torch.zeros(shape, dtype=torch.int16, device="cuda")
+            sv = torch.zeros_like(sk)
+            torch.cuda.synchronize()
+            torch.mm(busy, busy)
+            sk.copy_(rk)
+            sv.copy_(rv)
+            sfb.sf_kv_write(eng.cache, 0, sk, sv, n, 128)
+            kg = torch.zeros(shape, dtype=torch.int16, device="cuda")
+            vg = torch.zeros_like(kg)
+            sfb.sf_kv_read(eng.cache, 0, kg, vg, n, 128)
+            torch.cuda.synchronize()
+            assert torch.equal(kg[:, :, :n], rk[:, :, :n]) and torch.equal(vg[:, :, :n], rv[:, :, :n])
     finally:
         eng.close()
 
